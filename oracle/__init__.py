@@ -1,0 +1,215 @@
+"""CPU oracle for the dense and grouped FP16/BF16 GEMM -- TEST INFRASTRUCTURE.
+
+Only tests/, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The product path (``bf16_gemm_amd``)
+never imports it, and this package never imports the product.
+
+The arithmetic lives in ``oracle.c`` (plain fp64 sums, its own 16-bit
+codecs, RNE output rounding); this module only marshals numpy arrays across
+ctypes and walks experts in order for the grouped form.  What is computed,
+and from which passage of the pages:
+
+* ``gemm_ref`` -- each output element is the exact-product, ascending-k,
+  double-precision sum that "B200 的 2CTA 怎样调优" (section 七, the
+  accumulate-then-epilogue sketch) describes: accumulate A[i,k]*B[k,j] along
+  all of K, then hand the finished sum to the epilogue.
+* ``encode`` -- the epilogue's type conversion, read as IEEE
+  round-to-nearest-even applied once to the double sum.
+* ``silu_gate`` -- up x SiLU(gate) (same page, section 七, "Gate／SwiGLU"),
+  with gate/up interleaved in blocks of eight output columns, gate first
+  ("MegaMoE：Blackwell 与 Hopper 的融合算子解读", Hopper section 10).
+* ``grouped_ref`` / ``moe_ref`` -- the per-expert form: expert e owns rows
+  [off[e], off[e+1]) of the routed activations and multiplies them by its
+  own weight matrix ("MegaMoE", Recap 1 on the MoE stages: FC1 -> activation
+  -> FC2 per expert).  The intermediate h is rounded to bf16 before FC2.
+
+Parity status: every function here is pinned by the CPU tests in
+``tests/test_oracle.py`` (exhaustive codec checks, exact rational brute force,
+closed forms); none is "parity unpinned".
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SO = os.path.join(_HERE, "liboracle.so")
+
+F16, BF16, F32, F64 = 1, 2, 3, 4
+ROW, COL = 0, 1
+_DT = {"f16": F16, "bf16": BF16, "f32": F32, "f64": F64}
+_LAYOUT = {"row": ROW, "col": COL}
+
+#: gate/up interleave granularity (output columns per block), gate first
+GATE_UP_INTERLEAVE = 8
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_SO) or os.path.getmtime(_SO) < os.path.getmtime(os.path.join(_HERE, "oracle.c")):
+        from . import build as _b
+        _b.build()
+    lib = ctypes.CDLL(_SO)
+    i64, i32, vp, dp = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p
+    lib.oracle_f16_to_double.argtypes = [ctypes.c_uint16]
+    lib.oracle_f16_to_double.restype = ctypes.c_double
+    lib.oracle_bf16_to_double.argtypes = [ctypes.c_uint16]
+    lib.oracle_bf16_to_double.restype = ctypes.c_double
+    lib.oracle_double_to_bf16.argtypes = [ctypes.c_double]
+    lib.oracle_double_to_bf16.restype = ctypes.c_uint16
+    lib.oracle_double_to_f16.argtypes = [ctypes.c_double]
+    lib.oracle_double_to_f16.restype = ctypes.c_uint16
+    lib.oracle_double_to_f32_bits.argtypes = [ctypes.c_double]
+    lib.oracle_double_to_f32_bits.restype = ctypes.c_uint32
+    lib.oracle_decode.argtypes = [i32, vp, i64, dp]
+    lib.oracle_encode.argtypes = [i32, dp, i64, vp]
+    lib.oracle_gemm_ref.argtypes = [i64, i64, i64, i32, i32, vp, i64, i32, i32, vp, i64, dp]
+    lib.oracle_gemm_ref.restype = i32
+    lib.oracle_gemm_ref_sampled.argtypes = [i64, i32, i32, vp, i64, i32, i32, vp, i64, vp, vp, i64, dp]
+    lib.oracle_silu.argtypes = [ctypes.c_double]
+    lib.oracle_silu.restype = ctypes.c_double
+    lib.oracle_silu_gate.argtypes = [i64, i64, i64, dp, dp]
+    lib.oracle_num_threads.restype = i32
+    _lib = lib
+    return lib
+
+
+def _p(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def num_threads() -> int:
+    """OpenMP threads the oracle's parallel loops use."""
+    return int(_load().oracle_num_threads())
+
+
+def decode(bits: np.ndarray, dtype: str) -> np.ndarray:
+    """Exact values (float64) of 16-bit ``dtype`` bit patterns."""
+    b = np.ascontiguousarray(bits, dtype=np.uint16)
+    out = np.empty(b.shape, dtype=np.float64)
+    _load().oracle_decode(_DT[dtype], _p(b), b.size, _p(out))
+    return out
+
+
+def encode(ref: np.ndarray, dtype: str) -> np.ndarray:
+    """Round doubles to ``dtype`` (RNE).  Returns uint16 bits for f16/bf16,
+    uint32 bits for f32."""
+    r = np.ascontiguousarray(ref, dtype=np.float64)
+    out = np.empty(r.shape, dtype=np.uint32 if dtype == "f32" else np.uint16)
+    _load().oracle_encode(_DT[dtype], _p(r), r.size, _p(out))
+    return out
+
+
+def to_dtype_value(ref: np.ndarray, dtype: str) -> np.ndarray:
+    """The value (float64) of ``ref`` after RNE rounding to ``dtype``."""
+    bits = encode(ref, dtype)
+    if dtype == "f32":
+        return bits.view(np.float32).astype(np.float64)
+    return decode(bits, dtype)
+
+
+def _check2d(x: np.ndarray, name: str):
+    if x.dtype != np.uint16 or x.ndim != 2:
+        raise TypeError(f"{name} must be a 2-D uint16 bit array, got {x.dtype} {x.shape}")
+
+
+def gemm_ref(A: np.ndarray, B: np.ndarray, a_type: str, b_type: str,
+             a_layout: str = "row", b_layout: str = "row") -> np.ndarray:
+    """Unrounded fp64 product of the logical M x K matrix A and K x N matrix B.
+
+    ``A``/``B`` are uint16 bit arrays in their storage layout: a row-major
+    operand is stored [rows][cols], a column-major one [cols][rows].
+    Returns an M x N float64 array (ascending-k double sums).
+    """
+    _check2d(A, "A")
+    _check2d(B, "B")
+    A = np.ascontiguousarray(A)
+    B = np.ascontiguousarray(B)
+    if a_layout == "row":
+        M, K = A.shape
+    else:
+        K, M = A.shape
+    if b_layout == "row":
+        K2, N = B.shape
+    else:
+        N, K2 = B.shape
+    if K2 != K:
+        raise ValueError(f"inner dimensions differ: {K} vs {K2}")
+    lda, ldb = A.shape[1], B.shape[1]
+    ref = np.empty((M, N), dtype=np.float64)
+    rc = _load().oracle_gemm_ref(M, N, K, _DT[a_type], _LAYOUT[a_layout], _p(A), lda,
+                                 _DT[b_type], _LAYOUT[b_layout], _p(B), ldb, _p(ref))
+    if rc != 0:
+        raise MemoryError("oracle_gemm_ref could not allocate its temporaries")
+    return ref
+
+
+def gemm_ref_sampled(A: np.ndarray, B: np.ndarray, rows, cols, a_type: str, b_type: str,
+                     a_layout: str = "row", b_layout: str = "row") -> np.ndarray:
+    """The fp64 sums of ``gemm_ref`` at the elements (rows[t], cols[t]) only."""
+    _check2d(A, "A")
+    _check2d(B, "B")
+    A = np.ascontiguousarray(A)
+    B = np.ascontiguousarray(B)
+    K = A.shape[1] if a_layout == "row" else A.shape[0]
+    r = np.ascontiguousarray(rows, dtype=np.int64)
+    c = np.ascontiguousarray(cols, dtype=np.int64)
+    out = np.empty(r.shape, dtype=np.float64)
+    _load().oracle_gemm_ref_sampled(K, _DT[a_type], _LAYOUT[a_layout], _p(A), A.shape[1],
+                                    _DT[b_type], _LAYOUT[b_layout], _p(B), B.shape[1],
+                                    _p(r), _p(c), r.size, _p(out))
+    return out
+
+
+def silu(x: float) -> float:
+    return float(_load().oracle_silu(float(x)))
+
+
+def silu_gate(G: np.ndarray, interleave: int = GATE_UP_INTERLEAVE) -> np.ndarray:
+    """h = SiLU(gate) * up (fp64, unrounded) from an rows x N fp64 GEMM output
+    whose columns interleave gate and up in blocks of ``interleave``."""
+    G = np.ascontiguousarray(G, dtype=np.float64)
+    rows, N = G.shape
+    if N % (2 * interleave):
+        raise ValueError("N must be a multiple of twice the interleave")
+    h = np.empty((rows, N // 2), dtype=np.float64)
+    _load().oracle_silu_gate(rows, N, interleave, _p(G), _p(h))
+    return h
+
+
+def grouped_ref(A: np.ndarray, W: np.ndarray, offsets, a_type: str = "bf16",
+                w_type: str = "bf16", w_layout: str = "row") -> np.ndarray:
+    """Per-expert product: rows [off[e], off[e+1]) of A times W[e].
+
+    ``A``: routed rows, [total_rows][K] uint16 (row-major).
+    ``W``: [G][K][N] (row layout) or [G][N][K] (col layout) uint16.
+    Returns [total_rows][N] float64; rows past off[G] are not produced.
+    """
+    off = [int(x) for x in offsets]
+    G = len(off) - 1
+    N = W.shape[2] if w_layout == "row" else W.shape[1]
+    out = np.zeros((off[G], N), dtype=np.float64)
+    for e in range(G):
+        lo, hi = off[e], off[e + 1]
+        if hi > lo:
+            out[lo:hi] = gemm_ref(A[lo:hi], W[e], a_type, w_type, "row", w_layout)
+    return out
+
+
+def moe_ref(A: np.ndarray, W1: np.ndarray, W2: np.ndarray, offsets):
+    """FC1 -> SiLU gate -> bf16 h -> FC2 for every expert.
+
+    Returns (h_ref, h_bits, y_ref): the unrounded gated activations, their
+    bf16 rounding (the FC2 input), and the unrounded FC2 sums on that input.
+    """
+    g = grouped_ref(A, W1, offsets)
+    h_ref = silu_gate(g)
+    h_bits = encode(h_ref, "bf16")
+    y_ref = grouped_ref(h_bits, W2, offsets)
+    return h_ref, h_bits, y_ref
