@@ -1,0 +1,177 @@
+"""Throughput of the MI355X GEMM library on one GPU.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one pass of the hot path over the workload's inputs, which are
+resident in HBM before timing starts: for a dense workload one gemm_run, for
+the MoE workload FC1 (SiLU-gated) plus FC2 over all experts.  W untimed
+steps, then K steps bracketed by device synchronisation; events recorded on
+the stream the kernels are launched on give the average step duration.
+
+Prints one JSON line: the metric (TFLOPS of algorithmic work, 2*M*N*K per
+GEMM, no padding), the roofline of the dominant kernel against MI355X's
+dense MFMA peak, and the CPU oracle timed on a bounded sample of the same
+workload (rank 0, N=1 only).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+# MI355X dense MFMA peak for 16-bit inputs: 256 CUs x 2.4 GHz x 4096 FLOP per
+# clock per CU = 2516.6 TFLOP/s (AMD's "2.5 PFLOP/s" dense bf16/fp16 figure).
+PEAK_TFLOPS = {"bf16": 256 * 2.4e9 * 4096 / 1e12, "f16": 256 * 2.4e9 * 4096 / 1e12}
+HBM_GBPS = 8000.0
+METRIC = "GEMM TFLOPS and % of MI355X bf16 dense peak at 4096^3/8192^3 (1 GPU)"
+DEFAULT_WORKLOAD = "gemm8192_bf16_bcol"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle sample time")
+    return ap.parse_args()
+
+
+def dev16(torch, bits, dt):
+    import numpy as np
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(
+        torch.bfloat16 if dt == "bf16" else torch.float16)
+
+
+def dense_case(torch, mg, datagen, name):
+    cfg = datagen.DENSE[name]
+    a, b = datagen.gemm_inputs(cfg, "random")
+    A, B = dev16(torch, a, cfg.in_dtype), dev16(torch, b, cfg.in_dtype)
+    out = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[cfg.out_dtype]
+    D = torch.empty((cfg.M, cfg.N), dtype=out, device="cuda")
+    plan = mg.gemm_plan(cfg.M, cfg.N, cfg.K, cfg.in_dtype, d_type=cfg.out_dtype, a_layout=cfg.a_layout,
+                        b_layout=cfg.b_layout)
+
+    def step():
+        mg.gemm_run(plan, A, B, D)
+
+    esz = 4 if cfg.out_dtype == "f32" else 2
+    info = dict(flops=cfg.flops, bytes=2 * (cfg.M * cfg.K + cfg.K * cfg.N) + esz * cfg.M * cfg.N,
+                plan=plan.describe(), dtype=cfg.in_dtype,
+                config={"workload": name, "M": cfg.M, "N": cfg.N, "K": cfg.K, "in": cfg.in_dtype,
+                        "out": cfg.out_dtype, "a_layout": cfg.a_layout, "b_layout": cfg.b_layout},
+                launches_per_step=1)
+    return step, info, (cfg, a, b)
+
+
+def moe_case(torch, mg, datagen):
+    cfg = datagen.MOE["moe64"]
+    r, A, W1, W2 = datagen.moe_inputs_device(cfg, "cuda")
+    rows = int(r.offsets[-1])
+    H, I, E = cfg.hidden, cfg.inter, cfg.num_experts
+    offs = torch.from_numpy(r.offsets).cuda()
+    h = torch.empty((rows, I), dtype=torch.bfloat16, device="cuda")
+    y = torch.empty((rows, H), dtype=torch.bfloat16, device="cuda")
+    p1 = mg.grouped_gemm_plan(E, rows, 2 * I, H, stride_b=H * 2 * I, epilogue=mg.EPI_SILU_GATE_I8)
+    p2 = mg.grouped_gemm_plan(E, rows, H, I, stride_b=I * H)
+
+    def step():
+        mg.grouped_gemm_run(p1, A, W1, h, offs)
+        mg.grouped_gemm_run(p2, h, W2, y, offs)
+
+    flops = 2.0 * rows * (2 * I) * H + 2.0 * rows * H * I
+    active = int((r.counts > 0).sum())
+    wbytes = active * (H * 2 * I + I * H) * 2
+    abytes = rows * H * 2 + rows * I * 2 * 2 + rows * H * 2
+    info = dict(flops=flops, bytes=wbytes + abytes, plan=p1.describe() + " | " + p2.describe(), dtype="bf16",
+                config={"workload": "moe64", "experts": E, "hidden": H, "inter": I, "tokens": cfg.num_tokens,
+                        "top_k": cfg.top_k, "routed_rows": rows, "active_experts": active},
+                launches_per_step=len(p1.describe().split("grid=")) - 1 + len(p2.describe().split("grid=")) - 1)
+    return step, info, None
+
+
+def cpu_baseline(case, target_s):
+    """The oracle, as it stands, on the first R rows of the same product."""
+    import numpy as np
+
+    import oracle
+    if case is None:
+        return None
+    cfg, a, b = case
+    a_rows = (lambda R: a[:R]) if cfg.a_layout == "row" else (lambda R: np.ascontiguousarray(a[:, :R]))
+    R = 2
+    t0 = time.perf_counter()
+    oracle.gemm_ref(a_rows(R), b, cfg.in_dtype, cfg.in_dtype, cfg.a_layout, cfg.b_layout)
+    t1 = time.perf_counter() - t0
+    R2 = int(min(cfg.M, max(R, R * target_s / max(t1, 1e-3))))
+    t0 = time.perf_counter()
+    oracle.gemm_ref(a_rows(R2), b, cfg.in_dtype, cfg.in_dtype, cfg.a_layout, cfg.b_layout)
+    t = time.perf_counter() - t0
+    flops = 2.0 * R2 * cfg.N * cfg.K
+    return {"value": flops / t / 1e12, "unit": "TFLOPS", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"first {R2} of {cfg.M} output rows (all {cfg.N} columns, full K={cfg.K}), "
+                      f"{t:.1f} s incl. operand decode"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: runs on one GPU only (asked for --gpus {args.gpus}); multi-GPU runs are not "
+              "supported by this benchmark", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import bf16_gemm_amd as mg
+    import datagen
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+
+    if args.workload == "moe64":
+        step, info, case = moe_case(torch, mg, datagen)
+    else:
+        step, info, case = dense_case(torch, mg, datagen, args.workload)
+    print(f"# plan: {info['plan']}", file=sys.stderr, flush=True)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()     # the stream every launch above goes to
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = ev0.elapsed_time(ev1) / args.steps
+    tflops = info["flops"] / (ms * 1e-3) / 1e12
+    print(f"# {args.steps} steps: {ms * 1e3:.1f} us/step (events), wall {wall * 1e3 / args.steps:.1f} us/step",
+          file=sys.stderr, flush=True)
+
+    peak = PEAK_TFLOPS[info["dtype"]]
+    roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": round(peak, 1), "unit": "TFLOP/s",
+            "frac": round(tflops / peak, 4), "traffic": None,
+            "kernel": info["plan"], "algorithmic_bytes_per_launch": info["bytes"],
+            "achieved_hbm_gbps_algorithmic": round(info["bytes"] / (ms * 1e-3) / 1e9, 1)}
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(case, args.cpu_seconds)
+    line = {"metric": METRIC, "value": round(tflops, 2), "unit": "TFLOPS", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": info["dtype"], "data": "synthetic",
+            "config": info["config"], "pct_of_peak": round(100 * tflops / peak, 2),
+            "roofline": roof, "cpu_baseline": cpu}
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,226 @@
+"""Python binding of the MI355X GEMM library (include/mgemm.h).
+
+Argument marshalling only: every computation runs in the HIP kernels of
+``libmgemm.so``.  torch supplies device memory and streams.  torch is
+imported before the library is loaded so that both share torch's HIP
+runtime.  If the library has not been built this module raises on import
+-- there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch  # noqa: F401  (must be loaded first: one HIP runtime per process)
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmgemm.so")
+
+F16, BF16, F32 = 1, 2, 3
+ROW_MAJOR, COL_MAJOR = 0, 1
+EPI_NONE, EPI_SILU_GATE_I8 = 0, 1
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_NO_MEMORY, ERR_HIP = range(6)
+
+PLAN_FORCE_TILE_256x256 = 0x1
+PLAN_FORCE_TILE_128x128 = 0x2
+PLAN_FORCE_TILE_32x256 = 0x4
+PLAN_FORCE_TILE_64x256 = 0x8
+PLAN_NO_XCD_REMAP = 0x100
+
+DTYPE = {"f16": F16, "bf16": BF16, "f32": F32}
+TORCH_DTYPE = {torch.float16: F16, torch.bfloat16: BF16, torch.float32: F32}
+LAYOUT = {"row": ROW_MAJOR, "col": COL_MAJOR}
+
+
+class Desc(ctypes.Structure):
+    _fields_ = [("M", ctypes.c_int64), ("N", ctypes.c_int64), ("K", ctypes.c_int64),
+                ("a_type", ctypes.c_int), ("b_type", ctypes.c_int), ("d_type", ctypes.c_int),
+                ("a_layout", ctypes.c_int), ("b_layout", ctypes.c_int),
+                ("lda", ctypes.c_int64), ("ldb", ctypes.c_int64), ("ldd", ctypes.c_int64)]
+
+
+class GroupedDesc(ctypes.Structure):
+    _fields_ = [("num_groups", ctypes.c_int32), ("max_total_rows", ctypes.c_int64),
+                ("N", ctypes.c_int64), ("K", ctypes.c_int64),
+                ("a_type", ctypes.c_int), ("b_type", ctypes.c_int), ("d_type", ctypes.c_int),
+                ("b_layout", ctypes.c_int),
+                ("lda", ctypes.c_int64), ("ldb", ctypes.c_int64), ("stride_b", ctypes.c_int64),
+                ("ldd", ctypes.c_int64), ("epilogue", ctypes.c_int)]
+
+
+class PlanInfo(ctypes.Structure):
+    _fields_ = [("block_m", ctypes.c_int32), ("block_n", ctypes.c_int32), ("block_k", ctypes.c_int32),
+                ("waves_m", ctypes.c_int32), ("waves_n", ctypes.c_int32), ("stages", ctypes.c_int32),
+                ("lds_bytes", ctypes.c_int32), ("tiles_m", ctypes.c_int64), ("tiles_n", ctypes.c_int64),
+                ("tiles", ctypes.c_int64), ("k_steps", ctypes.c_int64), ("coverage", ctypes.c_double),
+                ("grid", ctypes.c_int32), ("group_m", ctypes.c_int32), ("xcd_remap", ctypes.c_int32),
+                ("num_cus", ctypes.c_int32)]
+
+
+class Budget(ctypes.Structure):
+    _fields_ = [("tiles", ctypes.c_int64), ("coverage", ctypes.c_double),
+                ("lds_bytes", ctypes.c_int64), ("k_steps", ctypes.c_int64)]
+
+
+#: every symbol include/mgemm.h declares
+EXPORTS = ["gemm_plan", "grouped_gemm_plan", "gemm_plan_workspace_size", "gemm_run", "grouped_gemm_run",
+           "gemm_plan_describe", "gemm_plan_info", "gemm_plan_destroy", "gemm_status_string",
+           "gemm_last_error_message", "mgemm_tile_budget", "mgemm_group_working_set", "mgemm_round_tokens",
+           "mgemm_version"]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python bf16_gemm_amd/build.py` "
+                          "(or __graft_entry__.build()) first")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i64, u32, st = ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint32, ctypes.c_int
+    lib.gemm_plan.argtypes = [ctypes.POINTER(Desc), u32, ctypes.POINTER(vp)]
+    lib.gemm_plan.restype = st
+    lib.grouped_gemm_plan.argtypes = [ctypes.POINTER(GroupedDesc), u32, ctypes.POINTER(vp)]
+    lib.grouped_gemm_plan.restype = st
+    lib.gemm_plan_workspace_size.argtypes = [vp, ctypes.POINTER(ctypes.c_size_t)]
+    lib.gemm_plan_workspace_size.restype = st
+    lib.gemm_run.argtypes = [vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.gemm_run.restype = st
+    lib.grouped_gemm_run.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.grouped_gemm_run.restype = st
+    lib.gemm_plan_describe.argtypes = [vp, ctypes.c_char_p, ctypes.c_size_t]
+    lib.gemm_plan_describe.restype = st
+    lib.gemm_plan_info.argtypes = [vp, ctypes.POINTER(PlanInfo)]
+    lib.gemm_plan_info.restype = st
+    lib.gemm_plan_destroy.argtypes = [vp]
+    lib.gemm_plan_destroy.restype = None
+    lib.gemm_status_string.argtypes = [st]
+    lib.gemm_status_string.restype = ctypes.c_char_p
+    lib.gemm_last_error_message.argtypes = []
+    lib.gemm_last_error_message.restype = ctypes.c_char_p
+    lib.mgemm_tile_budget.argtypes = [i64, i64, i64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                      ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(Budget)]
+    lib.mgemm_tile_budget.restype = st
+    lib.mgemm_group_working_set.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                            i64, ctypes.c_int32]
+    lib.mgemm_group_working_set.restype = i64
+    lib.mgemm_round_tokens.argtypes = [i64, ctypes.c_int32]
+    lib.mgemm_round_tokens.restype = i64
+    lib.mgemm_version.restype = ctypes.c_char_p
+    return lib
+
+
+lib = _load()
+
+
+class MgemmError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = lib.gemm_last_error_message().decode(errors="replace")
+        super().__init__(f"{where}: {lib.gemm_status_string(status).decode()}: {msg}")
+
+
+def _check(status: int, where: str):
+    if status != OK:
+        raise MgemmError(status, where)
+
+
+def _ptr(x) -> int | None:
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+class Plan:
+    """An immutable plan (owns the C handle)."""
+
+    def __init__(self, handle: int, desc):
+        self.handle = handle
+        self.desc = desc
+
+    def __del__(self):
+        h, self.handle = getattr(self, "handle", None), None
+        if h and lib is not None:
+            lib.gemm_plan_destroy(h)
+
+    def describe(self) -> str:
+        buf = ctypes.create_string_buffer(512)
+        _check(lib.gemm_plan_describe(self.handle, buf, 512), "gemm_plan_describe")
+        return buf.value.decode()
+
+    def info(self) -> PlanInfo:
+        inf = PlanInfo()
+        _check(lib.gemm_plan_info(self.handle, ctypes.byref(inf)), "gemm_plan_info")
+        return inf
+
+    def workspace_size(self) -> int:
+        n = ctypes.c_size_t(0)
+        _check(lib.gemm_plan_workspace_size(self.handle, ctypes.byref(n)), "gemm_plan_workspace_size")
+        return n.value
+
+
+def gemm_plan(M, N, K, a_type="bf16", b_type=None, d_type="f32", a_layout="row", b_layout="row",
+              lda=None, ldb=None, ldd=None, flags: int = 0) -> Plan:
+    """Plan D[M,N] = A[M,K] x B[K,N].  Types "f16"/"bf16"/"f32", layouts
+    "row"/"col"; leading dimensions default to the packed ones."""
+    b_type = b_type or a_type
+    d = Desc(M, N, K, DTYPE[a_type], DTYPE[b_type], DTYPE[d_type], LAYOUT[a_layout], LAYOUT[b_layout],
+             lda if lda is not None else (K if a_layout == "row" else M),
+             ldb if ldb is not None else (N if b_layout == "row" else K),
+             ldd if ldd is not None else N)
+    h = ctypes.c_void_p()
+    _check(lib.gemm_plan(ctypes.byref(d), flags, ctypes.byref(h)), "gemm_plan")
+    return Plan(h.value, d)
+
+
+def grouped_gemm_plan(num_groups, max_total_rows, N, K, a_type="bf16", b_type=None, d_type="bf16",
+                      b_layout="row", lda=None, ldb=None, stride_b=None, ldd=None,
+                      epilogue: int = EPI_NONE, flags: int = 0) -> Plan:
+    b_type = b_type or a_type
+    ldb_v = ldb if ldb is not None else (N if b_layout == "row" else K)
+    d = GroupedDesc(num_groups, max_total_rows, N, K, DTYPE[a_type], DTYPE[b_type], DTYPE[d_type],
+                    LAYOUT[b_layout], lda if lda is not None else K, ldb_v,
+                    stride_b if stride_b is not None else K * N,
+                    ldd if ldd is not None else (N // 2 if epilogue == EPI_SILU_GATE_I8 else N), epilogue)
+    h = ctypes.c_void_p()
+    _check(lib.grouped_gemm_plan(ctypes.byref(d), flags, ctypes.byref(h)), "grouped_gemm_plan")
+    return Plan(h.value, d)
+
+
+def gemm_run(plan: Plan, A, B, D, workspace=None, workspace_bytes: int = 0, stream=None):
+    """Enqueue the planned product on ``stream`` (default: torch's current
+    stream).  A, B, D: device tensors (or raw device addresses)."""
+    _check(lib.gemm_run(plan.handle, _ptr(A), _ptr(B), _ptr(D), _ptr(workspace), workspace_bytes,
+                        _stream(stream)), "gemm_run")
+
+
+def grouped_gemm_run(plan: Plan, A, B, D, row_offsets, workspace=None, workspace_bytes: int = 0, stream=None):
+    """Enqueue the planned grouped product; ``row_offsets`` is a device int32
+    tensor of num_groups + 1 prefix sums."""
+    _check(lib.grouped_gemm_run(plan.handle, _ptr(A), _ptr(B), _ptr(D), _ptr(row_offsets), _ptr(workspace),
+                                workspace_bytes, _stream(stream)), "grouped_gemm_run")
+
+
+def tile_budget(M, N, K, BM, BN, BK, stages, elt_bytes) -> Budget:
+    b = Budget()
+    _check(lib.mgemm_tile_budget(M, N, K, BM, BN, BK, stages, elt_bytes, ctypes.byref(b)), "mgemm_tile_budget")
+    return b
+
+
+def group_working_set(group_m, group_n, BM, BN, K, elt_bytes) -> int:
+    return int(lib.mgemm_group_working_set(group_m, group_n, BM, BN, K, elt_bytes))
+
+
+def round_tokens(n, granule) -> int:
+    return int(lib.mgemm_round_tokens(n, granule))
+
+
+def version() -> str:
+    return lib.mgemm_version().decode()

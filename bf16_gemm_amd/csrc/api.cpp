@@ -1,0 +1,185 @@
+// api.cpp -- the run entry points of the C ABI and its error reporting.
+//
+// A run call validates its pointers and workspace, fills the kernel
+// argument block from the plan and enqueues the kernels on the caller's
+// stream.  It never synchronises and never allocates device memory.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "internal.hpp"
+
+namespace mgemm {
+
+static thread_local char g_err[512];
+
+void set_error(const char *fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+}
+
+int in_code(mgemm_dtype_t t);
+int out_code(mgemm_dtype_t t);
+int dtype_size(mgemm_dtype_t t);
+
+static bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+static mgemm_status_t hip_status(hipError_t e, const char *what)
+{
+    if (e == hipSuccess)
+        return MGEMM_OK;
+    set_error("%s: %s", what, hipGetErrorString(e));
+    return MGEMM_ERR_HIP;
+}
+
+}  // namespace mgemm
+
+using namespace mgemm;
+
+extern "C" mgemm_status_t gemm_run(mgemm_plan_t plan, const void *A, const void *B, void *D, void *workspace,
+                                   size_t workspace_bytes, mgemm_stream_t stream)
+{
+    (void)workspace;
+    (void)workspace_bytes;
+    if (!plan || plan->kind != PLAN_DENSE) {
+        set_error("gemm_run: null or non-dense plan");
+        return MGEMM_ERR_INVALID_ARG;
+    }
+    const mgemm_desc_t &d = plan->dense;
+    if (plan->noop)
+        return MGEMM_OK;
+    hipStream_t s = (hipStream_t)stream;
+    const int esz = dtype_size(d.d_type);
+    if (!D || (!plan->zero_fill && (!A || !B))) {
+        set_error("gemm_run: null operand pointer");
+        return MGEMM_ERR_INVALID_ARG;
+    }
+    if (!aligned16(A) || !aligned16(B) || !aligned16(D)) {
+        set_error("gemm_run: A, B and D must be 16-byte aligned");
+        return MGEMM_ERR_UNSUPPORTED;
+    }
+    if (plan->zero_fill)
+        return hip_status(launch_zero_fill(D, (int)d.M, (int)d.N, d.ldd * esz, esz, s), "gemm_run zero fill");
+
+    const bool ak = d.a_layout == MGEMM_ROW_MAJOR;
+    const bool bk = d.b_layout == MGEMM_COL_MAJOR;
+    const int in = in_code(d.a_type), out = out_code(d.d_type);
+    DenseArgs a;
+    a.A = A;
+    a.B = B;
+    a.D = D;
+    a.M = (int)d.M;
+    a.N = (int)(d.N & ~(int64_t)3);
+    a.K = (int)d.K;
+    a.lda = (int)d.lda;
+    a.ldb = (int)d.ldb;
+    a.ldd = (int)d.ldd;
+    a.tiles_m = (int)plan->tiles_m;
+    a.tiles_n = (int)plan->tiles_n;
+    a.tiles = (int)plan->tiles;
+    a.group_m = plan->group_m;
+    a.xcd_remap = plan->xcd_remap;
+    if (a.tiles > 0) {
+        DenseFn f = dense_fn(plan->tile, ak, bk, in, out);
+        if (!f) {
+            set_error("gemm_run: kernel missing for the planned variant");
+            return MGEMM_ERR_UNSUPPORTED;
+        }
+        if (mgemm_status_t st = hip_status(f(a, plan->grid, s), "gemm_run launch"))
+            return st;
+    }
+    if (a.N != d.N) {
+        DenseArgs e = a;
+        e.N = (int)d.N;
+        EdgeFn ef = edge_fn(in, out);
+        if (!ef) {
+            set_error("gemm_run: edge kernel missing");
+            return MGEMM_ERR_UNSUPPORTED;
+        }
+        return hip_status(ef(e, ak ? 1 : 0, bk ? 1 : 0, a.N, s), "gemm_run edge launch");
+    }
+    return MGEMM_OK;
+}
+
+extern "C" mgemm_status_t grouped_gemm_run(mgemm_plan_t plan, const void *A, const void *B, void *D,
+                                           const int32_t *d_row_offsets, void *workspace, size_t workspace_bytes,
+                                           mgemm_stream_t stream)
+{
+    (void)workspace;
+    (void)workspace_bytes;
+    if (!plan || plan->kind != PLAN_GROUPED) {
+        set_error("grouped_gemm_run: null or non-grouped plan");
+        return MGEMM_ERR_INVALID_ARG;
+    }
+    const mgemm_grouped_desc_t &d = plan->grouped;
+    if (plan->noop)
+        return MGEMM_OK;
+    if (!D || !d_row_offsets || (!plan->zero_fill && (!A || !B))) {
+        set_error("grouped_gemm_run: null pointer");
+        return MGEMM_ERR_INVALID_ARG;
+    }
+    if (!aligned16(A) || !aligned16(B) || !aligned16(D)) {
+        set_error("grouped_gemm_run: A, B and D must be 16-byte aligned");
+        return MGEMM_ERR_UNSUPPORTED;
+    }
+    hipStream_t s = (hipStream_t)stream;
+    const bool silu = d.epilogue == MGEMM_EPI_SILU_GATE_I8;
+    const int esz = dtype_size(d.d_type);
+    if (plan->zero_fill) {
+        // K == 0: every existing output row is the empty sum (and SiLU(0)*0 = 0)
+        return hip_status(launch_zero_fill(D, (int)d.max_total_rows, (int)(silu ? d.N / 2 : d.N), d.ldd * esz, esz, s),
+                          "grouped_gemm_run zero fill");
+    }
+    const bool bk = d.b_layout == MGEMM_COL_MAJOR;
+    const int in = in_code(d.a_type), out = out_code(d.d_type), epi = silu ? EPI_SILU_GATE : EPI_NONE;
+    for (const GroupedLaunch &L : plan->launches) {
+        const TileShape &ts = tile_shape(L.tile);
+        GroupedArgs a;
+        a.A = A;
+        a.B = B;
+        a.D = D;
+        a.offs = d_row_offsets;
+        a.G = d.num_groups;
+        a.N = (int)d.N;
+        a.K = (int)d.K;
+        a.lda = (int)d.lda;
+        a.ldb = (int)d.ldb;
+        a.ldd = (int)d.ldd;
+        a.stride_b = d.stride_b;
+        a.max_rows = (int)d.max_total_rows;
+        a.tiles_n = (int)((d.N + ts.bn - 1) / ts.bn);
+        a.bucket_lo = L.lo;
+        a.bucket_hi = L.hi;
+        a.xcd_remap = plan->xcd_remap;
+        GroupedFn f = grouped_fn(L.tile, bk, in, out, epi);
+        if (!f) {
+            set_error("grouped_gemm_run: kernel missing for the planned variant");
+            return MGEMM_ERR_UNSUPPORTED;
+        }
+        if (mgemm_status_t st = hip_status(f(a, L.grid, s), "grouped_gemm_run launch"))
+            return st;
+    }
+    return MGEMM_OK;
+}
+
+extern "C" const char *gemm_status_string(mgemm_status_t s)
+{
+    switch (s) {
+    case MGEMM_OK: return "MGEMM_OK";
+    case MGEMM_ERR_INVALID_ARG: return "MGEMM_ERR_INVALID_ARG";
+    case MGEMM_ERR_UNSUPPORTED: return "MGEMM_ERR_UNSUPPORTED";
+    case MGEMM_ERR_WORKSPACE: return "MGEMM_ERR_WORKSPACE";
+    case MGEMM_ERR_NO_MEMORY: return "MGEMM_ERR_NO_MEMORY";
+    case MGEMM_ERR_HIP: return "MGEMM_ERR_HIP";
+    default: return "MGEMM_ERR_UNKNOWN";
+    }
+}
+
+extern "C" const char *gemm_last_error_message(void) { return g_err; }
+
+extern "C" const char *mgemm_version(void) { return "mgemm 0.1 gfx950"; }

@@ -1,0 +1,486 @@
+// engine.hpp -- the gfx950 tile engine shared by the dense and grouped kernels.
+//
+// One workgroup computes one BM x BN output tile at a time:
+//
+//   * operands are staged through a two-slot LDS ring, 64 k per slot
+//     (block_k), each tile row 128 bytes wide;
+//   * global -> register loads are 16 bytes per lane through buffer
+//     resources, so out-of-range rows and k read as zero without branches;
+//   * a k-contiguous operand is written to LDS as loaded; an operand whose
+//     rows run along M/N (row-major B, column-major A) is transposed in
+//     registers in 8x8 blocks with v_perm_b32 so that both operands sit in
+//     LDS as [row][k];
+//   * inside a 128-byte LDS row the eight 16-byte chunks are XOR-permuted by
+//     a function of the row.  The idea is the 128B swizzle of "GEMM优化（三）
+//     大矩阵适配和极致优化" (section 2.1: a chunk's physical index is its
+//     logical index XORed with the row), here with the row's bits 0-2 and
+//     3-5 both folded in, because the transposing writer stores eight rows
+//     that are eight apart while the MFMA fragment reader reads eight
+//     consecutive rows: both groups land in eight distinct chunks;
+//   * the K loop is a software pipeline: while the MFMAs of step k run on
+//     one LDS slot, the registers holding step k+1 are written to the other
+//     slot and the global loads of step k+2 are issued -- the load/compute
+//     overlap that "从 CUDA 代码到 GPU 执行" (Warp Specialization section)
+//     and "使用 Warp Specialization 和 Cluster 扩展 GEMM" (step 7) obtain with
+//     separate roles, obtained here inside every wave;
+//   * the MFMA is v_mfma_f32_32x32x16_{bf16,f16}; the B-tile fragment is
+//     passed as the instruction's first operand and the A-tile fragment as
+//     the second, so each lane's accumulator registers hold four consecutive
+//     output columns of one output row and the epilogue writes 16-byte
+//     (fp32) or 8-byte (16-bit) vectors directly from registers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mgemm {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr int kBK = 64;                 // k per LDS slot
+constexpr int kRowBytes = kBK * 2;      // bytes of one tile row in LDS
+constexpr uint32_t kOOB = 0x80000000u;  // a buffer offset past every range
+constexpr uint32_t kMaxRecords = 0x7ffffff0u;
+
+enum InType { IN_BF16 = 0, IN_F16 = 1 };
+enum OutType { OUT_F32 = 0, OUT_BF16 = 1, OUT_F16 = 2 };
+enum EpiKind { EPI_NONE = 0, EPI_SILU_GATE = 1 };
+
+// Physical 16-byte chunk of logical chunk c in LDS row `row` is
+// c ^ swz(row).  Any 8 consecutive rows, and any 8 rows spaced 8 apart
+// starting on a multiple of 8, get 8 distinct values.
+__device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint64_t bytes)
+{
+    uint32_t n = bytes > kMaxRecords ? kMaxRecords : (uint32_t)bytes;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)n, 0x00020000);
+}
+
+__device__ __forceinline__ u32x4_t bload16(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+// Hide a value from loop-invariant code motion: the compiler must assume the
+// value changes here, so expressions built from it are recomputed where
+// they are used (a few adds) instead of being precomputed and held in
+// registers for the whole kernel.
+template <class V>
+__device__ __forceinline__ V opaque(V v)
+{
+    asm volatile("" : "+v"(v));
+    return v;
+}
+
+// LDS barrier: wait for this wave's LDS traffic, then meet the other waves.
+// Global loads in flight are deliberately not waited for.
+__device__ __forceinline__ void lds_barrier()
+{
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// ---------------------------------------------------------------------------
+// Loaders: one operand tile of R rows (M or N) x 64 k per K step.
+//
+// The buffer resource passed to load() already points at the current K
+// step (its base advances by one step per iteration and its record count
+// shrinks by the same amount), so every per-lane offset below is fixed for
+// the whole K loop and only a handful of registers hold addresses.
+// ---------------------------------------------------------------------------
+
+template <int R, int NT, bool KMAJOR>
+struct Loader;
+
+// k-contiguous storage: row r of the tile is 64 consecutive k, 8 chunks of
+// 16 B.  Thread t handles chunk (t & 7) of rows (t >> 3) + j * NT/8, so
+// eight consecutive lanes read one whole 128-byte row segment.
+template <int R, int NT>
+struct Loader<R, NT, true> {
+    static constexpr int RSTEP = NT / 8;        // rows between a thread's chunks
+    static constexpr int NC = R / RSTEP;        // chunks per thread
+    static_assert(R % RSTEP == 0 && NC >= 1, "tile rows must cover the workgroup");
+    static_assert(RSTEP % 64 == 0 || RSTEP == 32, "row step must keep the swizzle periodic");
+    u32x4_t v[NC];
+    uint32_t goff;      // byte offset of this lane's first chunk
+    uint32_t gstep;     // bytes between consecutive chunks of this lane (uniform)
+    int kc;             // k of this lane's chunk inside the step
+    int lds_even, lds_odd;  // LDS byte offsets of chunk 0 / chunk 1
+
+    __device__ __forceinline__ void init(int tid, int ld)
+    {
+        const int row = tid >> 3, c = tid & 7;
+        goff = (uint32_t)row * (uint32_t)ld * 2u + (uint32_t)c * 16u;
+        gstep = (uint32_t)RSTEP * (uint32_t)ld * 2u;
+        kc = c * 8;
+        lds_even = row * kRowBytes + ((c ^ swz(row)) << 4);
+        lds_odd = (row + RSTEP) * kRowBytes + ((c ^ swz(row + RSTEP)) << 4) - RSTEP * kRowBytes;
+    }
+    // k_left: k remaining from this step's first k (>= 64 means a full step)
+    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, int k_left)
+    {
+        const uint32_t base = opaque(kc < k_left ? goff : kOOB);
+#pragma unroll
+        for (int j = 0; j < NC; ++j)
+            v[j] = bload16(r, base + (uint32_t)j * gstep);
+    }
+    __device__ __forceinline__ void store(char *lds) const
+    {
+        // rows r and r + 2*RSTEP share a swizzle (RSTEP is 32 or a multiple
+        // of 64), so chunk j sits j * RSTEP rows below chunk (j & 1)
+#pragma unroll
+        for (int j = 0; j < NC; ++j)
+            *(u32x4_t *)(lds + ((j & 1) ? lds_odd : lds_even) + j * RSTEP * kRowBytes) = v[j];
+    }
+    // The same work split into NP parts (chunks j with j % NP == P), so the
+    // steady-state K loop can spread it between MFMA groups.  Part P's loads
+    // reuse the registers that part P's store has just written out.
+    template <int P, int NP>
+    __device__ __forceinline__ void store_part(char *lds) const
+    {
+#pragma unroll
+        for (int j = P; j < NC; j += NP)
+            *(u32x4_t *)(lds + ((j & 1) ? lds_odd : lds_even) + j * RSTEP * kRowBytes) = v[j];
+    }
+    template <int P, int NP>
+    __device__ __forceinline__ void load_part(__amdgpu_buffer_rsrc_t r, int k_left)
+    {
+        if constexpr (P < NC) {
+            const uint32_t base = opaque(kc < k_left ? goff : kOOB);
+#pragma unroll
+            for (int j = P; j < NC; j += NP)
+                v[j] = bload16(r, base + (uint32_t)j * gstep);
+        }
+    }
+};
+
+// Two 16-bit halves from two dwords: lo16(a) | lo16(b) << 16 (sel 0x05040100)
+// or hi16(a) | hi16(b) << 16 (sel 0x07060302).
+__device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x05040100u); }
+__device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x07060302u); }
+
+// Row-contiguous storage ([k][row], rows contiguous): each thread loads KB
+// consecutive k of 8 consecutive rows (KB x 16 B), transposes the KB x 8
+// block in registers and writes 8 LDS rows of KB k each.  Lanes of a wave
+// take consecutive 8-row groups, so every load instruction reads whole
+// contiguous segments of a k row.
+template <int R, int NT>
+struct Loader<R, NT, false> {
+    static constexpr int NGR = R / 8;                                             // 8-row groups
+    static constexpr int KB = (NGR * 8 >= NT) ? 8 : ((NGR * 16 >= NT) ? 4 : 2);   // k per block
+    static constexpr int NKG = kBK / KB;                                           // k groups
+    static_assert(R % 8 == 0 && NGR * NKG == NT, "transposing loader: one block per thread");
+    u32x4_t v[KB];
+    uint32_t goff;   // byte offset of this lane's first k row segment
+    uint32_t gstep;  // bytes between consecutive k rows (uniform)
+    int g, kg;       // 8-row group and k group of this lane
+
+    __device__ __forceinline__ void init(int tid, int ld)
+    {
+        g = tid % NGR;
+        kg = tid / NGR;
+        goff = (uint32_t)(kg * KB) * (uint32_t)ld * 2u + (uint32_t)g * 16u;
+        gstep = (uint32_t)ld * 2u;
+    }
+    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, int /*k_left*/)
+    {
+        // k past the end lies beyond the resource's records and reads as 0
+        const uint32_t base = opaque(goff);
+#pragma unroll
+        for (int i = 0; i < KB; ++i)
+            v[i] = bload16(r, base + (uint32_t)i * gstep);
+    }
+    // LDS rows g*8 + j for j in [J0, J1)
+    template <int J0, int J1>
+    __device__ __forceinline__ void store_rows(char *lds) const
+    {
+#pragma unroll
+        for (int j = J0; j < J1; ++j) {
+            const int row = g * 8 + j;
+            const int d = j >> 1;
+            // swz(8g + j) = (j ^ g) & 7
+            if constexpr (KB == 8) {
+                u32x4_t o;
+#pragma unroll
+                for (int p = 0; p < 4; ++p)
+                    o[p] = (j & 1) ? pack_hi(v[2 * p][d], v[2 * p + 1][d]) : pack_lo(v[2 * p][d], v[2 * p + 1][d]);
+                *(u32x4_t *)(lds + row * kRowBytes + ((kg ^ swz(row)) << 4)) = o;
+            } else if constexpr (KB == 4) {
+                u32x2_t o;
+#pragma unroll
+                for (int p = 0; p < 2; ++p)
+                    o[p] = (j & 1) ? pack_hi(v[2 * p][d], v[2 * p + 1][d]) : pack_lo(v[2 * p][d], v[2 * p + 1][d]);
+                const int chunk = kg >> 1, sub = (kg & 1) * 8;
+                *(u32x2_t *)(lds + row * kRowBytes + ((chunk ^ swz(row)) << 4) + sub) = o;
+            } else {
+                const uint32_t o = (j & 1) ? pack_hi(v[0][d], v[1][d]) : pack_lo(v[0][d], v[1][d]);
+                const int chunk = kg >> 2, sub = (kg & 3) * 4;
+                *(uint32_t *)(lds + row * kRowBytes + ((chunk ^ swz(row)) << 4) + sub) = o;
+            }
+        }
+    }
+    __device__ __forceinline__ void store(char *lds) const { store_rows<0, 8>(lds); }
+    // NP parts: part P writes rows [8P/NP, 8(P+1)/NP); every row needs all KB
+    // loaded registers, so the next step's loads go out with the last part.
+    template <int P, int NP>
+    __device__ __forceinline__ void store_part(char *lds) const
+    {
+        store_rows<8 * P / NP, 8 * (P + 1) / NP>(lds);
+    }
+    template <int P, int NP>
+    __device__ __forceinline__ void load_part(__amdgpu_buffer_rsrc_t r, int k_left)
+    {
+        if constexpr (P == NP - 1)
+            load(r, k_left);
+    }
+};
+
+// Operand source: the tile's origin in global memory, the bytes that exist
+// from there on, and how far one K step moves the origin.
+struct OperandSrc {
+    const char *base;
+    uint64_t bytes;
+    uint32_t step_bytes;  // 128 (k-contiguous) or 64 * ld * 2 (row-contiguous)
+    __device__ __forceinline__ __amdgpu_buffer_rsrc_t at_step(int kt) const
+    {
+        uint64_t adv = (uint64_t)kt * step_bytes;
+        return make_rsrc(base + adv, bytes > adv ? bytes - adv : 0);
+    }
+};
+
+// ---------------------------------------------------------------------------
+// The tile: accumulators, main loop, epilogue.
+// ---------------------------------------------------------------------------
+
+template <int IN>
+__device__ __forceinline__ f32x16_t mfma32(u32x4_t a, u32x4_t b, f32x16_t c)
+{
+    if constexpr (IN == IN_BF16)
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                       __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a),
+                                                      __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+}
+
+template <int BM_, int BN_, int WM_, int WN_, bool A_KMAJOR, bool B_KMAJOR, int IN>
+struct Tile {
+    static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
+    static constexpr int NT = 64 * WM * WN;
+    static constexpr int TM = BM / WM, TN = BN / WN;  // wave sub-tile
+    static constexpr int FM = TM / 32, FN = TN / 32;  // 32x32 MFMA blocks per wave
+    static constexpr int SLOT = (BM + BN) * kRowBytes;
+    static constexpr int LDS_BYTES = 2 * SLOT;
+    static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be a multiple of 32");
+
+    f32x16_t acc[FM][FN];
+
+    // Accumulate the tile over k in [0, K).  sa: rows of A (M side),
+    // sb: rows of B^T (N side).
+    // tid: threadIdx.x, passed in (through opaque()) by the caller so that
+    // per-lane address arithmetic is not hoisted out of the persistent tile
+    // loop and held in registers across it.
+    __device__ __forceinline__ void mainloop(char *lds, const OperandSrc &sa, int lda, const OperandSrc &sb, int ldb,
+                                             int K, int tid)
+    {
+        const int lane = tid & 63;
+        const int wave = tid >> 6;
+        const int wm0 = (wave / WN) * TM;
+        const int wn0 = (wave % WN) * TN;
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+                acc[i][j] = f32x16_t{};
+
+        const int ksteps = (K + kBK - 1) / kBK;
+        if (ksteps <= 0)
+            return;
+        Loader<BM, NT, A_KMAJOR> la;
+        Loader<BN, NT, B_KMAJOR> lb;
+        la.init(tid, lda);
+        lb.init(tid, ldb);
+
+        // Fragment read offsets.  Lane l reads row (l & 31) of a 32-row
+        // block at 16-byte chunk 2*ks + (l >> 5).  Rows 32 apart differ in
+        // swizzle by an XOR of 4 on the chunk, i.e. of 2 on ks, so block i
+        // reads with base[ks ^ 2*(i & 1)] + 32*i rows.
+        const int frow = lane & 31, fk = lane >> 5;
+        int abase[4], bbase[4];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            const int ra = wm0 + frow, rb = wn0 + frow;
+            abase[ks] = ra * kRowBytes + (((2 * ks + fk) ^ swz(ra)) << 4);
+            bbase[ks] = BM * kRowBytes + rb * kRowBytes + (((2 * ks + fk) ^ swz(rb)) << 4);
+        }
+
+        la.load(sa.at_step(0), K);
+        lb.load(sb.at_step(0), K);
+        la.store(lds);
+        lb.store(lds + BM * kRowBytes);
+        if (ksteps > 1) {
+            la.load(sa.at_step(1), K - kBK);
+            lb.load(sb.at_step(1), K - kBK);
+        }
+        lds_barrier();
+
+        // steady state: write step kt+1 into the other slot and fetch step
+        // kt+2; the last two steps are peeled so that this body has no
+        // branches and the scheduler can interleave its parts with MFMAs
+        int kt = 0;
+        for (; kt + 2 < ksteps; ++kt)
+            step<true, true>(lds, kt, la, lb, sa, sb, K, abase, bbase);
+        if (kt + 1 < ksteps) {
+            step<true, false>(lds, kt, la, lb, sa, sb, K, abase, bbase);
+            ++kt;
+        }
+        step<false, false>(lds, kt, la, lb, sa, sb, K, abase, bbase);
+    }
+
+    // One K step on slot kt & 1.  STORE: write the staged registers (step
+    // kt+1) into the other slot; LOAD: then fetch step kt+2 into them.
+    template <bool STORE, bool LOAD>
+    __device__ __forceinline__ void step(char *lds, int kt, Loader<BM, NT, A_KMAJOR> &la, Loader<BN, NT, B_KMAJOR> &lb,
+                                         const OperandSrc &sa, const OperandSrc &sb, int K, const int (&abase)[4],
+                                         const int (&bbase)[4])
+    {
+        char *cur = lds + (kt & 1) * SLOT;
+        char *nxt = lds + ((kt + 1) & 1) * SLOT;
+        __amdgpu_buffer_rsrc_t ra2, rb2;
+        if constexpr (LOAD) {
+            ra2 = sa.at_step(kt + 2);
+            rb2 = sb.at_step(kt + 2);
+        }
+        const int kleft2 = K - (kt + 2) * kBK;
+        sub_step<0, STORE, LOAD>(cur, nxt, la, lb, ra2, rb2, kleft2, abase, bbase);
+        sub_step<1, STORE, LOAD>(cur, nxt, la, lb, ra2, rb2, kleft2, abase, bbase);
+        sub_step<2, STORE, LOAD>(cur, nxt, la, lb, ra2, rb2, kleft2, abase, bbase);
+        sub_step<3, STORE, LOAD>(cur, nxt, la, lb, ra2, rb2, kleft2, abase, bbase);
+        lds_barrier();
+    }
+
+    template <int KS, bool STORE, bool LOAD>
+    __device__ __forceinline__ void sub_step(const char *cur, char *nxt, Loader<BM, NT, A_KMAJOR> &la,
+                                             Loader<BN, NT, B_KMAJOR> &lb, __amdgpu_buffer_rsrc_t ra2,
+                                             __amdgpu_buffer_rsrc_t rb2, int kleft2, const int (&abase)[4],
+                                             const int (&bbase)[4])
+    {
+        u32x4_t af[FM], bf[FN];
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+            af[i] = *(const u32x4_t *)(cur + abase[KS ^ ((i & 1) * 2)] + i * 32 * kRowBytes);
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+            bf[j] = *(const u32x4_t *)(cur + bbase[KS ^ ((j & 1) * 2)] + j * 32 * kRowBytes);
+        if constexpr (STORE) {
+            la.template store_part<KS, 4>(nxt);
+            lb.template store_part<KS, 4>(nxt + BM * kRowBytes);
+        }
+        if constexpr (LOAD) {
+            la.template load_part<KS, 4>(ra2, kleft2);
+            lb.template load_part<KS, 4>(rb2, kleft2);
+        }
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+                acc[i][j] = mfma32<IN>(bf[j], af[i], acc[i][j]);
+    }
+};
+
+// ---------------------------------------------------------------------------
+// Epilogue helpers
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ uint32_t pack2_bf16(float a, float b)
+{
+    return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)a) | ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)b) << 16);
+}
+__device__ __forceinline__ uint32_t pack2_f16(float a, float b)
+{
+    return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)a) | ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)b) << 16);
+}
+
+__device__ __forceinline__ float silu_mul(float g, float u)
+{
+    // SiLU(g) * u = g / (1 + e^-g) * u, with the hardware exp2 and reciprocal
+    float e = __builtin_amdgcn_exp2f(-g * 1.4426950408889634f);
+    return g * __builtin_amdgcn_rcpf(1.0f + e) * u;
+}
+
+// Four consecutive outputs -> one store of 16 B (fp32) or 8 B (16-bit) at
+// byte offset `off` of resource r; offsets past the resource are dropped.
+template <int OUT>
+__device__ __forceinline__ void bstore4(__amdgpu_buffer_rsrc_t r, uint32_t off, float v0, float v1, float v2,
+                                        float v3)
+{
+    if constexpr (OUT == OUT_F32) {
+        u32x4_t d = {__builtin_bit_cast(uint32_t, v0), __builtin_bit_cast(uint32_t, v1),
+                     __builtin_bit_cast(uint32_t, v2), __builtin_bit_cast(uint32_t, v3)};
+        __builtin_amdgcn_raw_buffer_store_b128(d, r, off, 0, 0);
+    } else if constexpr (OUT == OUT_BF16) {
+        __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{pack2_bf16(v0, v1), pack2_bf16(v2, v3)}, r, off, 0, 0);
+    } else {
+        __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{pack2_f16(v0, v1), pack2_f16(v2, v3)}, r, off, 0, 0);
+    }
+}
+
+constexpr int out_size(int out) { return out == OUT_F32 ? 4 : 2; }
+
+// Write the tile.  D points at the tile's (row 0, column 0) output element
+// (for SILU_GATE: the tile's first h column); m_valid / n_valid are the rows
+// and GEMM columns of this tile that exist.  n_valid is a multiple of 4
+// (ragged columns are written by a separate edge kernel), so each lane's
+// 4-column group is wholly in or out: rows past m_valid fall beyond the
+// resource and are dropped by the hardware, column groups past n_valid get
+// an out-of-range offset.  No branches, so accumulators are read out one
+// fragment at a time.
+template <class T, int EPI, int OUT>
+__device__ __forceinline__ void epilogue(const T &t, void *D, int64_t ldd, int m_valid, int n_valid, int tid)
+{
+    constexpr int esize = out_size(OUT);
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wm0 = (wave / T::WN) * T::TM;
+    const int wn0 = (wave % T::WN) * T::TN;
+    const int out_cols = EPI == EPI_SILU_GATE ? n_valid / 2 : n_valid;
+    const uint32_t row_bytes = (uint32_t)ldd * (uint32_t)esize;
+    if (m_valid <= 0 || n_valid <= 0)
+        return;
+    const __amdgpu_buffer_rsrc_t r =
+        make_rsrc(D, ((uint64_t)(m_valid - 1) * (uint64_t)ldd + (uint64_t)out_cols) * (uint64_t)esize);
+#pragma unroll
+    for (int i = 0; i < T::FM; ++i) {
+        const int m = wm0 + 32 * i + (lane & 31);
+        const uint32_t rowoff = (uint32_t)m * row_bytes;
+#pragma unroll
+        for (int j = 0; j < T::FN; ++j) {
+            const f32x16_t &a = t.acc[i][j];
+            if constexpr (EPI == EPI_NONE) {
+#pragma unroll
+                for (int rg = 0; rg < 4; ++rg) {
+                    const int n = wn0 + 32 * j + 8 * rg + 4 * (lane >> 5);
+                    const uint32_t off = n < n_valid ? rowoff + (uint32_t)n * esize : kOOB;
+                    bstore4<OUT>(r, off, a[4 * rg], a[4 * rg + 1], a[4 * rg + 2], a[4 * rg + 3]);
+                }
+            } else {
+                // columns 8*rg..8*rg+7 of a 32-wide block are gate for rg
+                // even; the next eight are the matching up
+#pragma unroll
+                for (int rg = 0; rg < 4; rg += 2) {
+                    const int n = wn0 + 32 * j + 8 * rg + 4 * (lane >> 5);
+                    const int hc = (n >> 4) * 8 + (n & 15);
+                    const uint32_t off = n < n_valid ? rowoff + (uint32_t)hc * esize : kOOB;
+                    bstore4<OUT>(r, off, silu_mul(a[4 * rg + 0], a[4 * rg + 4]), silu_mul(a[4 * rg + 1], a[4 * rg + 5]),
+                                 silu_mul(a[4 * rg + 2], a[4 * rg + 6]), silu_mul(a[4 * rg + 3], a[4 * rg + 7]));
+                }
+            }
+        }
+    }
+}
+
+}  // namespace mgemm

@@ -1,0 +1,83 @@
+// internal.hpp -- host-side declarations shared by the planner, the C ABI
+// and the per-tile kernel translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <string>
+#include <vector>
+
+#include "../../include/mgemm.h"
+#include "kernels.hpp"
+
+namespace mgemm {
+
+using DenseFn = hipError_t (*)(const DenseArgs &, int grid, hipStream_t);
+using GroupedFn = hipError_t (*)(const GroupedArgs &, int grid, hipStream_t);
+
+// Macro-tile variants compiled into the library.
+enum TileId { TILE_256x256 = 0, TILE_128x128 = 1, TILE_32x256 = 2, TILE_64x256 = 3, NUM_TILES = 4 };
+
+struct TileShape {
+    int bm, bn, wm, wn;
+    int lds_bytes;   // LDS of the two-slot ring
+    int occupancy;   // workgroups per CU the planner assumes
+    double eff;      // relative MFMA efficiency the planner assumes
+    bool narrow;     // narrow-M (few tokens) shape: needs a k-contiguous A
+};
+
+const TileShape &tile_shape(int tile);
+
+// Kernel tables, one per (tile, input type) translation unit.
+// nullptr = that combination is not compiled.
+DenseFn dense_fn(int tile, bool a_kmajor, bool b_kmajor, int in, int out);
+GroupedFn grouped_fn(int tile, bool b_kmajor, int in, int out, int epi);
+
+#define MGEMM_DECLARE_TU(NAME)                              \
+    DenseFn dense_fn_##NAME(bool ak, bool bk, int out);     \
+    GroupedFn grouped_fn_##NAME(bool bk, int out, int epi);
+MGEMM_DECLARE_TU(256x256_bf16)
+MGEMM_DECLARE_TU(256x256_f16)
+MGEMM_DECLARE_TU(128x128_bf16)
+MGEMM_DECLARE_TU(128x128_f16)
+MGEMM_DECLARE_TU(32x256_bf16)
+MGEMM_DECLARE_TU(32x256_f16)
+MGEMM_DECLARE_TU(64x256_bf16)
+MGEMM_DECLARE_TU(64x256_f16)
+#undef MGEMM_DECLARE_TU
+
+using EdgeFn = hipError_t (*)(const DenseArgs &, int a_kmajor, int b_kmajor, int n_first, hipStream_t);
+EdgeFn edge_fn(int in, int out);
+hipError_t launch_zero_fill(void *D, int rows, int cols, int64_t ld_bytes, int esize, hipStream_t s);
+
+// One kernel launch of a grouped plan: experts whose row count lies in
+// [lo, hi) run with tile `tile` on `grid` workgroups.
+struct GroupedLaunch {
+    int tile;
+    int lo, hi;
+    int grid;
+};
+
+enum PlanKind { PLAN_DENSE = 1, PLAN_GROUPED = 2 };
+
+}  // namespace mgemm
+
+struct mgemm_plan {
+    int kind;
+    mgemm_desc_t dense;
+    mgemm_grouped_desc_t grouped;
+    uint32_t flags;
+    int num_cus;
+    // dense
+    int tile;
+    int64_t tiles_m, tiles_n, tiles;
+    int grid;
+    int group_m;
+    int xcd_remap;
+    bool zero_fill;  // K == 0
+    bool noop;       // M == 0 or N == 0
+    // grouped
+    std::vector<mgemm::GroupedLaunch> launches;
+    std::string description;
+};

@@ -1,0 +1,7 @@
+// kern_128x128_bf16.hip -- bf16 kernels of the 128 x 128 macro-tile (2 x 2 wavefronts).
+#include "tile_tables.hpp"
+
+namespace mgemm {
+DenseFn dense_fn_128x128_bf16(bool ak, bool bk, int out) { return dense_table<128, 128, 2, 2, IN_BF16, true>(ak, bk, out); }
+GroupedFn grouped_fn_128x128_bf16(bool bk, int out, int epi) { return grouped_table<128, 128, 2, 2, IN_BF16>(bk, out, epi); }
+}  // namespace mgemm

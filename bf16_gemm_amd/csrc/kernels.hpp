@@ -1,0 +1,223 @@
+// kernels.hpp -- dense and grouped GEMM kernels built on the tile engine,
+// and the launch-side argument structs shared with the host code.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "engine.hpp"
+
+namespace mgemm {
+
+struct DenseArgs {
+    const void *A;
+    const void *B;
+    void *D;
+    int M, N, K;
+    int lda, ldb, ldd;
+    int tiles_m, tiles_n, tiles;
+    int group_m;      // tile rows per L2 group (m fastest inside a group)
+    int xcd_remap;    // 1: give each XCD a contiguous run of tiles
+};
+
+struct GroupedArgs {
+    const void *A;           // [rows][K] row-major
+    const void *B;           // expert weights, expert e at B + e * stride_b
+    void *D;
+    const int32_t *offs;     // [G + 1] device prefix sums
+    int G, N, K;
+    int lda, ldb, ldd;
+    int64_t stride_b;
+    int max_rows;            // rows of A / D that exist
+    int tiles_n;
+    int bucket_lo, bucket_hi;  // only experts with bucket_lo <= rows < bucket_hi
+    int xcd_remap;
+};
+
+// Workgroup id -> logical id.  Workgroups are handed to the eight XCDs
+// round-robin, so id w runs on XCD w % 8.  Mapping w to
+// (w % 8) * (grid / 8) + w / 8 gives every XCD a contiguous block of logical
+// ids, and therefore of neighbouring tiles that share operand rows and
+// columns in that XCD's L2.
+__device__ __forceinline__ int logical_block(int w, int grid, int remap)
+{
+    if (!remap || (grid & 7))
+        return w;
+    return (w & 7) * (grid >> 3) + (w >> 3);
+}
+
+// Tile id -> (mb, nb) in L2 groups: group_m tile rows at a time, m fastest
+// inside a group, so consecutive tiles share a column block of B and the
+// group's rows of A stay resident ("GEMM优化（三）", sections 3.2-3.4: the
+// super-tile order that bounds the re-read passes of the other operand).
+__device__ __forceinline__ void tile_coords(int t, int tiles_m, int tiles_n, int group_m, int &mb, int &nb)
+{
+    int per_group = group_m * tiles_n;
+    int g = t / per_group;
+    int first_m = g * group_m;
+    int gm = min(group_m, tiles_m - first_m);
+    int within = t - g * per_group;
+    mb = first_m + within % gm;
+    nb = within / gm;
+}
+
+// Where one tile's operand lives.  k-contiguous operand ([rows][K]): the
+// origin is the tile's first row; the bytes that exist end after the last
+// existing row; one K step moves 64 elements along the row.  Row-contiguous
+// operand ([K][rows]): the origin is the tile's first column; the bytes end
+// after element (K-1, last existing column), so every k >= K reads as zero;
+// one K step moves 64 rows of ld elements.
+template <bool KMAJOR>
+__device__ __forceinline__ OperandSrc operand_src(const uint16_t *tile_origin, int ld, int rows_left, int K)
+{
+    OperandSrc s;
+    s.base = (const char *)tile_origin;
+    if constexpr (KMAJOR) {
+        s.bytes = (uint64_t)rows_left * (uint64_t)ld * 2u;
+        s.step_bytes = kBK * 2;
+    } else {
+        s.bytes = K > 0 ? ((uint64_t)(K - 1) * (uint64_t)ld + (uint64_t)rows_left) * 2u : 0;
+        s.step_bytes = (uint32_t)kBK * (uint32_t)ld * 2u;
+    }
+    return s;
+}
+
+template <class T, bool A_KMAJOR, bool B_KMAJOR, int IN, int OUT>
+__global__ void __launch_bounds__(T::NT) dense_kernel(DenseArgs p)
+{
+    __shared__ __attribute__((aligned(16))) char lds[T::LDS_BYTES];
+    T tile;
+    const int grid = gridDim.x;
+    const int L = logical_block(blockIdx.x, grid, p.xcd_remap);
+    const uint16_t *A = (const uint16_t *)p.A;
+    const uint16_t *B = (const uint16_t *)p.B;
+    constexpr int esize = out_size(OUT);
+    for (int t = L; t < p.tiles; t += grid) {
+        int mb, nb;
+        tile_coords(t, p.tiles_m, p.tiles_n, p.group_m, mb, nb);
+        const int m0 = mb * T::BM, n0 = nb * T::BN;
+        const uint16_t *At = A_KMAJOR ? A + (int64_t)m0 * p.lda : A + m0;
+        const uint16_t *Bt = B_KMAJOR ? B + (int64_t)n0 * p.ldb : B + n0;
+        const OperandSrc sa = operand_src<A_KMAJOR>(At, p.lda, p.M - m0, p.K);
+        const OperandSrc sb = operand_src<B_KMAJOR>(Bt, p.ldb, p.N - n0, p.K);
+        tile.mainloop(lds, sa, p.lda, sb, p.ldb, p.K, opaque((int)threadIdx.x));
+        char *Dt = (char *)p.D + ((int64_t)m0 * p.ldd + n0) * esize;
+        epilogue<T, EPI_NONE, OUT>(tile, Dt, p.ldd, min(T::BM, p.M - m0), min(T::BN, p.N - n0),
+                                   opaque((int)threadIdx.x));
+    }
+}
+
+template <class T, bool B_KMAJOR, int IN, int OUT, int EPI>
+__global__ void __launch_bounds__(T::NT) grouped_kernel(GroupedArgs p)
+{
+    static_assert(T::NT >= 64, "");
+    __shared__ __attribute__((aligned(16))) char lds[T::LDS_BYTES];
+    __shared__ int task_start[257];  // exclusive prefix of tasks per expert
+    __shared__ int row_start[257];
+    const int tid = threadIdx.x;
+
+    // Task table from the device offsets: expert e contributes
+    // ceil(rows_e / BM) * tiles_n tasks when its rows fall in the bucket.
+    int cnt = 0;
+    if (tid < p.G) {
+        int lo = min(max(p.offs[tid], 0), p.max_rows);
+        int hi = min(max(p.offs[tid + 1], lo), p.max_rows);
+        int rows = hi - lo;
+        row_start[tid] = lo;
+        if (rows > 0 && rows >= p.bucket_lo && rows < p.bucket_hi)
+            cnt = (rows + T::BM - 1) / T::BM * p.tiles_n;
+        if (tid == p.G - 1)
+            row_start[p.G] = hi;
+    }
+    task_start[tid + 1] = cnt;
+    if (tid == 0)
+        task_start[0] = 0;
+    __syncthreads();
+    // inclusive scan of task_start[1..NT] (Hillis-Steele)
+    for (int s = 1; s < T::NT; s <<= 1) {
+        int v = (tid >= s) ? task_start[tid + 1 - s] : 0;
+        __syncthreads();
+        task_start[tid + 1] += v;
+        __syncthreads();
+    }
+    const int total = task_start[p.G];
+
+    T tile;
+    const int grid = gridDim.x;
+    const int L = logical_block(blockIdx.x, grid, p.xcd_remap);
+    const uint16_t *A = (const uint16_t *)p.A;
+    const uint16_t *B = (const uint16_t *)p.B;
+    constexpr int esize = out_size(OUT);
+    for (int t = L; t < total; t += grid) {
+        // expert: the last e with task_start[e] <= t
+        int lo = 0, hi = p.G;  // invariant: task_start[lo] <= t < task_start[hi]
+        while (hi - lo > 1) {
+            int mid = (lo + hi) >> 1;
+            if (task_start[mid] <= t)
+                lo = mid;
+            else
+                hi = mid;
+        }
+        const int e = lo;
+        const int local = t - task_start[e];
+        const int rows0 = row_start[e];
+        const int rows_e = row_start[e + 1] - rows0;
+        const int tm = (rows_e + T::BM - 1) / T::BM;
+        const int mb = local % tm, nb = local / tm;
+        const int m0 = rows0 + mb * T::BM, n0 = nb * T::BN;
+        const int m_valid = min(T::BM, rows_e - mb * T::BM);
+        const uint16_t *At = A + (int64_t)m0 * p.lda;
+        const uint16_t *Be = B + (int64_t)e * p.stride_b;
+        const uint16_t *Bt = B_KMAJOR ? Be + (int64_t)n0 * p.ldb : Be + n0;
+        const OperandSrc sa = operand_src<true>(At, p.lda, m_valid, p.K);
+        const OperandSrc sb = operand_src<B_KMAJOR>(Bt, p.ldb, p.N - n0, p.K);
+        tile.mainloop(lds, sa, p.lda, sb, p.ldb, p.K, opaque((int)threadIdx.x));
+        const int dcol0 = EPI == EPI_SILU_GATE ? n0 / 2 : n0;
+        char *Dt = (char *)p.D + ((int64_t)m0 * p.ldd + dcol0) * esize;
+        epilogue<T, EPI, OUT>(tile, Dt, p.ldd, m_valid, min(T::BN, p.N - n0), opaque((int)threadIdx.x));
+    }
+}
+
+// The last N % 4 output columns (at most three) when N is not a multiple of
+// four: one wave per (row, column) pair, fp32 partial sums over k reduced
+// across the wave.  Tiny next to the tiles, so kept plain.
+template <int IN>
+__device__ __forceinline__ float in_value(const uint16_t *p, int64_t i)
+{
+    if constexpr (IN == IN_BF16)
+        return (float)__builtin_bit_cast(__bf16, p[i]);
+    else
+        return (float)__builtin_bit_cast(_Float16, p[i]);
+}
+
+template <int IN, int OUT>
+__global__ void __launch_bounds__(256) edge_cols_kernel(DenseArgs p, int a_kmajor, int b_kmajor, int n_first)
+{
+    const int ncols = p.N - n_first;
+    const int lane = threadIdx.x & 63;
+    const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (item >= (int64_t)p.M * ncols)
+        return;
+    const int m = (int)(item / ncols), n = n_first + (int)(item % ncols);
+    const uint16_t *A = (const uint16_t *)p.A, *B = (const uint16_t *)p.B;
+    float s = 0.0f;
+    for (int k = lane; k < p.K; k += 64) {
+        const float a = in_value<IN>(A, a_kmajor ? (int64_t)m * p.lda + k : (int64_t)k * p.lda + m);
+        const float b = in_value<IN>(B, b_kmajor ? (int64_t)n * p.ldb + k : (int64_t)k * p.ldb + n);
+        s += a * b;
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1)
+        s += __shfl_xor(s, o, 64);
+    if (lane == 0) {
+        char *d = (char *)p.D + ((int64_t)m * p.ldd + n) * out_size(OUT);
+        if constexpr (OUT == OUT_F32)
+            *(float *)d = s;
+        else if constexpr (OUT == OUT_BF16)
+            *(__bf16 *)d = (__bf16)s;
+        else
+            *(_Float16 *)d = (_Float16)s;
+    }
+}
+
+}  // namespace mgemm

@@ -1,0 +1,473 @@
+// plan.cpp -- validation, variant choice and launch geometry (host only).
+//
+// A plan is made once per problem shape and reused: it fixes the macro-tile,
+// the number of workgroups, the L2 group size and, for the grouped form, the
+// token-count buckets and the tile each bucket runs with.  Nothing here
+// touches device memory.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+
+#include "internal.hpp"
+
+namespace mgemm {
+
+void set_error(const char *fmt, ...);
+
+// eff: relative MFMA efficiency the cost model assumes for the shape.
+static const TileShape kTiles[NUM_TILES] = {
+    /* 256x256 */ {256, 256, 2, 2, 2 * (256 + 256) * 128, 1, 1.00, false},
+    /* 128x128 */ {128, 128, 2, 2, 2 * (128 + 128) * 128, 2, 0.80, false},
+    /* 32x256  */ {32, 256, 1, 4, 2 * (32 + 256) * 128, 2, 0.55, true},
+    /* 64x256  */ {64, 256, 1, 4, 2 * (64 + 256) * 128, 1, 0.70, true},
+};
+
+const TileShape &tile_shape(int tile) { return kTiles[tile]; }
+
+static const char *tile_name(int tile)
+{
+    static const char *n[NUM_TILES] = {"256x256", "128x128", "32x256", "64x256"};
+    return n[tile];
+}
+
+DenseFn dense_fn(int tile, bool ak, bool bk, int in, int out)
+{
+    const bool bf = in == IN_BF16;
+    switch (tile) {
+    case TILE_256x256: return bf ? dense_fn_256x256_bf16(ak, bk, out) : dense_fn_256x256_f16(ak, bk, out);
+    case TILE_128x128: return bf ? dense_fn_128x128_bf16(ak, bk, out) : dense_fn_128x128_f16(ak, bk, out);
+    case TILE_32x256: return bf ? dense_fn_32x256_bf16(ak, bk, out) : dense_fn_32x256_f16(ak, bk, out);
+    case TILE_64x256: return bf ? dense_fn_64x256_bf16(ak, bk, out) : dense_fn_64x256_f16(ak, bk, out);
+    default: return nullptr;
+    }
+}
+
+GroupedFn grouped_fn(int tile, bool bk, int in, int out, int epi)
+{
+    const bool bf = in == IN_BF16;
+    switch (tile) {
+    case TILE_256x256: return bf ? grouped_fn_256x256_bf16(bk, out, epi) : grouped_fn_256x256_f16(bk, out, epi);
+    case TILE_128x128: return bf ? grouped_fn_128x128_bf16(bk, out, epi) : grouped_fn_128x128_f16(bk, out, epi);
+    case TILE_32x256: return bf ? grouped_fn_32x256_bf16(bk, out, epi) : grouped_fn_32x256_f16(bk, out, epi);
+    case TILE_64x256: return bf ? grouped_fn_64x256_bf16(bk, out, epi) : grouped_fn_64x256_f16(bk, out, epi);
+    default: return nullptr;
+    }
+}
+
+int in_code(mgemm_dtype_t t) { return t == MGEMM_BF16 ? IN_BF16 : IN_F16; }
+int out_code(mgemm_dtype_t t) { return t == MGEMM_F32 ? OUT_F32 : (t == MGEMM_BF16 ? OUT_BF16 : OUT_F16); }
+int dtype_size(mgemm_dtype_t t) { return t == MGEMM_F32 ? 4 : 2; }
+
+// Compute units of the current device; a 256-CU gfx950 when none is visible
+// (plans can then still be made and inspected on a host without a GPU).
+static int device_cus()
+{
+    int n = 0;
+    if (hipGetDeviceCount(&n) != hipSuccess || n <= 0) {
+        (void)hipGetLastError();
+        return 256;
+    }
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess)
+        return 256;
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+        return 256;
+    return cus;
+}
+
+static int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Cost model for one tile choice, in CU clocks: the busiest CU runs
+// ceil(tiles / CUs) tiles, each bound by its MFMA work at the shape's
+// efficiency or by the operand bytes it stages (about 64 B per clock per CU
+// from L2), whichever is larger.
+static double tile_cost(const TileShape &t, int64_t M, int64_t N, int64_t K, int cus)
+{
+    const int64_t tiles = cdiv(M, t.bm) * cdiv(N, t.bn);
+    const double per_cu = (double)cdiv(tiles, cus);
+    const double flops = 2.0 * t.bm * t.bn * (double)std::max<int64_t>(K, 64);
+    const double mfma_clk = flops / (4096.0 * t.eff);
+    const double load_clk = (double)(t.bm + t.bn) * 2.0 * (double)std::max<int64_t>(K, 64) / 64.0;
+    return per_cu * std::max(mfma_clk, load_clk);
+}
+
+static bool is_in_type(mgemm_dtype_t t) { return t == MGEMM_F16 || t == MGEMM_BF16; }
+static bool is_out_type(mgemm_dtype_t t) { return t == MGEMM_F16 || t == MGEMM_BF16 || t == MGEMM_F32; }
+static bool is_layout(mgemm_layout_t l) { return l == MGEMM_ROW_MAJOR || l == MGEMM_COL_MAJOR; }
+
+constexpr int64_t kMaxDim = (int64_t)1 << 30;
+constexpr int64_t kMaxLd = (int64_t)1 << 20;
+
+static mgemm_status_t check_types(mgemm_dtype_t a, mgemm_dtype_t b, mgemm_dtype_t d)
+{
+    if (!is_in_type(a) || !is_in_type(b) || !is_out_type(d)) {
+        set_error("invalid dtype codes (a=%d b=%d d=%d)", (int)a, (int)b, (int)d);
+        return MGEMM_ERR_INVALID_ARG;
+    }
+    if (a != b) {
+        set_error("a_type and b_type must match");
+        return MGEMM_ERR_UNSUPPORTED;
+    }
+    if (d != MGEMM_F32 && d != a) {
+        set_error("d_type must be F32 or the input type");
+        return MGEMM_ERR_UNSUPPORTED;
+    }
+    return MGEMM_OK;
+}
+
+static int forced_tile(uint32_t flags)
+{
+    if (flags & MGEMM_PLAN_FORCE_TILE_256x256) return TILE_256x256;
+    if (flags & MGEMM_PLAN_FORCE_TILE_128x128) return TILE_128x128;
+    if (flags & MGEMM_PLAN_FORCE_TILE_32x256) return TILE_32x256;
+    if (flags & MGEMM_PLAN_FORCE_TILE_64x256) return TILE_64x256;
+    return -1;
+}
+
+static mgemm_status_t plan_dense(const mgemm_desc_t *d, uint32_t flags, mgemm_plan *p)
+{
+    if (d->M < 0 || d->N < 0 || d->K < 0 || d->M >= kMaxDim || d->N >= kMaxDim || d->K >= kMaxDim) {
+        set_error("M, N, K must lie in [0, 2^30): got %lld %lld %lld", (long long)d->M, (long long)d->N,
+                  (long long)d->K);
+        return MGEMM_ERR_INVALID_ARG;
+    }
+    if (mgemm_status_t s = check_types(d->a_type, d->b_type, d->d_type))
+        return s;
+    if (!is_layout(d->a_layout) || !is_layout(d->b_layout)) {
+        set_error("invalid layout code");
+        return MGEMM_ERR_INVALID_ARG;
+    }
+    const int64_t need_lda = d->a_layout == MGEMM_ROW_MAJOR ? d->K : d->M;
+    const int64_t need_ldb = d->b_layout == MGEMM_ROW_MAJOR ? d->N : d->K;
+    if (d->lda < std::max<int64_t>(need_lda, 1) || d->ldb < std::max<int64_t>(need_ldb, 1) ||
+        d->ldd < std::max<int64_t>(d->N, 1)) {
+        set_error("leading dimension too small (lda=%lld need %lld, ldb=%lld need %lld, ldd=%lld need %lld)",
+                  (long long)d->lda, (long long)need_lda, (long long)d->ldb, (long long)need_ldb,
+                  (long long)d->ldd, (long long)d->N);
+        return MGEMM_ERR_INVALID_ARG;
+    }
+    if (d->K % 8) {
+        set_error("K must be a multiple of 8 (got %lld)", (long long)d->K);
+        return MGEMM_ERR_UNSUPPORTED;
+    }
+    const int esz = dtype_size(d->d_type);
+    if (d->lda % 8 || d->ldb % 8 || (d->ldd * esz) % 16) {
+        set_error("leading dimensions must give 16-byte aligned rows (lda, ldb multiples of 8; ldd*%d %% 16 == 0)",
+                  esz);
+        return MGEMM_ERR_UNSUPPORTED;
+    }
+    if (d->lda > kMaxLd || d->ldb > kMaxLd || d->ldd > kMaxLd) {
+        set_error("leading dimensions above 2^20 elements are not supported");
+        return MGEMM_ERR_UNSUPPORTED;
+    }
+    p->kind = PLAN_DENSE;
+    p->dense = *d;
+    p->flags = flags;
+    p->num_cus = device_cus();
+    p->noop = d->M == 0 || d->N == 0;
+    p->zero_fill = !p->noop && d->K == 0;
+    const bool ak = d->a_layout == MGEMM_ROW_MAJOR;
+    const bool bk = d->b_layout == MGEMM_COL_MAJOR;
+    const int in = in_code(d->a_type), out = out_code(d->d_type);
+
+    int tile = forced_tile(flags);
+    if (tile >= 0) {
+        if (!dense_fn(tile, ak, bk, in, out)) {
+            set_error("forced tile %s is not compiled for this layout/dtype", tile_name(tile));
+            return MGEMM_ERR_UNSUPPORTED;
+        }
+    } else {
+        double best = 0;
+        for (int t = 0; t < NUM_TILES; ++t) {
+            if (!dense_fn(t, ak, bk, in, out))
+                continue;
+            const double c = tile_cost(kTiles[t], d->M, d->N & ~(int64_t)3, d->K, p->num_cus);
+            if (tile < 0 || c < best * 0.999) {
+                best = c;
+                tile = t;
+            }
+        }
+    }
+    if (tile < 0) {
+        set_error("no kernel compiled for this layout/dtype combination");
+        return MGEMM_ERR_UNSUPPORTED;
+    }
+    const TileShape &ts = kTiles[tile];
+    const int64_t n_main = d->N & ~(int64_t)3;
+    p->tile = tile;
+    p->tiles_m = cdiv(d->M, ts.bm);
+    p->tiles_n = cdiv(n_main, ts.bn);
+    p->tiles = p->tiles_m * p->tiles_n;
+    const int64_t slots = (int64_t)p->num_cus * ts.occupancy;
+    p->grid = (int)std::max<int64_t>(1, std::min<int64_t>(p->tiles, slots));
+    p->group_m = (int)std::max<int64_t>(1, std::min<int64_t>(8, p->tiles_m));
+    p->xcd_remap = (flags & MGEMM_PLAN_NO_XCD_REMAP) ? 0 : (p->grid % 8 == 0 ? 1 : 0);
+    char buf[256];
+    snprintf(buf, sizeof buf,
+             "dense M=%lld N=%lld K=%lld %s%s->%s tile=%s waves=%dx%d bk=64 stages=2 tiles=%lld grid=%d "
+             "group_m=%d xcd_remap=%d edge_cols=%lld",
+             (long long)d->M, (long long)d->N, (long long)d->K, d->a_type == MGEMM_BF16 ? "bf16" : "f16",
+             ak ? (bk ? " NT" : " NN") : (bk ? " TT" : " TN"),
+             d->d_type == MGEMM_F32 ? "f32" : (d->d_type == MGEMM_BF16 ? "bf16" : "f16"), tile_name(tile), ts.wm,
+             ts.wn, (long long)p->tiles, p->grid, p->group_m, p->xcd_remap, (long long)(d->N - n_main));
+    p->description = buf;
+    return MGEMM_OK;
+}
+
+static mgemm_status_t plan_grouped(const mgemm_grouped_desc_t *d, uint32_t flags, mgemm_plan *p)
+{
+    if (d->num_groups < 1 || d->num_groups > 256) {
+        set_error("num_groups must lie in [1, 256] (got %d)", d->num_groups);
+        return d->num_groups < 1 ? MGEMM_ERR_INVALID_ARG : MGEMM_ERR_UNSUPPORTED;
+    }
+    if (d->max_total_rows < 0 || d->N < 0 || d->K < 0 || d->max_total_rows >= kMaxDim || d->N >= kMaxDim ||
+        d->K >= kMaxDim || d->stride_b < 0) {
+        set_error("sizes must lie in [0, 2^30)");
+        return MGEMM_ERR_INVALID_ARG;
+    }
+    if (mgemm_status_t s = check_types(d->a_type, d->b_type, d->d_type))
+        return s;
+    if (!is_layout(d->b_layout) || (d->epilogue != MGEMM_EPI_NONE && d->epilogue != MGEMM_EPI_SILU_GATE_I8)) {
+        set_error("invalid layout or epilogue code");
+        return MGEMM_ERR_INVALID_ARG;
+    }
+    const bool silu = d->epilogue == MGEMM_EPI_SILU_GATE_I8;
+    const int64_t out_cols = silu ? d->N / 2 : d->N;
+    const int64_t need_ldb = d->b_layout == MGEMM_ROW_MAJOR ? d->N : d->K;
+    if (d->lda < std::max<int64_t>(d->K, 1) || d->ldb < std::max<int64_t>(need_ldb, 1) ||
+        d->ldd < std::max<int64_t>(out_cols, 1)) {
+        set_error("leading dimension too small");
+        return MGEMM_ERR_INVALID_ARG;
+    }
+    const int64_t wsize = d->b_layout == MGEMM_ROW_MAJOR ? (d->K > 0 ? (d->K - 1) * d->ldb + d->N : 0)
+                                                          : (d->N > 0 ? (d->N - 1) * d->ldb + d->K : 0);
+    if (d->num_groups > 1 && d->stride_b < wsize) {
+        set_error("stride_b smaller than one expert's weight matrix");
+        return MGEMM_ERR_INVALID_ARG;
+    }
+    if (d->K % 8 || d->N % 4 || (silu && d->N % 16)) {
+        set_error("grouped form needs K %% 8 == 0 and N %% 4 == 0 (N %% 16 == 0 with the SiLU gate)");
+        return MGEMM_ERR_UNSUPPORTED;
+    }
+    const int esz = dtype_size(d->d_type);
+    if (d->lda % 8 || d->ldb % 8 || (d->ldd * esz) % 16 || d->stride_b % 8) {
+        set_error("leading dimensions / expert stride must give 16-byte aligned rows");
+        return MGEMM_ERR_UNSUPPORTED;
+    }
+    if (d->lda > kMaxLd || d->ldb > kMaxLd || d->ldd > kMaxLd) {
+        set_error("leading dimensions above 2^20 elements are not supported");
+        return MGEMM_ERR_UNSUPPORTED;
+    }
+    p->kind = PLAN_GROUPED;
+    p->grouped = *d;
+    p->flags = flags;
+    p->num_cus = device_cus();
+    p->noop = d->max_total_rows == 0 || d->N == 0;
+    p->zero_fill = !p->noop && d->K == 0;
+    const bool bk = d->b_layout == MGEMM_COL_MAJOR;
+    const int in = in_code(d->a_type), out = out_code(d->d_type), epi = silu ? EPI_SILU_GATE : EPI_NONE;
+
+    // Token-count buckets, each with the tile that wastes least on it:
+    // experts with few rows take a narrow-M tile so that the padding stays
+    // small (MegaMoE, Blackwell section 04 and Hopper section 03: put the
+    // few tokens on the narrow tile dimension and size it to the token
+    // count), large experts take the full macro-tile.
+    struct B { int tile, lo, hi; };
+    B buckets[4] = {{TILE_32x256, 1, 33}, {TILE_64x256, 33, 65}, {TILE_128x128, 65, 129}, {TILE_256x256, 129, 1 << 30}};
+    int nb = 4;
+    const int ft = forced_tile(flags);
+    if (ft >= 0) {
+        buckets[0] = {ft, 1, 1 << 30};
+        nb = 1;
+    }
+    p->launches.clear();
+    std::string desc;
+    char buf[256];
+    snprintf(buf, sizeof buf, "grouped G=%d rows<=%lld N=%lld K=%lld %s%s->%s epi=%s", d->num_groups,
+             (long long)d->max_total_rows, (long long)d->N, (long long)d->K, d->a_type == MGEMM_BF16 ? "bf16" : "f16",
+             bk ? " NT" : " NN", d->d_type == MGEMM_F32 ? "f32" : (d->d_type == MGEMM_BF16 ? "bf16" : "f16"),
+             silu ? "silu_gate_i8" : "none");
+    desc = buf;
+    for (int i = 0; i < nb; ++i) {
+        const TileShape &ts = kTiles[buckets[i].tile];
+        if (!grouped_fn(buckets[i].tile, bk, in, out, epi)) {
+            set_error("grouped kernel %s not compiled for this layout/dtype", tile_name(buckets[i].tile));
+            return MGEMM_ERR_UNSUPPORTED;
+        }
+        if (ts.bn % 32) {
+            set_error("internal: grouped tile width must be a multiple of 32");
+            return MGEMM_ERR_UNSUPPORTED;
+        }
+        // upper bound on this bucket's tasks
+        const int64_t lo = buckets[i].lo;
+        const int64_t experts = std::min<int64_t>(d->num_groups, std::max<int64_t>(1, d->max_total_rows / lo));
+        const int64_t hi_rows = std::min<int64_t>(buckets[i].hi - 1, d->max_total_rows);
+        const int64_t mblocks = std::min<int64_t>(experts * cdiv(hi_rows, ts.bm), cdiv(d->max_total_rows, ts.bm) + experts);
+        const int64_t tasks = mblocks * cdiv(d->N, ts.bn);
+        const int64_t slots = (int64_t)p->num_cus * ts.occupancy;
+        GroupedLaunch L;
+        L.tile = buckets[i].tile;
+        L.lo = buckets[i].lo;
+        L.hi = buckets[i].hi;
+        L.grid = (int)std::max<int64_t>(1, std::min<int64_t>(tasks, slots));
+        if (tasks <= 0 || lo > d->max_total_rows)
+            continue;
+        p->launches.push_back(L);
+        snprintf(buf, sizeof buf, " [%d,%s)->%s grid=%d", L.lo, L.hi >= (1 << 30) ? "inf" : std::to_string(L.hi).c_str(),
+                 tile_name(L.tile), L.grid);
+        desc += buf;
+    }
+    p->tile = p->launches.empty() ? TILE_256x256 : p->launches.back().tile;
+    p->tiles_m = p->tiles_n = p->tiles = 0;
+    p->grid = p->launches.empty() ? 0 : p->launches.back().grid;
+    p->group_m = 1;
+    p->xcd_remap = (flags & MGEMM_PLAN_NO_XCD_REMAP) ? 0 : 1;
+    p->description = desc;
+    return MGEMM_OK;
+}
+
+}  // namespace mgemm
+
+using namespace mgemm;
+
+extern "C" mgemm_status_t gemm_plan(const mgemm_desc_t *desc, uint32_t flags, mgemm_plan_t *out)
+{
+    if (!desc || !out) {
+        set_error("gemm_plan: null argument");
+        return MGEMM_ERR_INVALID_ARG;
+    }
+    *out = nullptr;
+    mgemm_plan *p = new (std::nothrow) mgemm_plan();
+    if (!p) {
+        set_error("gemm_plan: out of host memory");
+        return MGEMM_ERR_NO_MEMORY;
+    }
+    mgemm_status_t s;
+    try {
+        s = plan_dense(desc, flags, p);
+    } catch (...) {
+        s = MGEMM_ERR_NO_MEMORY;
+        set_error("gemm_plan: exception while planning");
+    }
+    if (s != MGEMM_OK) {
+        delete p;
+        return s;
+    }
+    *out = p;
+    return MGEMM_OK;
+}
+
+extern "C" mgemm_status_t grouped_gemm_plan(const mgemm_grouped_desc_t *desc, uint32_t flags, mgemm_plan_t *out)
+{
+    if (!desc || !out) {
+        set_error("grouped_gemm_plan: null argument");
+        return MGEMM_ERR_INVALID_ARG;
+    }
+    *out = nullptr;
+    mgemm_plan *p = new (std::nothrow) mgemm_plan();
+    if (!p) {
+        set_error("grouped_gemm_plan: out of host memory");
+        return MGEMM_ERR_NO_MEMORY;
+    }
+    mgemm_status_t s;
+    try {
+        s = plan_grouped(desc, flags, p);
+    } catch (...) {
+        s = MGEMM_ERR_NO_MEMORY;
+        set_error("grouped_gemm_plan: exception while planning");
+    }
+    if (s != MGEMM_OK) {
+        delete p;
+        return s;
+    }
+    *out = p;
+    return MGEMM_OK;
+}
+
+extern "C" mgemm_status_t gemm_plan_workspace_size(mgemm_plan_t plan, size_t *bytes)
+{
+    if (!plan || !bytes) {
+        set_error("gemm_plan_workspace_size: null argument");
+        return MGEMM_ERR_INVALID_ARG;
+    }
+    *bytes = 0;
+    return MGEMM_OK;
+}
+
+extern "C" mgemm_status_t gemm_plan_describe(mgemm_plan_t plan, char *buf, size_t len)
+{
+    if (!plan || !buf || len == 0) {
+        set_error("gemm_plan_describe: null argument");
+        return MGEMM_ERR_INVALID_ARG;
+    }
+    const std::string &d = plan->description;
+    size_t n = std::min(len - 1, d.size());
+    memcpy(buf, d.data(), n);
+    buf[n] = 0;
+    return MGEMM_OK;
+}
+
+extern "C" mgemm_status_t gemm_plan_info(mgemm_plan_t plan, mgemm_plan_info_t *info)
+{
+    if (!plan || !info) {
+        set_error("gemm_plan_info: null argument");
+        return MGEMM_ERR_INVALID_ARG;
+    }
+    const TileShape &ts = tile_shape(plan->tile);
+    memset(info, 0, sizeof *info);
+    info->block_m = ts.bm;
+    info->block_n = ts.bn;
+    info->block_k = kBK;
+    info->waves_m = ts.wm;
+    info->waves_n = ts.wn;
+    info->stages = 2;
+    info->lds_bytes = ts.lds_bytes;
+    info->tiles_m = plan->tiles_m;
+    info->tiles_n = plan->tiles_n;
+    info->tiles = plan->tiles;
+    const int64_t K = plan->kind == PLAN_DENSE ? plan->dense.K : plan->grouped.K;
+    info->k_steps = cdiv(K, kBK);
+    if (plan->kind == PLAN_DENSE && plan->tiles > 0)
+        info->coverage = (double)plan->dense.M * (double)(plan->dense.N & ~(int64_t)3) /
+                         ((double)plan->tiles * ts.bm * ts.bn);
+    info->grid = plan->grid;
+    info->group_m = plan->group_m;
+    info->xcd_remap = plan->xcd_remap;
+    info->num_cus = plan->num_cus;
+    return MGEMM_OK;
+}
+
+extern "C" void gemm_plan_destroy(mgemm_plan_t plan) { delete plan; }
+
+extern "C" mgemm_status_t mgemm_tile_budget(int64_t M, int64_t N, int64_t K, int32_t BM, int32_t BN, int32_t BK,
+                                            int32_t stages, int32_t elt_bytes, mgemm_budget_t *out)
+{
+    if (!out || M < 0 || N < 0 || K < 0 || BM <= 0 || BN <= 0 || BK <= 0 || stages <= 0 || elt_bytes <= 0) {
+        set_error("mgemm_tile_budget: invalid argument");
+        return MGEMM_ERR_INVALID_ARG;
+    }
+    out->tiles = cdiv(M, BM) * cdiv(N, BN);
+    out->coverage = out->tiles > 0 ? (double)M * (double)N / ((double)out->tiles * BM * BN) : 0.0;
+    out->lds_bytes = (int64_t)stages * ((int64_t)BM * BK + (int64_t)BK * BN) * elt_bytes;
+    out->k_steps = cdiv(K, BK);
+    return MGEMM_OK;
+}
+
+extern "C" int64_t mgemm_group_working_set(int32_t group_m, int32_t group_n, int32_t BM, int32_t BN, int64_t K,
+                                           int32_t elt_bytes)
+{
+    return ((int64_t)group_m * BM + (int64_t)group_n * BN) * K * elt_bytes;
+}
+
+extern "C" int64_t mgemm_round_tokens(int64_t n, int32_t granule)
+{
+    if (granule <= 0 || (granule & (granule - 1)))
+        return -1;
+    return (n + granule - 1) & ~(int64_t)(granule - 1);
+}

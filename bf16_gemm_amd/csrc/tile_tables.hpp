@@ -1,0 +1,61 @@
+// tile_tables.hpp -- instantiate every kernel of one macro-tile shape and
+// return launchers by (layout, dtype, epilogue).  Included once by each
+// per-tile translation unit so the shapes compile in parallel.
+#pragma once
+
+#include "internal.hpp"
+
+namespace mgemm {
+
+template <int BM, int BN, int WM, int WN, bool AK, bool BK, int IN, int OUT>
+hipError_t launch_dense(const DenseArgs &a, int grid, hipStream_t s)
+{
+    using T = Tile<BM, BN, WM, WN, AK, BK, IN>;
+    hipLaunchKernelGGL((dense_kernel<T, AK, BK, IN, OUT>), dim3(grid), dim3(T::NT), 0, s, a);
+    return hipGetLastError();
+}
+
+template <int BM, int BN, int WM, int WN, bool BK, int IN, int OUT, int EPI>
+hipError_t launch_grouped(const GroupedArgs &a, int grid, hipStream_t s)
+{
+    using T = Tile<BM, BN, WM, WN, true, BK, IN>;
+    hipLaunchKernelGGL((grouped_kernel<T, BK, IN, OUT, EPI>), dim3(grid), dim3(T::NT), 0, s, a);
+    return hipGetLastError();
+}
+
+// Output types compiled: fp32, and the 16-bit type of the inputs.
+template <int IN>
+constexpr int same16() { return IN == IN_BF16 ? OUT_BF16 : OUT_F16; }
+
+// ALL_A: also compile the row-contiguous (column-major) A loader.
+template <int BM, int BN, int WM, int WN, int IN, bool ALL_A>
+DenseFn dense_table(bool ak, bool bk, int out)
+{
+    if (out != OUT_F32 && out != same16<IN>())
+        return nullptr;
+    const bool f32 = out == OUT_F32;
+#define MG_D(AKV, BKV) (f32 ? launch_dense<BM, BN, WM, WN, AKV, BKV, IN, OUT_F32> \
+                            : launch_dense<BM, BN, WM, WN, AKV, BKV, IN, same16<IN>()>)
+    if (ak)
+        return bk ? MG_D(true, true) : MG_D(true, false);
+    if constexpr (ALL_A)
+        return bk ? MG_D(false, true) : MG_D(false, false);
+    return nullptr;
+#undef MG_D
+}
+
+template <int BM, int BN, int WM, int WN, int IN>
+GroupedFn grouped_table(bool bk, int out, int epi)
+{
+    if (out != OUT_F32 && out != same16<IN>())
+        return nullptr;
+    const bool f32 = out == OUT_F32;
+#define MG_G(BKV, OUTV) (epi == EPI_NONE ? launch_grouped<BM, BN, WM, WN, BKV, IN, OUTV, EPI_NONE> \
+                                         : launch_grouped<BM, BN, WM, WN, BKV, IN, OUTV, EPI_SILU_GATE>)
+    if (bk)
+        return f32 ? MG_G(true, OUT_F32) : MG_G(true, same16<IN>());
+    return f32 ? MG_G(false, OUT_F32) : MG_G(false, same16<IN>());
+#undef MG_G
+}
+
+}  // namespace mgemm

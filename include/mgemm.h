@@ -1,0 +1,201 @@
+/*
+ * mgemm.h -- C ABI of the MI355X (gfx950) dense and grouped FP16/BF16 GEMM.
+ *
+ * The operation.  D[M,N] = A[M,K] x B[K,N]: every output element is the sum
+ * over k of A[i,k]*B[k,j], accumulated in fp32, and only the finished sum is
+ * converted to the output type by the epilogue ("B200 的 2CTA 怎样调优：从矩阵
+ * 分块到流水线", section 七, the accumulate-then-epilogue sketch).  The
+ * conversion is IEEE round-to-nearest-even.  The grouped form applies one
+ * such product per expert to that expert's slice of rows, as an MoE expert
+ * layer does ("MegaMoE：Blackwell 与 Hopper 的融合算子解读", Recap 1 on the MoE
+ * stages), and can fuse the SwiGLU gate, h = up x SiLU(gate), into the
+ * epilogue (first page, section 七, "Gate／SwiGLU"; gate and up columns
+ * interleaved in blocks of eight, gate first, MegaMoE Hopper section 10).
+ *
+ * Launch semantics follow the execution-model page ("从 CUDA 代码到 GPU 执行",
+ * the launch-configuration and Stream sections): a run call only enqueues
+ * kernels on the caller's stream and returns; results are valid once that
+ * stream has been synchronised, and work on one stream runs in order.
+ *
+ * Memory ownership.  The caller owns every device buffer (operands, output,
+ * row offsets, workspace).  The library never allocates or frees device
+ * memory inside a run call.  A plan holds only host memory, is immutable once
+ * made, and may be used from several threads and streams at once.
+ *
+ * Errors.  Every call returns an mgemm_status_t; no C++ exception crosses
+ * this boundary.  Argument errors are detected before anything is enqueued
+ * and leave the output untouched.  gemm_last_error_message() gives a
+ * thread-local description of the last failure.
+ *
+ * Pointers passed to run calls are device pointers on the current HIP
+ * device; the stream is a hipStream_t (NULL = that device's null stream).
+ */
+#ifndef MGEMM_H
+#define MGEMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Same type as HIP's hipStream_t, declared here so that this header does not
+ * require the HIP headers. */
+struct ihipStream_t;
+typedef struct ihipStream_t *mgemm_stream_t;
+
+typedef enum { MGEMM_F16 = 1, MGEMM_BF16 = 2, MGEMM_F32 = 3 } mgemm_dtype_t;
+
+/* Storage of a logical rows x cols operand.  ROW_MAJOR: element (r,c) at
+ * r*ld + c.  COL_MAJOR: element (r,c) at c*ld + r.  D is always row-major. */
+typedef enum { MGEMM_ROW_MAJOR = 0, MGEMM_COL_MAJOR = 1 } mgemm_layout_t;
+
+/* Epilogue of the grouped form.  SILU_GATE_I8: the GEMM's N output columns
+ * alternate gate and up in blocks of 8 (gate[0:8], up[0:8], gate[8:16], ...);
+ * the run writes N/2 columns h[r,c] = SiLU(gate) * up, with SiLU(x) =
+ * x / (1 + exp(-x)), computed from the fp32 accumulators and rounded once to
+ * the output type. */
+typedef enum { MGEMM_EPI_NONE = 0, MGEMM_EPI_SILU_GATE_I8 = 1 } mgemm_epilogue_t;
+
+typedef enum {
+    MGEMM_OK = 0,
+    MGEMM_ERR_INVALID_ARG = 1,  /* null/negative/inconsistent arguments        */
+    MGEMM_ERR_UNSUPPORTED = 2,  /* valid but not supported (dtype, alignment)  */
+    MGEMM_ERR_WORKSPACE = 3,    /* workspace missing or smaller than required  */
+    MGEMM_ERR_NO_MEMORY = 4,    /* host allocation of a plan failed            */
+    MGEMM_ERR_HIP = 5           /* a HIP call or kernel launch failed          */
+} mgemm_status_t;
+
+typedef struct mgemm_plan *mgemm_plan_t;
+
+/* Dense problem.  Sizes and leading dimensions are in elements.
+ *  - M, N, K >= 0.  M == 0 or N == 0: the run is a no-op.  K == 0: D is
+ *    filled with zeros (the empty sum).
+ *  - a_type == b_type, one of F16 / BF16.  d_type: F32, BF16 or F16.
+ *  - K % 8 == 0; A, B, D base addresses 16-byte aligned; lda, ldb a
+ *    multiple of 8 elements; ldd * sizeof(d_type) a multiple of 16 bytes.
+ *    Otherwise MGEMM_ERR_UNSUPPORTED.
+ *  - lda >= K (row-major A) or >= M (col-major A); ldb >= N (row-major B) or
+ *    >= K (col-major B); ldd >= N.  Otherwise MGEMM_ERR_INVALID_ARG.
+ *  - D must not overlap A or B. */
+typedef struct {
+    int64_t M, N, K;
+    mgemm_dtype_t a_type, b_type, d_type;
+    mgemm_layout_t a_layout, b_layout;
+    int64_t lda, ldb, ldd;
+} mgemm_desc_t;
+
+/* Grouped problem: num_groups experts; expert e owns rows
+ * [off[e], off[e+1]) of A and of D, where off is the device array given to
+ * grouped_gemm_run (num_groups + 1 non-decreasing int32 prefix sums, off[0]
+ * == 0, off[num_groups] <= max_total_rows).  Expert e's weight is the K x N
+ * matrix at B + e * stride_b (elements), stored row-major ([K][N], ldb >= N)
+ * or column-major ([N][K], ldb >= K).  A is row-major [rows][K] (lda >= K).
+ * D is row-major with ldd >= N (EPI_NONE) or >= N/2 (SILU_GATE_I8).
+ * Same dtype and alignment rules as the dense form; SILU_GATE_I8 needs
+ * N % 16 == 0.  Rows of D past off[num_groups] are not written. */
+typedef struct {
+    int32_t num_groups;
+    int64_t max_total_rows;
+    int64_t N, K;
+    mgemm_dtype_t a_type, b_type, d_type;
+    mgemm_layout_t b_layout;
+    int64_t lda, ldb, stride_b, ldd;
+    mgemm_epilogue_t epilogue;
+} mgemm_grouped_desc_t;
+
+/* Plan flags (bitwise or).  0 = let the planner choose. */
+#define MGEMM_PLAN_FORCE_TILE_256x256 0x1u   /* the 256x256 macro-tile  */
+#define MGEMM_PLAN_FORCE_TILE_128x128 0x2u   /* the 128x128 macro-tile  */
+#define MGEMM_PLAN_FORCE_TILE_32x256  0x4u   /* narrow-M (few tokens)   */
+#define MGEMM_PLAN_FORCE_TILE_64x256  0x8u   /* narrow-M (few tokens)   */
+#define MGEMM_PLAN_NO_XCD_REMAP       0x100u /* plain tile order        */
+
+/* Make a plan for a dense problem on the current HIP device (or, when no
+ * device is visible, for a 256-CU gfx950).  *out receives the plan; free it
+ * with gemm_plan_destroy. */
+mgemm_status_t gemm_plan(const mgemm_desc_t *desc, uint32_t flags, mgemm_plan_t *out);
+
+/* Make a plan for a grouped problem (same conventions). */
+mgemm_status_t grouped_gemm_plan(const mgemm_grouped_desc_t *desc, uint32_t flags, mgemm_plan_t *out);
+
+/* Device workspace in bytes that run calls with this plan need (may be 0). */
+mgemm_status_t gemm_plan_workspace_size(mgemm_plan_t plan, size_t *bytes);
+
+/* Enqueue D = A x B on `stream`.  A, B, D are device pointers in the layouts
+ * of the plan's descriptor.  workspace may be NULL when the plan needs none. */
+mgemm_status_t gemm_run(mgemm_plan_t plan, const void *A, const void *B, void *D,
+                        void *workspace, size_t workspace_bytes, mgemm_stream_t stream);
+
+/* Enqueue the grouped product on `stream`.  d_row_offsets is a device array
+ * of num_groups + 1 int32 prefix sums; it is read by the kernels only (no
+ * host synchronisation).  Offsets that break the descriptor's rules give
+ * undefined results but never out-of-bounds accesses beyond max_total_rows. */
+mgemm_status_t grouped_gemm_run(mgemm_plan_t plan, const void *A, const void *B, void *D,
+                                const int32_t *d_row_offsets,
+                                void *workspace, size_t workspace_bytes, mgemm_stream_t stream);
+
+/* Human-readable description of the chosen variant (tile, waves, grid,
+ * order); writes at most len bytes including the terminating NUL. */
+mgemm_status_t gemm_plan_describe(mgemm_plan_t plan, char *buf, size_t len);
+
+/* Numeric plan details, for logs and tests. */
+typedef struct {
+    int32_t block_m, block_n, block_k;   /* macro-tile                        */
+    int32_t waves_m, waves_n;            /* wavefront grid inside a tile      */
+    int32_t stages;                      /* LDS ring depth                    */
+    int32_t lds_bytes;                   /* LDS per workgroup                 */
+    int64_t tiles_m, tiles_n, tiles;     /* output tiles (dense form)         */
+    int64_t k_steps;                     /* ceil(K / block_k)                 */
+    double coverage;                     /* M*N / (tiles * block_m * block_n) */
+    int32_t grid;                        /* workgroups launched               */
+    int32_t group_m;                     /* tile rows per L2 group            */
+    int32_t xcd_remap;                   /* 1 if the XCD-aware order is used  */
+    int32_t num_cus;                     /* compute units planned for         */
+} mgemm_plan_info_t;
+
+mgemm_status_t gemm_plan_info(mgemm_plan_t plan, mgemm_plan_info_t *info);
+
+void gemm_plan_destroy(mgemm_plan_t plan);
+
+const char *gemm_status_string(mgemm_status_t status);
+
+/* Thread-local text of the last error raised on this thread ("" if none). */
+const char *gemm_last_error_message(void);
+
+/* Tile budget arithmetic of the planner (host only, no device needed):
+ * tiles = ceil(M/BM) * ceil(N/BN); coverage = M*N / (tiles*BM*BN);
+ * lds_bytes = stages * (BM*BK + BK*BN) * elt_bytes; k_steps = ceil(K/BK).
+ * The tile-and-stage budget rule is the one "B200 的 2CTA 怎样调优" (section
+ * 三, the CPU tile calculator) prints, without its split of the tile over a
+ * CTA pair: on a CU the whole macro-tile lives in one workgroup's LDS. */
+typedef struct {
+    int64_t tiles;
+    double coverage;
+    int64_t lds_bytes;
+    int64_t k_steps;
+} mgemm_budget_t;
+
+mgemm_status_t mgemm_tile_budget(int64_t M, int64_t N, int64_t K, int32_t BM, int32_t BN, int32_t BK,
+                                 int32_t stages, int32_t elt_bytes, mgemm_budget_t *out);
+
+/* L2 working set of a group of tiles: (group_m*BM + group_n*BN) * K * elt
+ * bytes -- the operand rows and columns that a group of output tiles
+ * shares ("GEMM优化（三）", section 3.4 on choosing the super-tile). */
+int64_t mgemm_group_working_set(int32_t group_m, int32_t group_n, int32_t BM, int32_t BN,
+                                int64_t K, int32_t elt_bytes);
+
+/* Token count rounded up to the narrow tile granularity: (n + g - 1) / g * g
+ * for g a power of two (MegaMoE Blackwell section 04 rounds valid tokens up
+ * to a multiple of 16 before sizing the MMA). */
+int64_t mgemm_round_tokens(int64_t n, int32_t granule);
+
+/* Library version, e.g. "mgemm 0.1 gfx950". */
+const char *mgemm_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MGEMM_H */

@@ -1,0 +1,222 @@
+"""GPU parity of the dense GEMM against the CPU oracle, through the C ABI.
+
+Small and ragged shapes are compared element by element with the full
+oracle; the full-size workloads are compared on sampled elements (random
+ones plus every tile edge) in the same launch configuration the bench
+times.  Integer-valued inputs must match bit for bit; random inputs must
+meet the acceptance rule in helpers.py.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+
+import datagen
+import oracle
+from helpers import (TORCH_OUT, assert_bits_equal, assert_close, from_dev_bits, sample_positions, to_dev)
+
+torch = pytest.importorskip("torch")
+mg = pytest.importorskip("bf16_gemm_amd")
+
+pytestmark = pytest.mark.gpu
+
+TILES = {"auto": 0, "256": mg.PLAN_FORCE_TILE_256x256, "128": mg.PLAN_FORCE_TILE_128x128,
+         "32n": mg.PLAN_FORCE_TILE_32x256, "64n": mg.PLAN_FORCE_TILE_64x256}
+
+
+def log(*a):
+    print(*a, flush=True, file=sys.stderr)
+
+
+ESIZE = {"f32": 4, "bf16": 2, "f16": 2}
+
+
+def pad8(x: np.ndarray) -> np.ndarray:
+    """Storage with its row length padded (with zeros) to a multiple of 8."""
+    r, c = x.shape
+    if c % 8 == 0:
+        return x
+    y = np.zeros((r, (c + 7) // 8 * 8), dtype=x.dtype)
+    y[:, :c] = x
+    return y
+
+
+def run_dense(a_bits, b_bits, M, N, K, in_t, out_t, a_layout="row", b_layout="row", flags=0, ldd=None,
+              sentinel=False, stream=None):
+    """Run the library on host bit arrays; returns (D bits [M][N], plan).
+
+    With ``sentinel`` the output lives in a byte buffer pre-filled with 0xFF
+    that extends three rows and 64 bytes past D; every byte outside the
+    M x N window (the ldd padding and the tail) must still be 0xFF."""
+    a_bits, b_bits = pad8(a_bits), pad8(b_bits)   # 16-byte aligned rows
+    A = to_dev(a_bits, in_t)
+    B = to_dev(b_bits, in_t)
+    ldd = ldd or (N + 7) // 8 * 8
+    es = ESIZE[out_t]
+    nbytes = M * ldd * es + ((3 * ldd * es + 64) if sentinel else 0)
+    raw = torch.full((max(nbytes, 16),), 0xFF, dtype=torch.uint8, device="cuda")
+    D = raw[: M * ldd * es].view(TORCH_OUT[out_t]).view(M, ldd)
+    plan = mg.gemm_plan(M, N, K, in_t, d_type=out_t, a_layout=a_layout, b_layout=b_layout,
+                        lda=a_bits.shape[1], ldb=b_bits.shape[1], ldd=ldd, flags=flags)
+    mg.gemm_run(plan, A, B, D, stream=stream)
+    torch.cuda.synchronize()
+    if sentinel:
+        tail = raw[M * ldd * es:].cpu().numpy()
+        assert np.all(tail == 0xFF), "write past the last row of D"
+        if ldd > N and M > 0:
+            pad = raw[: M * ldd * es].view(M, ldd * es)[:, N * es:].cpu().numpy()
+            assert np.all(pad == 0xFF), "write into D's padding columns"
+    return from_dev_bits(D[:, :N]), plan
+
+
+COMBOS = [("bf16", "f32"), ("bf16", "bf16"), ("f16", "f32"), ("f16", "f16")]
+LAYOUTS = [("row", "row"), ("row", "col"), ("col", "row"), ("col", "col")]
+
+
+@pytest.mark.parametrize("in_t,out_t", COMBOS)
+@pytest.mark.parametrize("al,bl", LAYOUTS)
+@pytest.mark.parametrize("tile", ["256", "128", "32n", "64n"])
+def test_ragged_random_and_integer(in_t, out_t, al, bl, tile):
+    if tile in ("32n", "64n") and al == "col":
+        pytest.skip("narrow-M tiles take a k-contiguous A only")
+    M, N, K = 300, 520, 200   # several tiles, ragged in M, N and K
+    log(f"case ragged tile={tile} {in_t}->{out_t} {al}/{bl} M={M} N={N} K={K}")
+    cfg = datagen.GemmConfig("t", M, N, K, in_t, out_t, al, bl, ("uniform", 1.0), ("normal", 1.0), seed=7, int_seed=8)
+    a, b = datagen.gemm_inputs(cfg, "random")
+    got, plan = run_dense(a, b, M, N, K, in_t, out_t, al, bl, TILES[tile], sentinel=True)
+    ref = oracle.gemm_ref(a, b, in_t, in_t, al, bl)
+    assert_close(got, ref, K, out_t, plan.describe())
+    a, b = datagen.gemm_inputs(cfg, "int")
+    got, plan = run_dense(a, b, M, N, K, in_t, out_t, al, bl, TILES[tile])
+    assert_bits_equal(got, oracle.gemm_ref(a, b, in_t, in_t, al, bl), out_t, plan.describe())
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 4, 8), (7, 9, 16), (33, 3, 24), (64, 61, 64), (257, 255, 72), (5, 1030, 8),
+                                   (2, 2, 512)])
+@pytest.mark.parametrize("in_t,out_t", [("bf16", "f32"), ("f16", "f16")])
+def test_tiny_and_ragged_shapes(M, N, K, in_t, out_t):
+    log(f"case tiny {in_t}->{out_t} M={M} N={N} K={K}")
+    cfg = datagen.GemmConfig("t", M, N, K, in_t, out_t, seed=M * 7 + N, int_seed=K)
+    a, b = datagen.gemm_inputs(cfg, "int")
+    ldd = (N + 7) // 8 * 8 + 8
+    got, plan = run_dense(a, b, M, N, K, in_t, out_t, ldd=ldd, sentinel=True)
+    assert_bits_equal(got, oracle.gemm_ref(a, b, in_t, in_t), out_t, plan.describe())
+
+
+def test_empty_shapes():
+    log("case empty shapes")
+    D = torch.full((4, 8), 7.0, device="cuda")
+    A = torch.zeros((4, 0), dtype=torch.bfloat16, device="cuda")
+    B = torch.zeros((0, 8), dtype=torch.bfloat16, device="cuda")
+    plan = mg.gemm_plan(4, 8, 0, "bf16", d_type="f32", lda=8, ldb=8)
+    mg.gemm_run(plan, torch.zeros(8, dtype=torch.bfloat16, device="cuda"),
+                torch.zeros(8, dtype=torch.bfloat16, device="cuda"), D)
+    torch.cuda.synchronize()
+    assert torch.all(D == 0)           # the empty sum
+    D.fill_(7.0)
+    plan = mg.gemm_plan(0, 8, 16, "bf16", d_type="f32", lda=16)
+    mg.gemm_run(plan, None, None, D)   # no-op: nothing touched, nulls allowed
+    plan = mg.gemm_plan(4, 0, 16, "bf16", d_type="f32", lda=16, ldb=8, ldd=8)
+    mg.gemm_run(plan, None, None, D)
+    torch.cuda.synchronize()
+    assert torch.all(D == 7.0)
+
+
+@pytest.mark.parametrize("in_t", ["bf16", "f16"])
+def test_identity_ones_permutation_exact(in_t):
+    log(f"case identity/ones/permutation {in_t}")
+    rs = np.random.RandomState(4)
+    K = 320
+    X = datagen.matrix((K, 272), ("normal", 1.0), in_t, rs)
+    I = datagen._to_bits(np.eye(K, dtype=np.float32), in_t)
+    got, _ = run_dense(I, X, K, 272, K, in_t, "f32")
+    assert np.array_equal(got.view(np.float32).astype(np.float64), oracle.decode(X, in_t))
+    ones_a = datagen._to_bits(np.ones((130, 4096), np.float32), in_t)
+    ones_b = datagen._to_bits(np.ones((4096, 260), np.float32), in_t)
+    got, _ = run_dense(ones_a, ones_b, 130, 260, 4096, in_t, in_t)
+    assert np.all(oracle.decode(got, in_t) == 4096.0)
+    # B a permutation: D is a column permutation of A, bit-exact for any values
+    A = datagen.matrix((200, K), ("normal", 3.0), in_t, rs)
+    perm = rs.permutation(K)
+    P = np.zeros((K, K), np.float32)
+    P[perm, np.arange(K)] = 1.0
+    for bl in ("row", "col"):
+        Pb = datagen.store(datagen._to_bits(P, in_t), bl)
+        got, _ = run_dense(A, Pb, 200, K, K, in_t, "f32", "row", bl)
+        assert np.array_equal(got.view(np.float32).astype(np.float64), oracle.decode(A, in_t)[:, perm])
+
+
+def test_stream_and_event_ordering():
+    log("case stream ordering")
+    M = N = K = 512
+    cfg = datagen.DENSE["gemm512_f16"]
+    a, b = datagen.gemm_inputs(cfg, "int")
+    A, B = to_dev(a, "f16"), to_dev(b, "f16")
+    D = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    plan = mg.gemm_plan(M, N, K, "f16", d_type="f32")
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    ev = torch.cuda.Event()
+    with torch.cuda.stream(s1):
+        A2 = A * 1       # produced on s1
+        ev.record(s1)
+    s2.wait_event(ev)
+    mg.gemm_run(plan, A2, B, D, stream=s2)
+    with torch.cuda.stream(s2):
+        D2 = D.clone()   # consumer on the same stream: ordered after the GEMM
+    torch.cuda.synchronize()
+    assert_bits_equal(from_dev_bits(D2), oracle.gemm_ref(a, b, "f16", "f16"), "f32", "stream")
+
+
+def test_deterministic():
+    log("case determinism")
+    cfg = datagen.DENSE["gemm4096_bf16"]
+    a, b = datagen.gemm_inputs(cfg, "random", M=1024, N=1024, K=2048)
+    g1, _ = run_dense(a, b, 1024, 1024, 2048, "bf16", "bf16")
+    g2, _ = run_dense(a, b, 1024, 1024, 2048, "bf16", "bf16")
+    assert np.array_equal(g1, g2)
+
+
+def test_run_errors():
+    plan = mg.gemm_plan(64, 64, 64, "bf16", d_type="f32")
+    A = torch.zeros(64 * 64 + 8, dtype=torch.bfloat16, device="cuda")
+    D = torch.zeros(64 * 64, dtype=torch.float32, device="cuda")
+    st = mg.lib.gemm_run(plan.handle, A.data_ptr() + 2, A.data_ptr(), D.data_ptr(), None, 0, None)
+    assert st == mg.ERR_UNSUPPORTED
+
+
+# --------------------------------------------------------------- full size
+
+FULL = ["gemm512_f16", "gemm4096_bf16", "gemm8192_bf16_bcol", "ts16384x2048x7168", "decode128x7168x2048"]
+
+
+@pytest.mark.parametrize("name", FULL)
+@pytest.mark.parametrize("variant", ["random", "int"])
+def test_full_size_workloads(name, variant):
+    cfg = datagen.DENSE[name]
+    log(f"case full {name} {variant}")
+    a, b = datagen.gemm_inputs(cfg, variant)
+    A, B = to_dev(a, cfg.in_dtype), to_dev(b, cfg.in_dtype)
+    D = torch.empty((cfg.M, cfg.N), dtype=TORCH_OUT[cfg.out_dtype], device="cuda")
+    plan = mg.gemm_plan(cfg.M, cfg.N, cfg.K, cfg.in_dtype, d_type=cfg.out_dtype, a_layout=cfg.a_layout,
+                        b_layout=cfg.b_layout)
+    mg.gemm_run(plan, A, B, D)
+    torch.cuda.synchronize()
+    got = from_dev_bits(D)
+    if cfg.M * cfg.N * cfg.K <= 512 ** 3:
+        ref = oracle.gemm_ref(a, b, cfg.in_dtype, cfg.in_dtype, cfg.a_layout, cfg.b_layout)
+        sel = (slice(None), slice(None))
+        g = got
+    else:
+        inf = plan.info()
+        r, c = sample_positions(cfg.M, cfg.N, 3000, (inf.block_m, inf.block_n), seed=hash(name) % 1000)
+        ref = oracle.gemm_ref_sampled(a, b, r, c, cfg.in_dtype, cfg.in_dtype, cfg.a_layout, cfg.b_layout)
+        g = got[r, c]
+    if variant == "int":
+        assert_bits_equal(g, ref, cfg.out_dtype, plan.describe())
+    else:
+        err = assert_close(g, ref, cfg.K, cfg.out_dtype, plan.describe())
+        log(f"  max abs err {err:.3e} (tol base {1e-4 * math.sqrt(cfg.K):.3e})")
+    # no NaN/Inf anywhere in the output
+    vals = D.float()
+    assert torch.isfinite(vals).all()

@@ -1,0 +1,128 @@
+"""CPU tests of the C-ABI library: it loads, exports every declared symbol,
+its planner reproduces the pages' worked budget numbers, and argument
+errors are reported before anything is enqueued (no GPU needed)."""
+import json
+import os
+import re
+
+import pytest
+
+import bf16_gemm_amd as mg
+
+GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "planner_pins.json")))
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "mgemm.h")
+
+
+def test_exports_match_header():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)      # drop comments
+    declared = set(re.findall(r"\b((?:gemm|grouped_gemm|mgemm)_\w+)\s*\(", text))
+    assert declared == set(mg.EXPORTS), declared ^ set(mg.EXPORTS)
+    for name in declared:
+        assert hasattr(mg.lib, name), name
+    assert mg.version().startswith("mgemm")
+
+
+def test_tile_calculator_pin():
+    g = GOLD["tile_calculator"]
+    b = mg.tile_budget(g["M"], g["N"], g["K"], g["BM"], g["BN"], g["BK"], g["stages"], g["elt_bytes"])
+    assert b.tiles == g["tiles"]
+    assert b.coverage == pytest.approx(g["coverage"])
+    assert b.k_steps == g["k_steps"]
+    # one CTA of the page's pair holds half of each tile side
+    half = mg.tile_budget(g["M"], g["N"], g["K"], g["BM"] // 2, g["BN"] // 2, g["BK"], g["stages"], g["elt_bytes"])
+    assert half.lds_bytes == g["per_cta_input_kib_with_pair_split"] * 1024
+    assert b.lds_bytes == 2 * half.lds_bytes
+
+
+def test_k_tile_doubling_pin():
+    g = GOLD["k_tile_doubling"]
+    for bk, kib in g["stage_kib"].items():
+        b = mg.tile_budget(256, 256, 4096, g["BM_per_cta"], g["BN_per_cta"], int(bk), 1, 2)
+        assert b.lds_bytes == kib * 1024
+        b3 = mg.tile_budget(256, 256, 4096, g["BM_per_cta"], g["BN_per_cta"], int(bk), 3, 2)
+        assert b3.lds_bytes == g["three_stage_kib"][bk] * 1024
+
+
+def test_stage_cost_pin():
+    g = GOLD["stage_cost"]
+    b = mg.tile_budget(4096, 4096, 4096, g["BM"], g["BN"], g["BK"], 1, g["elt_bytes"])
+    assert b.lds_bytes == g["stage_bytes"]
+    for depth, kb in g["depth_total_kb"].items():
+        tot = mg.tile_budget(4096, 4096, 4096, g["BM"], g["BN"], g["BK"], int(depth), 2).lds_bytes + g["writeback_bytes"]
+        assert tot == kb * 1024
+
+
+def test_supertile_working_set_pin():
+    g = GOLD["supertile_working_set"]
+    for c in g["cases"]:
+        ws = mg.group_working_set(c["group_m"], c["group_n"], g["BM"], g["BN"], g["K"], g["elt_bytes"])
+        assert ws == c["bytes"]
+        if "a_part_bytes" in c:
+            assert mg.group_working_set(c["group_m"], 0, g["BM"], g["BN"], g["K"], g["elt_bytes"]) == c["a_part_bytes"]
+    p = g["b_reread_passes"]
+    assert p["grid_m"] // p["super_m"] == p["passes"]
+
+
+def test_dynamic_n_pin():
+    g = GOLD["dynamic_n"]
+    assert mg.round_tokens(g["tokens"], g["granule"]) == g["rounded"]
+    assert g["static_n"] - g["tokens"] == g["padding_before"]
+    assert g["rounded"] - g["tokens"] == g["padding_after"]
+    assert mg.round_tokens(0, 16) == 0 and mg.round_tokens(16, 16) == 16 and mg.round_tokens(17, 16) == 32
+    assert mg.round_tokens(5, 12) == -1
+
+
+def test_plan_choices_for_workloads():
+    p = mg.gemm_plan(8192, 8192, 8192, "bf16", d_type="f32", b_layout="col")
+    i = p.info()
+    assert (i.block_m, i.block_n, i.block_k) == (256, 256, 64)
+    assert i.tiles == 1024 and i.coverage == 1.0 and i.lds_bytes <= 160 * 1024
+    assert i.grid == min(1024, i.num_cus)
+    p = mg.gemm_plan(128, 7168, 2048, "bf16", d_type="bf16")
+    assert p.info().block_m <= 64, p.describe()   # narrow-M tile for the decode shape
+    p = mg.grouped_gemm_plan(64, 32768, 4096, 7168, epilogue=mg.EPI_SILU_GATE_I8)
+    assert "32x256" in p.describe() and "256x256" in p.describe()
+
+
+def test_lds_budget_rejects_three_stage_macro_tile():
+    # three 256x256x64 bf16 stages would need 192 KiB: more than a CU's 160 KiB
+    assert mg.tile_budget(256, 256, 64, 256, 256, 64, 3, 2).lds_bytes == 192 * 1024 > 160 * 1024
+    assert mg.tile_budget(256, 256, 64, 256, 256, 64, 2, 2).lds_bytes == 128 * 1024
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(M=-1, N=4, K=8), mg.ERR_INVALID_ARG),
+    (dict(M=4, N=8, K=12), mg.ERR_UNSUPPORTED),
+    (dict(M=4, N=8, K=16, lda=8), mg.ERR_INVALID_ARG),
+    (dict(M=4, N=8, K=8, lda=12), mg.ERR_UNSUPPORTED),
+    (dict(M=4, N=8, K=8, ldd=10), mg.ERR_UNSUPPORTED),
+    (dict(M=4, N=8, K=8, a_type="f16", b_type="bf16"), mg.ERR_UNSUPPORTED),
+    (dict(M=4, N=8, K=8, a_type="bf16", d_type="f16"), mg.ERR_UNSUPPORTED),
+])
+def test_plan_argument_errors(kw, status):
+    args = dict(M=4, N=8, K=8, a_type="bf16")
+    args.update(kw)
+    with pytest.raises(mg.MgemmError) as e:
+        mg.gemm_plan(**args)
+    assert e.value.status == status
+    assert mg.lib.gemm_last_error_message().decode()
+
+
+def test_grouped_plan_errors():
+    with pytest.raises(mg.MgemmError) as e:
+        mg.grouped_gemm_plan(0, 10, 32, 32)
+    assert e.value.status == mg.ERR_INVALID_ARG
+    with pytest.raises(mg.MgemmError) as e:
+        mg.grouped_gemm_plan(4, 10, 40, 32, epilogue=mg.EPI_SILU_GATE_I8)
+    assert e.value.status == mg.ERR_UNSUPPORTED
+    with pytest.raises(mg.MgemmError):
+        mg.grouped_gemm_plan(4, 10, 32, 32, stride_b=8)
+
+
+def test_null_arguments_rejected():
+    assert mg.lib.gemm_plan(None, 0, None) == mg.ERR_INVALID_ARG
+    assert mg.lib.gemm_run(None, None, None, None, None, 0, None) == mg.ERR_INVALID_ARG
+    p = mg.gemm_plan(4, 8, 8, "bf16")
+    assert mg.lib.gemm_run(p.handle, None, None, None, None, 0, None) == mg.ERR_INVALID_ARG
+    assert mg.lib.gemm_status_string(mg.ERR_HIP) == b"MGEMM_ERR_HIP"
