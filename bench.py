@@ -106,11 +106,16 @@ def cpu_baseline(case, target_s):
         return None
     cfg, a, b = case
     a_rows = (lambda R: a[:R]) if cfg.a_layout == "row" else (lambda R: np.ascontiguousarray(a[:, :R]))
-    R = 2
-    t0 = time.perf_counter()
-    oracle.gemm_ref(a_rows(R), b, cfg.in_dtype, cfg.in_dtype, cfg.a_layout, cfg.b_layout)
-    t1 = time.perf_counter() - t0
-    R2 = int(min(cfg.M, max(R, R * target_s / max(t1, 1e-3))))
+    # two calibration runs give the fixed cost (decoding B) and the per-row
+    # cost; the timed run then covers about target_s seconds
+    def timed(R):
+        t0 = time.perf_counter()
+        oracle.gemm_ref(a_rows(R), b, cfg.in_dtype, cfg.in_dtype, cfg.a_layout, cfg.b_layout)
+        return time.perf_counter() - t0
+    r1, r2 = 4, 36
+    t1, t2 = timed(r1), timed(r2)
+    per_row = max((t2 - t1) / (r2 - r1), 1e-6)
+    R2 = int(min(cfg.M, max(r2, (target_s - max(t1 - r1 * per_row, 0.0)) / per_row)))
     t0 = time.perf_counter()
     oracle.gemm_ref(a_rows(R2), b, cfg.in_dtype, cfg.in_dtype, cfg.a_layout, cfg.b_layout)
     t = time.perf_counter() - t0
@@ -154,7 +159,7 @@ def main():
     wall = time.perf_counter() - t0
     ms = ev0.elapsed_time(ev1) / args.steps
     tflops = info["flops"] / (ms * 1e-3) / 1e12
-    print(f"# {args.steps} steps: {ms * 1e3:.1f} us/step (events), wall {wall * 1e3 / args.steps:.1f} us/step",
+    print(f"# {args.steps} steps: {ms * 1e3:.1f} us/step (events), wall {wall * 1e6 / args.steps:.1f} us/step",
           file=sys.stderr, flush=True)
 
     peak = PEAK_TFLOPS[info["dtype"]]
