@@ -139,6 +139,12 @@ struct Loader<R, NT, true> {
     // The same work split into NP parts (chunks j with j % NP == P), so the
     // steady-state K loop can spread it between MFMA groups.  Part P's loads
     // reuse the registers that part P's store has just written out.
+    // LDS writes / global loads that part P of NP issues
+    template <int P, int NP>
+    static constexpr int part_writes() { return P < NC ? (NC - P + NP - 1) / NP : 0; }
+    template <int P, int NP>
+    static constexpr int part_loads() { return part_writes<P, NP>(); }
+
     template <int P, int NP>
     __device__ __forceinline__ void store_part(char *lds) const
     {
@@ -224,6 +230,11 @@ struct Loader<R, NT, false> {
         }
     }
     __device__ __forceinline__ void store(char *lds) const { store_rows<0, 8>(lds); }
+    template <int P, int NP>
+    static constexpr int part_writes() { return 8 * (P + 1) / NP - 8 * P / NP; }
+    template <int P, int NP>
+    static constexpr int part_loads() { return P == NP - 1 ? KB : 0; }
+
     // NP parts: part P writes rows [8P/NP, 8(P+1)/NP); every row needs all KB
     // loaded registers, so the next step's loads go out with the last part.
     template <int P, int NP>
@@ -255,6 +266,28 @@ struct OperandSrc {
 // ---------------------------------------------------------------------------
 // The tile: accumulators, main loop, epilogue.
 // ---------------------------------------------------------------------------
+
+// Instruction interleave for one sub-step, as scheduling-group barriers:
+// after MFMA i comes the i-th LDS read (the next sub-step's fragments, so
+// they have the rest of the group to arrive), then the LDS writes of the
+// staged step and, one slot later each, the global loads that refill those
+// registers.  Groups the code does not have are simply empty.
+enum : int { SG_MFMA = 0x008, SG_VMEM_READ = 0x020, SG_DS_READ = 0x100, SG_DS_WRITE = 0x200 };
+
+template <int I, int NM, int NR, int NW, int NV>
+__device__ __forceinline__ void sched_pattern()
+{
+    if constexpr (I < NM) {
+        __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+        if constexpr (I < NR)
+            __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 1, 0);
+        else if constexpr (I - NR < NW)
+            __builtin_amdgcn_sched_group_barrier(SG_DS_WRITE, 1, 0);
+        if constexpr (I - NR - 1 >= 0 && I - NR - 1 < NV)
+            __builtin_amdgcn_sched_group_barrier(SG_VMEM_READ, 1, 0);
+        sched_pattern<I + 1, NM, NR, NW, NV>();
+    }
+}
 
 template <int IN>
 __device__ __forceinline__ f32x16_t mfma32(u32x4_t a, u32x4_t b, f32x16_t c)
@@ -300,10 +333,15 @@ struct Tile {
         const int ksteps = (K + kBK - 1) / kBK;
         if (ksteps <= 0)
             return;
-        Loader<BM, NT, A_KMAJOR> la;
-        Loader<BN, NT, B_KMAJOR> lb;
-        la.init(tid, lda);
-        lb.init(tid, ldb);
+        // Two sets of staging registers: the set written to LDS in step k
+        // is refilled with step k+3 at once, so each global load has two
+        // full K steps to arrive before its data is needed.
+        Loader<BM, NT, A_KMAJOR> la0, la1;
+        Loader<BN, NT, B_KMAJOR> lb0, lb1;
+        la0.init(tid, lda);
+        lb0.init(tid, ldb);
+        la1.init(tid, lda);
+        lb1.init(tid, ldb);
 
         // Fragment read offsets.  Lane l reads row (l & 31) of a 32-row
         // block at 16-byte chunk 2*ks + (l >> 5).  Rows 32 apart differ in
@@ -318,77 +356,149 @@ struct Tile {
             bbase[ks] = BM * kRowBytes + rb * kRowBytes + (((2 * ks + fk) ^ swz(rb)) << 4);
         }
 
-        la.load(sa.at_step(0), K);
-        lb.load(sb.at_step(0), K);
-        la.store(lds);
-        lb.store(lds + BM * kRowBytes);
-        if (ksteps > 1) {
-            la.load(sa.at_step(1), K - kBK);
-            lb.load(sb.at_step(1), K - kBK);
-        }
+        // Prologue: stage step 0 into slot 0 and fetch steps 1 and 2.  The
+        // loads go out part by part in the same order as in the steady-state
+        // body, so the wait counts the compiler derives for the loop are
+        // exact (waiting only for the part about to be written).
+        load_parts(la0, lb0, sa.at_step(0), sb.at_step(0), K);
+        load_parts(la1, lb1, sa.at_step(1), sb.at_step(1), K - kBK);
+        la0.store(lds);
+        lb0.store(lds + BM * kRowBytes);
+        load_parts(la0, lb0, sa.at_step(2), sb.at_step(2), K - 2 * kBK);
         lds_barrier();
 
-        // steady state: write step kt+1 into the other slot and fetch step
-        // kt+2; the last two steps are peeled so that this body has no
-        // branches and the scheduler can interleave its parts with MFMAs
-        int kt = 0;
-        for (; kt + 2 < ksteps; ++kt)
-            step<true, true>(lds, kt, la, lb, sa, sb, K, abase, bbase);
-        if (kt + 1 < ksteps) {
-            step<true, false>(lds, kt, la, lb, sa, sb, K, abase, bbase);
-            ++kt;
+        // Fragments are double-buffered: while the MFMAs of one 16-k
+        // sub-step run from registers, the next sub-step's fragments are
+        // already being read, so no MFMA waits on a fresh LDS read.
+        Frags f0, f1;
+        read_frags<0>(lds, abase, bbase, f0);
+
+        // Every step runs the same branch-free body, two steps per trip:
+        // step kt writes step kt+1 (held in set (kt+1) & 1) into the other
+        // slot and refills that set with step kt+3.  Near the end those
+        // loads fall past the operand's records (the hardware returns zeros
+        // without touching memory) and the writes fill a slot nobody reads,
+        // so no tail variants are needed.
+        // An odd step count runs one extra step on an all-zero slot (both
+        // operands read as zero past K), which adds exactly nothing.
+        for (int kt = 0; kt < ksteps; kt += 2) {
+            step<true, true, true>(lds, kt, la1, lb1, sa, sb, K, abase, bbase, f0, f1);
+            step<true, true, true>(lds, kt + 1, la0, lb0, sa, sb, K, abase, bbase, f0, f1);
         }
-        step<false, false>(lds, kt, la, lb, sa, sb, K, abase, bbase);
     }
 
-    // One K step on slot kt & 1.  STORE: write the staged registers (step
-    // kt+1) into the other slot; LOAD: then fetch step kt+2 into them.
-    template <bool STORE, bool LOAD>
+    struct Frags {
+        u32x4_t a[FM], b[FN];
+    };
+
+    __device__ __forceinline__ static void load_parts(Loader<BM, NT, A_KMAJOR> &la, Loader<BN, NT, B_KMAJOR> &lb,
+                                                      __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb, int kleft)
+    {
+        la.template load_part<0, 3>(ra, kleft);
+        lb.template load_part<0, 3>(rb, kleft);
+        la.template load_part<1, 3>(ra, kleft);
+        lb.template load_part<1, 3>(rb, kleft);
+        la.template load_part<2, 3>(ra, kleft);
+        lb.template load_part<2, 3>(rb, kleft);
+    }
+    using LoaderA = Loader<BM, NT, A_KMAJOR>;
+    using LoaderB = Loader<BN, NT, B_KMAJOR>;
+    template <int P> static constexpr int WA() { return LoaderA::template part_writes<P, 3>(); }
+    template <int P> static constexpr int WB() { return LoaderB::template part_writes<P, 3>(); }
+    template <int P> static constexpr int LA() { return LoaderA::template part_loads<P, 3>(); }
+    template <int P> static constexpr int LB() { return LoaderB::template part_loads<P, 3>(); }
+
+    template <int KS>
+    __device__ __forceinline__ void read_frags(const char *slot, const int (&abase)[4], const int (&bbase)[4],
+                                               Frags &f) const
+    {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+            f.a[i] = *(const u32x4_t *)(slot + abase[KS ^ ((i & 1) * 2)] + i * 32 * kRowBytes);
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+            f.b[j] = *(const u32x4_t *)(slot + bbase[KS ^ ((j & 1) * 2)] + j * 32 * kRowBytes);
+    }
+
+    __device__ __forceinline__ void mfmas(const Frags &f)
+    {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+                acc[i][j] = mfma32<IN>(f.b[j], f.a[i], acc[i][j]);
+    }
+
+    // One K step on slot kt & 1; on entry f0 holds its first sub-step's
+    // fragments, on exit (NEXT) f0 holds the next step's.
+    //   STORE: write the staged registers (step kt+1) into the other slot,
+    //          spread over sub-steps 0-2;
+    //   LOAD:  after each part is written, fetch that part of step kt+3 into
+    //          the same registers;
+    //   NEXT:  after the barrier, read the next step's first fragments.
+    // The barrier sits between the last fragment read of this step and the
+    // last MFMA group, so that group covers the barrier and the next reads.
+    template <bool STORE, bool LOAD, bool NEXT>
     __device__ __forceinline__ void step(char *lds, int kt, Loader<BM, NT, A_KMAJOR> &la, Loader<BN, NT, B_KMAJOR> &lb,
                                          const OperandSrc &sa, const OperandSrc &sb, int K, const int (&abase)[4],
-                                         const int (&bbase)[4])
+                                         const int (&bbase)[4], Frags &f0, Frags &f1)
     {
         char *cur = lds + (kt & 1) * SLOT;
         char *nxt = lds + ((kt + 1) & 1) * SLOT;
         __amdgpu_buffer_rsrc_t ra2, rb2;
         if constexpr (LOAD) {
-            ra2 = sa.at_step(kt + 2);
-            rb2 = sb.at_step(kt + 2);
+            ra2 = sa.at_step(kt + 3);
+            rb2 = sb.at_step(kt + 3);
         }
-        const int kleft2 = K - (kt + 2) * kBK;
-        sub_step<0, STORE, LOAD>(cur, nxt, la, lb, ra2, rb2, kleft2, abase, bbase);
-        sub_step<1, STORE, LOAD>(cur, nxt, la, lb, ra2, rb2, kleft2, abase, bbase);
-        sub_step<2, STORE, LOAD>(cur, nxt, la, lb, ra2, rb2, kleft2, abase, bbase);
-        sub_step<3, STORE, LOAD>(cur, nxt, la, lb, ra2, rb2, kleft2, abase, bbase);
-        lds_barrier();
-    }
+        const int kleft2 = K - (kt + 3) * kBK;
 
-    template <int KS, bool STORE, bool LOAD>
-    __device__ __forceinline__ void sub_step(const char *cur, char *nxt, Loader<BM, NT, A_KMAJOR> &la,
-                                             Loader<BN, NT, B_KMAJOR> &lb, __amdgpu_buffer_rsrc_t ra2,
-                                             __amdgpu_buffer_rsrc_t rb2, int kleft2, const int (&abase)[4],
-                                             const int (&bbase)[4])
-    {
-        u32x4_t af[FM], bf[FN];
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-            af[i] = *(const u32x4_t *)(cur + abase[KS ^ ((i & 1) * 2)] + i * 32 * kRowBytes);
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-            bf[j] = *(const u32x4_t *)(cur + bbase[KS ^ ((j & 1) * 2)] + j * 32 * kRowBytes);
+        // sub-step 0
+        read_frags<1>(cur, abase, bbase, f1);
         if constexpr (STORE) {
-            la.template store_part<KS, 4>(nxt);
-            lb.template store_part<KS, 4>(nxt + BM * kRowBytes);
+            la.template store_part<0, 3>(nxt);
+            lb.template store_part<0, 3>(nxt + BM * kRowBytes);
         }
         if constexpr (LOAD) {
-            la.template load_part<KS, 4>(ra2, kleft2);
-            lb.template load_part<KS, 4>(rb2, kleft2);
+            la.template load_part<0, 3>(ra2, kleft2);
+            lb.template load_part<0, 3>(rb2, kleft2);
         }
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-            for (int j = 0; j < FN; ++j)
-                acc[i][j] = mfma32<IN>(bf[j], af[i], acc[i][j]);
+        mfmas(f0);
+        sched_pattern<0, FM * FN, FM + FN, STORE ? WA<0>() + WB<0>() : 0, LOAD ? LA<0>() + LB<0>() : 0>();
+        __builtin_amdgcn_sched_barrier(0);
+        // sub-step 1
+        read_frags<2>(cur, abase, bbase, f0);
+        if constexpr (STORE) {
+            la.template store_part<1, 3>(nxt);
+            lb.template store_part<1, 3>(nxt + BM * kRowBytes);
+        }
+        if constexpr (LOAD) {
+            la.template load_part<1, 3>(ra2, kleft2);
+            lb.template load_part<1, 3>(rb2, kleft2);
+        }
+        mfmas(f1);
+        sched_pattern<0, FM * FN, FM + FN, STORE ? WA<1>() + WB<1>() : 0, LOAD ? LA<1>() + LB<1>() : 0>();
+        __builtin_amdgcn_sched_barrier(0);
+        // sub-step 2
+        read_frags<3>(cur, abase, bbase, f1);
+        if constexpr (STORE) {
+            la.template store_part<2, 3>(nxt);
+            lb.template store_part<2, 3>(nxt + BM * kRowBytes);
+        }
+        if constexpr (LOAD) {
+            la.template load_part<2, 3>(ra2, kleft2);
+            lb.template load_part<2, 3>(rb2, kleft2);
+        }
+        mfmas(f0);
+        sched_pattern<0, FM * FN, FM + FN, STORE ? WA<2>() + WB<2>() : 0, LOAD ? LA<2>() + LB<2>() : 0>();
+        __builtin_amdgcn_sched_barrier(0);
+        // sub-step 3: every read of `cur` and write of `nxt` by this wave
+        // is done; meet the other waves, then start on the next slot
+        lds_barrier();
+        if constexpr (NEXT)
+            read_frags<0>(nxt, abase, bbase, f0);
+        mfmas(f1);
+        sched_pattern<0, FM * FN, NEXT ? FM + FN : 0, 0, 0>();
+        __builtin_amdgcn_sched_barrier(0);
     }
 };
 
