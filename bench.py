@@ -41,7 +41,55 @@ def parse():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle sample time")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run only a plain 256 MiB device copy (the reference kernel that scales the "
+                         "FETCH_SIZE / WRITE_SIZE counters to bytes)")
     return ap.parse_args()
+
+
+KERNEL_SOURCES = ["bf16_gemm_amd/csrc/engine.hpp", "bf16_gemm_amd/csrc/kernels.hpp",
+                  "bf16_gemm_amd/csrc/tile_tables.hpp"]
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def profiled_traffic(workload: str):
+    """HBM-side bytes per launch measured with rocprofv3 (FETCH_SIZE and
+    WRITE_SIZE, each scaled by the same counter on a plain copy), read from
+    the workload's summary under profiles/; None unless that summary was
+    taken on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and line.split(":", 1)[0].strip() in ("source_hash", "traffic_bytes_per_launch"):
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip().strip("`")
+    if fields.get("source_hash") != kernel_source_hash():
+        return None
+    try:
+        return int(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def calibrate_copy():
+    import torch
+    x = torch.empty(256 * 1024 * 1024 // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    y = torch.empty_like(x)
+    for _ in range(3):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "device copy", "bytes_read": x.numel() * 4, "bytes_written": y.numel() * 4,
+                      "launches": 3}), flush=True)
 
 
 def dev16(torch, bits, dt):
@@ -127,6 +175,9 @@ def cpu_baseline(case, target_s):
 
 def main():
     args = parse()
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
     if args.gpus != 1:
         print(f"bench.py: runs on one GPU only (asked for --gpus {args.gpus}); multi-GPU runs are not "
               "supported by this benchmark", file=sys.stderr)
@@ -164,9 +215,10 @@ def main():
 
     peak = PEAK_TFLOPS[info["dtype"]]
     roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": round(peak, 1), "unit": "TFLOP/s",
-            "frac": round(tflops / peak, 4), "traffic": None,
+            "frac": round(tflops / peak, 4), "traffic": profiled_traffic(info["config"]["workload"]),
             "kernel": info["plan"], "algorithmic_bytes_per_launch": info["bytes"],
-            "achieved_hbm_gbps_algorithmic": round(info["bytes"] / (ms * 1e-3) / 1e9, 1)}
+            "achieved_hbm_gbps_algorithmic": round(info["bytes"] / (ms * 1e-3) / 1e9, 1),
+            "kernel_source_hash": kernel_source_hash()}
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(case, args.cpu_seconds)
