@@ -47,8 +47,10 @@ def parse():
     return ap.parse_args()
 
 
+# the kernels and the planner that picks their launch (tile, grid, tile order):
+# a change to any of them makes stored traffic counts stale
 KERNEL_SOURCES = ["bf16_gemm_amd/csrc/engine.hpp", "bf16_gemm_amd/csrc/kernels.hpp",
-                  "bf16_gemm_amd/csrc/tile_tables.hpp"]
+                  "bf16_gemm_amd/csrc/tile_tables.hpp", "bf16_gemm_amd/csrc/plan.cpp"]
 
 
 def kernel_source_hash() -> str:
