@@ -108,16 +108,18 @@ def dense_case(torch, mg, datagen, name):
     D = torch.empty((cfg.M, cfg.N), dtype=out, device="cuda")
     plan = mg.gemm_plan(cfg.M, cfg.N, cfg.K, cfg.in_dtype, d_type=cfg.out_dtype, a_layout=cfg.a_layout,
                         b_layout=cfg.b_layout)
+    ws = mg.workspace_for(plan)      # split-K scratch, allocated before timing
 
     def step():
-        mg.gemm_run(plan, A, B, D)
+        mg.gemm_run(plan, A, B, D, workspace=ws)
 
     esz = 4 if cfg.out_dtype == "f32" else 2
+    inf = plan.info()
     info = dict(flops=cfg.flops, bytes=2 * (cfg.M * cfg.K + cfg.K * cfg.N) + esz * cfg.M * cfg.N,
                 plan=plan.describe(), dtype=cfg.in_dtype,
                 config={"workload": name, "M": cfg.M, "N": cfg.N, "K": cfg.K, "in": cfg.in_dtype,
                         "out": cfg.out_dtype, "a_layout": cfg.a_layout, "b_layout": cfg.b_layout},
-                launches_per_step=1)
+                launches_per_step=1 + (inf.splits > 1) + (cfg.N % 4 != 0))
     return step, info, (cfg, a, b)
 
 
@@ -216,10 +218,20 @@ def main():
           file=sys.stderr, flush=True)
 
     peak = PEAK_TFLOPS[info["dtype"]]
-    roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": round(peak, 1), "unit": "TFLOP/s",
-            "frac": round(tflops / peak, 4), "traffic": profiled_traffic(info["config"]["workload"]),
-            "kernel": info["plan"], "algorithmic_bytes_per_launch": info["bytes"],
-            "achieved_hbm_gbps_algorithmic": round(info["bytes"] / (ms * 1e-3) / 1e9, 1),
+    # the bound is the one the algorithmic intensity falls under: below the
+    # ridge (peak FLOP/s over 8 TB/s, ~315 FLOP/B) a step is HBM-bound
+    gbps = info["bytes"] / (ms * 1e-3) / 1e9
+    hbm_bound = info["flops"] / info["bytes"] < peak * 1e12 / (HBM_GBPS * 1e9)
+    roof = {"bound": "hbm" if hbm_bound else "mfma",
+            "achieved": round(gbps, 1) if hbm_bound else round(tflops, 2),
+            "peak": HBM_GBPS if hbm_bound else round(peak, 1),
+            "unit": "GB/s" if hbm_bound else "TFLOP/s",
+            "frac": round(gbps / HBM_GBPS, 4) if hbm_bound else round(tflops / peak, 4),
+            "traffic": profiled_traffic(info["config"]["workload"]),
+            "kernel": info["plan"], "launches_per_step": info["launches_per_step"],
+            "algorithmic_bytes_per_step": info["bytes"],
+            "algorithmic_flops_per_step": info["flops"],
+            "achieved_hbm_gbps_algorithmic": round(gbps, 1),
             "kernel_source_hash": kernel_source_hash()}
     cpu = None
     if not args.no_cpu_baseline:

@@ -27,6 +27,11 @@ PLAN_FORCE_TILE_32x256 = 0x4
 PLAN_FORCE_TILE_64x256 = 0x8
 PLAN_NO_XCD_REMAP = 0x100
 
+
+def PLAN_SPLIT_K(n: int) -> int:
+    """Plan flag fixing the number of K ranges per output tile (1 = no split)."""
+    return (int(n) & 0xFF) << 16
+
 DTYPE = {"f16": F16, "bf16": BF16, "f32": F32}
 TORCH_DTYPE = {torch.float16: F16, torch.bfloat16: BF16, torch.float32: F32}
 LAYOUT = {"row": ROW_MAJOR, "col": COL_MAJOR}
@@ -54,7 +59,7 @@ class PlanInfo(ctypes.Structure):
                 ("lds_bytes", ctypes.c_int32), ("tiles_m", ctypes.c_int64), ("tiles_n", ctypes.c_int64),
                 ("tiles", ctypes.c_int64), ("k_steps", ctypes.c_int64), ("coverage", ctypes.c_double),
                 ("grid", ctypes.c_int32), ("group_m", ctypes.c_int32), ("xcd_remap", ctypes.c_int32),
-                ("num_cus", ctypes.c_int32)]
+                ("num_cus", ctypes.c_int32), ("splits", ctypes.c_int32)]
 
 
 class Budget(ctypes.Structure):
@@ -194,10 +199,26 @@ def grouped_gemm_plan(num_groups, max_total_rows, N, K, a_type="bf16", b_type=No
     return Plan(h.value, d)
 
 
+def workspace_for(plan: Plan, device="cuda"):
+    """A device buffer of the plan's workspace size (None if it needs none)."""
+    n = plan.workspace_size()
+    return torch.empty(n, dtype=torch.uint8, device=device) if n else None
+
+
+def _nbytes(x, given: int) -> int:
+    if given or x is None or isinstance(x, int):
+        return given
+    return x.numel() * x.element_size()
+
+
 def gemm_run(plan: Plan, A, B, D, workspace=None, workspace_bytes: int = 0, stream=None):
     """Enqueue the planned product on ``stream`` (default: torch's current
-    stream).  A, B, D: device tensors (or raw device addresses)."""
-    _check(lib.gemm_run(plan.handle, _ptr(A), _ptr(B), _ptr(D), _ptr(workspace), workspace_bytes,
+    stream).  A, B, D: device tensors (or raw device addresses).  A plan that
+    splits K needs a workspace (``workspace_for(plan)``); when none is given
+    for such a plan, one is taken from torch's allocator on D's device."""
+    if workspace is None and plan.workspace_size() and isinstance(D, torch.Tensor):
+        workspace = workspace_for(plan, D.device)
+    _check(lib.gemm_run(plan.handle, _ptr(A), _ptr(B), _ptr(D), _ptr(workspace), _nbytes(workspace, workspace_bytes),
                         _stream(stream)), "gemm_run")
 
 
@@ -205,7 +226,7 @@ def grouped_gemm_run(plan: Plan, A, B, D, row_offsets, workspace=None, workspace
     """Enqueue the planned grouped product; ``row_offsets`` is a device int32
     tensor of num_groups + 1 prefix sums."""
     _check(lib.grouped_gemm_run(plan.handle, _ptr(A), _ptr(B), _ptr(D), _ptr(row_offsets), _ptr(workspace),
-                                workspace_bytes, _stream(stream)), "grouped_gemm_run")
+                                _nbytes(workspace, workspace_bytes), _stream(stream)), "grouped_gemm_run")
 
 
 def tile_budget(M, N, K, BM, BN, BK, stages, elt_bytes) -> Budget:

@@ -44,8 +44,6 @@ using namespace mgemm;
 extern "C" mgemm_status_t gemm_run(mgemm_plan_t plan, const void *A, const void *B, void *D, void *workspace,
                                    size_t workspace_bytes, mgemm_stream_t stream)
 {
-    (void)workspace;
-    (void)workspace_bytes;
     if (!plan || plan->kind != PLAN_DENSE) {
         set_error("gemm_run: null or non-dense plan");
         return MGEMM_ERR_INVALID_ARG;
@@ -65,6 +63,12 @@ extern "C" mgemm_status_t gemm_run(mgemm_plan_t plan, const void *A, const void 
     }
     if (plan->zero_fill)
         return hip_status(launch_zero_fill(D, (int)d.M, (int)d.N, d.ldd * esz, esz, s), "gemm_run zero fill");
+    const bool split = plan->splits > 1 && plan->tiles > 0;
+    if (split && (!workspace || workspace_bytes < plan->workspace_bytes || !aligned16(workspace))) {
+        set_error("gemm_run: the plan splits K and needs a 16-byte aligned workspace of %zu bytes (got %zu at %p)",
+                  plan->workspace_bytes, workspace_bytes, workspace);
+        return MGEMM_ERR_WORKSPACE;
+    }
 
     const bool ak = d.a_layout == MGEMM_ROW_MAJOR;
     const bool bk = d.b_layout == MGEMM_COL_MAJOR;
@@ -84,7 +88,31 @@ extern "C" mgemm_status_t gemm_run(mgemm_plan_t plan, const void *A, const void 
     a.tiles = (int)plan->tiles;
     a.group_m = plan->group_m;
     a.xcd_remap = plan->xcd_remap;
-    if (a.tiles > 0) {
+    a.splits = 1;
+    a.kchunk = (int)d.K;
+    a.split_stride = 0;
+    if (split) {
+        // every K range writes its fp32 partial tile into its own slab of
+        // the workspace; the reduction adds the slabs into D
+        DenseArgs w = a;
+        w.D = workspace;
+        w.ldd = a.N;
+        w.splits = plan->splits;
+        w.kchunk = plan->kchunk;
+        w.split_stride = (int64_t)a.M * a.N;
+        w.tiles = a.tiles * plan->splits;
+        DenseFn f = dense_fn(plan->tile, ak, bk, in, OUT_F32);
+        if (!f) {
+            set_error("gemm_run: kernel missing for the planned variant");
+            return MGEMM_ERR_UNSUPPORTED;
+        }
+        if (mgemm_status_t st = hip_status(f(w, plan->grid, s), "gemm_run launch"))
+            return st;
+        if (mgemm_status_t st = hip_status(launch_reduce_splits((const float *)workspace, D, a.M, a.N, a.N,
+                                                                w.split_stride, plan->splits, d.ldd, out, s),
+                                           "gemm_run reduce launch"))
+            return st;
+    } else if (a.tiles > 0) {
         DenseFn f = dense_fn(plan->tile, ak, bk, in, out);
         if (!f) {
             set_error("gemm_run: kernel missing for the planned variant");

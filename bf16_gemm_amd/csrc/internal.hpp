@@ -50,6 +50,10 @@ MGEMM_DECLARE_TU(64x256_f16)
 using EdgeFn = hipError_t (*)(const DenseArgs &, int a_kmajor, int b_kmajor, int n_first, hipStream_t);
 EdgeFn edge_fn(int in, int out);
 hipError_t launch_zero_fill(void *D, int rows, int cols, int64_t ld_bytes, int esize, hipStream_t s);
+// D[M x N] = sum over r < splits of W[r][M x N] (fp32, row pitch ldw, slabs
+// split_stride apart), added in increasing r and rounded once to D's type.
+hipError_t launch_reduce_splits(const float *W, void *D, int M, int N, int ldw, int64_t split_stride, int splits,
+                                int64_t ldd, int out, hipStream_t s);
 
 // One kernel launch of a grouped plan: experts whose row count lies in
 // [lo, hi) run with tile `tile` on `grid` workgroups.
@@ -75,6 +79,9 @@ struct mgemm_plan {
     int grid;
     int group_m;
     int xcd_remap;
+    int splits;      // K ranges per output tile; > 1 writes fp32 partials to the workspace
+    int kchunk;      // elements of K per range
+    size_t workspace_bytes;
     bool zero_fill;  // K == 0
     bool noop;       // M == 0 or N == 0
     // grouped

@@ -15,9 +15,13 @@ struct DenseArgs {
     void *D;
     int M, N, K;
     int lda, ldb, ldd;
-    int tiles_m, tiles_n, tiles;
+    int tiles_m, tiles_n;
+    int tiles;        // tasks: output tiles x splits
     int group_m;      // tile rows per L2 group (m fastest inside a group)
     int xcd_remap;    // 1: give each XCD a contiguous run of tiles
+    int splits;       // K ranges per output tile (1: the whole K)
+    int kchunk;       // elements of K per range, a multiple of 64
+    int64_t split_stride;  // elements of D between the partial results of consecutive ranges
 };
 
 struct GroupedArgs {
@@ -93,15 +97,21 @@ __global__ void __launch_bounds__(T::NT) dense_kernel(DenseArgs p)
     const uint16_t *B = (const uint16_t *)p.B;
     constexpr int esize = out_size(OUT);
     for (int t = L; t < p.tiles; t += grid) {
+        // task t: output tile t / splits, K range t % splits (consecutive
+        // tasks, which share an XCD, are the ranges of one tile)
+        const int tile_id = t / p.splits;
+        const int r = t - tile_id * p.splits;
         int mb, nb;
-        tile_coords(t, p.tiles_m, p.tiles_n, p.group_m, mb, nb);
+        tile_coords(tile_id, p.tiles_m, p.tiles_n, p.group_m, mb, nb);
         const int m0 = mb * T::BM, n0 = nb * T::BN;
-        const uint16_t *At = A_KMAJOR ? A + (int64_t)m0 * p.lda : A + m0;
-        const uint16_t *Bt = B_KMAJOR ? B + (int64_t)n0 * p.ldb : B + n0;
-        const OperandSrc sa = operand_src<A_KMAJOR>(At, p.lda, p.M - m0, p.K);
-        const OperandSrc sb = operand_src<B_KMAJOR>(Bt, p.ldb, p.N - n0, p.K);
-        tile.mainloop(lds, sa, p.lda, sb, p.ldb, p.K, opaque((int)threadIdx.x));
-        char *Dt = (char *)p.D + ((int64_t)m0 * p.ldd + n0) * esize;
+        const int k0 = r * p.kchunk;
+        const int klen = min(p.kchunk, p.K - k0);
+        const uint16_t *At = A_KMAJOR ? A + (int64_t)m0 * p.lda + k0 : A + (int64_t)k0 * p.lda + m0;
+        const uint16_t *Bt = B_KMAJOR ? B + (int64_t)n0 * p.ldb + k0 : B + (int64_t)k0 * p.ldb + n0;
+        const OperandSrc sa = operand_src<A_KMAJOR>(At, p.lda, p.M - m0, klen);
+        const OperandSrc sb = operand_src<B_KMAJOR>(Bt, p.ldb, p.N - n0, klen);
+        tile.mainloop(lds, sa, p.lda, sb, p.ldb, klen, opaque((int)threadIdx.x));
+        char *Dt = (char *)p.D + ((int64_t)r * p.split_stride + (int64_t)m0 * p.ldd + n0) * esize;
         epilogue<T, EPI_NONE, OUT>(tile, Dt, p.ldd, min(T::BM, p.M - m0), min(T::BN, p.N - n0),
                                    opaque((int)threadIdx.x));
     }

@@ -97,6 +97,24 @@ static double tile_cost(const TileShape &t, int64_t M, int64_t N, int64_t K, int
     return per_cu * std::max(mfma_clk, load_clk);
 }
 
+// Time model (microseconds) for the split-K decision, fitted to measured
+// small-M runs on MI355X: a task (one K range of one output tile) streams
+// its operand rows at about 24 B per clock per CU (2.1 GHz) plus ~2.5 us of
+// prologue and epilogue; the busiest CU runs ceil(tasks / CUs) tasks.  A
+// split adds a second launch (~3 us) and its fp32 partials, written once and
+// read once at ~4 TB/s.
+static double task_model_us(const TileShape &t, int64_t M, int64_t N, int64_t K, int splits, int cus)
+{
+    const int64_t tasks = cdiv(M, t.bm) * cdiv(N, t.bn) * splits;
+    const double per_cu = (double)cdiv(tasks, cus);
+    const double kr = (double)std::max<int64_t>(cdiv(K, splits), 64);
+    const double rows = (double)(std::min<int64_t>(t.bm, M) + std::min<int64_t>(t.bn, N));
+    double us = per_cu * (rows * 2.0 * kr / (24.0 * 2100.0) + 2.5);
+    if (splits > 1)
+        us += 3.0 + 2.0 * (double)splits * (double)M * (double)N * 4.0 / 4.0e6;
+    return us;
+}
+
 static bool is_in_type(mgemm_dtype_t t) { return t == MGEMM_F16 || t == MGEMM_BF16; }
 static bool is_out_type(mgemm_dtype_t t) { return t == MGEMM_F16 || t == MGEMM_BF16 || t == MGEMM_F32; }
 static bool is_layout(mgemm_layout_t l) { return l == MGEMM_ROW_MAJOR || l == MGEMM_COL_MAJOR; }
@@ -198,14 +216,57 @@ static mgemm_status_t plan_dense(const mgemm_desc_t *d, uint32_t flags, mgemm_pl
         set_error("no kernel compiled for this layout/dtype combination");
         return MGEMM_ERR_UNSUPPORTED;
     }
-    const TileShape &ts = kTiles[tile];
     const int64_t n_main = d->N & ~(int64_t)3;
+    const int64_t ksteps = cdiv(d->K, kBK);
+    const int forced_splits = (int)((flags >> 16) & 0xFF);
+    if (forced_splits > 64) {
+        set_error("split count must lie in [1, 64] (got %d)", forced_splits);
+        return MGEMM_ERR_INVALID_ARG;
+    }
+    int splits = 1;
+    if (forced_splits > 0) {
+        splits = (int)std::min<int64_t>(forced_splits, std::max<int64_t>(ksteps, 1));
+    } else if (forced_tile(flags) < 0 && n_main > 0 && d->M > 0) {
+        // Split K when the chosen tiles leave most compute units idle: the
+        // tile and range count with the lowest modelled time wins if it beats
+        // the unsplit plan by 10 %.
+        const int64_t tl0 = cdiv(d->M, kTiles[tile].bm) * cdiv(n_main, kTiles[tile].bn);
+        if (tl0 * 2 <= p->num_cus && ksteps >= 8) {
+            double best = 0.9 * task_model_us(kTiles[tile], d->M, n_main, d->K, 1, p->num_cus);
+            for (int t = 0; t < NUM_TILES; ++t) {
+                if (!dense_fn(t, ak, bk, in, OUT_F32))
+                    continue;
+                const int64_t tl = cdiv(d->M, kTiles[t].bm) * cdiv(n_main, kTiles[t].bn);
+                for (int sp = 2; sp <= 16; sp *= 2) {
+                    const int64_t steps = cdiv(ksteps, sp);
+                    if (steps < 4 || tl * sp > 2 * (int64_t)p->num_cus)
+                        break;
+                    const int real = (int)cdiv(ksteps, steps);
+                    const double c = task_model_us(kTiles[t], d->M, n_main, d->K, real, p->num_cus);
+                    if (c < best) {
+                        best = c;
+                        tile = t;
+                        splits = real;
+                    }
+                }
+            }
+        }
+    }
+    const TileShape &ts = kTiles[tile];
     p->tile = tile;
     p->tiles_m = cdiv(d->M, ts.bm);
     p->tiles_n = cdiv(n_main, ts.bn);
     p->tiles = p->tiles_m * p->tiles_n;
+    p->kchunk = (int)(cdiv(ksteps, splits) * kBK);
+    p->splits = splits > 1 ? (int)cdiv(d->K, p->kchunk) : 1;
+    if (p->splits > 1 && !dense_fn(tile, ak, bk, in, OUT_F32)) {
+        set_error("split-K needs the fp32-output kernel of tile %s, which is not compiled", tile_name(tile));
+        return MGEMM_ERR_UNSUPPORTED;
+    }
+    p->workspace_bytes = p->splits > 1 ? (size_t)p->splits * (size_t)d->M * (size_t)n_main * 4u : 0;
+    const int64_t tasks = p->tiles * p->splits;
     const int64_t slots = (int64_t)p->num_cus * ts.occupancy;
-    p->grid = (int)std::max<int64_t>(1, std::min<int64_t>(p->tiles, slots));
+    p->grid = (int)std::max<int64_t>(1, std::min<int64_t>(tasks, slots));
     // Tiles are issued in groups of group_m tile rows, m fastest; with the XCD
     // remap each XCD takes a run of consecutive tiles, so group_m sets the
     // shape of the tile block that shares one XCD's L2.  Four rows measured
@@ -214,12 +275,12 @@ static mgemm_status_t plan_dense(const mgemm_desc_t *d, uint32_t flags, mgemm_pl
     p->xcd_remap = (flags & MGEMM_PLAN_NO_XCD_REMAP) ? 0 : (p->grid % 8 == 0 ? 1 : 0);
     char buf[256];
     snprintf(buf, sizeof buf,
-             "dense M=%lld N=%lld K=%lld %s%s->%s tile=%s waves=%dx%d bk=64 stages=2 tiles=%lld grid=%d "
-             "group_m=%d xcd_remap=%d edge_cols=%lld",
+             "dense M=%lld N=%lld K=%lld %s%s->%s tile=%s waves=%dx%d bk=64 stages=2 tiles=%lld splits=%d "
+             "grid=%d group_m=%d xcd_remap=%d edge_cols=%lld",
              (long long)d->M, (long long)d->N, (long long)d->K, d->a_type == MGEMM_BF16 ? "bf16" : "f16",
              ak ? (bk ? " NT" : " NN") : (bk ? " TT" : " TN"),
              d->d_type == MGEMM_F32 ? "f32" : (d->d_type == MGEMM_BF16 ? "bf16" : "f16"), tile_name(tile), ts.wm,
-             ts.wn, (long long)p->tiles, p->grid, p->group_m, p->xcd_remap, (long long)(d->N - n_main));
+             ts.wn, (long long)p->tiles, p->splits, p->grid, p->group_m, p->xcd_remap, (long long)(d->N - n_main));
     p->description = buf;
     return MGEMM_OK;
 }
@@ -400,7 +461,7 @@ extern "C" mgemm_status_t gemm_plan_workspace_size(mgemm_plan_t plan, size_t *by
         set_error("gemm_plan_workspace_size: null argument");
         return MGEMM_ERR_INVALID_ARG;
     }
-    *bytes = 0;
+    *bytes = plan->kind == PLAN_DENSE ? plan->workspace_bytes : 0;
     return MGEMM_OK;
 }
 
@@ -444,6 +505,7 @@ extern "C" mgemm_status_t gemm_plan_info(mgemm_plan_t plan, mgemm_plan_info_t *i
     info->group_m = plan->group_m;
     info->xcd_remap = plan->xcd_remap;
     info->num_cus = plan->num_cus;
+    info->splits = plan->kind == PLAN_DENSE ? plan->splits : 1;
     return MGEMM_OK;
 }
 

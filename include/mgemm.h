@@ -111,6 +111,15 @@ typedef struct {
 #define MGEMM_PLAN_FORCE_TILE_32x256  0x4u   /* narrow-M (few tokens)   */
 #define MGEMM_PLAN_FORCE_TILE_64x256  0x8u   /* narrow-M (few tokens)   */
 #define MGEMM_PLAN_NO_XCD_REMAP       0x100u /* plain tile order        */
+/* Dense plans: fix the number of K ranges per output tile (1..64; 1 turns
+ * splitting off).  Without it the planner splits K only when the output
+ * tiles alone leave compute units idle and K is long, and charges the
+ * reduction to the split ("B200 的 2CTA 怎样调优", section 八: for small M/N
+ * with a long K, split-K raises task parallelism at the cost of a
+ * reduction).  A split plan writes fp32 partial sums to the workspace
+ * (gemm_plan_workspace_size) and adds them in a fixed order, so results are
+ * reproducible run to run. */
+#define MGEMM_PLAN_SPLIT_K(n)         ((((uint32_t)(n)) & 0xFFu) << 16)
 
 /* Make a plan for a dense problem on the current HIP device (or, when no
  * device is visible, for a 256-CU gfx950).  *out receives the plan; free it
@@ -120,11 +129,16 @@ mgemm_status_t gemm_plan(const mgemm_desc_t *desc, uint32_t flags, mgemm_plan_t 
 /* Make a plan for a grouped problem (same conventions). */
 mgemm_status_t grouped_gemm_plan(const mgemm_grouped_desc_t *desc, uint32_t flags, mgemm_plan_t *out);
 
-/* Device workspace in bytes that run calls with this plan need (may be 0). */
+/* Device workspace in bytes that run calls with this plan need (may be 0):
+ * splits * M * (N rounded down to a multiple of 4) * 4 for a split dense
+ * plan, else 0.  The workspace is scratch owned by the caller; it must be
+ * 16-byte aligned, and two runs in flight at once must not share it. */
 mgemm_status_t gemm_plan_workspace_size(mgemm_plan_t plan, size_t *bytes);
 
 /* Enqueue D = A x B on `stream`.  A, B, D are device pointers in the layouts
- * of the plan's descriptor.  workspace may be NULL when the plan needs none. */
+ * of the plan's descriptor.  workspace may be NULL when the plan needs none;
+ * a split plan returns MGEMM_ERR_WORKSPACE (and launches nothing) when it is
+ * missing, misaligned or smaller than gemm_plan_workspace_size. */
 mgemm_status_t gemm_run(mgemm_plan_t plan, const void *A, const void *B, void *D,
                         void *workspace, size_t workspace_bytes, mgemm_stream_t stream);
 
@@ -153,6 +167,7 @@ typedef struct {
     int32_t group_m;                     /* tile rows per L2 group            */
     int32_t xcd_remap;                   /* 1 if the XCD-aware order is used  */
     int32_t num_cus;                     /* compute units planned for         */
+    int32_t splits;                      /* K ranges per output tile (dense)  */
 } mgemm_plan_info_t;
 
 mgemm_status_t gemm_plan_info(mgemm_plan_t plan, mgemm_plan_info_t *info);

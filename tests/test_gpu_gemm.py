@@ -43,7 +43,7 @@ def pad8(x: np.ndarray) -> np.ndarray:
 
 
 def run_dense(a_bits, b_bits, M, N, K, in_t, out_t, a_layout="row", b_layout="row", flags=0, ldd=None,
-              sentinel=False, stream=None):
+              sentinel=False, stream=None, workspace_fill=None):
     """Run the library on host bit arrays; returns (D bits [M][N], plan).
 
     With ``sentinel`` the output lives in a byte buffer pre-filled with 0xFF
@@ -59,7 +59,10 @@ def run_dense(a_bits, b_bits, M, N, K, in_t, out_t, a_layout="row", b_layout="ro
     D = raw[: M * ldd * es].view(TORCH_OUT[out_t]).view(M, ldd)
     plan = mg.gemm_plan(M, N, K, in_t, d_type=out_t, a_layout=a_layout, b_layout=b_layout,
                         lda=a_bits.shape[1], ldb=b_bits.shape[1], ldd=ldd, flags=flags)
-    mg.gemm_run(plan, A, B, D, stream=stream)
+    ws = mg.workspace_for(plan)
+    if ws is not None and workspace_fill is not None:
+        ws.fill_(workspace_fill)   # stale scratch contents must not matter
+    mg.gemm_run(plan, A, B, D, workspace=ws, stream=stream)
     torch.cuda.synchronize()
     if sentinel:
         tail = raw[M * ldd * es:].cpu().numpy()
@@ -183,6 +186,63 @@ def test_run_errors():
     D = torch.zeros(64 * 64, dtype=torch.float32, device="cuda")
     st = mg.lib.gemm_run(plan.handle, A.data_ptr() + 2, A.data_ptr(), D.data_ptr(), None, 0, None)
     assert st == mg.ERR_UNSUPPORTED
+
+
+# ------------------------------------------------------------------ split-K
+
+
+@pytest.mark.parametrize("in_t,out_t", [("bf16", "bf16"), ("f16", "f32")])
+@pytest.mark.parametrize("al,bl", LAYOUTS)
+@pytest.mark.parametrize("tile", ["256", "128", "32n", "64n"])
+def test_split_k_random_and_integer(in_t, out_t, al, bl, tile):
+    """K split into ranges whose fp32 partial tiles are added by the
+    reduction: ragged M, N (two edge columns) and K (a short last step)."""
+    if tile in ("32n", "64n") and al == "col":
+        pytest.skip("narrow-M tiles take a k-contiguous A only")
+    M, N, K = 150, 302, 1000
+    cfg = datagen.GemmConfig("t", M, N, K, in_t, out_t, al, bl, ("uniform", 1.0), ("normal", 1.0), seed=17,
+                             int_seed=18)
+    for S in (2, 3, 7):
+        log(f"case split-K tile={tile} S={S} {in_t}->{out_t} {al}/{bl} M={M} N={N} K={K}")
+        flags = TILES[tile] | mg.PLAN_SPLIT_K(S)
+        a, b = datagen.gemm_inputs(cfg, "random")
+        got, plan = run_dense(a, b, M, N, K, in_t, out_t, al, bl, flags, sentinel=True, workspace_fill=0xFF)
+        assert plan.info().splits > 1, plan.describe()
+        assert_close(got, oracle.gemm_ref(a, b, in_t, in_t, al, bl), K, out_t, plan.describe())
+        a, b = datagen.gemm_inputs(cfg, "int")
+        got, plan = run_dense(a, b, M, N, K, in_t, out_t, al, bl, flags)
+        assert_bits_equal(got, oracle.gemm_ref(a, b, in_t, in_t, al, bl), out_t, plan.describe())
+
+
+def test_split_k_workspace_checked_before_launch():
+    log("case split-K workspace errors")
+    plan = mg.gemm_plan(64, 256, 1024, "bf16", d_type="bf16", flags=mg.PLAN_SPLIT_K(4))
+    need = plan.workspace_size()
+    assert need == 4 * 64 * 256 * 4
+    A = torch.zeros((64, 1024), dtype=torch.bfloat16, device="cuda")
+    B = torch.zeros((1024, 256), dtype=torch.bfloat16, device="cuda")
+    D = torch.full((64, 256), -1.0, dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(need + 64, dtype=torch.uint8, device="cuda")
+    h, a, b, d = plan.handle, A.data_ptr(), B.data_ptr(), D.data_ptr()
+    assert mg.lib.gemm_run(h, a, b, d, None, 0, None) == mg.ERR_WORKSPACE
+    assert mg.lib.gemm_run(h, a, b, d, ws.data_ptr(), need - 1, None) == mg.ERR_WORKSPACE
+    assert mg.lib.gemm_run(h, a, b, d, ws.data_ptr() + 8, need, None) == mg.ERR_WORKSPACE
+    assert b"workspace" in mg.lib.gemm_last_error_message()
+    torch.cuda.synchronize()
+    assert torch.all(D == -1.0)        # nothing was launched
+    mg.gemm_run(plan, A, B, D, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.all(D == 0.0)
+
+
+def test_split_k_deterministic():
+    log("case split-K determinism")
+    M, N, K = 128, 1024, 4096
+    cfg = datagen.GemmConfig("t", M, N, K, "bf16", "bf16", seed=21, int_seed=22)
+    a, b = datagen.gemm_inputs(cfg, "random")
+    g1, p1 = run_dense(a, b, M, N, K, "bf16", "bf16", flags=mg.PLAN_SPLIT_K(8), workspace_fill=0)
+    g2, _ = run_dense(a, b, M, N, K, "bf16", "bf16", flags=mg.PLAN_SPLIT_K(8), workspace_fill=0x7F)
+    assert p1.info().splits == 8 and np.array_equal(g1, g2)
 
 
 # --------------------------------------------------------------- full size

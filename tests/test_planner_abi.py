@@ -79,10 +79,40 @@ def test_plan_choices_for_workloads():
     assert (i.block_m, i.block_n, i.block_k) == (256, 256, 64)
     assert i.tiles == 1024 and i.coverage == 1.0 and i.lds_bytes <= 160 * 1024
     assert i.grid == min(1024, i.num_cus)
+    # the decode shape: 128 rows cannot fill the chip with output tiles, so
+    # K is split (each range a task) instead of narrowing the tile further
     p = mg.gemm_plan(128, 7168, 2048, "bf16", d_type="bf16")
-    assert p.info().block_m <= 64, p.describe()   # narrow-M tile for the decode shape
+    i = p.info()
+    assert i.block_m <= 128 and i.splits > 1 and i.tiles * i.splits <= 2 * i.num_cus, p.describe()
+    p = mg.gemm_plan(128, 7168, 2048, "bf16", d_type="bf16", flags=mg.PLAN_SPLIT_K(1))
+    assert p.info().block_m <= 64 and p.info().splits == 1, p.describe()   # narrow-M tile when unsplit
     p = mg.grouped_gemm_plan(64, 32768, 4096, 7168, epilogue=mg.EPI_SILU_GATE_I8)
     assert "32x256" in p.describe() and "256x256" in p.describe()
+
+
+def test_split_k_plans():
+    # whole-chip shapes are never split and need no workspace
+    for (M, N, K) in [(8192, 8192, 8192), (4096, 4096, 4096), (16384, 2048, 7168), (512, 512, 512)]:
+        p = mg.gemm_plan(M, N, K, "bf16", d_type="bf16")
+        assert p.info().splits == 1 and p.workspace_size() == 0 and "splits=1" in p.describe(), p.describe()
+    # a split plan needs splits partial slabs of M x (N rounded down to 4) fp32
+    p = mg.gemm_plan(128, 7170, 2048, "bf16", d_type="bf16", ldb=7176, ldd=7176)
+    i = p.info()
+    assert i.splits > 1 and f"splits={i.splits}" in p.describe()
+    assert p.workspace_size() == i.splits * 128 * 7168 * 4
+    # forced counts: K = 2048 is 32 steps; 3 ranges of 11 steps
+    p = mg.gemm_plan(128, 7168, 2048, "bf16", d_type="bf16", flags=mg.PLAN_SPLIT_K(3))
+    assert p.info().splits == 3 and p.workspace_size() == 3 * 128 * 7168 * 4
+    p = mg.gemm_plan(64, 64, 128, "bf16", d_type="f32", flags=mg.PLAN_SPLIT_K(16))
+    assert p.info().splits == 2   # never more ranges than K steps
+    p = mg.gemm_plan(8192, 8192, 8192, "bf16", flags=mg.PLAN_SPLIT_K(2) | mg.PLAN_FORCE_TILE_256x256)
+    assert p.info().splits == 2 and p.workspace_size() == 2 * 8192 * 8192 * 4
+    with pytest.raises(mg.MgemmError) as e:
+        mg.gemm_plan(128, 7168, 2048, "bf16", flags=mg.PLAN_SPLIT_K(65))
+    assert e.value.status == mg.ERR_INVALID_ARG
+    # K == 0 and empty shapes: nothing to split
+    assert mg.gemm_plan(4, 8, 0, "bf16", lda=8, flags=mg.PLAN_SPLIT_K(4)).workspace_size() == 0
+    assert mg.gemm_plan(0, 8, 64, "bf16", flags=mg.PLAN_SPLIT_K(4)).workspace_size() == 0
 
 
 def test_lds_budget_rejects_three_stage_macro_tile():
