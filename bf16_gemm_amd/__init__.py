@@ -25,6 +25,7 @@ PLAN_FORCE_TILE_256x256 = 0x1
 PLAN_FORCE_TILE_128x128 = 0x2
 PLAN_FORCE_TILE_32x256 = 0x4
 PLAN_FORCE_TILE_64x256 = 0x8
+PLAN_FORCE_TILE_256x256_DTL = 0x10
 PLAN_NO_XCD_REMAP = 0x100
 
 

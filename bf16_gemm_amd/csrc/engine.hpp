@@ -23,6 +23,8 @@
 //     overlap that "从 CUDA 代码到 GPU 执行" (Warp Specialization section)
 //     and "使用 Warp Specialization 和 Cluster 扩展 GEMM" (step 7) obtain with
 //     separate roles, obtained here inside every wave;
+//   * for 256 x 256 tiles whose operands are both k-contiguous, DtlTile
+//     replaces the register staging with loads that write LDS directly;
 //   * the MFMA is v_mfma_f32_32x32x16_{bf16,f16}; the B-tile fragment is
 //     passed as the instruction's first operand and the A-tile fragment as
 //     the second, so each lane's accumulator registers hold four consecutive
@@ -499,6 +501,213 @@ struct Tile {
         mfmas(f1);
         sched_pattern<0, FM * FN, NEXT ? FM + FN : 0, 0, 0>();
         __builtin_amdgcn_sched_barrier(0);
+    }
+};
+
+// ---------------------------------------------------------------------------
+// Direct-to-LDS tile: 256 x 256, both operands k-contiguous.
+//
+// Global loads write LDS themselves (buffer_load ... lds: each lane's 16
+// bytes land at M0 + 16 * lane), so no staging registers and no LDS-write
+// instructions are involved -- the role the asynchronous tensor copy plays
+// on the pages' hardware ("B200 的 2CTA 怎样调优", sections 四-五: the copy
+// engine fills later K segments while the matrix unit works on the current
+// one, and an issued copy is not yet usable data).  On gfx950 the LDS write
+// path of ds_write_b128 is the busiest resource of the register-staged
+// loop; this variant takes it out.
+//
+// LDS (160 KiB): a three-slot ring for A and a two-slot ring for B, 32 KiB
+// per operand step (256 rows x 128 bytes, chunks swizzled as in Tile).
+// During step k the B rows of step k+1 and the A rows of step k+2 are
+// fetched into slots freed by the barrier that ended step k-1, so A has two
+// steps to arrive and B one.  The wait before each barrier names exactly the
+// loads that must have landed: everything but this step's A loads.
+//
+// One load instruction covers 8 rows x 128 bytes = 1 KiB of LDS, which is
+// contiguous, so the swizzle is applied on the global side: lane l of row
+// group g fetches logical chunk (l & 7) ^ swz(row) of row 8g + (l >> 3).
+// Row and chunk offsets are per-lane VGPR offsets (range-checked against the
+// resource, so rows past M or N read as zero); the LDS address is uniform.
+template <int n>
+__device__ __forceinline__ void wait_vm()
+{
+    // s_waitcnt with vmcnt = n (bits 3:0 and 15:14), expcnt and lgkmcnt not waited
+    __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+template <int IN>
+struct DtlTile {
+    static constexpr int BM = 256, BN = 256, WM = 2, WN = 2;
+    static constexpr int NT = 256;
+    static constexpr int TM = 128, TN = 128, FM = 4, FN = 4;
+    static constexpr int OPS = 256 * kRowBytes;              // one operand, one K step
+    static constexpr int A_SLOTS = 3, B_SLOTS = 2;
+    static constexpr int LDS_BYTES = (A_SLOTS + B_SLOTS) * OPS;
+
+    f32x16_t acc[FM][FN];
+    struct Frags {
+        u32x4_t a[FM], b[FN];
+    };
+
+    // per lane: byte offset (within a step) of its chunk in row group j of
+    // its wave's 64-row band, and the k of that chunk
+    uint32_t va[8], vb[8];
+    int kc[8];
+
+    __device__ __forceinline__ void setup(int lane, int wave, int lda, int ldb)
+    {
+        const int r = lane >> 3;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int row = wave * 64 + j * 8 + r;
+            const int c = (lane & 7) ^ swz(row);
+            kc[j] = c * 8;
+            va[j] = (uint32_t)row * (uint32_t)lda * 2u + (uint32_t)c * 16u;
+            vb[j] = (uint32_t)row * (uint32_t)ldb * 2u + (uint32_t)c * 16u;
+        }
+    }
+    // row group j of one operand's step into `slot`; k_left = k remaining
+    // from the step's first k (chunks at or past it read as zero)
+    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, const uint32_t (&v)[8], char *slot, int wave, int j,
+                                         int k_left) const
+    {
+        const uint32_t off = kc[j] < k_left ? v[j] : kOOB;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)(slot + wave * 8192 + j * 1024), 16, off, 0, 0, 0);
+    }
+
+    template <int KS>
+    __device__ __forceinline__ void read_frags(const char *as, const char *bs, const int (&abase)[4],
+                                               const int (&bbase)[4], Frags &f) const
+    {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+            f.a[i] = *(const u32x4_t *)(as + abase[KS ^ ((i & 1) * 2)] + i * 32 * kRowBytes);
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+            f.b[j] = *(const u32x4_t *)(bs + bbase[KS ^ ((j & 1) * 2)] + j * 32 * kRowBytes);
+    }
+    __device__ __forceinline__ void mfmas(const Frags &f)
+    {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+                acc[i][j] = mfma32<IN>(f.b[j], f.a[i], acc[i][j]);
+    }
+    // 16 MFMAs; the first 8 each followed by a fragment read (NR of them),
+    // NV loads spread evenly after them
+    template <int I, int NR, int NV>
+    static __device__ __forceinline__ void pattern()
+    {
+        if constexpr (I < 16) {
+            __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+            if constexpr (I < NR)
+                __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 1, 0);
+            if constexpr (NV > 0 && I % (16 / (NV > 0 ? NV : 1)) == 0 && I / (16 / (NV > 0 ? NV : 1)) < NV)
+                __builtin_amdgcn_sched_group_barrier(SG_VMEM_READ, 1, 0);
+            pattern<I + 1, NR, NV>();
+        }
+    }
+
+    __device__ __forceinline__ void mainloop(char *lds, const OperandSrc &sa, int lda, const OperandSrc &sb, int ldb,
+                                             int K, int tid)
+    {
+        const int lane = tid & 63;
+        const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+        const int wm0 = (wave / WN) * TM, wn0 = (wave % WN) * TN;
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+                acc[i][j] = f32x16_t{};
+        const int ksteps = (K + kBK - 1) / kBK;
+        if (ksteps <= 0)
+            return;
+        setup(lane, wave, lda, ldb);
+        char *const A0 = lds;
+        char *const B0 = lds + A_SLOTS * OPS;
+        const int frow = lane & 31, fk = lane >> 5;
+        int abase[4], bbase[4];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            const int ra = wm0 + frow, rb = wn0 + frow;
+            abase[ks] = ra * kRowBytes + (((2 * ks + fk) ^ swz(ra)) << 4);
+            bbase[ks] = rb * kRowBytes + (((2 * ks + fk) ^ swz(rb)) << 4);
+        }
+        // steps past the end load from an empty range (zeros, no memory access)
+        auto rsrc = [&](const OperandSrc &s, int st) { return st < ksteps ? s.at_step(st) : make_rsrc(s.base, 0); };
+
+        // prologue: A(0), B(0), A(1); wait for the first two
+        {
+            const auto ra0 = rsrc(sa, 0), rb0 = rsrc(sb, 0), ra1 = rsrc(sa, 1);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                load(ra0, va, A0, wave, j, K);
+                load(rb0, vb, B0, wave, j, K);
+            }
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                load(ra1, va, A0 + OPS, wave, j, K - kBK);
+            wait_vm<8>();
+        }
+        lds_barrier();
+        Frags f0, f1;
+        read_frags<0>(A0, B0, abase, bbase, f0);
+        int sa_cur = 0, sa_next = 1, sa_fill = 2;   // A slots of steps kt, kt+1, kt+2
+        for (int kt = 0; kt < ksteps; ++kt) {
+            const char *ac = A0 + sa_cur * OPS;
+            const char *bc = B0 + (kt & 1) * OPS;
+            char *an = A0 + sa_next * OPS;
+            char *bn = B0 + ((kt + 1) & 1) * OPS;
+            char *aw = A0 + sa_fill * OPS;
+            const auto rB = rsrc(sb, kt + 1);
+            const auto rA = rsrc(sa, kt + 2);
+            const int kb = K - (kt + 1) * kBK, ka = K - (kt + 2) * kBK;
+            // sub-step 0: half of B(kt+1)
+            read_frags<1>(ac, bc, abase, bbase, f1);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                load(rB, vb, bn, wave, j, kb);
+            mfmas(f0);
+            pattern<0, FM + FN, 4>();
+            __builtin_amdgcn_sched_barrier(0);
+            // sub-step 1: the rest of B(kt+1)
+            read_frags<2>(ac, bc, abase, bbase, f0);
+#pragma unroll
+            for (int j = 4; j < 8; ++j)
+                load(rB, vb, bn, wave, j, kb);
+            mfmas(f1);
+            pattern<0, FM + FN, 4>();
+            __builtin_amdgcn_sched_barrier(0);
+            // sub-step 2: half of A(kt+2)
+            read_frags<3>(ac, bc, abase, bbase, f1);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                load(rA, va, aw, wave, j, ka);
+            mfmas(f0);
+            pattern<0, FM + FN, 4>();
+            __builtin_amdgcn_sched_barrier(0);
+            // sub-step 3: step kt+1 must be in LDS (only this step's four
+            // A loads may still be in flight), and every wave must be done
+            // with step kt before its slots are refilled
+            wait_vm<4>();
+            lds_barrier();
+            read_frags<0>(an, bn, abase, bbase, f0);
+#pragma unroll
+            for (int j = 4; j < 8; ++j)
+                load(rA, va, aw, wave, j, ka);
+            mfmas(f1);
+            pattern<0, FM + FN, 4>();
+            __builtin_amdgcn_sched_barrier(0);
+            const int t = sa_cur;
+            sa_cur = sa_next;
+            sa_next = sa_fill;
+            sa_fill = t;
+        }
+        // nothing may still be writing LDS when the next tile starts
+        wait_vm<0>();
     }
 };
 

@@ -17,7 +17,14 @@ using DenseFn = hipError_t (*)(const DenseArgs &, int grid, hipStream_t);
 using GroupedFn = hipError_t (*)(const GroupedArgs &, int grid, hipStream_t);
 
 // Macro-tile variants compiled into the library.
-enum TileId { TILE_256x256 = 0, TILE_128x128 = 1, TILE_32x256 = 2, TILE_64x256 = 3, NUM_TILES = 4 };
+enum TileId {
+    TILE_256x256 = 0,
+    TILE_128x128 = 1,
+    TILE_32x256 = 2,
+    TILE_64x256 = 3,
+    TILE_256x256_DTL = 4,  // 256 x 256 with direct-to-LDS loads (k-contiguous A and B only)
+    NUM_TILES = 5
+};
 
 struct TileShape {
     int bm, bn, wm, wn;
@@ -25,6 +32,7 @@ struct TileShape {
     int occupancy;   // workgroups per CU the planner assumes
     double eff;      // relative MFMA efficiency the planner assumes
     bool narrow;     // narrow-M (few tokens) shape: needs a k-contiguous A
+    bool forced_only;  // never chosen by the planner, only by a FORCE_TILE flag
 };
 
 const TileShape &tile_shape(int tile);
@@ -46,6 +54,8 @@ MGEMM_DECLARE_TU(32x256_f16)
 MGEMM_DECLARE_TU(64x256_bf16)
 MGEMM_DECLARE_TU(64x256_f16)
 #undef MGEMM_DECLARE_TU
+DenseFn dense_fn_256x256dtl_bf16(bool ak, bool bk, int out);
+DenseFn dense_fn_256x256dtl_f16(bool ak, bool bk, int out);
 
 using EdgeFn = hipError_t (*)(const DenseArgs &, int a_kmajor, int b_kmajor, int n_first, hipStream_t);
 EdgeFn edge_fn(int in, int out);

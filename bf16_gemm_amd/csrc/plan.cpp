@@ -21,17 +21,18 @@ void set_error(const char *fmt, ...);
 
 // eff: relative MFMA efficiency the cost model assumes for the shape.
 static const TileShape kTiles[NUM_TILES] = {
-    /* 256x256 */ {256, 256, 2, 2, 2 * (256 + 256) * 128, 1, 1.00, false},
-    /* 128x128 */ {128, 128, 2, 2, 2 * (128 + 128) * 128, 2, 0.80, false},
-    /* 32x256  */ {32, 256, 1, 4, 2 * (32 + 256) * 128, 2, 0.55, true},
-    /* 64x256  */ {64, 256, 1, 4, 2 * (64 + 256) * 128, 1, 0.70, true},
+    /* 256x256    */ {256, 256, 2, 2, 2 * (256 + 256) * 128, 1, 1.00, false, false},
+    /* 128x128    */ {128, 128, 2, 2, 2 * (128 + 128) * 128, 2, 0.80, false, false},
+    /* 32x256     */ {32, 256, 1, 4, 2 * (32 + 256) * 128, 2, 0.55, true, false},
+    /* 64x256     */ {64, 256, 1, 4, 2 * (64 + 256) * 128, 1, 0.70, true, false},
+    /* 256x256dtl */ {256, 256, 2, 2, (3 + 2) * 256 * 128, 1, 1.00, false, true},
 };
 
 const TileShape &tile_shape(int tile) { return kTiles[tile]; }
 
 static const char *tile_name(int tile)
 {
-    static const char *n[NUM_TILES] = {"256x256", "128x128", "32x256", "64x256"};
+    static const char *n[NUM_TILES] = {"256x256", "128x128", "32x256", "64x256", "256x256dtl"};
     return n[tile];
 }
 
@@ -43,6 +44,7 @@ DenseFn dense_fn(int tile, bool ak, bool bk, int in, int out)
     case TILE_128x128: return bf ? dense_fn_128x128_bf16(ak, bk, out) : dense_fn_128x128_f16(ak, bk, out);
     case TILE_32x256: return bf ? dense_fn_32x256_bf16(ak, bk, out) : dense_fn_32x256_f16(ak, bk, out);
     case TILE_64x256: return bf ? dense_fn_64x256_bf16(ak, bk, out) : dense_fn_64x256_f16(ak, bk, out);
+    case TILE_256x256_DTL: return bf ? dense_fn_256x256dtl_bf16(ak, bk, out) : dense_fn_256x256dtl_f16(ak, bk, out);
     default: return nullptr;
     }
 }
@@ -145,6 +147,7 @@ static int forced_tile(uint32_t flags)
     if (flags & MGEMM_PLAN_FORCE_TILE_128x128) return TILE_128x128;
     if (flags & MGEMM_PLAN_FORCE_TILE_32x256) return TILE_32x256;
     if (flags & MGEMM_PLAN_FORCE_TILE_64x256) return TILE_64x256;
+    if (flags & MGEMM_PLAN_FORCE_TILE_256x256_DTL) return TILE_256x256_DTL;
     return -1;
 }
 
@@ -203,7 +206,7 @@ static mgemm_status_t plan_dense(const mgemm_desc_t *d, uint32_t flags, mgemm_pl
     } else {
         double best = 0;
         for (int t = 0; t < NUM_TILES; ++t) {
-            if (!dense_fn(t, ak, bk, in, out))
+            if (kTiles[t].forced_only || !dense_fn(t, ak, bk, in, out))
                 continue;
             const double c = tile_cost(kTiles[t], d->M, d->N & ~(int64_t)3, d->K, p->num_cus);
             if (tile < 0 || c < best * 0.999) {
@@ -234,7 +237,7 @@ static mgemm_status_t plan_dense(const mgemm_desc_t *d, uint32_t flags, mgemm_pl
         if (tl0 * 2 <= p->num_cus && ksteps >= 8) {
             double best = 0.9 * task_model_us(kTiles[tile], d->M, n_main, d->K, 1, p->num_cus);
             for (int t = 0; t < NUM_TILES; ++t) {
-                if (!dense_fn(t, ak, bk, in, OUT_F32))
+                if (kTiles[t].forced_only || !dense_fn(t, ak, bk, in, OUT_F32))
                     continue;
                 const int64_t tl = cdiv(d->M, kTiles[t].bm) * cdiv(n_main, kTiles[t].bn);
                 for (int sp = 2; sp <= 16; sp *= 2) {

@@ -7,12 +7,17 @@
 
 namespace mgemm {
 
+template <class T, bool AK, bool BK, int IN, int OUT>
+hipError_t launch_dense_tile(const DenseArgs &a, int grid, hipStream_t s)
+{
+    hipLaunchKernelGGL((dense_kernel<T, AK, BK, IN, OUT>), dim3(grid), dim3(T::NT), 0, s, a);
+    return hipGetLastError();
+}
+
 template <int BM, int BN, int WM, int WN, bool AK, bool BK, int IN, int OUT>
 hipError_t launch_dense(const DenseArgs &a, int grid, hipStream_t s)
 {
-    using T = Tile<BM, BN, WM, WN, AK, BK, IN>;
-    hipLaunchKernelGGL((dense_kernel<T, AK, BK, IN, OUT>), dim3(grid), dim3(T::NT), 0, s, a);
-    return hipGetLastError();
+    return launch_dense_tile<Tile<BM, BN, WM, WN, AK, BK, IN>, AK, BK, IN, OUT>(a, grid, s);
 }
 
 template <int BM, int BN, int WM, int WN, bool BK, int IN, int OUT, int EPI>
@@ -42,6 +47,16 @@ DenseFn dense_table(bool ak, bool bk, int out)
         return bk ? MG_D(false, true) : MG_D(false, false);
     return nullptr;
 #undef MG_D
+}
+
+// The direct-to-LDS 256 x 256 engine: k-contiguous A and B only.
+template <int IN>
+DenseFn dense_dtl_table(bool ak, bool bk, int out)
+{
+    if (!ak || !bk || (out != OUT_F32 && out != same16<IN>()))
+        return nullptr;
+    return out == OUT_F32 ? launch_dense_tile<DtlTile<IN>, true, true, IN, OUT_F32>
+                          : launch_dense_tile<DtlTile<IN>, true, true, IN, same16<IN>()>;
 }
 
 template <int BM, int BN, int WM, int WN, int IN>

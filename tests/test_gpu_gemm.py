@@ -22,7 +22,15 @@ mg = pytest.importorskip("bf16_gemm_amd")
 pytestmark = pytest.mark.gpu
 
 TILES = {"auto": 0, "256": mg.PLAN_FORCE_TILE_256x256, "128": mg.PLAN_FORCE_TILE_128x128,
-         "32n": mg.PLAN_FORCE_TILE_32x256, "64n": mg.PLAN_FORCE_TILE_64x256}
+         "32n": mg.PLAN_FORCE_TILE_32x256, "64n": mg.PLAN_FORCE_TILE_64x256,
+         "256d": mg.PLAN_FORCE_TILE_256x256_DTL}
+
+
+def tile_skip(tile, al, bl):
+    if tile in ("32n", "64n") and al == "col":
+        pytest.skip("narrow-M tiles take a k-contiguous A only")
+    if tile == "256d" and (al, bl) != ("row", "col"):
+        pytest.skip("the direct-to-LDS tile takes k-contiguous A and B only")
 
 
 def log(*a):
@@ -79,10 +87,9 @@ LAYOUTS = [("row", "row"), ("row", "col"), ("col", "row"), ("col", "col")]
 
 @pytest.mark.parametrize("in_t,out_t", COMBOS)
 @pytest.mark.parametrize("al,bl", LAYOUTS)
-@pytest.mark.parametrize("tile", ["256", "128", "32n", "64n"])
+@pytest.mark.parametrize("tile", ["256", "128", "32n", "64n", "256d"])
 def test_ragged_random_and_integer(in_t, out_t, al, bl, tile):
-    if tile in ("32n", "64n") and al == "col":
-        pytest.skip("narrow-M tiles take a k-contiguous A only")
+    tile_skip(tile, al, bl)
     M, N, K = 300, 520, 200   # several tiles, ragged in M, N and K
     log(f"case ragged tile={tile} {in_t}->{out_t} {al}/{bl} M={M} N={N} K={K}")
     cfg = datagen.GemmConfig("t", M, N, K, in_t, out_t, al, bl, ("uniform", 1.0), ("normal", 1.0), seed=7, int_seed=8)
@@ -193,12 +200,11 @@ def test_run_errors():
 
 @pytest.mark.parametrize("in_t,out_t", [("bf16", "bf16"), ("f16", "f32")])
 @pytest.mark.parametrize("al,bl", LAYOUTS)
-@pytest.mark.parametrize("tile", ["256", "128", "32n", "64n"])
+@pytest.mark.parametrize("tile", ["256", "128", "32n", "64n", "256d"])
 def test_split_k_random_and_integer(in_t, out_t, al, bl, tile):
     """K split into ranges whose fp32 partial tiles are added by the
     reduction: ragged M, N (two edge columns) and K (a short last step)."""
-    if tile in ("32n", "64n") and al == "col":
-        pytest.skip("narrow-M tiles take a k-contiguous A only")
+    tile_skip(tile, al, bl)
     M, N, K = 150, 302, 1000
     cfg = datagen.GemmConfig("t", M, N, K, in_t, out_t, al, bl, ("uniform", 1.0), ("normal", 1.0), seed=17,
                              int_seed=18)
@@ -250,16 +256,17 @@ def test_split_k_deterministic():
 FULL = ["gemm512_f16", "gemm4096_bf16", "gemm8192_bf16_bcol", "ts16384x2048x7168", "decode128x7168x2048"]
 
 
-@pytest.mark.parametrize("name", FULL)
+@pytest.mark.parametrize("name,flags", [(n, 0) for n in FULL] +
+                         [("gemm8192_bf16_bcol", mg.PLAN_FORCE_TILE_256x256_DTL)])
 @pytest.mark.parametrize("variant", ["random", "int"])
-def test_full_size_workloads(name, variant):
+def test_full_size_workloads(name, flags, variant):
     cfg = datagen.DENSE[name]
-    log(f"case full {name} {variant}")
+    log(f"case full {name} flags={flags:#x} {variant}")
     a, b = datagen.gemm_inputs(cfg, variant)
     A, B = to_dev(a, cfg.in_dtype), to_dev(b, cfg.in_dtype)
     D = torch.empty((cfg.M, cfg.N), dtype=TORCH_OUT[cfg.out_dtype], device="cuda")
     plan = mg.gemm_plan(cfg.M, cfg.N, cfg.K, cfg.in_dtype, d_type=cfg.out_dtype, a_layout=cfg.a_layout,
-                        b_layout=cfg.b_layout)
+                        b_layout=cfg.b_layout, flags=flags)
     mg.gemm_run(plan, A, B, D)
     torch.cuda.synchronize()
     got = from_dev_bits(D)

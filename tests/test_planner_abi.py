@@ -115,6 +115,21 @@ def test_split_k_plans():
     assert mg.gemm_plan(0, 8, 64, "bf16", flags=mg.PLAN_SPLIT_K(4)).workspace_size() == 0
 
 
+def test_direct_to_lds_tile_is_forced_only():
+    p = mg.gemm_plan(8192, 8192, 8192, "bf16", d_type="f32", b_layout="col")
+    assert "tile=256x256 " in p.describe()          # never the planner's own choice
+    p = mg.gemm_plan(8192, 8192, 8192, "bf16", d_type="f32", b_layout="col", flags=mg.PLAN_FORCE_TILE_256x256_DTL)
+    i = p.info()
+    assert "tile=256x256dtl" in p.describe() and i.lds_bytes == 160 * 1024 and (i.block_m, i.block_n) == (256, 256)
+    for kw in (dict(b_layout="row"), dict(a_layout="col", b_layout="col")):
+        with pytest.raises(mg.MgemmError) as e:
+            mg.gemm_plan(512, 512, 512, "bf16", flags=mg.PLAN_FORCE_TILE_256x256_DTL, **kw)
+        assert e.value.status == mg.ERR_UNSUPPORTED
+    with pytest.raises(mg.MgemmError) as e:
+        mg.grouped_gemm_plan(4, 64, 256, 128, b_layout="col", flags=mg.PLAN_FORCE_TILE_256x256_DTL)
+    assert e.value.status == mg.ERR_UNSUPPORTED
+
+
 def test_lds_budget_rejects_three_stage_macro_tile():
     # three 256x256x64 bf16 stages would need 192 KiB: more than a CU's 160 KiB
     assert mg.tile_budget(256, 256, 64, 256, 256, 64, 3, 2).lds_bytes == 192 * 1024 > 160 * 1024
