@@ -19,7 +19,8 @@
 //     consecutive rows: both groups land in eight distinct chunks;
 //   * the K loop is a software pipeline: while the MFMAs of step k run on
 //     one LDS slot, the registers holding step k+1 are written to the other
-//     slot and the global loads of step k+2 are issued -- the load/compute
+//     slot and the global loads of a later step (k+NS+1, with NS register
+//     staging sets) are issued -- the load/compute
 //     overlap that "从 CUDA 代码到 GPU 执行" (Warp Specialization section)
 //     and "使用 Warp Specialization 和 Cluster 扩展 GEMM" (step 7) obtain with
 //     separate roles, obtained here inside every wave;
@@ -302,9 +303,10 @@ __device__ __forceinline__ f32x16_t mfma32(u32x4_t a, u32x4_t b, f32x16_t c)
                                                       __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
 }
 
-template <int BM_, int BN_, int WM_, int WN_, bool A_KMAJOR, bool B_KMAJOR, int IN>
+template <int BM_, int BN_, int WM_, int WN_, bool A_KMAJOR, bool B_KMAJOR, int IN, int NS_ = 2>
 struct Tile {
     static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
+    static constexpr int NS = NS_;  // staging register sets (global loads NS steps ahead)
     static constexpr int NT = 64 * WM * WN;
     static constexpr int TM = BM / WM, TN = BN / WN;  // wave sub-tile
     static constexpr int FM = TM / 32, FN = TN / 32;  // 32x32 MFMA blocks per wave
@@ -335,15 +337,18 @@ struct Tile {
         const int ksteps = (K + kBK - 1) / kBK;
         if (ksteps <= 0)
             return;
-        // Two sets of staging registers: the set written to LDS in step k
-        // is refilled with step k+3 at once, so each global load has two
-        // full K steps to arrive before its data is needed.
-        Loader<BM, NT, A_KMAJOR> la0, la1;
-        Loader<BN, NT, B_KMAJOR> lb0, lb1;
-        la0.init(tid, lda);
-        lb0.init(tid, ldb);
-        la1.init(tid, lda);
-        lb1.init(tid, ldb);
+        // NS sets of staging registers: the set written to LDS in step k is
+        // refilled with step k+1+NS at once, so each global load has NS full
+        // K steps to arrive before its data is needed.  Narrow tiles, whose
+        // sets are small and whose operands stream from HBM (few tokens
+        // against a whole weight matrix), keep more steps in flight.
+        Loader<BM, NT, A_KMAJOR> la[NS];
+        Loader<BN, NT, B_KMAJOR> lb[NS];
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            la[s].init(tid, lda);
+            lb[s].init(tid, ldb);
+        }
 
         // Fragment read offsets.  Lane l reads row (l & 31) of a 32-row
         // block at 16-byte chunk 2*ks + (l >> 5).  Rows 32 apart differ in
@@ -358,15 +363,17 @@ struct Tile {
             bbase[ks] = BM * kRowBytes + rb * kRowBytes + (((2 * ks + fk) ^ swz(rb)) << 4);
         }
 
-        // Prologue: stage step 0 into slot 0 and fetch steps 1 and 2.  The
-        // loads go out part by part in the same order as in the steady-state
-        // body, so the wait counts the compiler derives for the loop are
-        // exact (waiting only for the part about to be written).
-        load_parts(la0, lb0, sa.at_step(0), sb.at_step(0), K);
-        load_parts(la1, lb1, sa.at_step(1), sb.at_step(1), K - kBK);
-        la0.store(lds);
-        lb0.store(lds + BM * kRowBytes);
-        load_parts(la0, lb0, sa.at_step(2), sb.at_step(2), K - 2 * kBK);
+        // Prologue: fetch steps 0 .. NS-1 into the sets, stage step 0 into
+        // slot 0 and refill its set with step NS.  The loads go out part by
+        // part in the same order as in the steady-state body, so the wait
+        // counts the compiler derives for the loop are exact (waiting only
+        // for the part about to be written).
+#pragma unroll
+        for (int s = 0; s < NS; ++s)
+            load_parts(la[s], lb[s], sa.at_step(s), sb.at_step(s), K - s * kBK);
+        la[0].store(lds);
+        lb[0].store(lds + BM * kRowBytes);
+        load_parts(la[0], lb[0], sa.at_step(NS), sb.at_step(NS), K - NS * kBK);
         lds_barrier();
 
         // Fragments are double-buffered: while the MFMAs of one 16-k
@@ -375,17 +382,19 @@ struct Tile {
         Frags f0, f1;
         read_frags<0>(lds, abase, bbase, f0);
 
-        // Every step runs the same branch-free body, two steps per trip:
-        // step kt writes step kt+1 (held in set (kt+1) & 1) into the other
-        // slot and refills that set with step kt+3.  Near the end those
+        // Every step runs the same branch-free body, NS steps per trip:
+        // step kt writes step kt+1 (held in set (kt+1) % NS) into the other
+        // slot and refills that set with step kt+1+NS.  Near the end those
         // loads fall past the operand's records (the hardware returns zeros
         // without touching memory) and the writes fill a slot nobody reads,
         // so no tail variants are needed.
-        // An odd step count runs one extra step on an all-zero slot (both
-        // operands read as zero past K), which adds exactly nothing.
-        for (int kt = 0; kt < ksteps; kt += 2) {
-            step<true, true, true>(lds, kt, la1, lb1, sa, sb, K, abase, bbase, f0, f1);
-            step<true, true, true>(lds, kt + 1, la0, lb0, sa, sb, K, abase, bbase, f0, f1);
+        // A step count that is not a multiple of NS runs up to NS-1 extra
+        // steps on all-zero slots (both operands read as zero past K), which
+        // add exactly nothing.
+        for (int kt = 0; kt < ksteps; kt += NS) {
+#pragma unroll
+            for (int u = 0; u < NS; ++u)
+                step<true, true, true>(lds, kt + u, la[(u + 1) % NS], lb[(u + 1) % NS], sa, sb, K, abase, bbase, f0, f1);
         }
     }
 
@@ -435,7 +444,7 @@ struct Tile {
     // fragments, on exit (NEXT) f0 holds the next step's.
     //   STORE: write the staged registers (step kt+1) into the other slot,
     //          spread over sub-steps 0-2;
-    //   LOAD:  after each part is written, fetch that part of step kt+3 into
+    //   LOAD:  after each part is written, fetch that part of step kt+1+NS into
     //          the same registers;
     //   NEXT:  after the barrier, read the next step's first fragments.
     // The barrier sits between the last fragment read of this step and the
@@ -449,10 +458,10 @@ struct Tile {
         char *nxt = lds + ((kt + 1) & 1) * SLOT;
         __amdgpu_buffer_rsrc_t ra2, rb2;
         if constexpr (LOAD) {
-            ra2 = sa.at_step(kt + 3);
-            rb2 = sb.at_step(kt + 3);
+            ra2 = sa.at_step(kt + 1 + NS);
+            rb2 = sb.at_step(kt + 1 + NS);
         }
-        const int kleft2 = K - (kt + 3) * kBK;
+        const int kleft2 = K - (kt + 1 + NS) * kBK;
 
         // sub-step 0
         read_frags<1>(cur, abase, bbase, f1);

@@ -341,14 +341,19 @@ static mgemm_status_t plan_grouped(const mgemm_grouped_desc_t *d, uint32_t flags
     const bool bk = d->b_layout == MGEMM_COL_MAJOR;
     const int in = in_code(d->a_type), out = out_code(d->d_type), epi = silu ? EPI_SILU_GATE : EPI_NONE;
 
-    // Token-count buckets, each with the tile that wastes least on it:
-    // experts with few rows take a narrow-M tile so that the padding stays
-    // small (MegaMoE, Blackwell section 04 and Hopper section 03: put the
-    // few tokens on the narrow tile dimension and size it to the token
-    // count), large experts take the full macro-tile.
+    // Token-count buckets, each with its own launch: experts with few rows
+    // take the narrow-M tile so that the padding stays small (MegaMoE,
+    // Blackwell section 04 and Hopper section 03: put the few tokens on the
+    // narrow tile dimension and size it to the token count), large experts
+    // take the full macro-tile.  One narrow bucket up to 128 rows rather
+    // than one per row class: each launch runs alone on the stream, and the
+    // small classes alone (64-192 tasks) leave most CUs idle while their
+    // weights stream; merged they fill the chip (measured on the 64-expert
+    // layer: 3.32 ms against 3.61 ms with 32/64/128-row classes; boundaries
+    // at 97 or 193 rows and a third 128x128 class were slower).
     struct B { int tile, lo, hi; };
-    B buckets[4] = {{TILE_32x256, 1, 33}, {TILE_64x256, 33, 65}, {TILE_128x128, 65, 129}, {TILE_256x256, 129, 1 << 30}};
-    int nb = 4;
+    B buckets[2] = {{TILE_32x256, 1, 129}, {TILE_256x256, 129, 1 << 30}};
+    int nb = 2;
     const int ft = forced_tile(flags);
     if (ft >= 0) {
         buckets[0] = {ft, 1, 1 << 30};

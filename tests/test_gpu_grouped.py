@@ -60,16 +60,23 @@ def make_case(counts, N, K, seed, variant="random"):
 BUCKET_COUNTS = [0, 1, 5, 31, 32, 33, 64, 65, 100, 128, 129, 200, 256, 257, 300, 0, 2]
 
 
+GROUPED_TILES = {"auto": 0, "256": mg.PLAN_FORCE_TILE_256x256, "128": mg.PLAN_FORCE_TILE_128x128,
+                 "32n": mg.PLAN_FORCE_TILE_32x256, "64n": mg.PLAN_FORCE_TILE_64x256}
+
+
+@pytest.mark.parametrize("tile", list(GROUPED_TILES))
 @pytest.mark.parametrize("b_layout", ["row", "col"])
 @pytest.mark.parametrize("variant", ["random", "int"])
-def test_grouped_plain_all_buckets(b_layout, variant):
+def test_grouped_plain_all_buckets(tile, b_layout, variant):
+    """Every expert size class with the planner's buckets, and with each
+    compiled tile forced for all experts."""
     N, K = 512, 264
-    log(f"case grouped plain {b_layout} {variant}")
+    log(f"case grouped plain tile={tile} {b_layout} {variant}")
     A, W, off = make_case(BUCKET_COUNTS, N, K, 3, variant)
     Wst = W if b_layout == "row" else np.ascontiguousarray(W.transpose(0, 2, 1))
     rows = int(off[-1])
     D, raw, plan = grouped(to_dev(A, "bf16"), to_dev(Wst, "bf16"), torch.from_numpy(off).cuda(), len(BUCKET_COUNTS),
-                           rows, N, K, b_layout=b_layout, extra_rows=3)
+                           rows, N, K, b_layout=b_layout, extra_rows=3, flags=GROUPED_TILES[tile])
     ref = oracle.grouped_ref(A, Wst, off, w_layout=b_layout)
     got = from_dev_bits(D[:rows])
     if variant == "int":
