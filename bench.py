@@ -63,22 +63,22 @@ def kernel_source_hash() -> str:
 
 
 def profiled_traffic(workload: str):
-    """HBM-side bytes per launch measured with rocprofv3 (FETCH_SIZE and
-    WRITE_SIZE, each scaled by the same counter on a plain copy), read from
-    the workload's summary under profiles/; None unless that summary was
-    taken on the current kernel sources."""
+    """HBM-side bytes per step (the step's kernels once each) measured with
+    rocprofv3 (FETCH_SIZE and WRITE_SIZE, each scaled by the same counter on
+    a plain copy), read from the workload's summary under profiles/; None
+    unless that summary was taken on the current kernel sources."""
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}.md")
     if not os.path.exists(path):
         return None
     fields = {}
     for line in open(path):
-        if ":" in line and line.split(":", 1)[0].strip() in ("source_hash", "traffic_bytes_per_launch"):
+        if ":" in line and line.split(":", 1)[0].strip() in ("source_hash", "traffic_bytes_per_step"):
             k, v = line.split(":", 1)
             fields[k.strip()] = v.strip().strip("`")
     if fields.get("source_hash") != kernel_source_hash():
         return None
     try:
-        return int(fields["traffic_bytes_per_launch"])
+        return int(fields["traffic_bytes_per_step"])
     except (KeyError, ValueError):
         return None
 
