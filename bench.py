@@ -41,6 +41,8 @@ def parse():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle sample time")
+    ap.add_argument("--no-secondary", action="store_true",
+                    help="skip the second square size the metric is quoted at (4096^3 next to 8192^3)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a plain 256 MiB device copy (the reference kernel that scales the "
                          "FETCH_SIZE / WRITE_SIZE counters to bytes)")
@@ -198,25 +200,56 @@ def main():
     else:
         step, info, case = dense_case(torch, mg, datagen, args.workload)
     print(f"# plan: {info['plan']}", file=sys.stderr, flush=True)
+    ms = time_steps(torch, step, args.steps, args.warmup)
+    roof, tflops, peak = roofline(info, ms)
+    secondary = []
+    if args.workload == DEFAULT_WORKLOAD and not args.no_secondary:
+        # the metric is quoted at 4096^3 as well: same timing, reported beside
+        del step
+        step2, info2, _ = dense_case(torch, mg, datagen, "gemm4096_bf16")
+        print(f"# plan: {info2['plan']}", file=sys.stderr, flush=True)
+        ms2 = time_steps(torch, step2, args.steps, args.warmup)
+        roof2, tflops2, peak2 = roofline(info2, ms2)
+        secondary.append({"config": info2["config"], "value": round(tflops2, 2), "unit": "TFLOPS",
+                          "ms_per_step": round(ms2, 5), "pct_of_peak": round(100 * tflops2 / peak2, 2),
+                          "roofline": roof2})
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(case, args.cpu_seconds)
+    line = {"metric": METRIC, "value": round(tflops, 2), "unit": "TFLOPS", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": info["dtype"], "data": "synthetic",
+            "config": info["config"], "pct_of_peak": round(100 * tflops / peak, 2),
+            "roofline": roof, "cpu_baseline": cpu}
+    if secondary:
+        line["also"] = secondary
+    print(json.dumps(line), flush=True)
 
-    for _ in range(args.warmup):
+
+def time_steps(torch, step, steps, warmup):
+    """Average step time in ms: events on the stream the launches go to,
+    bracketed by device synchronisation."""
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()     # the stream every launch above goes to
+    stream = torch.cuda.current_stream()     # the stream every launch goes to
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     ev0.record(stream)
-    for _ in range(args.steps):
+    for _ in range(steps):
         step()
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms = ev0.elapsed_time(ev1) / args.steps
-    tflops = info["flops"] / (ms * 1e-3) / 1e12
-    print(f"# {args.steps} steps: {ms * 1e3:.1f} us/step (events), wall {wall * 1e6 / args.steps:.1f} us/step",
+    ms = ev0.elapsed_time(ev1) / steps
+    print(f"# {steps} steps: {ms * 1e3:.1f} us/step (events), wall {wall * 1e6 / steps:.1f} us/step",
           file=sys.stderr, flush=True)
+    return ms
 
+
+def roofline(info, ms):
+    tflops = info["flops"] / (ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[info["dtype"]]
     # the bound is the one the algorithmic intensity falls under: below the
     # ridge (peak FLOP/s over 8 TB/s, ~315 FLOP/B) a step is HBM-bound
@@ -233,15 +266,7 @@ def main():
             "algorithmic_flops_per_step": info["flops"],
             "achieved_hbm_gbps_algorithmic": round(gbps, 1),
             "kernel_source_hash": kernel_source_hash()}
-    cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(case, args.cpu_seconds)
-    line = {"metric": METRIC, "value": round(tflops, 2), "unit": "TFLOPS", "n_gpus": 1, "steps": args.steps,
-            "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
-            "vs_baseline": None, "dtype": info["dtype"], "data": "synthetic",
-            "config": info["config"], "pct_of_peak": round(100 * tflops / peak, 2),
-            "roofline": roof, "cpu_baseline": cpu}
-    print(json.dumps(line), flush=True)
+    return roof, tflops, peak
 
 
 if __name__ == "__main__":
