@@ -25,7 +25,8 @@
 //     and "使用 Warp Specialization 和 Cluster 扩展 GEMM" (step 7) obtain with
 //     separate roles, obtained here inside every wave;
 //   * for 256 x 256 tiles whose operands are both k-contiguous, DtlTile
-//     replaces the register staging with loads that write LDS directly;
+//     replaces the register staging with loads that write LDS directly and
+//     runs eight waves instead of four;
 //   * the MFMA is v_mfma_f32_32x32x16_{bf16,f16}; the B-tile fragment is
 //     passed as the instruction's first operand and the A-tile fragment as
 //     the second, so each lane's accumulator registers hold four consecutive
@@ -514,23 +515,25 @@ struct Tile {
 };
 
 // ---------------------------------------------------------------------------
-// Direct-to-LDS tile: 256 x 256, both operands k-contiguous.
+// Direct-to-LDS tile: 256 x 256, both operands k-contiguous, eight waves.
 //
 // Global loads write LDS themselves (buffer_load ... lds: each lane's 16
 // bytes land at M0 + 16 * lane), so no staging registers and no LDS-write
 // instructions are involved -- the role the asynchronous tensor copy plays
 // on the pages' hardware ("B200 的 2CTA 怎样调优", sections 四-五: the copy
 // engine fills later K segments while the matrix unit works on the current
-// one, and an issued copy is not yet usable data).  On gfx950 the LDS write
-// path of ds_write_b128 is the busiest resource of the register-staged
-// loop; this variant takes it out.
+// one, and an issued copy is not yet usable data).  Without staging
+// registers a wave needs ~80 VGPRs besides its accumulators, so the tile
+// runs eight waves (two per SIMD, each 128 x 64 outputs, 128 accumulator
+// registers): while one wave of a SIMD waits on a fragment read or the
+// barrier, the other issues MFMAs.
 //
 // LDS (160 KiB): a three-slot ring for A and a two-slot ring for B, 32 KiB
 // per operand step (256 rows x 128 bytes, chunks swizzled as in Tile).
 // During step k the B rows of step k+1 and the A rows of step k+2 are
 // fetched into slots freed by the barrier that ended step k-1, so A has two
 // steps to arrive and B one.  The wait before each barrier names exactly the
-// loads that must have landed: everything but this step's A loads.
+// loads that must have landed: everything but this step's last A loads.
 //
 // One load instruction covers 8 rows x 128 bytes = 1 KiB of LDS, which is
 // contiguous, so the swizzle is applied on the global side: lane l of row
@@ -548,12 +551,13 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 
 template <int IN>
 struct DtlTile {
-    static constexpr int BM = 256, BN = 256, WM = 2, WN = 2;
-    static constexpr int NT = 256;
-    static constexpr int TM = 128, TN = 128, FM = 4, FN = 4;
+    static constexpr int BM = 256, BN = 256, WM = 2, WN = 4;
+    static constexpr int NT = 64 * WM * WN;
+    static constexpr int TM = BM / WM, TN = BN / WN, FM = TM / 32, FN = TN / 32;
     static constexpr int OPS = 256 * kRowBytes;              // one operand, one K step
     static constexpr int A_SLOTS = 3, B_SLOTS = 2;
     static constexpr int LDS_BYTES = (A_SLOTS + B_SLOTS) * OPS;
+    static constexpr int LOADS = 256 / 8 / (NT / 64);        // row groups per wave per operand step
 
     f32x16_t acc[FM][FN];
     struct Frags {
@@ -561,29 +565,31 @@ struct DtlTile {
     };
 
     // per lane: byte offset (within a step) of its chunk in row group j of
-    // its wave's 64-row band, and the k of that chunk
-    uint32_t va[8], vb[8];
-    int kc[8];
+    // its wave's band, and the k of that chunk
+    uint32_t va[LOADS], vb[LOADS];
+    int kc[LOADS];
 
     __device__ __forceinline__ void setup(int lane, int wave, int lda, int ldb)
     {
         const int r = lane >> 3;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int row = wave * 64 + j * 8 + r;
+        for (int j = 0; j < LOADS; ++j) {
+            const int row = (wave * LOADS + j) * 8 + r;
             const int c = (lane & 7) ^ swz(row);
             kc[j] = c * 8;
             va[j] = (uint32_t)row * (uint32_t)lda * 2u + (uint32_t)c * 16u;
             vb[j] = (uint32_t)row * (uint32_t)ldb * 2u + (uint32_t)c * 16u;
         }
     }
-    // row group j of one operand's step into `slot`; k_left = k remaining
-    // from the step's first k (chunks at or past it read as zero)
-    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, const uint32_t (&v)[8], char *slot, int wave, int j,
-                                         int k_left) const
+    // row group j of this wave's band of one operand step into `slot`;
+    // k_left = k remaining from the step's first k (chunks at or past it
+    // read as zero)
+    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, const uint32_t (&v)[LOADS], char *slot, int wave,
+                                         int j, int k_left) const
     {
         const uint32_t off = kc[j] < k_left ? v[j] : kOOB;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)(slot + wave * 8192 + j * 1024), 16, off, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)(slot + (wave * LOADS + j) * 1024), 16, off, 0, 0,
+                                                 0);
     }
 
     template <int KS>
@@ -605,16 +611,17 @@ struct DtlTile {
             for (int j = 0; j < FN; ++j)
                 acc[i][j] = mfma32<IN>(f.b[j], f.a[i], acc[i][j]);
     }
-    // 16 MFMAs; the first 8 each followed by a fragment read (NR of them),
-    // NV loads spread evenly after them
+    // the FM*FN MFMAs of a sub-step, each of the first NR followed by a
+    // fragment read, NV loads spread evenly after them
     template <int I, int NR, int NV>
     static __device__ __forceinline__ void pattern()
     {
-        if constexpr (I < 16) {
+        constexpr int NM = FM * FN;
+        if constexpr (I < NM) {
             __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
             if constexpr (I < NR)
                 __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 1, 0);
-            if constexpr (NV > 0 && I % (16 / (NV > 0 ? NV : 1)) == 0 && I / (16 / (NV > 0 ? NV : 1)) < NV)
+            if constexpr (NV > 0 && I % (NM / (NV > 0 ? NV : 1)) == 0 && I / (NM / (NV > 0 ? NV : 1)) < NV)
                 __builtin_amdgcn_sched_group_barrier(SG_VMEM_READ, 1, 0);
             pattern<I + 1, NR, NV>();
         }
@@ -623,6 +630,8 @@ struct DtlTile {
     __device__ __forceinline__ void mainloop(char *lds, const OperandSrc &sa, int lda, const OperandSrc &sb, int ldb,
                                              int K, int tid)
     {
+        static_assert(LOADS % 2 == 0, "loads are issued in halves");
+        constexpr int H = LOADS / 2;
         const int lane = tid & 63;
         const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
         const int wm0 = (wave / WN) * TM, wn0 = (wave % WN) * TN;
@@ -652,14 +661,14 @@ struct DtlTile {
         {
             const auto ra0 = rsrc(sa, 0), rb0 = rsrc(sb, 0), ra1 = rsrc(sa, 1);
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
+            for (int j = 0; j < LOADS; ++j) {
                 load(ra0, va, A0, wave, j, K);
                 load(rb0, vb, B0, wave, j, K);
             }
 #pragma unroll
-            for (int j = 0; j < 8; ++j)
+            for (int j = 0; j < LOADS; ++j)
                 load(ra1, va, A0 + OPS, wave, j, K - kBK);
-            wait_vm<8>();
+            wait_vm<LOADS>();
         }
         lds_barrier();
         Frags f0, f1;
@@ -674,41 +683,41 @@ struct DtlTile {
             const auto rB = rsrc(sb, kt + 1);
             const auto rA = rsrc(sa, kt + 2);
             const int kb = K - (kt + 1) * kBK, ka = K - (kt + 2) * kBK;
-            // sub-step 0: half of B(kt+1)
+            // sub-step 0: first half of B(kt+1)
             read_frags<1>(ac, bc, abase, bbase, f1);
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+            for (int j = 0; j < H; ++j)
                 load(rB, vb, bn, wave, j, kb);
             mfmas(f0);
-            pattern<0, FM + FN, 4>();
+            pattern<0, FM + FN, H>();
             __builtin_amdgcn_sched_barrier(0);
             // sub-step 1: the rest of B(kt+1)
             read_frags<2>(ac, bc, abase, bbase, f0);
 #pragma unroll
-            for (int j = 4; j < 8; ++j)
+            for (int j = H; j < LOADS; ++j)
                 load(rB, vb, bn, wave, j, kb);
             mfmas(f1);
-            pattern<0, FM + FN, 4>();
+            pattern<0, FM + FN, H>();
             __builtin_amdgcn_sched_barrier(0);
-            // sub-step 2: half of A(kt+2)
+            // sub-step 2: first half of A(kt+2)
             read_frags<3>(ac, bc, abase, bbase, f1);
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+            for (int j = 0; j < H; ++j)
                 load(rA, va, aw, wave, j, ka);
             mfmas(f0);
-            pattern<0, FM + FN, 4>();
+            pattern<0, FM + FN, H>();
             __builtin_amdgcn_sched_barrier(0);
-            // sub-step 3: step kt+1 must be in LDS (only this step's four
-            // A loads may still be in flight), and every wave must be done
+            // sub-step 3: step kt+1 must be in LDS (only this step's A
+            // loads may still be in flight), and every wave must be done
             // with step kt before its slots are refilled
-            wait_vm<4>();
+            wait_vm<H>();
             lds_barrier();
             read_frags<0>(an, bn, abase, bbase, f0);
 #pragma unroll
-            for (int j = 4; j < 8; ++j)
+            for (int j = H; j < LOADS; ++j)
                 load(rA, va, aw, wave, j, ka);
             mfmas(f1);
-            pattern<0, FM + FN, 4>();
+            pattern<0, FM + FN, H>();
             __builtin_amdgcn_sched_barrier(0);
             const int t = sa_cur;
             sa_cur = sa_next;

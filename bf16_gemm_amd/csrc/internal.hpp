@@ -32,7 +32,7 @@ struct TileShape {
     int occupancy;   // workgroups per CU the planner assumes
     double eff;      // relative MFMA efficiency the planner assumes
     bool narrow;     // narrow-M (few tokens) shape: needs a k-contiguous A
-    bool forced_only;  // never chosen by the planner, only by a FORCE_TILE flag
+    bool forced_only;  // not scored by the cost model (a FORCE_TILE flag, or a rule, selects it)
 };
 
 const TileShape &tile_shape(int tile);

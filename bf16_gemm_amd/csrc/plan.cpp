@@ -25,7 +25,7 @@ static const TileShape kTiles[NUM_TILES] = {
     /* 128x128    */ {128, 128, 2, 2, 2 * (128 + 128) * 128, 2, 0.80, false, false},
     /* 32x256     */ {32, 256, 1, 4, 2 * (32 + 256) * 128, 2, 0.55, true, false},
     /* 64x256     */ {64, 256, 1, 4, 2 * (64 + 256) * 128, 1, 0.70, true, false},
-    /* 256x256dtl */ {256, 256, 2, 2, (3 + 2) * 256 * 128, 1, 1.00, false, true},
+    /* 256x256dtl */ {256, 256, 2, 4, (3 + 2) * 256 * 128, 1, 1.00, false, true},
 };
 
 const TileShape &tile_shape(int tile) { return kTiles[tile]; }
@@ -219,6 +219,10 @@ static mgemm_status_t plan_dense(const mgemm_desc_t *d, uint32_t flags, mgemm_pl
         set_error("no kernel compiled for this layout/dtype combination");
         return MGEMM_ERR_UNSUPPORTED;
     }
+    // the 256 x 256 tile with both operands k-contiguous runs on the
+    // direct-to-LDS engine (eight waves, no staging registers)
+    if (tile == TILE_256x256 && forced_tile(flags) < 0 && dense_fn(TILE_256x256_DTL, ak, bk, in, out))
+        tile = TILE_256x256_DTL;
     const int64_t n_main = d->N & ~(int64_t)3;
     const int64_t ksteps = cdiv(d->K, kBK);
     const int forced_splits = (int)((flags >> 16) & 0xFF);
@@ -278,12 +282,13 @@ static mgemm_status_t plan_dense(const mgemm_desc_t *d, uint32_t flags, mgemm_pl
     p->xcd_remap = (flags & MGEMM_PLAN_NO_XCD_REMAP) ? 0 : (p->grid % 8 == 0 ? 1 : 0);
     char buf[256];
     snprintf(buf, sizeof buf,
-             "dense M=%lld N=%lld K=%lld %s%s->%s tile=%s waves=%dx%d bk=64 stages=2 tiles=%lld splits=%d "
+             "dense M=%lld N=%lld K=%lld %s%s->%s tile=%s waves=%dx%d bk=64 stages=%s tiles=%lld splits=%d "
              "grid=%d group_m=%d xcd_remap=%d edge_cols=%lld",
              (long long)d->M, (long long)d->N, (long long)d->K, d->a_type == MGEMM_BF16 ? "bf16" : "f16",
              ak ? (bk ? " NT" : " NN") : (bk ? " TT" : " TN"),
              d->d_type == MGEMM_F32 ? "f32" : (d->d_type == MGEMM_BF16 ? "bf16" : "f16"), tile_name(tile), ts.wm,
-             ts.wn, (long long)p->tiles, p->splits, p->grid, p->group_m, p->xcd_remap, (long long)(d->N - n_main));
+             ts.wn, tile == TILE_256x256_DTL ? "3a/2b" : "2", (long long)p->tiles, p->splits, p->grid, p->group_m,
+             p->xcd_remap, (long long)(d->N - n_main));
     p->description = buf;
     return MGEMM_OK;
 }
@@ -499,7 +504,7 @@ extern "C" mgemm_status_t gemm_plan_info(mgemm_plan_t plan, mgemm_plan_info_t *i
     info->block_k = kBK;
     info->waves_m = ts.wm;
     info->waves_n = ts.wn;
-    info->stages = 2;
+    info->stages = plan->tile == TILE_256x256_DTL ? 3 : 2;   // A ring depth (the B ring has 2)
     info->lds_bytes = ts.lds_bytes;
     info->tiles_m = plan->tiles_m;
     info->tiles_n = plan->tiles_n;

@@ -110,10 +110,11 @@ typedef struct {
 #define MGEMM_PLAN_FORCE_TILE_128x128 0x2u   /* the 128x128 macro-tile  */
 #define MGEMM_PLAN_FORCE_TILE_32x256  0x4u   /* narrow-M (few tokens)   */
 #define MGEMM_PLAN_FORCE_TILE_64x256  0x8u   /* narrow-M (few tokens)   */
-/* 256x256 with loads that write LDS directly (no staging registers); dense
- * plans with row-major A and column-major B only, else UNSUPPORTED.  Never
- * chosen by the planner: on MI355X it is no faster than the default engine
- * on the benchmarked inputs, see the design notes. */
+/* 256x256 with loads that write LDS directly (no staging registers, eight
+ * waves); dense plans with row-major A and column-major B only, else
+ * UNSUPPORTED.  The planner uses it whenever it picks the 256x256 tile for
+ * that layout; MGEMM_PLAN_FORCE_TILE_256x256 then selects the
+ * register-staged engine instead. */
 #define MGEMM_PLAN_FORCE_TILE_256x256_DTL 0x10u
 #define MGEMM_PLAN_NO_XCD_REMAP       0x100u /* plain tile order        */
 /* Dense plans: fix the number of K ranges per output tile (1..64; 1 turns

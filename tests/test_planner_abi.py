@@ -115,9 +115,16 @@ def test_split_k_plans():
     assert mg.gemm_plan(0, 8, 64, "bf16", flags=mg.PLAN_SPLIT_K(4)).workspace_size() == 0
 
 
-def test_direct_to_lds_tile_is_forced_only():
+def test_direct_to_lds_tile_choice():
+    # k-contiguous A and B: the planner's 256x256 tile runs on the direct-to-LDS engine
     p = mg.gemm_plan(8192, 8192, 8192, "bf16", d_type="f32", b_layout="col")
-    assert "tile=256x256 " in p.describe()          # never the planner's own choice
+    i = p.info()
+    assert "tile=256x256dtl" in p.describe() and i.lds_bytes == 160 * 1024 and (i.waves_m, i.waves_n) == (2, 4)
+    # forcing the 256x256 tile keeps the register-staged engine
+    p = mg.gemm_plan(8192, 8192, 8192, "bf16", d_type="f32", b_layout="col", flags=mg.PLAN_FORCE_TILE_256x256)
+    assert "tile=256x256 " in p.describe() and p.info().lds_bytes == 128 * 1024
+    # other layouts never use it
+    assert "dtl" not in mg.gemm_plan(4096, 4096, 4096, "bf16", d_type="bf16").describe()
     p = mg.gemm_plan(8192, 8192, 8192, "bf16", d_type="f32", b_layout="col", flags=mg.PLAN_FORCE_TILE_256x256_DTL)
     i = p.info()
     assert "tile=256x256dtl" in p.describe() and i.lds_bytes == 160 * 1024 and (i.block_m, i.block_n) == (256, 256)
