@@ -549,27 +549,41 @@ __device__ __forceinline__ void wait_vm()
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
-template <int IN>
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+
+// BKM: B k-contiguous ([n][k], column-major B).  Otherwise B is row-major
+// ([k][n]) and is kept that way in LDS: 64 rows of 512 bytes per step, the
+// 64-byte segments of row k XOR-permuted by (k & 3), and its MFMA fragments
+// are read with ds_read_b64_tr_b16.  Within each group of 16 lanes that
+// instruction hands lane i the elements (4j + i/4, i % 4), j = 0..3, of the
+// 16 x 4 block formed by the lanes' 8-byte pieces; so when lane 4j + q of
+// the group points at B[k0 + j][n0 + 4q .. n0 + 4q + 3], lane i receives
+// B[k0 .. k0 + 3][n0 + i] -- four consecutive k of one column, half of the
+// eight a 32x32x16 MFMA lane needs.  The four rows one group reads lie in
+// distinct 64-byte bank groups thanks to the (k & 3) permutation.
+template <int IN, bool BKM>
 struct DtlTile {
     static constexpr int BM = 256, BN = 256, WM = 2, WN = 4;
     static constexpr int NT = 64 * WM * WN;
     static constexpr int TM = BM / WM, TN = BN / WN, FM = TM / 32, FN = TN / 32;
-    static constexpr int OPS = 256 * kRowBytes;              // one operand, one K step
+    static constexpr int OPS = 256 * kRowBytes;              // one operand, one K step (32 KiB)
     static constexpr int A_SLOTS = 3, B_SLOTS = 2;
     static constexpr int LDS_BYTES = (A_SLOTS + B_SLOTS) * OPS;
-    static constexpr int LOADS = 256 / 8 / (NT / 64);        // row groups per wave per operand step
+    static constexpr int LOADS = 256 / 8 / (NT / 64);        // 1-KiB loads per wave per operand step
+    static constexpr int BROW = 512;                         // bytes of one k row of a row-major B step
 
     f32x16_t acc[FM][FN];
     struct Frags {
         u32x4_t a[FM], b[FN];
     };
 
-    // per lane: byte offset (within a step) of its chunk in row group j of
-    // its wave's band, and the k of that chunk
+    // per lane: byte offset (within a step) of its 16 bytes in load j of
+    // its wave, and (k-contiguous rows) the k of that chunk
     uint32_t va[LOADS], vb[LOADS];
     int kc[LOADS];
+    int bfr[FN];   // row-major B: LDS offset of this lane's fragment piece of column block j (ks = 0, h = 0)
 
-    __device__ __forceinline__ void setup(int lane, int wave, int lda, int ldb)
+    __device__ __forceinline__ void setup(int lane, int wave, int wn0, int lda, int ldb)
     {
         const int r = lane >> 3;
 #pragma unroll
@@ -578,16 +592,38 @@ struct DtlTile {
             const int c = (lane & 7) ^ swz(row);
             kc[j] = c * 8;
             va[j] = (uint32_t)row * (uint32_t)lda * 2u + (uint32_t)c * 16u;
-            vb[j] = (uint32_t)row * (uint32_t)ldb * 2u + (uint32_t)c * 16u;
+            if constexpr (BKM) {
+                vb[j] = (uint32_t)row * (uint32_t)ldb * 2u + (uint32_t)c * 16u;
+            } else {
+                // two k rows of 512 bytes per load: lane l writes physical
+                // chunk l & 31 of row 2 * (wave * LOADS + j) + (l >> 5)
+                const int kr = (wave * LOADS + j) * 2 + (lane >> 5);
+                const int pc = lane & 31;
+                const int seg = (pc >> 2) ^ (kr & 3);
+                vb[j] = (uint32_t)kr * (uint32_t)ldb * 2u + (uint32_t)(seg * 64 + (pc & 3) * 16);
+            }
+        }
+        if constexpr (!BKM) {
+            const int g = lane >> 4, rr = lane & 15, j4 = rr >> 2, q = rr & 3;
+#pragma unroll
+            for (int jn = 0; jn < FN; ++jn)
+                bfr[jn] = (8 * (g >> 1) + j4) * BROW + (((wn0 >> 5) + jn) ^ j4) * 64 + 32 * (g & 1) + 8 * q;
         }
     }
-    // row group j of this wave's band of one operand step into `slot`;
-    // k_left = k remaining from the step's first k (chunks at or past it
-    // read as zero)
-    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, const uint32_t (&v)[LOADS], char *slot, int wave,
-                                         int j, int k_left) const
+    // load j of this wave into `slot`; for k-contiguous rows k_left = k
+    // remaining from the step's first k (chunks at or past it read as zero;
+    // a row-major B's rows past K lie beyond its resource)
+    __device__ __forceinline__ void load_a(__amdgpu_buffer_rsrc_t r, char *slot, int wave, int j, int k_left) const
     {
-        const uint32_t off = kc[j] < k_left ? v[j] : kOOB;
+        const uint32_t off = kc[j] < k_left ? va[j] : kOOB;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)(slot + (wave * LOADS + j) * 1024), 16, off, 0, 0,
+                                                 0);
+    }
+    __device__ __forceinline__ void load_b(__amdgpu_buffer_rsrc_t r, char *slot, int wave, int j, int k_left) const
+    {
+        uint32_t off = vb[j];
+        if constexpr (BKM)
+            off = kc[j] < k_left ? off : kOOB;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)(slot + (wave * LOADS + j) * 1024), 16, off, 0, 0,
                                                  0);
     }
@@ -599,9 +635,21 @@ struct DtlTile {
 #pragma unroll
         for (int i = 0; i < FM; ++i)
             f.a[i] = *(const u32x4_t *)(as + abase[KS ^ ((i & 1) * 2)] + i * 32 * kRowBytes);
+        if constexpr (BKM) {
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
-            f.b[j] = *(const u32x4_t *)(bs + bbase[KS ^ ((j & 1) * 2)] + j * 32 * kRowBytes);
+            for (int j = 0; j < FN; ++j)
+                f.b[j] = *(const u32x4_t *)(bs + bbase[KS ^ ((j & 1) * 2)] + j * 32 * kRowBytes);
+        } else {
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
+                const char *p = bs + bfr[j] + 16 * KS * BROW;
+                const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)p);
+                const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(p + 4 * BROW));
+                const u32x2_t l2 = __builtin_bit_cast(u32x2_t, lo), h2 = __builtin_bit_cast(u32x2_t, hi);
+                f.b[j] = u32x4_t{l2[0], l2[1], h2[0], h2[1]};
+            }
+        }
     }
     __device__ __forceinline__ void mfmas(const Frags &f)
     {
@@ -626,6 +674,7 @@ struct DtlTile {
             pattern<I + 1, NR, NV>();
         }
     }
+    static constexpr int NREADS = FM + (BKM ? FN : 2 * FN);   // LDS read instructions per sub-step
 
     __device__ __forceinline__ void mainloop(char *lds, const OperandSrc &sa, int lda, const OperandSrc &sb, int ldb,
                                              int K, int tid)
@@ -643,7 +692,7 @@ struct DtlTile {
         const int ksteps = (K + kBK - 1) / kBK;
         if (ksteps <= 0)
             return;
-        setup(lane, wave, lda, ldb);
+        setup(lane, wave, wn0, lda, ldb);
         char *const A0 = lds;
         char *const B0 = lds + A_SLOTS * OPS;
         const int frow = lane & 31, fk = lane >> 5;
@@ -662,12 +711,12 @@ struct DtlTile {
             const auto ra0 = rsrc(sa, 0), rb0 = rsrc(sb, 0), ra1 = rsrc(sa, 1);
 #pragma unroll
             for (int j = 0; j < LOADS; ++j) {
-                load(ra0, va, A0, wave, j, K);
-                load(rb0, vb, B0, wave, j, K);
+                load_a(ra0, A0, wave, j, K);
+                load_b(rb0, B0, wave, j, K);
             }
 #pragma unroll
             for (int j = 0; j < LOADS; ++j)
-                load(ra1, va, A0 + OPS, wave, j, K - kBK);
+                load_a(ra1, A0 + OPS, wave, j, K - kBK);
             wait_vm<LOADS>();
         }
         lds_barrier();
@@ -687,25 +736,25 @@ struct DtlTile {
             read_frags<1>(ac, bc, abase, bbase, f1);
 #pragma unroll
             for (int j = 0; j < H; ++j)
-                load(rB, vb, bn, wave, j, kb);
+                load_b(rB, bn, wave, j, kb);
             mfmas(f0);
-            pattern<0, FM + FN, H>();
+            pattern<0, NREADS, H>();
             __builtin_amdgcn_sched_barrier(0);
             // sub-step 1: the rest of B(kt+1)
             read_frags<2>(ac, bc, abase, bbase, f0);
 #pragma unroll
             for (int j = H; j < LOADS; ++j)
-                load(rB, vb, bn, wave, j, kb);
+                load_b(rB, bn, wave, j, kb);
             mfmas(f1);
-            pattern<0, FM + FN, H>();
+            pattern<0, NREADS, H>();
             __builtin_amdgcn_sched_barrier(0);
             // sub-step 2: first half of A(kt+2)
             read_frags<3>(ac, bc, abase, bbase, f1);
 #pragma unroll
             for (int j = 0; j < H; ++j)
-                load(rA, va, aw, wave, j, ka);
+                load_a(rA, aw, wave, j, ka);
             mfmas(f0);
-            pattern<0, FM + FN, H>();
+            pattern<0, NREADS, H>();
             __builtin_amdgcn_sched_barrier(0);
             // sub-step 3: step kt+1 must be in LDS (only this step's A
             // loads may still be in flight), and every wave must be done
@@ -715,9 +764,9 @@ struct DtlTile {
             read_frags<0>(an, bn, abase, bbase, f0);
 #pragma unroll
             for (int j = H; j < LOADS; ++j)
-                load(rA, va, aw, wave, j, ka);
+                load_a(rA, aw, wave, j, ka);
             mfmas(f1);
-            pattern<0, FM + FN, H>();
+            pattern<0, NREADS, H>();
             __builtin_amdgcn_sched_barrier(0);
             const int t = sa_cur;
             sa_cur = sa_next;

@@ -58,14 +58,17 @@ DenseFn dense_table(bool ak, bool bk, int out)
 #undef MG_D
 }
 
-// The direct-to-LDS 256 x 256 engine: k-contiguous A and B only.
+// The direct-to-LDS 256 x 256 engine: row-major (k-contiguous) A, B either way.
 template <int IN>
 DenseFn dense_dtl_table(bool ak, bool bk, int out)
 {
-    if (!ak || !bk || (out != OUT_F32 && out != same16<IN>()))
+    if (!ak || (out != OUT_F32 && out != same16<IN>()))
         return nullptr;
-    return out == OUT_F32 ? launch_dense_tile<DtlTile<IN>, true, true, IN, OUT_F32>
-                          : launch_dense_tile<DtlTile<IN>, true, true, IN, same16<IN>()>;
+    if (bk)
+        return out == OUT_F32 ? launch_dense_tile<DtlTile<IN, true>, true, true, IN, OUT_F32>
+                              : launch_dense_tile<DtlTile<IN, true>, true, true, IN, same16<IN>()>;
+    return out == OUT_F32 ? launch_dense_tile<DtlTile<IN, false>, true, false, IN, OUT_F32>
+                          : launch_dense_tile<DtlTile<IN, false>, true, false, IN, same16<IN>()>;
 }
 
 template <int BM, int BN, int WM, int WN, int IN>

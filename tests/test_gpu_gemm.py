@@ -29,8 +29,8 @@ TILES = {"auto": 0, "256": mg.PLAN_FORCE_TILE_256x256, "128": mg.PLAN_FORCE_TILE
 def tile_skip(tile, al, bl):
     if tile in ("32n", "64n") and al == "col":
         pytest.skip("narrow-M tiles take a k-contiguous A only")
-    if tile == "256d" and (al, bl) != ("row", "col"):
-        pytest.skip("the direct-to-LDS tile takes k-contiguous A and B only")
+    if tile == "256d" and al != "row":
+        pytest.skip("the direct-to-LDS tile takes a row-major (k-contiguous) A only")
 
 
 def log(*a):
@@ -257,7 +257,8 @@ FULL = ["gemm512_f16", "gemm4096_bf16", "gemm8192_bf16_bcol", "ts16384x2048x7168
 
 
 @pytest.mark.parametrize("name,flags", [(n, 0) for n in FULL] +
-                         [("gemm8192_bf16_bcol", mg.PLAN_FORCE_TILE_256x256_DTL)])
+                         [("gemm8192_bf16_bcol", mg.PLAN_FORCE_TILE_256x256),
+                          ("gemm4096_bf16", mg.PLAN_FORCE_TILE_256x256)])
 @pytest.mark.parametrize("variant", ["random", "int"])
 def test_full_size_workloads(name, flags, variant):
     cfg = datagen.DENSE[name]

@@ -123,12 +123,14 @@ def test_direct_to_lds_tile_choice():
     # forcing the 256x256 tile keeps the register-staged engine
     p = mg.gemm_plan(8192, 8192, 8192, "bf16", d_type="f32", b_layout="col", flags=mg.PLAN_FORCE_TILE_256x256)
     assert "tile=256x256 " in p.describe() and p.info().lds_bytes == 128 * 1024
-    # other layouts never use it
-    assert "dtl" not in mg.gemm_plan(4096, 4096, 4096, "bf16", d_type="bf16").describe()
+    # row-major B too (its fragments are read with LDS transpose reads); a
+    # column-major A never
+    assert "tile=256x256dtl" in mg.gemm_plan(4096, 4096, 4096, "bf16", d_type="bf16").describe()
+    assert "dtl" not in mg.gemm_plan(4096, 4096, 4096, "bf16", d_type="bf16", a_layout="col").describe()
     p = mg.gemm_plan(8192, 8192, 8192, "bf16", d_type="f32", b_layout="col", flags=mg.PLAN_FORCE_TILE_256x256_DTL)
     i = p.info()
     assert "tile=256x256dtl" in p.describe() and i.lds_bytes == 160 * 1024 and (i.block_m, i.block_n) == (256, 256)
-    for kw in (dict(b_layout="row"), dict(a_layout="col", b_layout="col")):
+    for kw in (dict(a_layout="col", b_layout="row"), dict(a_layout="col", b_layout="col")):
         with pytest.raises(mg.MgemmError) as e:
             mg.gemm_plan(512, 512, 512, "bf16", flags=mg.PLAN_FORCE_TILE_256x256_DTL, **kw)
         assert e.value.status == mg.ERR_UNSUPPORTED
