@@ -139,15 +139,20 @@ __global__ void __launch_bounds__(T::NT) grouped_kernel(GroupedArgs p)
         if (tid == p.G - 1)
             row_start[p.G] = hi;
     }
-    task_start[tid + 1] = cnt;
+    // the table has 256 entries (num_groups <= 256) whatever the workgroup
+    // size; threads past it only take part in the barriers
+    constexpr int TT = 256;
+    if (tid < TT)
+        task_start[tid + 1] = cnt;
     if (tid == 0)
         task_start[0] = 0;
     __syncthreads();
-    // inclusive scan of task_start[1..NT] (Hillis-Steele)
-    for (int s = 1; s < T::NT; s <<= 1) {
-        int v = (tid >= s) ? task_start[tid + 1 - s] : 0;
+    // inclusive scan of task_start[1..TT] (Hillis-Steele)
+    for (int s = 1; s < TT; s <<= 1) {
+        int v = (tid < TT && tid >= s) ? task_start[tid + 1 - s] : 0;
         __syncthreads();
-        task_start[tid + 1] += v;
+        if (tid < TT)
+            task_start[tid + 1] += v;
         __syncthreads();
     }
     const int total = task_start[p.G];

@@ -29,6 +29,9 @@ hipError_t launch_dense(const DenseArgs &a, int grid, hipStream_t s)
     return launch_dense_tile<TileOf<BM, BN, WM, WN, AK, BK, IN>, AK, BK, IN, OUT>(a, grid, s);
 }
 
+// Grouped launches keep the register-staged engine: on the 64-expert MoE
+// layer the direct-to-LDS engine measured 3-10 % slower (with either
+// operand on its deeper ring).
 template <int BM, int BN, int WM, int WN, bool BK, int IN, int OUT, int EPI>
 hipError_t launch_grouped(const GroupedArgs &a, int grid, hipStream_t s)
 {
