@@ -23,6 +23,23 @@ def test_exports_match_header():
     assert mg.version().startswith("mgemm")
 
 
+def test_header_constants_match_binding():
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    enums = dict((k, int(v)) for k, v in re.findall(r"\b(MGEMM_[A-Z0-9_]+)\s*=\s*(\d+)", text))
+    flags = dict((k, int(v, 16)) for k, v in re.findall(r"#define\s+(MGEMM_PLAN_\w+)\s+0x([0-9a-fA-F]+)u", text))
+    assert (enums["MGEMM_F16"], enums["MGEMM_BF16"], enums["MGEMM_F32"]) == (mg.F16, mg.BF16, mg.F32)
+    assert (enums["MGEMM_ROW_MAJOR"], enums["MGEMM_COL_MAJOR"]) == (mg.ROW_MAJOR, mg.COL_MAJOR)
+    assert (enums["MGEMM_EPI_NONE"], enums["MGEMM_EPI_SILU_GATE_I8"]) == (mg.EPI_NONE, mg.EPI_SILU_GATE_I8)
+    assert [enums[k] for k in ("MGEMM_OK", "MGEMM_ERR_INVALID_ARG", "MGEMM_ERR_UNSUPPORTED", "MGEMM_ERR_WORKSPACE",
+                               "MGEMM_ERR_NO_MEMORY", "MGEMM_ERR_HIP")] == [mg.OK, mg.ERR_INVALID_ARG,
+                                                                            mg.ERR_UNSUPPORTED, mg.ERR_WORKSPACE,
+                                                                            mg.ERR_NO_MEMORY, mg.ERR_HIP]
+    assert len(flags) == 6
+    for name, value in flags.items():
+        assert getattr(mg, name[len("MGEMM_"):]) == value, name
+    assert "((((uint32_t)(n)) & 0xFFu) << 16)" in text and mg.PLAN_SPLIT_K(5) == 5 << 16
+
+
 def test_tile_calculator_pin():
     g = GOLD["tile_calculator"]
     b = mg.tile_budget(g["M"], g["N"], g["K"], g["BM"], g["BN"], g["BK"], g["stages"], g["elt_bytes"])
