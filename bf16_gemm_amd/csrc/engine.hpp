@@ -706,9 +706,9 @@ struct DtlTile {
         // steps past the end load from an empty range (zeros, no memory access)
         auto rsrc = [&](const OperandSrc &s, int st) { return st < ksteps ? s.at_step(st) : make_rsrc(s.base, 0); };
 
-        // prologue: A(0), B(0), A(1); wait for the first two
+        // prologue: A(0), B(0), A(1), B(1); wait for the first two
         {
-            const auto ra0 = rsrc(sa, 0), rb0 = rsrc(sb, 0), ra1 = rsrc(sa, 1);
+            const auto ra0 = rsrc(sa, 0), rb0 = rsrc(sb, 0), ra1 = rsrc(sa, 1), rb1 = rsrc(sb, 1);
 #pragma unroll
             for (int j = 0; j < LOADS; ++j) {
                 load_a(ra0, A0, wave, j, K);
@@ -717,7 +717,10 @@ struct DtlTile {
 #pragma unroll
             for (int j = 0; j < LOADS; ++j)
                 load_a(ra1, A0 + OPS, wave, j, K - kBK);
-            wait_vm<LOADS>();
+#pragma unroll
+            for (int j = 0; j < LOADS; ++j)
+                load_b(rb1, B0 + OPS, wave, j, K - kBK);
+            wait_vm<2 * LOADS>();
         }
         lds_barrier();
         Frags f0, f1;
@@ -726,47 +729,47 @@ struct DtlTile {
         for (int kt = 0; kt < ksteps; ++kt) {
             const char *ac = A0 + sa_cur * OPS;
             const char *bc = B0 + (kt & 1) * OPS;
-            char *an = A0 + sa_next * OPS;
-            char *bn = B0 + ((kt + 1) & 1) * OPS;
+            const char *an = A0 + sa_next * OPS;
+            const char *bn = B0 + ((kt + 1) & 1) * OPS;
             char *aw = A0 + sa_fill * OPS;
-            const auto rB = rsrc(sb, kt + 1);
+            char *bw = B0 + (kt & 1) * OPS;
             const auto rA = rsrc(sa, kt + 2);
-            const int kb = K - (kt + 1) * kBK, ka = K - (kt + 2) * kBK;
-            // sub-step 0: first half of B(kt+1)
+            const int ka = K - (kt + 2) * kBK;
+            // sub-steps 0 and 1: A(kt+2), into the A slot step kt-1 used
             read_frags<1>(ac, bc, abase, bbase, f1);
 #pragma unroll
             for (int j = 0; j < H; ++j)
-                load_b(rB, bn, wave, j, kb);
+                load_a(rA, aw, wave, j, ka);
             mfmas(f0);
             pattern<0, NREADS, H>();
             __builtin_amdgcn_sched_barrier(0);
-            // sub-step 1: the rest of B(kt+1)
             read_frags<2>(ac, bc, abase, bbase, f0);
 #pragma unroll
             for (int j = H; j < LOADS; ++j)
-                load_b(rB, bn, wave, j, kb);
+                load_a(rA, aw, wave, j, ka);
             mfmas(f1);
             pattern<0, NREADS, H>();
             __builtin_amdgcn_sched_barrier(0);
-            // sub-step 2: first half of A(kt+2)
+            // sub-step 2: the last reads of step kt
             read_frags<3>(ac, bc, abase, bbase, f1);
-#pragma unroll
-            for (int j = 0; j < H; ++j)
-                load_a(rA, aw, wave, j, ka);
             mfmas(f0);
-            pattern<0, NREADS, H>();
+            pattern<0, NREADS, 0>();
             __builtin_amdgcn_sched_barrier(0);
-            // sub-step 3: step kt+1 must be in LDS (only this step's A
-            // loads may still be in flight), and every wave must be done
-            // with step kt before its slots are refilled
-            wait_vm<H>();
+            // sub-step 3: step kt+1 must be in LDS (only A(kt+2) may still be
+            // in flight), and every wave must be done with step kt; then
+            // B(kt+2) goes into the B slot step kt leaves
+            wait_vm<LOADS>();
             lds_barrier();
             read_frags<0>(an, bn, abase, bbase, f0);
+            {
+                const auto rB = rsrc(sb, kt + 2);
+                const int kb = K - (kt + 2) * kBK;
 #pragma unroll
-            for (int j = H; j < LOADS; ++j)
-                load_a(rA, aw, wave, j, ka);
+                for (int j = 0; j < LOADS; ++j)
+                    load_b(rB, bw, wave, j, kb);
+            }
             mfmas(f1);
-            pattern<0, NREADS, H>();
+            pattern<0, NREADS, LOADS>();
             __builtin_amdgcn_sched_barrier(0);
             const int t = sa_cur;
             sa_cur = sa_next;
