@@ -56,11 +56,18 @@ KERNEL_SOURCES = ["bf16_gemm_amd/csrc/engine.hpp", "bf16_gemm_amd/csrc/kernels.h
 
 
 def kernel_source_hash() -> str:
+    """Hash of the kernel sources' code: comments dropped and runs of white
+    space collapsed, so that an edit of the comments alone keeps the recorded
+    counters valid."""
     import hashlib
+    import re
+    tok = re.compile(r'"(?:\\.|[^"\\])*"|\'(?:\\.|[^\'\\])*\'|//[^\n]*|/\*.*?\*/', re.S)
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, p), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, p), encoding="utf-8") as f:
+            text = f.read()
+        code = tok.sub(lambda m: " " if m.group(0)[0] == "/" else m.group(0), text)
+        h.update(" ".join(code.split()).encode())
     return h.hexdigest()[:16]
 
 

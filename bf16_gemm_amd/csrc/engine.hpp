@@ -528,12 +528,13 @@ struct Tile {
 // registers): while one wave of a SIMD waits on a fragment read or the
 // barrier, the other issues MFMAs.
 //
-// LDS (160 KiB): a three-slot ring for A and a two-slot ring for B, 32 KiB
+// LDS (160 KiB): a three-slot ring for B and a two-slot ring for A, 32 KiB
 // per operand step (256 rows x 128 bytes, chunks swizzled as in Tile).
-// During step k the B rows of step k+1 and the A rows of step k+2 are
-// fetched into slots freed by the barrier that ended step k-1, so A has two
-// steps to arrive and B one.  The wait before each barrier names exactly the
-// loads that must have landed: everything but this step's last A loads.
+// During step k the B rows of step k+2 go into the slot freed by the
+// barrier that ended step k-1, and right after the barrier that ends step k
+// the A rows of step k+2 go into the A slot step k leaves: B has two steps
+// to arrive and A one.  The wait before each barrier names exactly the loads
+// that must have landed: everything but this step's B loads.
 //
 // One load instruction covers 8 rows x 128 bytes = 1 KiB of LDS, which is
 // contiguous, so the swizzle is applied on the global side: lane l of row
@@ -567,7 +568,11 @@ struct DtlTile {
     static constexpr int NT = 64 * WM * WN;
     static constexpr int TM = BM / WM, TN = BN / WN, FM = TM / 32, FN = TN / 32;
     static constexpr int OPS = 256 * kRowBytes;              // one operand, one K step (32 KiB)
-    static constexpr int A_SLOTS = 3, B_SLOTS = 2;
+    // B gets the 3-slot ring (loads two steps ahead), A the 2-slot one (one
+    // step ahead); the other assignment is as fast at 8192^3 and ~2 % slower
+    // on 16384x2048x7168
+    static constexpr bool DEEP_B = true;
+    static constexpr int A_SLOTS = DEEP_B ? 2 : 3, B_SLOTS = DEEP_B ? 3 : 2;
     static constexpr int LDS_BYTES = (A_SLOTS + B_SLOTS) * OPS;
     static constexpr int LOADS = 256 / 8 / (NT / 64);        // 1-KiB loads per wave per operand step
     static constexpr int BROW = 512;                         // bytes of one k row of a row-major B step
@@ -705,48 +710,67 @@ struct DtlTile {
         }
         // steps past the end load from an empty range (zeros, no memory access)
         auto rsrc = [&](const OperandSrc &s, int st) { return st < ksteps ? s.at_step(st) : make_rsrc(s.base, 0); };
+        // the operand with the 3-slot ring ("deep") and the one with 2 slots
+        char *const D0 = DEEP_B ? B0 : A0;
+        char *const S0 = DEEP_B ? A0 : B0;
+        const OperandSrc &sd = DEEP_B ? sb : sa;
+        const OperandSrc &ss = DEEP_B ? sa : sb;
+        auto load_d = [&](__amdgpu_buffer_rsrc_t r, char *slot, int j, int k_left) {
+            if constexpr (DEEP_B)
+                load_b(r, slot, wave, j, k_left);
+            else
+                load_a(r, slot, wave, j, k_left);
+        };
+        auto load_s = [&](__amdgpu_buffer_rsrc_t r, char *slot, int j, int k_left) {
+            if constexpr (DEEP_B)
+                load_a(r, slot, wave, j, k_left);
+            else
+                load_b(r, slot, wave, j, k_left);
+        };
 
-        // prologue: A(0), B(0), A(1), B(1); wait for the first two
+        // prologue: both operands of steps 0 and 1; wait for step 0
         {
-            const auto ra0 = rsrc(sa, 0), rb0 = rsrc(sb, 0), ra1 = rsrc(sa, 1), rb1 = rsrc(sb, 1);
+            const auto rd0 = rsrc(sd, 0), rs0 = rsrc(ss, 0), rd1 = rsrc(sd, 1), rs1 = rsrc(ss, 1);
 #pragma unroll
             for (int j = 0; j < LOADS; ++j) {
-                load_a(ra0, A0, wave, j, K);
-                load_b(rb0, B0, wave, j, K);
+                load_d(rd0, D0, j, K);
+                load_s(rs0, S0, j, K);
             }
 #pragma unroll
             for (int j = 0; j < LOADS; ++j)
-                load_a(ra1, A0 + OPS, wave, j, K - kBK);
+                load_d(rd1, D0 + OPS, j, K - kBK);
 #pragma unroll
             for (int j = 0; j < LOADS; ++j)
-                load_b(rb1, B0 + OPS, wave, j, K - kBK);
+                load_s(rs1, S0 + OPS, j, K - kBK);
             wait_vm<2 * LOADS>();
         }
         lds_barrier();
         Frags f0, f1;
         read_frags<0>(A0, B0, abase, bbase, f0);
-        int sa_cur = 0, sa_next = 1, sa_fill = 2;   // A slots of steps kt, kt+1, kt+2
+        int sd_cur = 0, sd_next = 1, sd_fill = 2;   // deep slots of steps kt, kt+1, kt+2
         for (int kt = 0; kt < ksteps; ++kt) {
-            const char *ac = A0 + sa_cur * OPS;
-            const char *bc = B0 + (kt & 1) * OPS;
-            const char *an = A0 + sa_next * OPS;
-            const char *bn = B0 + ((kt + 1) & 1) * OPS;
-            char *aw = A0 + sa_fill * OPS;
-            char *bw = B0 + (kt & 1) * OPS;
-            const auto rA = rsrc(sa, kt + 2);
-            const int ka = K - (kt + 2) * kBK;
-            // sub-steps 0 and 1: A(kt+2), into the A slot step kt-1 used
+            const int s_cur = kt & 1, s_next = (kt + 1) & 1;
+            const char *ac = (DEEP_B ? S0 + s_cur * OPS : D0 + sd_cur * OPS);
+            const char *bc = (DEEP_B ? D0 + sd_cur * OPS : S0 + s_cur * OPS);
+            const char *an = (DEEP_B ? S0 + s_next * OPS : D0 + sd_next * OPS);
+            const char *bn = (DEEP_B ? D0 + sd_next * OPS : S0 + s_next * OPS);
+            char *dw = D0 + sd_fill * OPS;
+            char *sw = S0 + s_cur * OPS;
+            const auto rD = rsrc(sd, kt + 2);
+            const int kd = K - (kt + 2) * kBK;
+            // sub-steps 0 and 1: the deep operand of step kt+2, into the slot
+            // step kt-1 used
             read_frags<1>(ac, bc, abase, bbase, f1);
 #pragma unroll
             for (int j = 0; j < H; ++j)
-                load_a(rA, aw, wave, j, ka);
+                load_d(rD, dw, j, kd);
             mfmas(f0);
             pattern<0, NREADS, H>();
             __builtin_amdgcn_sched_barrier(0);
             read_frags<2>(ac, bc, abase, bbase, f0);
 #pragma unroll
             for (int j = H; j < LOADS; ++j)
-                load_a(rA, aw, wave, j, ka);
+                load_d(rD, dw, j, kd);
             mfmas(f1);
             pattern<0, NREADS, H>();
             __builtin_amdgcn_sched_barrier(0);
@@ -755,26 +779,27 @@ struct DtlTile {
             mfmas(f0);
             pattern<0, NREADS, 0>();
             __builtin_amdgcn_sched_barrier(0);
-            // sub-step 3: step kt+1 must be in LDS (only A(kt+2) may still be
-            // in flight), and every wave must be done with step kt; then
-            // B(kt+2) goes into the B slot step kt leaves
+            // sub-step 3: step kt+1 must be in LDS (only the deep loads of
+            // step kt+2 may still be in flight), and every wave must be done
+            // with step kt; then the 2-slot operand of step kt+2 goes into
+            // the slot step kt leaves
             wait_vm<LOADS>();
             lds_barrier();
             read_frags<0>(an, bn, abase, bbase, f0);
             {
-                const auto rB = rsrc(sb, kt + 2);
-                const int kb = K - (kt + 2) * kBK;
+                const auto rS = rsrc(ss, kt + 2);
+                const int ks2 = K - (kt + 2) * kBK;
 #pragma unroll
                 for (int j = 0; j < LOADS; ++j)
-                    load_b(rB, bw, wave, j, kb);
+                    load_s(rS, sw, j, ks2);
             }
             mfmas(f1);
             pattern<0, NREADS, LOADS>();
             __builtin_amdgcn_sched_barrier(0);
-            const int t = sa_cur;
-            sa_cur = sa_next;
-            sa_next = sa_fill;
-            sa_fill = t;
+            const int t = sd_cur;
+            sd_cur = sd_next;
+            sd_next = sd_fill;
+            sd_fill = t;
         }
         // nothing may still be writing LDS when the next tile starts
         wait_vm<0>();
