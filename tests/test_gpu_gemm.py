@@ -251,6 +251,26 @@ def test_split_k_deterministic():
     assert p1.info().splits == 8 and np.array_equal(g1, g2)
 
 
+DTL_SHORT_K = ([(K, bl, "bf16", "f32") for K in (8, 64, 72, 136, 200) for bl in ("row", "col")]
+               + [(K, bl, "f16", "f16") for K in (72, 200) for bl in ("row", "col")])
+
+
+@pytest.mark.parametrize("K,bl,in_t,out_t", DTL_SHORT_K)
+def test_direct_to_lds_short_k_two_tiles_per_workgroup(K, bl, in_t, out_t):
+    """The direct-to-LDS tile with one to four K steps (the prologue's second
+    step and the ring's trailing loads fall past K) on 17 x 17 tiles, so 33
+    of the 256 workgroups run a second tile in the LDS the first one left:
+    every output element against the oracle, integer inputs, bit-exact."""
+    M, N = 4300, 4100
+    log(f"case dtl short-k M={M} N={N} K={K} {in_t}->{out_t} B {bl}")
+    cfg = datagen.GemmConfig("t", M, N, K, in_t, out_t, "row", bl, seed=11, int_seed=K + 3)
+    a, b = datagen.gemm_inputs(cfg, "int")
+    got, plan = run_dense(a, b, M, N, K, in_t, out_t, "row", bl, TILES["256d"])
+    assert "256x256dtl" in plan.describe() and "tiles=289" in plan.describe(), plan.describe()
+    ref = oracle.gemm_ref(a, b, in_t, in_t, "row", bl)
+    assert_bits_equal(got, ref, out_t, plan.describe())
+
+
 # --------------------------------------------------------------- full size
 
 FULL = ["gemm512_f16", "gemm4096_bf16", "gemm8192_bf16_bcol", "ts16384x2048x7168", "decode128x7168x2048"]
