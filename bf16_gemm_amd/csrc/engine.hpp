@@ -528,13 +528,15 @@ struct Tile {
 // registers): while one wave of a SIMD waits on a fragment read or the
 // barrier, the other issues MFMAs.
 //
-// LDS (160 KiB): a three-slot ring for B and a two-slot ring for A, 32 KiB
-// per operand step (256 rows x 128 bytes, chunks swizzled as in Tile).
-// During step k the B rows of step k+2 go into the slot freed by the
+// LDS (160 KiB): a three-slot ring for one operand ("deep": B when it is
+// k-contiguous, else A) and a two-slot ring for the other, 32 KiB per
+// operand step (256 rows x 128 bytes, chunks swizzled as in Tile).  During
+// step k the deep operand's rows of step k+2 go into the slot freed by the
 // barrier that ended step k-1, and right after the barrier that ends step k
-// the A rows of step k+2 go into the A slot step k leaves: B has two steps
-// to arrive and A one.  The wait before each barrier names exactly the loads
-// that must have landed: everything but this step's B loads.
+// the other operand's rows of step k+2 go into the slot step k leaves: the
+// deep operand has two steps to arrive, the other one.  The wait before
+// each barrier names exactly the loads that must have landed: everything
+// but this step's deep loads.
 //
 // One load instruction covers 8 rows x 128 bytes = 1 KiB of LDS, which is
 // contiguous, so the swizzle is applied on the global side: lane l of row
@@ -549,6 +551,26 @@ __device__ __forceinline__ void wait_vm()
 }
 
 typedef __attribute__((address_space(3))) void lds_void_t;
+
+// One 16-byte-per-lane load from the buffer straight into LDS: lane l's
+// bytes land at LDS address lds_addr + 16 l (lds_addr uniform).  Written as
+// inline assembly rather than with the compiler's builtin for this load on
+// purpose: the compiler's wait insertion cannot tell that a
+// ds_read_b64_tr_b16 does not read what such a load is still writing, and
+// puts a wait for every outstanding load (vmcnt(0)) before each transpose
+// read, which throws away the ring's prefetch depth.  The loops that use
+// this load count its completions themselves (s_waitcnt vmcnt before each
+// barrier) and nothing else in them uses M0.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void load_to_lds16(__amdgpu_buffer_rsrc_t r, uint32_t lds_addr, uint32_t voff)
+{
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(lds_addr), "v"(voff),
+                 "s"(r)
+                 : "m0");
+}
+#pragma clang diagnostic pop
+__device__ __forceinline__ uint32_t lds_addr(const char *p) { return (uint32_t)(uintptr_t)(const lds_void_t *)p; }
 
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 
@@ -568,10 +590,12 @@ struct DtlTile {
     static constexpr int NT = 64 * WM * WN;
     static constexpr int TM = BM / WM, TN = BN / WN, FM = TM / 32, FN = TN / 32;
     static constexpr int OPS = 256 * kRowBytes;              // one operand, one K step (32 KiB)
-    // B gets the 3-slot ring (loads two steps ahead), A the 2-slot one (one
-    // step ahead); the other assignment is as fast at 8192^3 and ~2 % slower
-    // on 16384x2048x7168
-    static constexpr bool DEEP_B = true;
+    // Which operand gets the 3-slot ring (loads two steps ahead; the other
+    // one step ahead): B when both operands are k-contiguous, A with a
+    // row-major B.  Measured: the two choices are alike at 8192^3; with a
+    // row-major B, the deep A ring is ~3 % faster at 4096^3 and alike on
+    // 16384x2048x7168.
+    static constexpr bool DEEP_B = BKM;
     static constexpr int A_SLOTS = DEEP_B ? 2 : 3, B_SLOTS = DEEP_B ? 3 : 2;
     static constexpr int LDS_BYTES = (A_SLOTS + B_SLOTS) * OPS;
     static constexpr int LOADS = 256 / 8 / (NT / 64);        // 1-KiB loads per wave per operand step
@@ -615,22 +639,31 @@ struct DtlTile {
                 bfr[jn] = (8 * (g >> 1) + j4) * BROW + (((wn0 >> 5) + jn) ^ j4) * 64 + 32 * (g & 1) + 8 * q;
         }
     }
+    // With a row-major B the loads go through inline assembly (see
+    // load_to_lds16: otherwise every transpose read waits for all of them);
+    // with k-contiguous operands only there are no transpose reads and the
+    // compiler's builtin measured ~0.5 % faster at 8192^3.
+    static __device__ __forceinline__ void dtl_load(__amdgpu_buffer_rsrc_t r, char *dst, uint32_t off)
+    {
+        if constexpr (BKM)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)dst, 16, off, 0, 0, 0);
+        else
+            load_to_lds16(r, lds_addr(dst), off);
+    }
     // load j of this wave into `slot`; for k-contiguous rows k_left = k
     // remaining from the step's first k (chunks at or past it read as zero;
     // a row-major B's rows past K lie beyond its resource)
     __device__ __forceinline__ void load_a(__amdgpu_buffer_rsrc_t r, char *slot, int wave, int j, int k_left) const
     {
         const uint32_t off = kc[j] < k_left ? va[j] : kOOB;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)(slot + (wave * LOADS + j) * 1024), 16, off, 0, 0,
-                                                 0);
+        dtl_load(r, slot + (wave * LOADS + j) * 1024, off);
     }
     __device__ __forceinline__ void load_b(__amdgpu_buffer_rsrc_t r, char *slot, int wave, int j, int k_left) const
     {
         uint32_t off = vb[j];
         if constexpr (BKM)
             off = kc[j] < k_left ? off : kOOB;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)(slot + (wave * LOADS + j) * 1024), 16, off, 0, 0,
-                                                 0);
+        dtl_load(r, slot + (wave * LOADS + j) * 1024, off);
     }
 
     template <int KS>
