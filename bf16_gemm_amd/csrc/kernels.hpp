@@ -193,6 +193,112 @@ __global__ void __launch_bounds__(T::NT) grouped_kernel(GroupedArgs p)
     }
 }
 
+// The grouped task list without LDS, for tiles that use all of it: every
+// wave builds the same per-expert task counts in registers.  Lane l holds
+// experts 4l .. 4l+3 (num_groups <= 256); a wave-wide inclusive scan of the
+// lanes' sums gives each lane the number of tasks before its experts, and
+// the lane holding task t is the number of lanes whose tasks all come
+// before t (a ballot: the prefix sums do not decrease).
+struct WaveTasks {
+    int cnt[4];   // tasks of experts 4 lane + i
+    int excl;     // tasks of all experts before 4 lane
+    int total;
+
+    __device__ __forceinline__ static void rows_of(const GroupedArgs &p, int e, int &lo, int &hi)
+    {
+        lo = min(max(p.offs[e], 0), p.max_rows);
+        hi = min(max(p.offs[e + 1], lo), p.max_rows);
+    }
+    __device__ __forceinline__ void build(const GroupedArgs &p, int bm, int lane)
+    {
+        int sum = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int e = 4 * lane + i;
+            int c = 0;
+            if (e < p.G) {
+                int lo, hi;
+                rows_of(p, e, lo, hi);
+                const int rows = hi - lo;
+                if (rows > 0 && rows >= p.bucket_lo && rows < p.bucket_hi)
+                    c = (rows + bm - 1) / bm * p.tiles_n;
+            }
+            cnt[i] = c;
+            sum += c;
+        }
+        int incl = sum;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int v = __shfl_up(incl, d, 64);
+            if (lane >= d)
+                incl += v;
+        }
+        excl = incl - sum;
+        total = __shfl(incl, 63, 64);
+    }
+    // expert e and index inside it of task t (uniform, 0 <= t < total)
+    __device__ __forceinline__ void find(int t, int &e, int &local) const
+    {
+        const int incl = excl + cnt[0] + cnt[1] + cnt[2] + cnt[3];
+        const int L = __popcll(__ballot(incl <= t));
+        int r = t - __builtin_amdgcn_readlane(excl, L);
+        const int c0 = __builtin_amdgcn_readlane(cnt[0], L);
+        const int c1 = __builtin_amdgcn_readlane(cnt[1], L);
+        const int c2 = __builtin_amdgcn_readlane(cnt[2], L);
+        int i = 0;
+        if (r >= c0) {
+            r -= c0;
+            i = 1;
+            if (r >= c1) {
+                r -= c1;
+                i = 2;
+                if (r >= c2) {
+                    r -= c2;
+                    i = 3;
+                }
+            }
+        }
+        e = 4 * L + i;
+        local = r;
+    }
+};
+
+// grouped_kernel with the task list in registers (WaveTasks), for tiles
+// whose rings fill the LDS.
+template <class T, bool B_KMAJOR, int IN, int OUT, int EPI>
+__global__ void __launch_bounds__(T::NT) grouped_kernel_wt(GroupedArgs p)
+{
+    __shared__ __attribute__((aligned(16))) char lds[T::LDS_BYTES];
+    WaveTasks wt;
+    wt.build(p, T::BM, (int)threadIdx.x & 63);
+    T tile;
+    const int grid = gridDim.x;
+    const int L = logical_block(blockIdx.x, grid, p.xcd_remap);
+    const uint16_t *A = (const uint16_t *)p.A;
+    const uint16_t *B = (const uint16_t *)p.B;
+    constexpr int esize = out_size(OUT);
+    for (int t = L; t < wt.total; t += grid) {
+        int e, local;
+        wt.find(t, e, local);
+        int rows0, rows1;
+        WaveTasks::rows_of(p, e, rows0, rows1);
+        const int rows_e = rows1 - rows0;
+        const int tm = (rows_e + T::BM - 1) / T::BM;
+        const int mb = local % tm, nb = local / tm;
+        const int m0 = rows0 + mb * T::BM, n0 = nb * T::BN;
+        const int m_valid = min(T::BM, rows_e - mb * T::BM);
+        const uint16_t *At = A + (int64_t)m0 * p.lda;
+        const uint16_t *Be = B + (int64_t)e * p.stride_b;
+        const uint16_t *Bt = B_KMAJOR ? Be + (int64_t)n0 * p.ldb : Be + n0;
+        const OperandSrc sa = operand_src<true>(At, p.lda, m_valid, p.K);
+        const OperandSrc sb = operand_src<B_KMAJOR>(Bt, p.ldb, p.N - n0, p.K);
+        tile.mainloop(lds, sa, p.lda, sb, p.ldb, p.K, opaque((int)threadIdx.x));
+        const int dcol0 = EPI == EPI_SILU_GATE ? n0 / 2 : n0;
+        char *Dt = (char *)p.D + ((int64_t)m0 * p.ldd + dcol0) * esize;
+        epilogue<T, EPI, OUT>(tile, Dt, p.ldd, m_valid, min(T::BN, p.N - n0), opaque((int)threadIdx.x));
+    }
+}
+
 // The last N % 4 output columns (at most three) when N is not a multiple of
 // four: one wave per (row, column) pair, fp32 partial sums over k reduced
 // across the wave.  Tiny next to the tiles, so kept plain.

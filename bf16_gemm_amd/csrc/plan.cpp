@@ -57,6 +57,8 @@ GroupedFn grouped_fn(int tile, bool bk, int in, int out, int epi)
     case TILE_128x128: return bf ? grouped_fn_128x128_bf16(bk, out, epi) : grouped_fn_128x128_f16(bk, out, epi);
     case TILE_32x256: return bf ? grouped_fn_32x256_bf16(bk, out, epi) : grouped_fn_32x256_f16(bk, out, epi);
     case TILE_64x256: return bf ? grouped_fn_64x256_bf16(bk, out, epi) : grouped_fn_64x256_f16(bk, out, epi);
+    case TILE_256x256_DTL:
+        return bf ? grouped_fn_256x256dtl_bf16(bk, out, epi) : grouped_fn_256x256dtl_f16(bk, out, epi);
     default: return nullptr;
     }
 }
@@ -357,7 +359,7 @@ static mgemm_status_t plan_grouped(const mgemm_grouped_desc_t *d, uint32_t flags
     // layer: 3.32 ms against 3.61 ms with 32/64/128-row classes; boundaries
     // at 97 or 193 rows and a third 128x128 class were slower).
     struct B { int tile, lo, hi; };
-    B buckets[2] = {{TILE_32x256, 1, 129}, {TILE_256x256, 129, 1 << 30}};
+    B buckets[2] = {{TILE_32x256, 1, 129}, {TILE_256x256_DTL, 129, 1 << 30}};
     int nb = 2;
     const int ft = forced_tile(flags);
     if (ft >= 0) {

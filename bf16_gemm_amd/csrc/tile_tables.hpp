@@ -29,9 +29,7 @@ hipError_t launch_dense(const DenseArgs &a, int grid, hipStream_t s)
     return launch_dense_tile<TileOf<BM, BN, WM, WN, AK, BK, IN>, AK, BK, IN, OUT>(a, grid, s);
 }
 
-// Grouped launches keep the register-staged engine: on the 64-expert MoE
-// layer the direct-to-LDS engine measured 3-10 % slower (with either
-// operand on its deeper ring).
+// Grouped launches of the register-staged tiles (task table in LDS).
 template <int BM, int BN, int WM, int WN, bool BK, int IN, int OUT, int EPI>
 hipError_t launch_grouped(const GroupedArgs &a, int grid, hipStream_t s)
 {
@@ -72,6 +70,30 @@ DenseFn dense_dtl_table(bool ak, bool bk, int out)
                               : launch_dense_tile<DtlTile<IN, true>, true, true, IN, same16<IN>()>;
     return out == OUT_F32 ? launch_dense_tile<DtlTile<IN, false>, true, false, IN, OUT_F32>
                           : launch_dense_tile<DtlTile<IN, false>, true, false, IN, same16<IN>()>;
+}
+
+// Grouped launches of the direct-to-LDS tile: its rings fill the LDS, so
+// the task list lives in registers (grouped_kernel_wt).
+template <bool BK, int IN, int OUT, int EPI>
+hipError_t launch_grouped_dtl(const GroupedArgs &a, int grid, hipStream_t s)
+{
+    using T = DtlTile<IN, BK>;
+    hipLaunchKernelGGL((grouped_kernel_wt<T, BK, IN, OUT, EPI>), dim3(grid), dim3(T::NT), 0, s, a);
+    return hipGetLastError();
+}
+
+template <int IN>
+GroupedFn grouped_dtl_table(bool bk, int out, int epi)
+{
+    if (out != OUT_F32 && out != same16<IN>())
+        return nullptr;
+    const bool f32 = out == OUT_F32;
+#define MG_G(BKV, OUTV) (epi == EPI_NONE ? launch_grouped_dtl<BKV, IN, OUTV, EPI_NONE> \
+                                         : launch_grouped_dtl<BKV, IN, OUTV, EPI_SILU_GATE>)
+    if (bk)
+        return f32 ? MG_G(true, OUT_F32) : MG_G(true, same16<IN>());
+    return f32 ? MG_G(false, OUT_F32) : MG_G(false, same16<IN>());
+#undef MG_G
 }
 
 template <int BM, int BN, int WM, int WN, int IN>

@@ -61,7 +61,8 @@ BUCKET_COUNTS = [0, 1, 5, 31, 32, 33, 64, 65, 100, 128, 129, 200, 256, 257, 300,
 
 
 GROUPED_TILES = {"auto": 0, "256": mg.PLAN_FORCE_TILE_256x256, "128": mg.PLAN_FORCE_TILE_128x128,
-                 "32n": mg.PLAN_FORCE_TILE_32x256, "64n": mg.PLAN_FORCE_TILE_64x256}
+                 "32n": mg.PLAN_FORCE_TILE_32x256, "64n": mg.PLAN_FORCE_TILE_64x256,
+                 "256d": mg.PLAN_FORCE_TILE_256x256_DTL}
 
 
 @pytest.mark.parametrize("tile", list(GROUPED_TILES))
@@ -87,16 +88,39 @@ def test_grouped_plain_all_buckets(tile, b_layout, variant):
     assert np.all(tail == 0xFF), "rows past the routed rows were written"
 
 
+@pytest.mark.parametrize("tile", ["auto", "256", "256d"])
+def test_grouped_256_experts(tile):
+    """The most experts a plan takes (256): many empty, the rest from 1 to
+    600 rows, so tasks sit in every lane and slot of the register task list
+    of the direct-to-LDS launch, and in every entry of the LDS table of the
+    register-staged one.  Integer data, bit-exact."""
+    rs = np.random.RandomState(5)
+    counts = [int(c) if rs.rand() < 0.7 else 0 for c in rs.randint(1, 600, size=256)]
+    counts[255] = 300   # the last expert is not empty
+    N, K = 256, 136
+    log(f"case grouped 256 experts tile={tile} rows={sum(counts)}")
+    A, W, off = make_case(counts, N, K, 6, "int")
+    rows = int(off[-1])
+    D, raw, plan = grouped(to_dev(A, "bf16"), to_dev(W, "bf16"), torch.from_numpy(off).cuda(), 256, rows, N, K,
+                           extra_rows=1, flags=GROUPED_TILES[tile])
+    ref = oracle.grouped_ref(A, W, off)
+    assert_bits_equal(from_dev_bits(D[:rows]), ref, "bf16", plan.describe())
+
+
+@pytest.mark.parametrize("tile", ["auto", "256"])
 @pytest.mark.parametrize("variant", ["random", "int"])
-def test_grouped_silu_gate_small_moe(variant):
+def test_grouped_silu_gate_small_moe(variant, tile):
+    """FC1 with the SiLU gate and FC2, planner buckets (large experts on the
+    direct-to-LDS tile) and the register-staged 256x256 tile for all."""
     cfg = datagen.MOE["moe_small"]
-    log(f"case grouped silu small {variant}")
+    fl = GROUPED_TILES[tile]
+    log(f"case grouped silu small {variant} tile={tile}")
     r, A, W1, W2 = datagen.moe_inputs_host(cfg, variant)
     rows = int(r.offsets[-1])
     offs = torch.from_numpy(r.offsets).cuda()
     H, I = cfg.hidden, cfg.inter
     h_dev, _, plan = grouped(to_dev(A, "bf16"), to_dev(W1, "bf16"), offs, cfg.num_experts, rows, 2 * I, H,
-                             epi=mg.EPI_SILU_GATE_I8, extra_rows=2)
+                             epi=mg.EPI_SILU_GATE_I8, extra_rows=2, flags=fl)
     g = oracle.grouped_ref(A, W1, r.offsets)
     h_ref = oracle.silu_gate(g)
     h_got = from_dev_bits(h_dev[:rows])
@@ -106,7 +130,8 @@ def test_grouped_silu_gate_small_moe(variant):
     # FC2 on the GPU's own h: its oracle input must not come from the GPU, so
     # FC2 is checked here on the oracle's h (bits), run on the GPU as well
     h_bits = oracle.encode(h_ref, "bf16")
-    y_dev, _, plan2 = grouped(to_dev(h_bits, "bf16"), to_dev(W2, "bf16"), offs, cfg.num_experts, rows, H, I)
+    y_dev, _, plan2 = grouped(to_dev(h_bits, "bf16"), to_dev(W2, "bf16"), offs, cfg.num_experts, rows, H, I,
+                              flags=fl)
     y_ref = oracle.grouped_ref(h_bits, W2, r.offsets)
     assert_close(from_dev_bits(y_dev[:rows]), y_ref, I, "bf16", plan2.describe())
 

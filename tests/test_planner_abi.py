@@ -151,9 +151,15 @@ def test_direct_to_lds_tile_choice():
         with pytest.raises(mg.MgemmError) as e:
             mg.gemm_plan(512, 512, 512, "bf16", flags=mg.PLAN_FORCE_TILE_256x256_DTL, **kw)
         assert e.value.status == mg.ERR_UNSUPPORTED
-    with pytest.raises(mg.MgemmError) as e:
-        mg.grouped_gemm_plan(4, 64, 256, 128, b_layout="col", flags=mg.PLAN_FORCE_TILE_256x256_DTL)
-    assert e.value.status == mg.ERR_UNSUPPORTED
+    # grouped: the large-expert bucket runs on the direct-to-LDS tile (task
+    # list in registers); forcing the 256x256 tile keeps the register engine
+    g = mg.grouped_gemm_plan(64, 32768, 4096, 7168)
+    assert "[129,inf)->256x256dtl" in g.describe() and "[1,129)->32x256" in g.describe()
+    for bl in ("row", "col"):
+        g = mg.grouped_gemm_plan(4, 64, 256, 128, b_layout=bl, flags=mg.PLAN_FORCE_TILE_256x256_DTL)
+        assert "->256x256dtl" in g.describe()
+        g = mg.grouped_gemm_plan(4, 64, 256, 128, b_layout=bl, flags=mg.PLAN_FORCE_TILE_256x256)
+        assert "->256x256 " in g.describe()
 
 
 def test_lds_budget_rejects_three_stage_macro_tile():
