@@ -741,8 +741,11 @@ struct DtlTile {
             abase[ks] = ra * kRowBytes + (((2 * ks + fk) ^ swz(ra)) << 4);
             bbase[ks] = rb * kRowBytes + (((2 * ks + fk) ^ swz(rb)) << 4);
         }
-        // steps past the end load from an empty range (zeros, no memory access)
-        auto rsrc = [&](const OperandSrc &s, int st) { return st < ksteps ? s.at_step(st) : make_rsrc(s.base, 0); };
+        // Steps past the end need no special resource: a k-contiguous
+        // operand's loads then all take the out-of-range offset (k_left <= 0),
+        // and a row-major B's resource ends at its last row, so they read
+        // zeros without touching memory.
+        auto rsrc = [&](const OperandSrc &s, int st) { return s.at_step(st); };
         // the operand with the 3-slot ring ("deep") and the one with 2 slots
         char *const D0 = DEEP_B ? B0 : A0;
         char *const S0 = DEEP_B ? A0 : B0;
