@@ -111,9 +111,11 @@ typedef struct {
 #define MGEMM_PLAN_FORCE_TILE_32x256  0x4u   /* narrow-M (few tokens)   */
 #define MGEMM_PLAN_FORCE_TILE_64x256  0x8u   /* narrow-M (few tokens)   */
 /* 256x256 with loads that write LDS directly (no staging registers, eight
- * waves); dense plans with a row-major A only, else UNSUPPORTED.  The
- * planner uses it whenever it picks the 256x256 tile for such a plan;
- * MGEMM_PLAN_FORCE_TILE_256x256 then selects the register-staged engine. */
+ * waves).  Dense plans: row-major A only, else UNSUPPORTED; the planner uses
+ * it whenever it picks the 256x256 tile for such a plan.  Grouped plans
+ * (whose A is always row-major): the planner uses it for the experts of 129
+ * rows or more.  In both, MGEMM_PLAN_FORCE_TILE_256x256 selects the
+ * register-staged 256x256 engine instead. */
 #define MGEMM_PLAN_FORCE_TILE_256x256_DTL 0x10u
 #define MGEMM_PLAN_NO_XCD_REMAP       0x100u /* plain tile order        */
 /* Dense plans: fix the number of K ranges per output tile (1..64; 1 turns
