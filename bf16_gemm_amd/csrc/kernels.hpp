@@ -201,6 +201,8 @@ __global__ void __launch_bounds__(T::NT) grouped_kernel(GroupedArgs p)
 // before t (a ballot: the prefix sums do not decrease).
 struct WaveTasks {
     int cnt[4];   // tasks of experts 4 lane + i
+    int row0[4];  // their first row and row count (clamped offsets)
+    int nrow[4];
     int excl;     // tasks of all experts before 4 lane
     int total;
 
@@ -215,14 +217,16 @@ struct WaveTasks {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int e = 4 * lane + i;
-            int c = 0;
+            int c = 0, lo = 0, rows = 0;
             if (e < p.G) {
-                int lo, hi;
+                int hi;
                 rows_of(p, e, lo, hi);
-                const int rows = hi - lo;
+                rows = hi - lo;
                 if (rows > 0 && rows >= p.bucket_lo && rows < p.bucket_hi)
                     c = (rows + bm - 1) / bm * p.tiles_n;
             }
+            row0[i] = lo;
+            nrow[i] = rows;
             cnt[i] = c;
             sum += c;
         }
@@ -236,8 +240,10 @@ struct WaveTasks {
         excl = incl - sum;
         total = __shfl(incl, 63, 64);
     }
-    // expert e and index inside it of task t (uniform, 0 <= t < total)
-    __device__ __forceinline__ void find(int t, int &e, int &local) const
+    // expert e, index inside it, first row and row count of task t
+    // (uniform, 0 <= t < total); lane reads only, no memory access, so no
+    // wait for the previous task's stores
+    __device__ __forceinline__ void find(int t, int &e, int &local, int &rows0, int &rows_e) const
     {
         const int incl = excl + cnt[0] + cnt[1] + cnt[2] + cnt[3];
         const int L = __popcll(__ballot(incl <= t));
@@ -260,6 +266,12 @@ struct WaveTasks {
         }
         e = 4 * L + i;
         local = r;
+        const int lo0 = __builtin_amdgcn_readlane(row0[0], L), lo1 = __builtin_amdgcn_readlane(row0[1], L);
+        const int lo2 = __builtin_amdgcn_readlane(row0[2], L), lo3 = __builtin_amdgcn_readlane(row0[3], L);
+        const int n0 = __builtin_amdgcn_readlane(nrow[0], L), n1 = __builtin_amdgcn_readlane(nrow[1], L);
+        const int n2 = __builtin_amdgcn_readlane(nrow[2], L), n3 = __builtin_amdgcn_readlane(nrow[3], L);
+        rows0 = i == 0 ? lo0 : i == 1 ? lo1 : i == 2 ? lo2 : lo3;
+        rows_e = i == 0 ? n0 : i == 1 ? n1 : i == 2 ? n2 : n3;
     }
 };
 
@@ -278,11 +290,8 @@ __global__ void __launch_bounds__(T::NT) grouped_kernel_wt(GroupedArgs p)
     const uint16_t *B = (const uint16_t *)p.B;
     constexpr int esize = out_size(OUT);
     for (int t = L; t < wt.total; t += grid) {
-        int e, local;
-        wt.find(t, e, local);
-        int rows0, rows1;
-        WaveTasks::rows_of(p, e, rows0, rows1);
-        const int rows_e = rows1 - rows0;
+        int e, local, rows0, rows_e;
+        wt.find(t, e, local, rows0, rows_e);
         const int tm = (rows_e + T::BM - 1) / T::BM;
         const int mb = local % tm, nb = local / tm;
         const int m0 = rows0 + mb * T::BM, n0 = nb * T::BN;
