@@ -44,6 +44,7 @@ typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kBK = 64;                 // k per LDS slot
 constexpr int kRowBytes = kBK * 2;      // bytes of one tile row in LDS
@@ -307,6 +308,7 @@ __device__ __forceinline__ f32x16_t mfma32(u32x4_t a, u32x4_t b, f32x16_t c)
 template <int BM_, int BN_, int WM_, int WN_, bool A_KMAJOR, bool B_KMAJOR, int IN, int NS_ = 2>
 struct Tile {
     static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
+    static constexpr int MI = 32;   // MFMA block edge (v_mfma_f32_32x32x16)
     static constexpr int NS = NS_;  // staging register sets (global loads NS steps ahead)
     static constexpr int NT = 64 * WM * WN;
     static constexpr int TM = BM / WM, TN = BN / WN;  // wave sub-tile
@@ -574,75 +576,116 @@ __device__ __forceinline__ uint32_t lds_addr(const char *p) { return (uint32_t)(
 
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 
+
+template <int IN>
+__device__ __forceinline__ f32x4_t mfma16(u32x4_t a, u32x4_t b, f32x4_t c)
+{
+    if constexpr (IN == IN_BF16)
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                       __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
+                                                      __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+}
+
+// The direct-to-LDS 256 x 256 tile.  MFMA v_mfma_f32_16x16x32 (under
+// sustained load it runs ~11 % more FLOP/s than v_mfma_f32_32x32x16 at the
+// power-managed clock: 1944-1976 against 1746-1790 TFLOP/s in a
+// register-only loop); each wave's 128 x 64 outputs are 8 x 4 blocks of
+// 16 x 16 (4 accumulators per lane each).  A 64-k step is two 32-k
+// sub-steps, each run as two halves of 16 MFMAs (m blocks 0-3, then 4-7).
+// A fragments rotate through two sets of four (X, Y) and B fragments
+// through two (P, Q), each set read one half-step before its MFMAs:
+//   half 0: MFMAs X.P (s0, m 0-3), reads Y = A(s0, m 4-7), Q = B(s1)
+//   half 1: MFMAs Y.P (s0, m 4-7), reads X = A(s1, m 0-3)
+//   half 2: MFMAs X.Q (s1, m 0-3), reads Y = A(s1, m 4-7)
+//   half 3: barrier, then MFMAs Y.Q, reads X = A'(s0, m 0-3), P = B'(s0)
+// Operand lanes: lane l holds row (l mod 16), k 8(l/16) .. 8(l/16)+7 of the
+// 32-k block; B is the instruction's first operand, so the accumulator of
+// lane l holds output row (l mod 16) of the block, columns 4(l/16) .. +3.
 // BKM: B k-contiguous ([n][k], column-major B).  Otherwise B is row-major
-// ([k][n]) and is kept that way in LDS: 64 rows of 512 bytes per step, the
-// 64-byte segments of row k XOR-permuted by (k & 3), and its MFMA fragments
-// are read with ds_read_b64_tr_b16.  Within each group of 16 lanes that
-// instruction hands lane i the elements (4j + i/4, i % 4), j = 0..3, of the
-// 16 x 4 block formed by the lanes' 8-byte pieces; so when lane 4j + q of
-// the group points at B[k0 + j][n0 + 4q .. n0 + 4q + 3], lane i receives
-// B[k0 .. k0 + 3][n0 + i] -- four consecutive k of one column, half of the
-// eight a 32x32x16 MFMA lane needs.  The four rows one group reads lie in
-// distinct 64-byte bank groups thanks to the (k & 3) permutation.
+// ([k][n]) and is kept that way in LDS: 64 rows of 512 bytes per step, its
+// fragments read with ds_read_b64_tr_b16.  Within each group of 16 lanes
+// that instruction hands lane i the elements (4j + i/4, i % 4), j = 0..3,
+// of the 16 x 4 block formed by the lanes' 8-byte pieces; so when lane
+// 4j + q of the group points at B[k0 + j][n0 + 4q .. n0 + 4q + 3], lane i
+// receives B[k0 .. k0 + 3][n0 + i], and two reads give the eight k of a
+// lane.  The 64-byte segments of row k are XOR-permuted by (k & 3), so the
+// four rows one group reads fall in distinct bank groups, and the 32-byte
+// halves of each segment are swapped on bit 3 of k, so that the groups
+// reading k rows 8 apart (0/1, 2/3) use disjoint banks.
 template <int IN, bool BKM>
 struct DtlTile {
     static constexpr int BM = 256, BN = 256, WM = 2, WN = 4;
+    static constexpr int MI = 16;
     static constexpr int NT = 64 * WM * WN;
-    static constexpr int TM = BM / WM, TN = BN / WN, FM = TM / 32, FN = TN / 32;
-    static constexpr int OPS = 256 * kRowBytes;              // one operand, one K step (32 KiB)
-    // Which operand gets the 3-slot ring (loads two steps ahead; the other
-    // one step ahead): B when both operands are k-contiguous, A with a
-    // row-major B.  Measured: the two choices are alike at 8192^3; with a
-    // row-major B, the deep A ring is ~3 % faster at 4096^3 and alike on
-    // 16384x2048x7168.
+    static constexpr int TM = BM / WM, TN = BN / WN, FM = TM / 16, FN = TN / 16;
+    static constexpr int OPS = 256 * kRowBytes;
     static constexpr bool DEEP_B = BKM;
     static constexpr int A_SLOTS = DEEP_B ? 2 : 3, B_SLOTS = DEEP_B ? 3 : 2;
     static constexpr int LDS_BYTES = (A_SLOTS + B_SLOTS) * OPS;
-    static constexpr int LOADS = 256 / 8 / (NT / 64);        // 1-KiB loads per wave per operand step
-    static constexpr int BROW = 512;                         // bytes of one k row of a row-major B step
+    static constexpr int LOADS = 256 / 8 / (NT / 64);
+    static constexpr int BROW = 512;
+    static_assert(FM == 8 && FN == 4, "the half-step rotation assumes 8 x 4 blocks per wave");
 
-    f32x16_t acc[FM][FN];
-    struct Frags {
-        u32x4_t a[FM], b[FN];
+    f32x4_t acc[FM][FN];
+    struct F4 {
+        u32x4_t v[4];
     };
 
-    // per lane: byte offset (within a step) of its 16 bytes in load j of
-    // its wave, and (k-contiguous rows) the k of that chunk
     uint32_t va[LOADS], vb[LOADS];
     int kc[LOADS];
-    int bfr[FN];   // row-major B: LDS offset of this lane's fragment piece of column block j (ks = 0, h = 0)
+    int abase[2], bbase[2];   // k-contiguous fragments of sub-step s (any block: add 16 rows per block)
 
-    __device__ __forceinline__ void setup(int lane, int wave, int wn0, int lda, int ldb)
+    // Chunk swizzle of this tile's 128-byte rows: bits (r1, r0 ^ r3, r2) of
+    // the row.  The LDS serves a 16-byte read to lanes l and l + 32 in the
+    // same cycle (with 64 four-byte banks); those lanes read one row at
+    // chunks c and c ^ 2, so the eight rows an 8-lane group reads must have
+    // swizzles in distinct classes of {x, x ^ 2} among rows of one parity:
+    // r1 and r2 give that, and r0 ^ r3 keeps 16 consecutive rows apart as
+    // well.  (Tile's swz gives rows 0, 2, 4, 6 the values 0, 2, 4, 6: a
+    // two-way conflict for this operand layout, measured.)  It depends on
+    // the low four bits only, so blocks 16 rows apart share it.
+    static __device__ __forceinline__ int dswz(int row)
     {
-        const int r = lane >> 3;
+        return ((row >> 1) & 1) | ((((row) ^ (row >> 3)) & 1) << 1) | (((row >> 2) & 1) << 2);
+    }
+    int bfr[4];               // row-major B: transpose-read piece of n block jb (s = 0, h = 0)
+
+    __device__ __forceinline__ void setup(int lane, int wave, int wm0, int wn0, int lda, int ldb)
+    {
+        const int r8 = lane >> 3;
 #pragma unroll
         for (int j = 0; j < LOADS; ++j) {
-            const int row = (wave * LOADS + j) * 8 + r;
-            const int c = (lane & 7) ^ swz(row);
+            const int row = (wave * LOADS + j) * 8 + r8;
+            const int c = (lane & 7) ^ dswz(row);
             kc[j] = c * 8;
             va[j] = (uint32_t)row * (uint32_t)lda * 2u + (uint32_t)c * 16u;
             if constexpr (BKM) {
                 vb[j] = (uint32_t)row * (uint32_t)ldb * 2u + (uint32_t)c * 16u;
             } else {
-                // two k rows of 512 bytes per load: lane l writes physical
-                // chunk l & 31 of row 2 * (wave * LOADS + j) + (l >> 5)
                 const int kr = (wave * LOADS + j) * 2 + (lane >> 5);
                 const int pc = lane & 31;
                 const int seg = (pc >> 2) ^ (kr & 3);
-                vb[j] = (uint32_t)kr * (uint32_t)ldb * 2u + (uint32_t)(seg * 64 + (pc & 3) * 16);
+                const int w = (pc & 3) ^ (((kr >> 3) & 1) << 1);
+                vb[j] = (uint32_t)kr * (uint32_t)ldb * 2u + (uint32_t)(seg * 64 + w * 16);
             }
         }
-        if constexpr (!BKM) {
-            const int g = lane >> 4, rr = lane & 15, j4 = rr >> 2, q = rr & 3;
+        const int r = lane & 15, q = lane >> 4;
+        const int c0 = q ^ dswz(r);
 #pragma unroll
-            for (int jn = 0; jn < FN; ++jn)
-                bfr[jn] = (8 * (g >> 1) + j4) * BROW + (((wn0 >> 5) + jn) ^ j4) * 64 + 32 * (g & 1) + 8 * q;
+        for (int s = 0; s < 2; ++s) {
+            abase[s] = (wm0 + r) * kRowBytes + ((c0 ^ (4 * s)) << 4);
+            bbase[s] = (wn0 + r) * kRowBytes + ((c0 ^ (4 * s)) << 4);
+        }
+        if constexpr (!BKM) {
+            const int jj = r >> 2, qq = r & 3;
+#pragma unroll
+            for (int jb = 0; jb < 4; ++jb)
+                bfr[jb] = (8 * q + jj) * BROW + ((((wn0 >> 5) + (jb >> 1)) ^ jj) * 64) +
+                          ((32 * (jb & 1) + 8 * qq) ^ (32 * (q & 1)));
         }
     }
-    // With a row-major B the loads go through inline assembly (see
-    // load_to_lds16: otherwise every transpose read waits for all of them);
-    // with k-contiguous operands only there are no transpose reads and the
-    // compiler's builtin measured ~0.5 % faster at 8192^3.
     static __device__ __forceinline__ void dtl_load(__amdgpu_buffer_rsrc_t r, char *dst, uint32_t off)
     {
         if constexpr (BKM)
@@ -650,9 +693,6 @@ struct DtlTile {
         else
             load_to_lds16(r, lds_addr(dst), off);
     }
-    // load j of this wave into `slot`; for k-contiguous rows k_left = k
-    // remaining from the step's first k (chunks at or past it read as zero;
-    // a row-major B's rows past K lie beyond its resource)
     __device__ __forceinline__ void load_a(__amdgpu_buffer_rsrc_t r, char *slot, int wave, int j, int k_left) const
     {
         const uint32_t off = kc[j] < k_left ? va[j] : kOOB;
@@ -666,43 +706,47 @@ struct DtlTile {
         dtl_load(r, slot + (wave * LOADS + j) * 1024, off);
     }
 
-    template <int KS>
-    __device__ __forceinline__ void read_frags(const char *as, const char *bs, const int (&abase)[4],
-                                               const int (&bbase)[4], Frags &f) const
+    // A fragments of m blocks 4 HM .. 4 HM + 3, sub-step S
+    template <int S, int HM>
+    __device__ __forceinline__ void read_a(const char *as, F4 &f) const
     {
 #pragma unroll
-        for (int i = 0; i < FM; ++i)
-            f.a[i] = *(const u32x4_t *)(as + abase[KS ^ ((i & 1) * 2)] + i * 32 * kRowBytes);
+        for (int ii = 0; ii < 4; ++ii)
+            f.v[ii] = *(const u32x4_t *)(as + abase[S] + (4 * HM + ii) * 16 * kRowBytes);
+    }
+    // B fragments of the four n blocks, sub-step S
+    template <int S>
+    __device__ __forceinline__ void read_b(const char *bs, F4 &f) const
+    {
         if constexpr (BKM) {
 #pragma unroll
-            for (int j = 0; j < FN; ++j)
-                f.b[j] = *(const u32x4_t *)(bs + bbase[KS ^ ((j & 1) * 2)] + j * 32 * kRowBytes);
+            for (int jb = 0; jb < 4; ++jb)
+                f.v[jb] = *(const u32x4_t *)(bs + bbase[S] + jb * 16 * kRowBytes);
         } else {
+            typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
 #pragma unroll
-            for (int j = 0; j < FN; ++j) {
-                typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
-                const char *p = bs + bfr[j] + 16 * KS * BROW;
+            for (int jb = 0; jb < 4; ++jb) {
+                const char *p = bs + bfr[jb] + 32 * S * BROW;
                 const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)p);
                 const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(p + 4 * BROW));
                 const u32x2_t l2 = __builtin_bit_cast(u32x2_t, lo), h2 = __builtin_bit_cast(u32x2_t, hi);
-                f.b[j] = u32x4_t{l2[0], l2[1], h2[0], h2[1]};
+                f.v[jb] = u32x4_t{l2[0], l2[1], h2[0], h2[1]};
             }
         }
     }
-    __device__ __forceinline__ void mfmas(const Frags &f)
+    template <int HM>
+    __device__ __forceinline__ void mfmas(const F4 &a, const F4 &b)
     {
 #pragma unroll
-        for (int i = 0; i < FM; ++i)
+        for (int ii = 0; ii < 4; ++ii)
 #pragma unroll
-            for (int j = 0; j < FN; ++j)
-                acc[i][j] = mfma32<IN>(f.b[j], f.a[i], acc[i][j]);
+            for (int jb = 0; jb < 4; ++jb)
+                acc[4 * HM + ii][jb] = mfma16<IN>(b.v[jb], a.v[ii], acc[4 * HM + ii][jb]);
     }
-    // the FM*FN MFMAs of a sub-step, each of the first NR followed by a
-    // fragment read, NV loads spread evenly after them
     template <int I, int NR, int NV>
     static __device__ __forceinline__ void pattern()
     {
-        constexpr int NM = FM * FN;
+        constexpr int NM = 16;
         if constexpr (I < NM) {
             __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
             if constexpr (I < NR)
@@ -712,7 +756,7 @@ struct DtlTile {
             pattern<I + 1, NR, NV>();
         }
     }
-    static constexpr int NREADS = FM + (BKM ? FN : 2 * FN);   // LDS read instructions per sub-step
+    static constexpr int RB = BKM ? 4 : 8;   // LDS read instructions for the four B fragments
 
     __device__ __forceinline__ void mainloop(char *lds, const OperandSrc &sa, int lda, const OperandSrc &sb, int ldb,
                                              int K, int tid)
@@ -726,27 +770,13 @@ struct DtlTile {
         for (int i = 0; i < FM; ++i)
 #pragma unroll
             for (int j = 0; j < FN; ++j)
-                acc[i][j] = f32x16_t{};
+                acc[i][j] = f32x4_t{};
         const int ksteps = (K + kBK - 1) / kBK;
         if (ksteps <= 0)
             return;
-        setup(lane, wave, wn0, lda, ldb);
+        setup(lane, wave, wm0, wn0, lda, ldb);
         char *const A0 = lds;
         char *const B0 = lds + A_SLOTS * OPS;
-        const int frow = lane & 31, fk = lane >> 5;
-        int abase[4], bbase[4];
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            const int ra = wm0 + frow, rb = wn0 + frow;
-            abase[ks] = ra * kRowBytes + (((2 * ks + fk) ^ swz(ra)) << 4);
-            bbase[ks] = rb * kRowBytes + (((2 * ks + fk) ^ swz(rb)) << 4);
-        }
-        // Steps past the end need no special resource: a k-contiguous
-        // operand's loads then all take the out-of-range offset (k_left <= 0),
-        // and a row-major B's resource ends at its last row, so they read
-        // zeros without touching memory.
-        auto rsrc = [&](const OperandSrc &s, int st) { return s.at_step(st); };
-        // the operand with the 3-slot ring ("deep") and the one with 2 slots
         char *const D0 = DEEP_B ? B0 : A0;
         char *const S0 = DEEP_B ? A0 : B0;
         const OperandSrc &sd = DEEP_B ? sb : sa;
@@ -763,10 +793,9 @@ struct DtlTile {
             else
                 load_b(r, slot, wave, j, k_left);
         };
-
         // prologue: both operands of steps 0 and 1; wait for step 0
         {
-            const auto rd0 = rsrc(sd, 0), rs0 = rsrc(ss, 0), rd1 = rsrc(sd, 1), rs1 = rsrc(ss, 1);
+            const auto rd0 = sd.at_step(0), rs0 = ss.at_step(0), rd1 = sd.at_step(1), rs1 = ss.at_step(1);
 #pragma unroll
             for (int j = 0; j < LOADS; ++j) {
                 load_d(rd0, D0, j, K);
@@ -781,8 +810,9 @@ struct DtlTile {
             wait_vm<2 * LOADS>();
         }
         lds_barrier();
-        Frags f0, f1;
-        read_frags<0>(A0, B0, abase, bbase, f0);
+        F4 X, Y, P, Q;
+        read_a<0, 0>(A0, X);
+        read_b<0>(B0, P);
         int sd_cur = 0, sd_next = 1, sd_fill = 2;   // deep slots of steps kt, kt+1, kt+2
         for (int kt = 0; kt < ksteps; ++kt) {
             const int s_cur = kt & 1, s_next = (kt + 1) & 1;
@@ -792,52 +822,53 @@ struct DtlTile {
             const char *bn = (DEEP_B ? D0 + sd_next * OPS : S0 + s_next * OPS);
             char *dw = D0 + sd_fill * OPS;
             char *sw = S0 + s_cur * OPS;
-            const auto rD = rsrc(sd, kt + 2);
+            const auto rD = sd.at_step(kt + 2);
             const int kd = K - (kt + 2) * kBK;
-            // sub-steps 0 and 1: the deep operand of step kt+2, into the slot
-            // step kt-1 used
-            read_frags<1>(ac, bc, abase, bbase, f1);
+            // half 0 (sub-step 0, m blocks 0-3): the deep operand's first loads
+            read_a<0, 1>(ac, Y);
+            read_b<1>(bc, Q);
 #pragma unroll
             for (int j = 0; j < H; ++j)
                 load_d(rD, dw, j, kd);
-            mfmas(f0);
-            pattern<0, NREADS, H>();
+            mfmas<0>(X, P);
+            pattern<0, 4 + RB, H>();
             __builtin_amdgcn_sched_barrier(0);
-            read_frags<2>(ac, bc, abase, bbase, f0);
+            // half 1 (sub-step 0, m blocks 4-7)
+            read_a<1, 0>(ac, X);
 #pragma unroll
             for (int j = H; j < LOADS; ++j)
                 load_d(rD, dw, j, kd);
-            mfmas(f1);
-            pattern<0, NREADS, H>();
+            mfmas<1>(Y, P);
+            pattern<0, 4, H>();
             __builtin_amdgcn_sched_barrier(0);
-            // sub-step 2: the last reads of step kt
-            read_frags<3>(ac, bc, abase, bbase, f1);
-            mfmas(f0);
-            pattern<0, NREADS, 0>();
+            // half 2 (sub-step 1, m blocks 0-3): the last reads of step kt
+            read_a<1, 1>(ac, Y);
+            mfmas<0>(X, Q);
+            pattern<0, 4, 0>();
             __builtin_amdgcn_sched_barrier(0);
-            // sub-step 3: step kt+1 must be in LDS (only the deep loads of
-            // step kt+2 may still be in flight), and every wave must be done
-            // with step kt; then the 2-slot operand of step kt+2 goes into
-            // the slot step kt leaves
+            // half 3 (sub-step 1, m blocks 4-7): step kt+1 must be in LDS and
+            // every wave done with step kt; then the 2-slot operand of step
+            // kt+2 goes into the slot step kt leaves
             wait_vm<LOADS>();
             lds_barrier();
-            read_frags<0>(an, bn, abase, bbase, f0);
+            read_a<0, 0>(an, X);
+            read_b<0>(bn, P);
             {
-                const auto rS = rsrc(ss, kt + 2);
+                const auto rS = ss.at_step(kt + 2);
                 const int ks2 = K - (kt + 2) * kBK;
 #pragma unroll
                 for (int j = 0; j < LOADS; ++j)
                     load_s(rS, sw, j, ks2);
             }
-            mfmas(f1);
-            pattern<0, NREADS, LOADS>();
+            mfmas<1>(Y, Q);
+            pattern<0, 4 + RB, LOADS>();
             __builtin_amdgcn_sched_barrier(0);
             const int t = sd_cur;
             sd_cur = sd_next;
             sd_next = sd_fill;
             sd_fill = t;
         }
-        // nothing may still be writing LDS when the next tile starts
+        // the trailing loads (empty ranges) have landed before the next tile
         wait_vm<0>();
     }
 };
@@ -903,30 +934,57 @@ __device__ __forceinline__ void epilogue(const T &t, void *D, int64_t ldd, int m
         return;
     const __amdgpu_buffer_rsrc_t r =
         make_rsrc(D, ((uint64_t)(m_valid - 1) * (uint64_t)ldd + (uint64_t)out_cols) * (uint64_t)esize);
+    if constexpr (T::MI == 16) {
+        // 16 x 16 blocks: lane l holds row (l mod 16), columns 4(l/16) .. +3
 #pragma unroll
-    for (int i = 0; i < T::FM; ++i) {
-        const int m = wm0 + 32 * i + (lane & 31);
-        const uint32_t rowoff = (uint32_t)m * row_bytes;
+        for (int i = 0; i < T::FM; ++i) {
+            const int m = wm0 + 16 * i + (lane & 15);
+            const uint32_t rowoff = (uint32_t)m * row_bytes;
 #pragma unroll
-        for (int j = 0; j < T::FN; ++j) {
-            const f32x16_t &a = t.acc[i][j];
-            if constexpr (EPI == EPI_NONE) {
-#pragma unroll
-                for (int rg = 0; rg < 4; ++rg) {
-                    const int n = wn0 + 32 * j + 8 * rg + 4 * (lane >> 5);
+            for (int j = 0; j < T::FN; ++j) {
+                const f32x4_t &a = t.acc[i][j];
+                const int n = wn0 + 16 * j + 4 * (lane >> 4);
+                if constexpr (EPI == EPI_NONE) {
                     const uint32_t off = n < n_valid ? rowoff + (uint32_t)n * esize : kOOB;
-                    bstore4<OUT>(r, off, a[4 * rg], a[4 * rg + 1], a[4 * rg + 2], a[4 * rg + 3]);
-                }
-            } else {
-                // columns 8*rg..8*rg+7 of a 32-wide block are gate for rg
-                // even; the next eight are the matching up
-#pragma unroll
-                for (int rg = 0; rg < 4; rg += 2) {
-                    const int n = wn0 + 32 * j + 8 * rg + 4 * (lane >> 5);
+                    bstore4<OUT>(r, off, a[0], a[1], a[2], a[3]);
+                } else {
+                    // gate: columns 0-7 of the block (lanes 0-31); up: 8-15,
+                    // 32 lanes further on
+                    const float u0 = __shfl_xor(a[0], 32, 64), u1 = __shfl_xor(a[1], 32, 64);
+                    const float u2 = __shfl_xor(a[2], 32, 64), u3 = __shfl_xor(a[3], 32, 64);
                     const int hc = (n >> 4) * 8 + (n & 15);
-                    const uint32_t off = n < n_valid ? rowoff + (uint32_t)hc * esize : kOOB;
-                    bstore4<OUT>(r, off, silu_mul(a[4 * rg + 0], a[4 * rg + 4]), silu_mul(a[4 * rg + 1], a[4 * rg + 5]),
-                                 silu_mul(a[4 * rg + 2], a[4 * rg + 6]), silu_mul(a[4 * rg + 3], a[4 * rg + 7]));
+                    const uint32_t off = (lane < 32 && n < n_valid) ? rowoff + (uint32_t)hc * esize : kOOB;
+                    bstore4<OUT>(r, off, silu_mul(a[0], u0), silu_mul(a[1], u1), silu_mul(a[2], u2),
+                                 silu_mul(a[3], u3));
+                }
+            }
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < T::FM; ++i) {
+            const int m = wm0 + 32 * i + (lane & 31);
+            const uint32_t rowoff = (uint32_t)m * row_bytes;
+#pragma unroll
+            for (int j = 0; j < T::FN; ++j) {
+                const f32x16_t &a = t.acc[i][j];
+                if constexpr (EPI == EPI_NONE) {
+#pragma unroll
+                    for (int rg = 0; rg < 4; ++rg) {
+                        const int n = wn0 + 32 * j + 8 * rg + 4 * (lane >> 5);
+                        const uint32_t off = n < n_valid ? rowoff + (uint32_t)n * esize : kOOB;
+                        bstore4<OUT>(r, off, a[4 * rg], a[4 * rg + 1], a[4 * rg + 2], a[4 * rg + 3]);
+                    }
+                } else {
+                    // columns 8*rg..8*rg+7 of a 32-wide block are gate for rg
+                    // even; the next eight are the matching up
+#pragma unroll
+                    for (int rg = 0; rg < 4; rg += 2) {
+                        const int n = wn0 + 32 * j + 8 * rg + 4 * (lane >> 5);
+                        const int hc = (n >> 4) * 8 + (n & 15);
+                        const uint32_t off = n < n_valid ? rowoff + (uint32_t)hc * esize : kOOB;
+                        bstore4<OUT>(r, off, silu_mul(a[4 * rg + 0], a[4 * rg + 4]), silu_mul(a[4 * rg + 1], a[4 * rg + 5]),
+                                     silu_mul(a[4 * rg + 2], a[4 * rg + 6]), silu_mul(a[4 * rg + 3], a[4 * rg + 7]));
+                    }
                 }
             }
         }
