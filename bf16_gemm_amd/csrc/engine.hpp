@@ -991,4 +991,68 @@ __device__ __forceinline__ void epilogue(const T &t, void *D, int64_t ldd, int m
     }
 }
 
+// Epilogue of the 16 x 16 direct-to-LDS tile (no gate): the accumulators
+// go through LDS, which the K loop no longer needs, so that every store
+// instruction writes one whole tile row (64 lanes x 4 outputs: 1 KiB of
+// fp32 or 512 B of 16-bit) instead of 16 rows x 64 B.  Half the tile's rows
+// at a time: each wave stages its m blocks 4h .. 4h+3 (128 rows x 256
+// fp32 in all = 128 KiB), the 16-byte chunks of staged row x XOR-permuted
+// by (x & 15) so that the writes of 16 rows hit distinct banks; then each
+// wave stores every eighth staged row.  Every wave must call it (it meets
+// the others at workgroup barriers, which wait for LDS accesses only, so the
+// stores of one half need not complete before the next is staged); each wave
+// enters it with its own loads into the rings complete, so after the first
+// barrier nothing writes the rings any more.
+template <class T, int OUT>
+__device__ __forceinline__ void epilogue_staged(const T &t, char *lds, void *D, int64_t ldd, int m_valid,
+                                                int n_valid, int tid)
+{
+    static_assert(T::MI == 16 && T::BN == 256 && T::NT == 512 && T::LDS_BYTES >= 128 * 1024, "");
+    constexpr int esize = out_size(OUT);
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wm0 = (wave / T::WN) * T::TM;
+    const int wn0 = (wave % T::WN) * T::TN;
+    if (m_valid <= 0 || n_valid <= 0)
+        return;
+    const uint32_t row_bytes = (uint32_t)ldd * (uint32_t)esize;
+    const __amdgpu_buffer_rsrc_t r =
+        make_rsrc(D, ((uint64_t)(m_valid - 1) * (uint64_t)ldd + (uint64_t)n_valid) * (uint64_t)esize);
+    const int n = 4 * lane;
+    lds_barrier();
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+            const int x = (wm0 >> 1) + 16 * ii + (lane & 15);
+#pragma unroll
+            for (int jb = 0; jb < 4; ++jb) {
+                const int c = (wn0 + 16 * jb + 4 * (lane >> 4)) >> 2;
+                *(f32x4_t *)(lds + x * 1024 + ((c ^ (x & 15)) << 4)) = t.acc[4 * h + ii][jb];
+            }
+        }
+        lds_barrier();
+#pragma unroll 4
+        for (int x = wave; x < 128; x += 8) {
+            const f32x4_t v = *(const f32x4_t *)(lds + x * 1024 + ((lane ^ (x & 15)) << 4));
+            const int m = (x >> 6) * T::TM + 64 * h + (x & 63);
+            const uint32_t off = n < n_valid ? (uint32_t)m * row_bytes + (uint32_t)n * esize : kOOB;
+            bstore4<OUT>(r, off, v[0], v[1], v[2], v[3]);
+        }
+        lds_barrier();
+    }
+}
+
+// The tile's epilogue: staged through LDS for the direct-to-LDS tile
+// without a gate, else straight from the registers.
+template <class T, int EPI, int OUT>
+__device__ __forceinline__ void tile_epilogue(const T &t, char *lds, void *D, int64_t ldd, int m_valid, int n_valid,
+                                              int tid)
+{
+    if constexpr (T::MI == 16 && EPI == EPI_NONE)
+        epilogue_staged<T, OUT>(t, lds, D, ldd, m_valid, n_valid, tid);
+    else
+        epilogue<T, EPI, OUT>(t, D, ldd, m_valid, n_valid, tid);
+}
+
 }  // namespace mgemm

@@ -112,8 +112,8 @@ __global__ void __launch_bounds__(T::NT) dense_kernel(DenseArgs p)
         const OperandSrc sb = operand_src<B_KMAJOR>(Bt, p.ldb, p.N - n0, klen);
         tile.mainloop(lds, sa, p.lda, sb, p.ldb, klen, opaque((int)threadIdx.x));
         char *Dt = (char *)p.D + ((int64_t)r * p.split_stride + (int64_t)m0 * p.ldd + n0) * esize;
-        epilogue<T, EPI_NONE, OUT>(tile, Dt, p.ldd, min(T::BM, p.M - m0), min(T::BN, p.N - n0),
-                                   opaque((int)threadIdx.x));
+        tile_epilogue<T, EPI_NONE, OUT>(tile, lds, Dt, p.ldd, min(T::BM, p.M - m0), min(T::BN, p.N - n0),
+                                        opaque((int)threadIdx.x));
     }
 }
 
@@ -189,7 +189,7 @@ __global__ void __launch_bounds__(T::NT) grouped_kernel(GroupedArgs p)
         tile.mainloop(lds, sa, p.lda, sb, p.ldb, p.K, opaque((int)threadIdx.x));
         const int dcol0 = EPI == EPI_SILU_GATE ? n0 / 2 : n0;
         char *Dt = (char *)p.D + ((int64_t)m0 * p.ldd + dcol0) * esize;
-        epilogue<T, EPI, OUT>(tile, Dt, p.ldd, m_valid, min(T::BN, p.N - n0), opaque((int)threadIdx.x));
+        tile_epilogue<T, EPI, OUT>(tile, lds, Dt, p.ldd, m_valid, min(T::BN, p.N - n0), opaque((int)threadIdx.x));
     }
 }
 
@@ -304,7 +304,7 @@ __global__ void __launch_bounds__(T::NT) grouped_kernel_wt(GroupedArgs p)
         tile.mainloop(lds, sa, p.lda, sb, p.ldb, p.K, opaque((int)threadIdx.x));
         const int dcol0 = EPI == EPI_SILU_GATE ? n0 / 2 : n0;
         char *Dt = (char *)p.D + ((int64_t)m0 * p.ldd + dcol0) * esize;
-        epilogue<T, EPI, OUT>(tile, Dt, p.ldd, m_valid, min(T::BN, p.N - n0), opaque((int)threadIdx.x));
+        tile_epilogue<T, EPI, OUT>(tile, lds, Dt, p.ldd, m_valid, min(T::BN, p.N - n0), opaque((int)threadIdx.x));
     }
 }
 
