@@ -251,6 +251,34 @@ def test_split_k_deterministic():
     assert p1.info().splits == 8 and np.array_equal(g1, g2)
 
 
+def embed(x: np.ndarray, cols: int, fill: int) -> np.ndarray:
+    """x in the first columns of a wider array whose other entries are `fill`."""
+    y = np.full((x.shape[0], cols), fill, dtype=x.dtype)
+    y[:, :x.shape[1]] = x
+    return y
+
+
+@pytest.mark.parametrize("al,bl", LAYOUTS)
+@pytest.mark.parametrize("tile", ["auto", "256", "128", "32n", "64n", "256d"])
+def test_wide_leading_dimensions(tile, al, bl):
+    """Leading dimensions well past the matrix (lda = K+24 etc., in elements
+    of the stored rows), the slack holding NaN bit patterns: any read of it
+    shows up as NaN in D.  Integer inputs, bit-exact; D's padding must stay
+    untouched."""
+    tile_skip(tile, al, bl)
+    M, N, K = 300, 520, 136
+    log(f"case wide-ld tile={tile} {al}{bl}")
+    cfg = datagen.GemmConfig("t", M, N, K, "bf16", "f32", al, bl, seed=21, int_seed=22)
+    a, b = datagen.gemm_inputs(cfg, "int")
+    nan16 = 0x7FC1
+    a_w = embed(a, a.shape[1] + 24, nan16)
+    b_w = embed(b, b.shape[1] + 40, nan16)
+    ldd = N + 72
+    got, plan = run_dense(a_w, b_w, M, N, K, "bf16", "f32", al, bl, TILES[tile], ldd=ldd, sentinel=True)
+    ref = oracle.gemm_ref(a, b, "bf16", "bf16", al, bl)
+    assert_bits_equal(got, ref, "f32", plan.describe())
+
+
 DTL_SHORT_K = ([(K, bl, "bf16", "f32") for K in (8, 64, 72, 136, 200) for bl in ("row", "col")]
                + [(K, bl, "f16", "f16") for K in (72, 200) for bl in ("row", "col")])
 

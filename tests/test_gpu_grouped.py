@@ -88,6 +88,40 @@ def test_grouped_plain_all_buckets(tile, b_layout, variant):
     assert np.all(tail == 0xFF), "rows past the routed rows were written"
 
 
+@pytest.mark.parametrize("b_layout", ["row", "col"])
+@pytest.mark.parametrize("tile", ["auto", "256", "256d"])
+def test_grouped_wide_strides(tile, b_layout):
+    """lda, ldb and ldd past the rows and a gap between the experts' weights,
+    all the slack NaN bit patterns (any read of it turns up as NaN in the
+    output).  Integer inputs, bit-exact."""
+    counts = [0, 3, 150, 40, 300, 0, 257]
+    N, K = 512, 200
+    log(f"case grouped wide strides tile={tile} {b_layout}")
+    A, W, off = make_case(counts, N, K, 9, "int")
+    rows = int(off[-1])
+    Wst = W if b_layout == "row" else np.ascontiguousarray(W.transpose(0, 2, 1))
+    nan16 = 0x7FC1
+    lda = K + 24
+    r_w, c_w = Wst.shape[1], Wst.shape[2]
+    ldb = c_w + 40
+    stride = r_w * ldb + 64
+    A_w = np.full((rows, lda), nan16, dtype=np.uint16)
+    A_w[:, :K] = A
+    W_w = np.full((len(counts) * stride,), nan16, dtype=np.uint16)
+    for e in range(len(counts)):
+        blk = W_w[e * stride:e * stride + r_w * ldb].reshape(r_w, ldb)
+        blk[:, :c_w] = Wst[e]
+    ldd = N + 72
+    D = torch.full((rows, ldd), float("nan"), dtype=torch.bfloat16, device="cuda")
+    plan = mg.grouped_gemm_plan(len(counts), rows, N, K, b_layout=b_layout, lda=lda, ldb=ldb, stride_b=stride,
+                                ldd=ldd, flags=GROUPED_TILES[tile])
+    mg.grouped_gemm_run(plan, to_dev(A_w, "bf16"), to_dev(W_w, "bf16"), D, torch.from_numpy(off).cuda())
+    torch.cuda.synchronize()
+    ref = oracle.grouped_ref(A, Wst, off, w_layout=b_layout)
+    assert_bits_equal(from_dev_bits(D[:, :N]), ref, "bf16", plan.describe())
+    assert torch.isnan(D[:, N:].float()).all(), "D's padding columns were written"
+
+
 @pytest.mark.parametrize("tile", ["auto", "256", "256d"])
 def test_grouped_256_experts(tile):
     """The most experts a plan takes (256): many empty, the rest from 1 to
