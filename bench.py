@@ -5,8 +5,10 @@
 A step is one pass of the hot path over the workload's inputs, which are
 resident in HBM before timing starts: for a dense workload one gemm_run, for
 the MoE workload FC1 (SiLU-gated) plus FC2 over all experts.  W untimed
-steps, then K steps bracketed by device synchronisation; events recorded on
-the stream the kernels are launched on give the average step duration.
+steps (without --warmup: as many as fill a quarter second, so that the
+clocks have settled), then K steps bracketed by device synchronisation;
+events recorded on the stream the kernels are launched on give the average
+step duration.
 
 Prints one JSON line: the metric (TFLOPS of algorithmic work, 2*M*N*K per
 GEMM, no padding), the roofline of the dominant kernel against MI355X's
@@ -37,7 +39,8 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed steps before the timed ones (default: as many as fill WARMUP_SECONDS, at least 10)")
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle sample time")
@@ -207,7 +210,7 @@ def main():
     else:
         step, info, case = dense_case(torch, mg, datagen, args.workload)
     print(f"# plan: {info['plan']}", file=sys.stderr, flush=True)
-    ms = time_steps(torch, step, args.steps, args.warmup)
+    ms, warmup_done = time_steps(torch, step, args.steps, args.warmup)
     roof, tflops, peak = roofline(info, ms)
     secondary = []
     if args.workload == DEFAULT_WORKLOAD and not args.no_secondary:
@@ -215,7 +218,7 @@ def main():
         del step
         step2, info2, _ = dense_case(torch, mg, datagen, "gemm4096_bf16")
         print(f"# plan: {info2['plan']}", file=sys.stderr, flush=True)
-        ms2 = time_steps(torch, step2, args.steps, args.warmup)
+        ms2, _ = time_steps(torch, step2, args.steps, args.warmup)
         roof2, tflops2, peak2 = roofline(info2, ms2)
         secondary.append({"config": info2["config"], "value": round(tflops2, 2), "unit": "TFLOPS",
                           "ms_per_step": round(ms2, 5), "pct_of_peak": round(100 * tflops2 / peak2, 2),
@@ -224,7 +227,7 @@ def main():
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(case, args.cpu_seconds)
     line = {"metric": METRIC, "value": round(tflops, 2), "unit": "TFLOPS", "n_gpus": 1, "steps": args.steps,
-            "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+            "warmup": warmup_done, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
             "vs_baseline": None, "dtype": info["dtype"], "data": "synthetic",
             "config": info["config"], "pct_of_peak": round(100 * tflops / peak, 2),
             "roofline": roof, "cpu_baseline": cpu}
@@ -233,11 +236,28 @@ def main():
     print(json.dumps(line), flush=True)
 
 
+# MI355X's clocks take tens of milliseconds of load to settle: 4096^3 runs
+# at ~121 us per step after 10 warmup steps and ~98 us after 400 (8192^3:
+# 793 against 768 us after 100).  Without --warmup the untimed steps
+# therefore fill at least this much time (and number at least 10).
+WARMUP_SECONDS = 0.25
+
+
 def time_steps(torch, step, steps, warmup):
-    """Average step time in ms: events on the stream the launches go to,
-    bracketed by device synchronisation."""
-    for _ in range(warmup):
-        step()
+    """(average step time in ms, warmup steps run): events on the stream the
+    launches go to, bracketed by device synchronisation.  warmup None: run
+    untimed steps until WARMUP_SECONDS have passed (at least 10)."""
+    if warmup is None:
+        n, t_end = 0, time.perf_counter() + WARMUP_SECONDS
+        while n < 10 or time.perf_counter() < t_end:
+            step()
+            n += 1
+            if n % 10 == 0:
+                torch.cuda.synchronize()
+        warmup = n
+    else:
+        for _ in range(warmup):
+            step()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()     # the stream every launch goes to
     ev0 = torch.cuda.Event(enable_timing=True)
@@ -250,9 +270,9 @@ def time_steps(torch, step, steps, warmup):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms = ev0.elapsed_time(ev1) / steps
-    print(f"# {steps} steps: {ms * 1e3:.1f} us/step (events), wall {wall * 1e6 / steps:.1f} us/step",
-          file=sys.stderr, flush=True)
-    return ms
+    print(f"# {steps} steps after {warmup} warmup steps: {ms * 1e3:.1f} us/step (events), "
+          f"wall {wall * 1e6 / steps:.1f} us/step", file=sys.stderr, flush=True)
+    return ms, warmup
 
 
 def roofline(info, ms):
