@@ -37,6 +37,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace mgemm {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -873,6 +875,287 @@ struct DtlTile {
     }
 };
 
+// acc += a . b on the matrix cores with the accumulator held in AGPRs.
+// Written as assembly because the compiler, left to place 256 accumulator
+// registers per lane itself, moves accumulators between AGPRs and VGPRs
+// around most MFMAs (hundreds of copies per K step).  The statements are
+// volatile so they keep their order with the LDS reads and loads placed
+// between them.  The compiler waits for the LDS reads that feed a and b
+// (it sees the registers) but inserts no wait states after these MFMAs,
+// so whoever reads the accumulators with other instructions waits first
+// (mfma_drain).
+template <int IN>
+__device__ __forceinline__ void mfma16_agpr(f32x4_t &c, const u32x4_t &a, const u32x4_t &b)
+{
+    if constexpr (IN == IN_BF16)
+        asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+    else
+        asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+}
+// More wait states than any MFMA result needs before other instructions
+// read it, and no instruction scheduled across.
+__device__ __forceinline__ void mfma_drain()
+{
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7");
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// The same 256 x 256 direct-to-LDS tile on four waves of 128 x 128 (8 x 8
+// blocks of 16 x 16, 256 accumulators per lane in AGPRs, one wave per
+// SIMD): each wave reads 128 rows of A and 128 of B per 32-k sub-step for
+// 64 MFMAs, two thirds of the LDS reads per MFMA of the eight-wave layout.
+// Rings, swizzles and fragment addressing are DtlTile's.  A sub-step is four
+// quarters of 16 MFMAs; the fragments of the next sub-step are read into the
+// other set, four reads (eight transpose reads) per quarter, one after each
+// of the quarter's first MFMAs:
+//   sub-step 0 (X.P): reads Y = A(s1), Q = B(s1) of step kt
+//   barrier (step kt+1 in LDS; every wave done with step kt's slots), then
+//   sub-step 1 (Y.Q): reads X = A(s0), P = B(s0) of step kt+1, and loads
+//     the shallow operand's step kt+2 (first quarter) and the deep one's
+//     step kt+3 (second quarter) into the slots step kt leaves.
+// The shallow operand thus has one step of lead, the deep one two.
+template <int IN, bool BKM>
+struct DtlTile4 {
+    using Base = DtlTile<IN, BKM>;
+    static constexpr int BM = 256, BN = 256, WM = 2, WN = 2;
+    static constexpr int MI = 16;
+    static constexpr int NT = 64 * WM * WN;
+    static constexpr int TM = BM / WM, TN = BN / WN, FM = TM / 16, FN = TN / 16;
+    static constexpr int OPS = Base::OPS;
+    static constexpr bool DEEP_B = BKM;
+    static constexpr int A_SLOTS = Base::A_SLOTS, B_SLOTS = Base::B_SLOTS;
+    static constexpr int LDS_BYTES = Base::LDS_BYTES;
+    static constexpr int LOADS = 256 / 8 / (NT / 64);
+    static constexpr int BROW = Base::BROW;
+    static constexpr int RB = Base::RB;   // LDS read instructions per four B fragments
+    static_assert(FM == 8 && FN == 8 && LOADS == 8, "the quarter rotation assumes 8 x 8 blocks per wave");
+    using F4 = typename Base::F4;
+
+    f32x4_t acc[FM][FN];
+    uint32_t va[LOADS], vb[LOADS];
+    int kc[LOADS];
+    int abase[2], bbase[2];
+    int bfr[FN];
+
+    __device__ __forceinline__ void setup(int lane, int wave, int wm0, int wn0, int lda, int ldb)
+    {
+        const int r8 = lane >> 3;
+#pragma unroll
+        for (int j = 0; j < LOADS; ++j) {
+            const int row = (wave * LOADS + j) * 8 + r8;
+            const int c = (lane & 7) ^ Base::dswz(row);
+            kc[j] = c * 8;
+            va[j] = (uint32_t)row * (uint32_t)lda * 2u + (uint32_t)c * 16u;
+            if constexpr (BKM) {
+                vb[j] = (uint32_t)row * (uint32_t)ldb * 2u + (uint32_t)c * 16u;
+            } else {
+                const int kr = (wave * LOADS + j) * 2 + (lane >> 5);
+                const int pc = lane & 31;
+                const int seg = (pc >> 2) ^ (kr & 3);
+                const int w = (pc & 3) ^ (((kr >> 3) & 1) << 1);
+                vb[j] = (uint32_t)kr * (uint32_t)ldb * 2u + (uint32_t)(seg * 64 + w * 16);
+            }
+        }
+        const int r = lane & 15, q = lane >> 4;
+        const int c0 = q ^ Base::dswz(r);
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            abase[s] = (wm0 + r) * kRowBytes + ((c0 ^ (4 * s)) << 4);
+            bbase[s] = (wn0 + r) * kRowBytes + ((c0 ^ (4 * s)) << 4);
+        }
+        if constexpr (!BKM) {
+            const int jj = r >> 2, qq = r & 3;
+#pragma unroll
+            for (int jb = 0; jb < FN; ++jb)
+                bfr[jb] = (8 * q + jj) * BROW + ((((wn0 >> 5) + (jb >> 1)) ^ jj) * 64) +
+                          ((32 * (jb & 1) + 8 * qq) ^ (32 * (q & 1)));
+        }
+    }
+    // MASK: the step may end past K (a k-contiguous operand's chunks past K
+    // must read as zero; a row-contiguous operand's resource already ends
+    // at row K - 1).  Steps that end at or before K skip the per-lane select.
+    template <bool MASK>
+    __device__ __forceinline__ void load_a(__amdgpu_buffer_rsrc_t r, char *slot, int wave, int j, int k_left) const
+    {
+        const uint32_t off = !MASK || kc[j] < k_left ? va[j] : kOOB;
+        Base::dtl_load(r, slot + (wave * LOADS + j) * 1024, off);
+    }
+    template <bool MASK>
+    __device__ __forceinline__ void load_b(__amdgpu_buffer_rsrc_t r, char *slot, int wave, int j, int k_left) const
+    {
+        uint32_t off = vb[j];
+        if constexpr (BKM && MASK)
+            off = kc[j] < k_left ? off : kOOB;
+        Base::dtl_load(r, slot + (wave * LOADS + j) * 1024, off);
+    }
+    // LDS read number i of the A fragments of m blocks 4 H .. 4 H + 3, sub-step S
+    template <int S, int H>
+    __device__ __forceinline__ void read_a(const char *as, F4 &f, int i) const
+    {
+        f.v[i] = *(const u32x4_t *)(as + abase[S] + (4 * H + i) * 16 * kRowBytes);
+    }
+    // LDS read number i (of RB) of the B fragments of n blocks 4 H .. 4 H + 3, sub-step S
+    template <int S, int H>
+    __device__ __forceinline__ void read_b(const char *bs, F4 &f, int i) const
+    {
+        if constexpr (BKM) {
+            f.v[i] = *(const u32x4_t *)(bs + bbase[S] + (4 * H + i) * 16 * kRowBytes);
+        } else {
+            typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
+            const int jb = i >> 1, hi = i & 1;
+            const char *p = bs + bfr[4 * H + jb] + 32 * S * BROW + 4 * BROW * hi;
+            const u32x2_t w = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)p));
+            f.v[jb][2 * hi] = w[0];
+            f.v[jb][2 * hi + 1] = w[1];
+        }
+    }
+    // 16 MFMAs on m blocks 4 HM .. +3 x n blocks 4 HN .. +3; read i (of NR)
+    // after MFMA i, global load j (of NL) after MFMA j * 16 / NL
+    static constexpr int LOFF = 0;   // MFMA after which a quarter's first load goes
+    template <int HM, int HN, int NR, int NL, class RD, class LD>
+    __device__ __forceinline__ void quarter(const F4 &a, const F4 &b, RD &&rd, LD &&ld)
+    {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            mfma16_agpr<IN>(acc[4 * HM + i / 4][4 * HN + i % 4], b.v[i % 4], a.v[i / 4]);
+            if (i < NR)
+                rd(i);
+            if constexpr (NL > 0) {
+                if (i % (16 / NL) == LOFF)
+                    ld(i / (16 / NL));
+            }
+        }
+    }
+
+    __device__ __forceinline__ void mainloop(char *lds, const OperandSrc &sa, int lda, const OperandSrc &sb, int ldb,
+                                             int K, int tid)
+    {
+        const int lane = tid & 63;
+        const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+        const int wm0 = (wave / WN) * TM, wn0 = (wave % WN) * TN;
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+                acc[i][j] = f32x4_t{};
+        const int ksteps = (K + kBK - 1) / kBK;
+        if (ksteps <= 0)
+            return;
+        // the zeros are written here, ahead of the wait states before the
+        // first MFMA (the compiler would otherwise sink them next to it)
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+                asm volatile("" : "+a"(acc[i][j]));
+        setup(lane, wave, wm0, wn0, lda, ldb);
+        char *const A0 = lds;
+        char *const B0 = lds + A_SLOTS * OPS;
+        char *const D0 = DEEP_B ? B0 : A0;
+        char *const S0 = DEEP_B ? A0 : B0;
+        const OperandSrc &sd = DEEP_B ? sb : sa;
+        const OperandSrc &ss = DEEP_B ? sa : sb;
+        auto load_d = [&](__amdgpu_buffer_rsrc_t r, char *slot, int j, int k_left, auto mask) {
+            if constexpr (DEEP_B)
+                load_b<decltype(mask)::value>(r, slot, wave, j, k_left);
+            else
+                load_a<decltype(mask)::value>(r, slot, wave, j, k_left);
+        };
+        auto load_s = [&](__amdgpu_buffer_rsrc_t r, char *slot, int j, int k_left, auto mask) {
+            if constexpr (DEEP_B)
+                load_a<decltype(mask)::value>(r, slot, wave, j, k_left);
+            else
+                load_b<decltype(mask)::value>(r, slot, wave, j, k_left);
+        };
+        constexpr std::true_type masked{};
+        constexpr std::false_type unmasked{};
+        // prologue: steps 0 and 1 of both operands; wait for step 0
+        {
+            const auto rd0 = sd.at_step(0), rs0 = ss.at_step(0), rd1 = sd.at_step(1), rs1 = ss.at_step(1);
+#pragma unroll
+            for (int j = 0; j < LOADS; ++j) {
+                load_d(rd0, D0, j, K, masked);
+                load_s(rs0, S0, j, K, masked);
+            }
+#pragma unroll
+            for (int j = 0; j < LOADS; ++j)
+                load_d(rd1, D0 + OPS, j, K - kBK, masked);
+#pragma unroll
+            for (int j = 0; j < LOADS; ++j)
+                load_s(rs1, S0 + OPS, j, K - kBK, masked);
+            wait_vm<2 * LOADS>();
+        }
+        lds_barrier();
+        F4 Xl, Xh, Pl, Ph, Yl, Yh, Ql, Qh;
+        // (in the order the loop reads them, so that the LDS-read counts
+        // at the loop head agree on both ways in)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            read_a<0, 0>(A0, Xl, i);
+#pragma unroll
+        for (int i = 0; i < RB; ++i)
+            read_b<0, 0>(B0, Pl, i);
+#pragma unroll
+        for (int i = 0; i < RB; ++i)
+            read_b<0, 1>(B0, Ph, i);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            read_a<0, 1>(A0, Xh, i);
+        // the zeroed accumulators are written by ordinary instructions
+        mfma_drain();
+        int sd_cur = 0;   // deep slot of step kt
+        // one K step; its loads are of step kt + 2
+        auto step = [&](int kt, auto mask) {
+            const int s_cur = kt & 1;
+            const int sd_next = sd_cur == 2 ? 0 : sd_cur + 1;
+            const int sd_fill = sd_next == 2 ? 0 : sd_next + 1;
+            const char *ac = DEEP_B ? S0 + s_cur * OPS : D0 + sd_cur * OPS;
+            const char *bc = DEEP_B ? D0 + sd_cur * OPS : S0 + s_cur * OPS;
+            const char *an = DEEP_B ? S0 + (s_cur ^ 1) * OPS : D0 + sd_next * OPS;
+            const char *bn = DEEP_B ? D0 + sd_next * OPS : S0 + (s_cur ^ 1) * OPS;
+            // sub-step 0; the deep operand's step kt+2, two loads a quarter,
+            // into the slot step kt-1 left
+            const auto rD = sd.at_step(kt + 2);
+            const int kd = K - (kt + 2) * kBK;
+            char *const dw = D0 + sd_fill * OPS;
+            quarter<0, 0, 4, 2>(Xl, Pl, [&](int i) { read_a<1, 0>(ac, Yl, i); },
+                                [&](int j) { load_d(rD, dw, j, kd, mask); });
+            quarter<0, 1, RB, 2>(Xl, Ph, [&](int i) { read_b<1, 0>(bc, Ql, i); },
+                                 [&](int j) { load_d(rD, dw, 2 + j, kd, mask); });
+            quarter<1, 0, RB, 2>(Xh, Pl, [&](int i) { read_b<1, 1>(bc, Qh, i); },
+                                 [&](int j) { load_d(rD, dw, 4 + j, kd, mask); });
+            quarter<1, 1, 4, 2>(Xh, Ph, [&](int i) { read_a<1, 1>(ac, Yh, i); },
+                                [&](int j) { load_d(rD, dw, 6 + j, kd, mask); });
+            wait_vm<LOADS>();
+            lds_barrier();
+            // sub-step 1; the shallow operand's step kt+2 into the slot step
+            // kt leaves
+            const auto rS = ss.at_step(kt + 2);
+            const int ks = K - (kt + 2) * kBK;
+            char *const sw = S0 + s_cur * OPS;
+            quarter<0, 0, 4, 4>(Yl, Ql, [&](int i) { read_a<0, 0>(an, Xl, i); },
+                                [&](int j) { load_s(rS, sw, j, ks, mask); });
+            quarter<0, 1, RB, 4>(Yl, Qh, [&](int i) { read_b<0, 0>(bn, Pl, i); },
+                                 [&](int j) { load_s(rS, sw, 4 + j, ks, mask); });
+            quarter<1, 0, RB, 0>(Yh, Ql, [&](int i) { read_b<0, 1>(bn, Ph, i); }, [](int) {});
+            quarter<1, 1, 4, 0>(Yh, Qh, [&](int i) { read_a<0, 1>(an, Xh, i); }, [](int) {});
+            sd_cur = sd_next;
+        };
+        // the loads of step kt + 2 need no K mask while that step is not
+        // the last (kt + 2 <= ksteps - 2)
+        int kt = 0;
+        for (; kt < ksteps - 3; ++kt)
+            step(kt, unmasked);
+        for (; kt < ksteps; ++kt)
+            step(kt, masked);
+        // the trailing loads (empty ranges) have landed before the next tile,
+        // and the last MFMAs' results before the epilogue reads them
+        wait_vm<0>();
+        mfma_drain();
+    }
+};
+
 // ---------------------------------------------------------------------------
 // Epilogue helpers
 // ---------------------------------------------------------------------------
@@ -1007,7 +1290,7 @@ template <class T, int OUT>
 __device__ __forceinline__ void epilogue_staged(const T &t, char *lds, void *D, int64_t ldd, int m_valid,
                                                 int n_valid, int tid)
 {
-    static_assert(T::MI == 16 && T::BN == 256 && T::NT == 512 && T::LDS_BYTES >= 128 * 1024, "");
+    static_assert(T::MI == 16 && T::BN == 256 && T::WM == 2 && T::TM == 128 && T::LDS_BYTES >= 128 * 1024, "");
     constexpr int esize = out_size(OUT);
     const int lane = tid & 63;
     const int wave = tid >> 6;
@@ -1026,14 +1309,14 @@ __device__ __forceinline__ void epilogue_staged(const T &t, char *lds, void *D, 
         for (int ii = 0; ii < 4; ++ii) {
             const int x = (wm0 >> 1) + 16 * ii + (lane & 15);
 #pragma unroll
-            for (int jb = 0; jb < 4; ++jb) {
+            for (int jb = 0; jb < T::FN; ++jb) {
                 const int c = (wn0 + 16 * jb + 4 * (lane >> 4)) >> 2;
                 *(f32x4_t *)(lds + x * 1024 + ((c ^ (x & 15)) << 4)) = t.acc[4 * h + ii][jb];
             }
         }
         lds_barrier();
 #pragma unroll 4
-        for (int x = wave; x < 128; x += 8) {
+        for (int x = wave; x < 128; x += T::NT / 64) {
             const f32x4_t v = *(const f32x4_t *)(lds + x * 1024 + ((lane ^ (x & 15)) << 4));
             const int m = (x >> 6) * T::TM + 64 * h + (x & 63);
             const uint32_t off = n < n_valid ? (uint32_t)m * row_bytes + (uint32_t)n * esize : kOOB;

@@ -30,6 +30,23 @@ static const TileShape kTiles[NUM_TILES] = {
 
 const TileShape &tile_shape(int tile) { return kTiles[tile]; }
 
+// Wave layout and ring depths of a dense plan's tile: the direct-to-LDS
+// tile runs column-major B on four waves of 128 x 128 with the 3-slot ring
+// on B, row-major B on eight waves of 128 x 64 with the 3-slot ring on A.
+static void dense_waves(int tile, bool bk, int &wm, int &wn, int &a_slots, int &b_slots)
+{
+    const TileShape &ts = tile_shape(tile);
+    wm = ts.wm;
+    wn = ts.wn;
+    a_slots = b_slots = 2;
+    if (tile == TILE_256x256_DTL) {
+        if (bk)
+            wn = 2;
+        a_slots = bk ? 2 : 3;
+        b_slots = bk ? 3 : 2;
+    }
+}
+
 static const char *tile_name(int tile)
 {
     static const char *n[NUM_TILES] = {"256x256", "128x128", "32x256", "64x256", "256x256dtl"};
@@ -282,15 +299,21 @@ static mgemm_status_t plan_dense(const mgemm_desc_t *d, uint32_t flags, mgemm_pl
     // fastest on the 256x256 tile at 8192^3 (2, 8, 16 and 32 were 3-20% slower).
     p->group_m = (int)std::max<int64_t>(1, std::min<int64_t>(4, p->tiles_m));
     p->xcd_remap = (flags & MGEMM_PLAN_NO_XCD_REMAP) ? 0 : (p->grid % 8 == 0 ? 1 : 0);
+    int wm, wn, a_slots, b_slots;
+    dense_waves(tile, bk, wm, wn, a_slots, b_slots);
+    char stages[16];
+    if (a_slots == b_slots)
+        snprintf(stages, sizeof stages, "%d", a_slots);
+    else
+        snprintf(stages, sizeof stages, "%da/%db", a_slots, b_slots);
     char buf[256];
     snprintf(buf, sizeof buf,
              "dense M=%lld N=%lld K=%lld %s%s->%s tile=%s waves=%dx%d bk=64 stages=%s tiles=%lld splits=%d "
              "grid=%d group_m=%d xcd_remap=%d edge_cols=%lld",
              (long long)d->M, (long long)d->N, (long long)d->K, d->a_type == MGEMM_BF16 ? "bf16" : "f16",
              ak ? (bk ? " NT" : " NN") : (bk ? " TT" : " TN"),
-             d->d_type == MGEMM_F32 ? "f32" : (d->d_type == MGEMM_BF16 ? "bf16" : "f16"), tile_name(tile), ts.wm,
-             ts.wn, tile == TILE_256x256_DTL ? "3a/2b" : "2", (long long)p->tiles, p->splits, p->grid, p->group_m,
-             p->xcd_remap, (long long)(d->N - n_main));
+             d->d_type == MGEMM_F32 ? "f32" : (d->d_type == MGEMM_BF16 ? "bf16" : "f16"), tile_name(tile), wm, wn,
+             stages, (long long)p->tiles, p->splits, p->grid, p->group_m, p->xcd_remap, (long long)(d->N - n_main));
     p->description = buf;
     return MGEMM_OK;
 }
@@ -506,7 +529,13 @@ extern "C" mgemm_status_t gemm_plan_info(mgemm_plan_t plan, mgemm_plan_info_t *i
     info->block_k = kBK;
     info->waves_m = ts.wm;
     info->waves_n = ts.wn;
-    info->stages = plan->tile == TILE_256x256_DTL ? 3 : 2;   // A ring depth (the B ring has 2)
+    info->stages = plan->tile == TILE_256x256_DTL ? 3 : 2;   // the deeper ring's slots
+    if (plan->kind == PLAN_DENSE) {
+        int a_slots, b_slots;
+        dense_waves(plan->tile, plan->dense.b_layout == MGEMM_COL_MAJOR, info->waves_m, info->waves_n, a_slots,
+                    b_slots);
+        info->stages = std::max(a_slots, b_slots);
+    }
     info->lds_bytes = ts.lds_bytes;
     info->tiles_m = plan->tiles_m;
     info->tiles_n = plan->tiles_n;

@@ -59,15 +59,17 @@ DenseFn dense_table(bool ak, bool bk, int out)
 #undef MG_D
 }
 
-// The direct-to-LDS 256 x 256 engine: row-major (k-contiguous) A, B either way.
+// The direct-to-LDS 256 x 256 engine: row-major (k-contiguous) A, B either
+// way.  Column-major B runs on four waves of 128 x 128 (DtlTile4), row-major
+// B on eight of 128 x 64 (DtlTile), the faster of the two for each layout.
 template <int IN>
 DenseFn dense_dtl_table(bool ak, bool bk, int out)
 {
     if (!ak || (out != OUT_F32 && out != same16<IN>()))
         return nullptr;
     if (bk)
-        return out == OUT_F32 ? launch_dense_tile<DtlTile<IN, true>, true, true, IN, OUT_F32>
-                              : launch_dense_tile<DtlTile<IN, true>, true, true, IN, same16<IN>()>;
+        return out == OUT_F32 ? launch_dense_tile<DtlTile4<IN, true>, true, true, IN, OUT_F32>
+                              : launch_dense_tile<DtlTile4<IN, true>, true, true, IN, same16<IN>()>;
     return out == OUT_F32 ? launch_dense_tile<DtlTile<IN, false>, true, false, IN, OUT_F32>
                           : launch_dense_tile<DtlTile<IN, false>, true, false, IN, same16<IN>()>;
 }

@@ -110,8 +110,9 @@ typedef struct {
 #define MGEMM_PLAN_FORCE_TILE_128x128 0x2u   /* the 128x128 macro-tile  */
 #define MGEMM_PLAN_FORCE_TILE_32x256  0x4u   /* narrow-M (few tokens)   */
 #define MGEMM_PLAN_FORCE_TILE_64x256  0x8u   /* narrow-M (few tokens)   */
-/* 256x256 with loads that write LDS directly (no staging registers, eight
- * waves).  Dense plans: row-major A only, else UNSUPPORTED; the planner uses
+/* 256x256 with loads that write LDS directly (no staging registers; four
+ * waves of 128x128 for a dense plan with column-major B, else eight waves of
+ * 128x64).  Dense plans: row-major A only, else UNSUPPORTED; the planner uses
  * it whenever it picks the 256x256 tile for such a plan.  Grouped plans
  * (whose A is always row-major): the planner uses it for the experts of 129
  * rows or more.  In both, MGEMM_PLAN_FORCE_TILE_256x256 selects the
@@ -165,7 +166,7 @@ mgemm_status_t gemm_plan_describe(mgemm_plan_t plan, char *buf, size_t len);
 typedef struct {
     int32_t block_m, block_n, block_k;   /* macro-tile                        */
     int32_t waves_m, waves_n;            /* wavefront grid inside a tile      */
-    int32_t stages;                      /* LDS ring depth                    */
+    int32_t stages;                      /* LDS ring depth (deeper operand)   */
     int32_t lds_bytes;                   /* LDS per workgroup                 */
     int64_t tiles_m, tiles_n, tiles;     /* output tiles (dense form)         */
     int64_t k_steps;                     /* ceil(K / block_k)                 */
