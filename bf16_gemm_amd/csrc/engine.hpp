@@ -270,6 +270,25 @@ struct OperandSrc {
     }
 };
 
+// The same source in scalar registers (the fields are wave-uniform, but the
+// compiler cannot always tell, and then builds every step's resource with
+// vector compares).
+__device__ __forceinline__ OperandSrc uniform_src(const OperandSrc &s)
+{
+    // (readfirstlane returns int: each half goes back through uint32_t, or
+    // a low half with bit 31 set would sign-extend over the high half)
+    auto u64 = [](uint64_t v) {
+        const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
+        const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+        return ((uint64_t)hi << 32) | (uint64_t)lo;
+    };
+    OperandSrc u;
+    u.base = (const char *)(uintptr_t)u64((uint64_t)(uintptr_t)s.base);
+    u.bytes = u64(s.bytes);
+    u.step_bytes = (uint32_t)__builtin_amdgcn_readfirstlane((int)s.step_bytes);
+    return u;
+}
+
 // ---------------------------------------------------------------------------
 // The tile: accumulators, main loop, epilogue.
 // ---------------------------------------------------------------------------
@@ -979,7 +998,7 @@ struct DtlTile4 {
     __device__ __forceinline__ void load_a(__amdgpu_buffer_rsrc_t r, char *slot, int wave, int j, int k_left) const
     {
         const uint32_t off = !MASK || kc[j] < k_left ? va[j] : kOOB;
-        Base::dtl_load(r, slot + (wave * LOADS + j) * 1024, off);
+        load_to_lds16(r, lds_addr(slot + (wave * LOADS + j) * 1024), off);
     }
     template <bool MASK>
     __device__ __forceinline__ void load_b(__amdgpu_buffer_rsrc_t r, char *slot, int wave, int j, int k_left) const
@@ -987,7 +1006,7 @@ struct DtlTile4 {
         uint32_t off = vb[j];
         if constexpr (BKM && MASK)
             off = kc[j] < k_left ? off : kOOB;
-        Base::dtl_load(r, slot + (wave * LOADS + j) * 1024, off);
+        load_to_lds16(r, lds_addr(slot + (wave * LOADS + j) * 1024), off);
     }
     // LDS read number i of the A fragments of m blocks 4 H .. 4 H + 3, sub-step S
     template <int S, int H>
@@ -1054,8 +1073,20 @@ struct DtlTile4 {
         char *const B0 = lds + A_SLOTS * OPS;
         char *const D0 = DEEP_B ? B0 : A0;
         char *const S0 = DEEP_B ? A0 : B0;
-        const OperandSrc &sd = DEEP_B ? sb : sa;
-        const OperandSrc &ss = DEEP_B ? sa : sb;
+        const OperandSrc ua = uniform_src(sa), ub = uniform_src(sb);
+        const OperandSrc &sd = DEEP_B ? ub : ua;
+        const OperandSrc &ss = DEEP_B ? ua : ub;
+        // The resource of a step that ends before K - 1's step: the base
+        // moved to the step, the length left as the rows bound it.  A
+        // k-contiguous operand's rows past the tile's last read as zero
+        // because their offsets pass the first step's length; a row-major
+        // B's lanes stay within one step of 64 rows, which such a step holds
+        // in full.
+        auto step_rsrc = [](const OperandSrc &u, bool kmajor, int kt) {
+            const uint64_t rec = kmajor ? u.bytes : (uint64_t)u.step_bytes;
+            return make_rsrc(u.base + (uint64_t)kt * u.step_bytes, rec);
+        };
+        constexpr bool D_KMAJOR = DEEP_B ? BKM : true, S_KMAJOR = DEEP_B ? true : BKM;
         auto load_d = [&](__amdgpu_buffer_rsrc_t r, char *slot, int j, int k_left, auto mask) {
             if constexpr (DEEP_B)
                 load_b<decltype(mask)::value>(r, slot, wave, j, k_left);
@@ -1116,7 +1147,7 @@ struct DtlTile4 {
             const char *bn = DEEP_B ? D0 + sd_next * OPS : S0 + (s_cur ^ 1) * OPS;
             // sub-step 0; the deep operand's step kt+2, two loads a quarter,
             // into the slot step kt-1 left
-            const auto rD = sd.at_step(kt + 2);
+            const auto rD = decltype(mask)::value ? sd.at_step(kt + 2) : step_rsrc(sd, D_KMAJOR, kt + 2);
             const int kd = K - (kt + 2) * kBK;
             char *const dw = D0 + sd_fill * OPS;
             quarter<0, 0, 4, 2>(Xl, Pl, [&](int i) { read_a<1, 0>(ac, Yl, i); },
@@ -1131,7 +1162,7 @@ struct DtlTile4 {
             lds_barrier();
             // sub-step 1; the shallow operand's step kt+2 into the slot step
             // kt leaves
-            const auto rS = ss.at_step(kt + 2);
+            const auto rS = decltype(mask)::value ? ss.at_step(kt + 2) : step_rsrc(ss, S_KMAJOR, kt + 2);
             const int ks = K - (kt + 2) * kBK;
             char *const sw = S0 + s_cur * OPS;
             quarter<0, 0, 4, 4>(Yl, Ql, [&](int i) { read_a<0, 0>(an, Xl, i); },
