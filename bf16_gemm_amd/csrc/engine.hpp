@@ -1031,15 +1031,15 @@ struct DtlTile4 {
     }
     // 16 MFMAs on m blocks 4 HM .. +3 x n blocks 4 HN .. +3; read i (of NR)
     // after MFMA i, global load j (of NL) after MFMA j * 16 / NL
-    static constexpr int LOFF = 0;   // MFMA after which a quarter's first load goes
+    static constexpr int LOFF = 2;   // MFMA after which a quarter's first load goes
     template <int HM, int HN, int NR, int NL, class RD, class LD>
     __device__ __forceinline__ void quarter(const F4 &a, const F4 &b, RD &&rd, LD &&ld)
     {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             mfma16_agpr<IN>(acc[4 * HM + i / 4][4 * HN + i % 4], b.v[i % 4], a.v[i / 4]);
-            if (i < NR)
-                rd(i);
+            if (i % (16 / NR) == 0)
+                rd(i / (16 / NR));
             if constexpr (NL > 0) {
                 if (i % (16 / NL) == LOFF)
                     ld(i / (16 / NL));
