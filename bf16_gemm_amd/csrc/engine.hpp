@@ -289,6 +289,18 @@ __device__ __forceinline__ OperandSrc uniform_src(const OperandSrc &s)
     return u;
 }
 
+// The resource of a step that ends before the operand's last step: the base
+// moved to the step, the length left as the rows bound it.  A k-contiguous
+// operand's rows past the tile's last read as zero because their offsets
+// pass the first step's length; a row-major B's lanes stay within one step
+// of 64 rows, which such a step holds in full.  (No 64-bit compare: the
+// scalar unit has none, so at_step's clamp runs on the vector unit.)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t step_rsrc(const OperandSrc &u, bool kmajor, int kt)
+{
+    const uint64_t rec = kmajor ? u.bytes : (uint64_t)u.step_bytes;
+    return make_rsrc(u.base + (uint64_t)kt * u.step_bytes, rec);
+}
+
 // ---------------------------------------------------------------------------
 // The tile: accumulators, main loop, epilogue.
 // ---------------------------------------------------------------------------
@@ -714,15 +726,20 @@ struct DtlTile {
         else
             load_to_lds16(r, lds_addr(dst), off);
     }
+    // MASK: the step may end past K (a k-contiguous operand's chunks past K
+    // must read as zero; a row-contiguous operand's resource already ends
+    // at row K - 1).  Steps that end before the last skip the per-lane select.
+    template <bool MASK = true>
     __device__ __forceinline__ void load_a(__amdgpu_buffer_rsrc_t r, char *slot, int wave, int j, int k_left) const
     {
-        const uint32_t off = kc[j] < k_left ? va[j] : kOOB;
+        const uint32_t off = !MASK || kc[j] < k_left ? va[j] : kOOB;
         dtl_load(r, slot + (wave * LOADS + j) * 1024, off);
     }
+    template <bool MASK = true>
     __device__ __forceinline__ void load_b(__amdgpu_buffer_rsrc_t r, char *slot, int wave, int j, int k_left) const
     {
         uint32_t off = vb[j];
-        if constexpr (BKM)
+        if constexpr (BKM && MASK)
             off = kc[j] < k_left ? off : kOOB;
         dtl_load(r, slot + (wave * LOADS + j) * 1024, off);
     }
@@ -800,34 +817,38 @@ struct DtlTile {
         char *const B0 = lds + A_SLOTS * OPS;
         char *const D0 = DEEP_B ? B0 : A0;
         char *const S0 = DEEP_B ? A0 : B0;
-        const OperandSrc &sd = DEEP_B ? sb : sa;
-        const OperandSrc &ss = DEEP_B ? sa : sb;
-        auto load_d = [&](__amdgpu_buffer_rsrc_t r, char *slot, int j, int k_left) {
+        const OperandSrc ua = uniform_src(sa), ub = uniform_src(sb);
+        const OperandSrc &sd = DEEP_B ? ub : ua;
+        const OperandSrc &ss = DEEP_B ? ua : ub;
+        constexpr bool D_KMAJOR = DEEP_B ? BKM : true, S_KMAJOR = DEEP_B ? true : BKM;
+        auto load_d = [&](__amdgpu_buffer_rsrc_t r, char *slot, int j, int k_left, auto mask) {
             if constexpr (DEEP_B)
-                load_b(r, slot, wave, j, k_left);
+                load_b<decltype(mask)::value>(r, slot, wave, j, k_left);
             else
-                load_a(r, slot, wave, j, k_left);
+                load_a<decltype(mask)::value>(r, slot, wave, j, k_left);
         };
-        auto load_s = [&](__amdgpu_buffer_rsrc_t r, char *slot, int j, int k_left) {
+        auto load_s = [&](__amdgpu_buffer_rsrc_t r, char *slot, int j, int k_left, auto mask) {
             if constexpr (DEEP_B)
-                load_a(r, slot, wave, j, k_left);
+                load_a<decltype(mask)::value>(r, slot, wave, j, k_left);
             else
-                load_b(r, slot, wave, j, k_left);
+                load_b<decltype(mask)::value>(r, slot, wave, j, k_left);
         };
+        constexpr std::true_type masked{};
+        constexpr std::false_type unmasked{};
         // prologue: both operands of steps 0 and 1; wait for step 0
         {
             const auto rd0 = sd.at_step(0), rs0 = ss.at_step(0), rd1 = sd.at_step(1), rs1 = ss.at_step(1);
 #pragma unroll
             for (int j = 0; j < LOADS; ++j) {
-                load_d(rd0, D0, j, K);
-                load_s(rs0, S0, j, K);
+                load_d(rd0, D0, j, K, masked);
+                load_s(rs0, S0, j, K, masked);
             }
 #pragma unroll
             for (int j = 0; j < LOADS; ++j)
-                load_d(rd1, D0 + OPS, j, K - kBK);
+                load_d(rd1, D0 + OPS, j, K - kBK, masked);
 #pragma unroll
             for (int j = 0; j < LOADS; ++j)
-                load_s(rs1, S0 + OPS, j, K - kBK);
+                load_s(rs1, S0 + OPS, j, K - kBK, masked);
             wait_vm<2 * LOADS>();
         }
         lds_barrier();
@@ -835,7 +856,9 @@ struct DtlTile {
         read_a<0, 0>(A0, X);
         read_b<0>(B0, P);
         int sd_cur = 0, sd_next = 1, sd_fill = 2;   // deep slots of steps kt, kt+1, kt+2
-        for (int kt = 0; kt < ksteps; ++kt) {
+        // one K step; its loads are of step kt + 2
+        auto step = [&](int kt, auto mask) {
+            constexpr bool M = decltype(mask)::value;
             const int s_cur = kt & 1, s_next = (kt + 1) & 1;
             const char *ac = (DEEP_B ? S0 + s_cur * OPS : D0 + sd_cur * OPS);
             const char *bc = (DEEP_B ? D0 + sd_cur * OPS : S0 + s_cur * OPS);
@@ -843,14 +866,14 @@ struct DtlTile {
             const char *bn = (DEEP_B ? D0 + sd_next * OPS : S0 + s_next * OPS);
             char *dw = D0 + sd_fill * OPS;
             char *sw = S0 + s_cur * OPS;
-            const auto rD = sd.at_step(kt + 2);
+            const auto rD = M ? sd.at_step(kt + 2) : step_rsrc(sd, D_KMAJOR, kt + 2);
             const int kd = K - (kt + 2) * kBK;
             // half 0 (sub-step 0, m blocks 0-3): the deep operand's first loads
             read_a<0, 1>(ac, Y);
             read_b<1>(bc, Q);
 #pragma unroll
             for (int j = 0; j < H; ++j)
-                load_d(rD, dw, j, kd);
+                load_d(rD, dw, j, kd, mask);
             mfmas<0>(X, P);
             pattern<0, 4 + RB, H>();
             __builtin_amdgcn_sched_barrier(0);
@@ -858,7 +881,7 @@ struct DtlTile {
             read_a<1, 0>(ac, X);
 #pragma unroll
             for (int j = H; j < LOADS; ++j)
-                load_d(rD, dw, j, kd);
+                load_d(rD, dw, j, kd, mask);
             mfmas<1>(Y, P);
             pattern<0, 4, H>();
             __builtin_amdgcn_sched_barrier(0);
@@ -875,11 +898,11 @@ struct DtlTile {
             read_a<0, 0>(an, X);
             read_b<0>(bn, P);
             {
-                const auto rS = ss.at_step(kt + 2);
+                const auto rS = M ? ss.at_step(kt + 2) : step_rsrc(ss, S_KMAJOR, kt + 2);
                 const int ks2 = K - (kt + 2) * kBK;
 #pragma unroll
                 for (int j = 0; j < LOADS; ++j)
-                    load_s(rS, sw, j, ks2);
+                    load_s(rS, sw, j, ks2, mask);
             }
             mfmas<1>(Y, Q);
             pattern<0, 4 + RB, LOADS>();
@@ -888,7 +911,14 @@ struct DtlTile {
             sd_cur = sd_next;
             sd_next = sd_fill;
             sd_fill = t;
-        }
+        };
+        // the loads of step kt + 2 need no K mask while that step is not
+        // the last (kt + 2 <= ksteps - 2)
+        int kt = 0;
+        for (; kt < ksteps - 3; ++kt)
+            step(kt, unmasked);
+        for (; kt < ksteps; ++kt)
+            step(kt, masked);
         // the trailing loads (empty ranges) have landed before the next tile
         wait_vm<0>();
     }
@@ -1076,16 +1106,6 @@ struct DtlTile4 {
         const OperandSrc ua = uniform_src(sa), ub = uniform_src(sb);
         const OperandSrc &sd = DEEP_B ? ub : ua;
         const OperandSrc &ss = DEEP_B ? ua : ub;
-        // The resource of a step that ends before K - 1's step: the base
-        // moved to the step, the length left as the rows bound it.  A
-        // k-contiguous operand's rows past the tile's last read as zero
-        // because their offsets pass the first step's length; a row-major
-        // B's lanes stay within one step of 64 rows, which such a step holds
-        // in full.
-        auto step_rsrc = [](const OperandSrc &u, bool kmajor, int kt) {
-            const uint64_t rec = kmajor ? u.bytes : (uint64_t)u.step_bytes;
-            return make_rsrc(u.base + (uint64_t)kt * u.step_bytes, rec);
-        };
         constexpr bool D_KMAJOR = DEEP_B ? BKM : true, S_KMAJOR = DEEP_B ? true : BKM;
         auto load_d = [&](__amdgpu_buffer_rsrc_t r, char *slot, int j, int k_left, auto mask) {
             if constexpr (DEEP_B)
