@@ -1229,18 +1229,20 @@ __device__ __forceinline__ float silu_mul(float g, float u)
 
 // Four consecutive outputs -> one store of 16 B (fp32) or 8 B (16-bit) at
 // byte offset `off` of resource r; offsets past the resource are dropped.
-template <int OUT>
+// AUX: the store's cache-policy bits (kStoreStream: non-temporal).
+constexpr int kStoreStream = 2;
+template <int OUT, int AUX = 0>
 __device__ __forceinline__ void bstore4(__amdgpu_buffer_rsrc_t r, uint32_t off, float v0, float v1, float v2,
                                         float v3)
 {
     if constexpr (OUT == OUT_F32) {
         u32x4_t d = {__builtin_bit_cast(uint32_t, v0), __builtin_bit_cast(uint32_t, v1),
                      __builtin_bit_cast(uint32_t, v2), __builtin_bit_cast(uint32_t, v3)};
-        __builtin_amdgcn_raw_buffer_store_b128(d, r, off, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(d, r, off, 0, AUX);
     } else if constexpr (OUT == OUT_BF16) {
-        __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{pack2_bf16(v0, v1), pack2_bf16(v2, v3)}, r, off, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{pack2_bf16(v0, v1), pack2_bf16(v2, v3)}, r, off, 0, AUX);
     } else {
-        __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{pack2_f16(v0, v1), pack2_f16(v2, v3)}, r, off, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{pack2_f16(v0, v1), pack2_f16(v2, v3)}, r, off, 0, AUX);
     }
 }
 
@@ -1371,7 +1373,8 @@ __device__ __forceinline__ void epilogue_staged(const T &t, char *lds, void *D, 
             const f32x4_t v = *(const f32x4_t *)(lds + x * 1024 + ((lane ^ (x & 15)) << 4));
             const int m = (x >> 6) * T::TM + 64 * h + (x & 63);
             const uint32_t off = n < n_valid ? (uint32_t)m * row_bytes + (uint32_t)n * esize : kOOB;
-            bstore4<OUT>(r, off, v[0], v[1], v[2], v[3]);
+            // whole rows, written once and not read again here: streaming
+            bstore4<OUT, kStoreStream>(r, off, v[0], v[1], v[2], v[3]);
         }
         lds_barrier();
     }
@@ -1387,6 +1390,13 @@ __device__ __forceinline__ void tile_epilogue(const T &t, char *lds, void *D, in
         epilogue_staged<T, OUT>(t, lds, D, ldd, m_valid, n_valid, tid);
     else
         epilogue<T, EPI, OUT>(t, D, ldd, m_valid, n_valid, tid);
+    // The direct-to-LDS loops count their own loads with vmcnt waits, and
+    // the counter also counts these stores.  Rather than rely on loads and
+    // earlier stores retiring in order (the compiler's own wait placement
+    // does not assume it), the next tile starts with nothing outstanding;
+    // measured free, as its first wait would cover the stores anyway.
+    if constexpr (T::MI == 16)
+        wait_vm<0>();
 }
 
 }  // namespace mgemm
