@@ -299,6 +299,26 @@ def test_direct_to_lds_short_k_two_tiles_per_workgroup(K, bl, in_t, out_t):
     assert_bits_equal(got, ref, out_t, plan.describe())
 
 
+@pytest.mark.parametrize("K", [1000, 2056])
+@pytest.mark.parametrize("bl", ["row", "col"])
+def test_direct_to_lds_long_k_ragged_tail(K, bl):
+    """The direct-to-LDS tile over many K steps with a partial last one: the
+    steps before the last take the unmasked loads, the last three the masked
+    ones; ragged M and N (partial tiles at both edges).  Integer inputs
+    bit-exact, random inputs within the tolerance."""
+    M, N = 300, 520
+    log(f"case dtl long-k M={M} N={N} K={K} B {bl}")
+    cfg = datagen.GemmConfig("t", M, N, K, "bf16", "f32", "row", bl, ("uniform", 1.0), ("normal", 1.0),
+                             seed=K, int_seed=K + 1)
+    a, b = datagen.gemm_inputs(cfg, "int")
+    got, plan = run_dense(a, b, M, N, K, "bf16", "f32", "row", bl, TILES["256d"], sentinel=True)
+    assert "256x256dtl" in plan.describe() and "splits=1" in plan.describe(), plan.describe()
+    assert_bits_equal(got, oracle.gemm_ref(a, b, "bf16", "bf16", "row", bl), "f32", plan.describe())
+    a, b = datagen.gemm_inputs(cfg, "random")
+    got, plan = run_dense(a, b, M, N, K, "bf16", "f32", "row", bl, TILES["256d"])
+    assert_close(got, oracle.gemm_ref(a, b, "bf16", "bf16", "row", bl), K, "f32", plan.describe())
+
+
 # --------------------------------------------------------------- full size
 
 FULL = ["gemm512_f16", "gemm4096_bf16", "gemm8192_bf16_bcol", "ts16384x2048x7168", "decode128x7168x2048"]
