@@ -986,6 +986,10 @@ struct DtlTile4 {
     int kc[LOADS];
     int abase[2], bbase[2];
     int bfr[FN];
+    // LDS byte addresses of the 2-slot operand's fragments, per slot: A
+    // (column-major B) or the transpose-read pieces of B (row-major B)
+    uint32_t a_sh[2][2];
+    uint32_t b_sh[2][FN];
 
     __device__ __forceinline__ void setup(int lane, int wave, int wm0, int wn0, int lda, int ldb)
     {
@@ -1059,6 +1063,34 @@ struct DtlTile4 {
             f.v[jb][2 * hi + 1] = w[1];
         }
     }
+    // The same reads with the slot known: Q = the 2-slot operand's slot
+    // (0 or 1), so the address is a register set up once plus an immediate
+    // offset; Q < 0, or the 3-slot operand: through the slot pointer.
+    template <int Q, int S, int H>
+    __device__ __forceinline__ void rd_a(const char *as, F4 &f, int i) const
+    {
+        if constexpr (BKM && Q >= 0) {
+            typedef __attribute__((address_space(3))) u32x4_t lds_u32x4;
+            f.v[i] = *(const lds_u32x4 *)(uintptr_t)(a_sh[Q][S] + (4 * H + i) * 16 * kRowBytes);
+        } else {
+            read_a<S, H>(as, f, i);
+        }
+    }
+    template <int Q, int S, int H>
+    __device__ __forceinline__ void rd_b(const char *bs, F4 &f, int i) const
+    {
+        if constexpr (!BKM && Q >= 0) {
+            typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
+            const int jb = i >> 1, hi = i & 1;
+            const uint32_t a = b_sh[Q][4 * H + jb] + 32 * S * BROW + 4 * BROW * hi;
+            const u32x2_t w =
+                __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(uintptr_t)a));
+            f.v[jb][2 * hi] = w[0];
+            f.v[jb][2 * hi + 1] = w[1];
+        } else {
+            read_b<S, H>(bs, f, i);
+        }
+    }
     // 16 MFMAs on m blocks 4 HM .. +3 x n blocks 4 HN .. +3; read i (of NR)
     // after MFMA i, global load j (of NL) after MFMA j * 16 / NL
     static constexpr int LOFF = 2;   // MFMA after which a quarter's first load goes
@@ -1103,6 +1135,19 @@ struct DtlTile4 {
         char *const B0 = lds + A_SLOTS * OPS;
         char *const D0 = DEEP_B ? B0 : A0;
         char *const S0 = DEEP_B ? A0 : B0;
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const uint32_t slot = lds_addr(S0 + q * OPS);
+            if constexpr (BKM) {
+#pragma unroll
+                for (int s = 0; s < 2; ++s)
+                    a_sh[q][s] = slot + (uint32_t)abase[s];
+            } else {
+#pragma unroll
+                for (int jb = 0; jb < FN; ++jb)
+                    b_sh[q][jb] = slot + (uint32_t)bfr[jb];
+            }
+        }
         const OperandSrc ua = uniform_src(sa), ub = uniform_src(sb);
         const OperandSrc &sd = DEEP_B ? ub : ua;
         const OperandSrc &ss = DEEP_B ? ua : ub;
@@ -1156,9 +1201,12 @@ struct DtlTile4 {
         // the zeroed accumulators are written by ordinary instructions
         mfma_drain();
         int sd_cur = 0;   // deep slot of step kt
-        // one K step; its loads are of step kt + 2
-        auto step = [&](int kt, auto mask) {
-            const int s_cur = kt & 1;
+        // one K step; its loads are of step kt + 2.  par: the 2-slot
+        // operand's slot of step kt when known at compile time (else -1)
+        auto step = [&](int kt, auto mask, auto par) {
+            constexpr int P = decltype(par)::value;
+            constexpr int QC = P, QN = P < 0 ? -1 : (P ^ 1);
+            const int s_cur = P < 0 ? (kt & 1) : P;
             const int sd_next = sd_cur == 2 ? 0 : sd_cur + 1;
             const int sd_fill = sd_next == 2 ? 0 : sd_next + 1;
             const char *ac = DEEP_B ? S0 + s_cur * OPS : D0 + sd_cur * OPS;
@@ -1170,13 +1218,13 @@ struct DtlTile4 {
             const auto rD = decltype(mask)::value ? sd.at_step(kt + 2) : step_rsrc(sd, D_KMAJOR, kt + 2);
             const int kd = K - (kt + 2) * kBK;
             char *const dw = D0 + sd_fill * OPS;
-            quarter<0, 0, 4, 2>(Xl, Pl, [&](int i) { read_a<1, 0>(ac, Yl, i); },
+            quarter<0, 0, 4, 2>(Xl, Pl, [&](int i) { rd_a<QC, 1, 0>(ac, Yl, i); },
                                 [&](int j) { load_d(rD, dw, j, kd, mask); });
-            quarter<0, 1, RB, 2>(Xl, Ph, [&](int i) { read_b<1, 0>(bc, Ql, i); },
+            quarter<0, 1, RB, 2>(Xl, Ph, [&](int i) { rd_b<QC, 1, 0>(bc, Ql, i); },
                                  [&](int j) { load_d(rD, dw, 2 + j, kd, mask); });
-            quarter<1, 0, RB, 2>(Xh, Pl, [&](int i) { read_b<1, 1>(bc, Qh, i); },
+            quarter<1, 0, RB, 2>(Xh, Pl, [&](int i) { rd_b<QC, 1, 1>(bc, Qh, i); },
                                  [&](int j) { load_d(rD, dw, 4 + j, kd, mask); });
-            quarter<1, 1, 4, 2>(Xh, Ph, [&](int i) { read_a<1, 1>(ac, Yh, i); },
+            quarter<1, 1, 4, 2>(Xh, Ph, [&](int i) { rd_a<QC, 1, 1>(ac, Yh, i); },
                                 [&](int j) { load_d(rD, dw, 6 + j, kd, mask); });
             wait_vm<LOADS>();
             lds_barrier();
@@ -1185,21 +1233,24 @@ struct DtlTile4 {
             const auto rS = decltype(mask)::value ? ss.at_step(kt + 2) : step_rsrc(ss, S_KMAJOR, kt + 2);
             const int ks = K - (kt + 2) * kBK;
             char *const sw = S0 + s_cur * OPS;
-            quarter<0, 0, 4, 4>(Yl, Ql, [&](int i) { read_a<0, 0>(an, Xl, i); },
+            quarter<0, 0, 4, 4>(Yl, Ql, [&](int i) { rd_a<QN, 0, 0>(an, Xl, i); },
                                 [&](int j) { load_s(rS, sw, j, ks, mask); });
-            quarter<0, 1, RB, 4>(Yl, Qh, [&](int i) { read_b<0, 0>(bn, Pl, i); },
+            quarter<0, 1, RB, 4>(Yl, Qh, [&](int i) { rd_b<QN, 0, 0>(bn, Pl, i); },
                                  [&](int j) { load_s(rS, sw, 4 + j, ks, mask); });
-            quarter<1, 0, RB, 0>(Yh, Ql, [&](int i) { read_b<0, 1>(bn, Ph, i); }, [](int) {});
-            quarter<1, 1, 4, 0>(Yh, Qh, [&](int i) { read_a<0, 1>(an, Xh, i); }, [](int) {});
+            quarter<1, 0, RB, 0>(Yh, Ql, [&](int i) { rd_b<QN, 0, 1>(bn, Ph, i); }, [](int) {});
+            quarter<1, 1, 4, 0>(Yh, Qh, [&](int i) { rd_a<QN, 0, 1>(an, Xh, i); }, [](int) {});
             sd_cur = sd_next;
         };
-        // the loads of step kt + 2 need no K mask while that step is not
-        // the last (kt + 2 <= ksteps - 2)
+        // Steps two at a time while the loads of step kt + 2 need no K mask
+        // (kt + 2 <= ksteps - 2), each with its 2-slot slot fixed; the rest
+        // (at most four) with the mask and the slot computed.
         int kt = 0;
-        for (; kt < ksteps - 3; ++kt)
-            step(kt, unmasked);
+        for (; kt + 1 < ksteps - 3; kt += 2) {
+            step(kt, unmasked, std::integral_constant<int, 0>{});
+            step(kt + 1, unmasked, std::integral_constant<int, 1>{});
+        }
         for (; kt < ksteps; ++kt)
-            step(kt, masked);
+            step(kt, masked, std::integral_constant<int, -1>{});
         // the trailing loads (empty ranges) have landed before the next tile,
         // and the last MFMAs' results before the epilogue reads them
         wait_vm<0>();

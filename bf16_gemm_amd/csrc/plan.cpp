@@ -31,8 +31,9 @@ static const TileShape kTiles[NUM_TILES] = {
 const TileShape &tile_shape(int tile) { return kTiles[tile]; }
 
 // Wave layout and ring depths of a dense plan's tile: the direct-to-LDS
-// tile runs column-major B on four waves of 128 x 128 with the 3-slot ring
-// on B, row-major B on eight waves of 128 x 64 with the 3-slot ring on A.
+// tile runs dense plans on four waves of 128 x 128 (the tile table's 2x4 is
+// its grouped launches' layout), with the 3-slot ring on B when B is
+// column-major, else on A.
 static void dense_waves(int tile, bool bk, int &wm, int &wn, int &a_slots, int &b_slots)
 {
     const TileShape &ts = tile_shape(tile);
@@ -40,8 +41,7 @@ static void dense_waves(int tile, bool bk, int &wm, int &wn, int &a_slots, int &
     wn = ts.wn;
     a_slots = b_slots = 2;
     if (tile == TILE_256x256_DTL) {
-        if (bk)
-            wn = 2;
+        wn = 2;
         a_slots = bk ? 2 : 3;
         b_slots = bk ? 3 : 2;
     }

@@ -59,9 +59,8 @@ DenseFn dense_table(bool ak, bool bk, int out)
 #undef MG_D
 }
 
-// The direct-to-LDS 256 x 256 engine: row-major (k-contiguous) A, B either
-// way.  Column-major B runs on four waves of 128 x 128 (DtlTile4), row-major
-// B on eight of 128 x 64 (DtlTile), the faster of the two for each layout.
+// The direct-to-LDS 256 x 256 engine for dense plans: row-major
+// (k-contiguous) A, B either way, on four waves of 128 x 128 (DtlTile4).
 template <int IN>
 DenseFn dense_dtl_table(bool ak, bool bk, int out)
 {
@@ -70,8 +69,8 @@ DenseFn dense_dtl_table(bool ak, bool bk, int out)
     if (bk)
         return out == OUT_F32 ? launch_dense_tile<DtlTile4<IN, true>, true, true, IN, OUT_F32>
                               : launch_dense_tile<DtlTile4<IN, true>, true, true, IN, same16<IN>()>;
-    return out == OUT_F32 ? launch_dense_tile<DtlTile<IN, false>, true, false, IN, OUT_F32>
-                          : launch_dense_tile<DtlTile<IN, false>, true, false, IN, same16<IN>()>;
+    return out == OUT_F32 ? launch_dense_tile<DtlTile4<IN, false>, true, false, IN, OUT_F32>
+                          : launch_dense_tile<DtlTile4<IN, false>, true, false, IN, same16<IN>()>;
 }
 
 // Grouped launches of the direct-to-LDS tile: its rings fill the LDS, so

@@ -111,8 +111,8 @@ typedef struct {
 #define MGEMM_PLAN_FORCE_TILE_32x256  0x4u   /* narrow-M (few tokens)   */
 #define MGEMM_PLAN_FORCE_TILE_64x256  0x8u   /* narrow-M (few tokens)   */
 /* 256x256 with loads that write LDS directly (no staging registers; four
- * waves of 128x128 for a dense plan with column-major B, else eight waves of
- * 128x64).  Dense plans: row-major A only, else UNSUPPORTED; the planner uses
+ * waves of 128x128 in dense plans, eight waves of 128x64 in grouped plans).
+ * Dense plans: row-major A only, else UNSUPPORTED; the planner uses
  * it whenever it picks the 256x256 tile for such a plan.  Grouped plans
  * (whose A is always row-major): the planner uses it for the experts of 129
  * rows or more.  In both, MGEMM_PLAN_FORCE_TILE_256x256 selects the
