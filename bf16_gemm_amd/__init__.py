@@ -72,7 +72,7 @@ class Budget(ctypes.Structure):
 EXPORTS = ["gemm_plan", "grouped_gemm_plan", "gemm_plan_workspace_size", "gemm_run", "grouped_gemm_run",
            "gemm_plan_describe", "gemm_plan_info", "gemm_plan_destroy", "gemm_status_string",
            "gemm_last_error_message", "mgemm_tile_budget", "mgemm_group_working_set", "mgemm_round_tokens",
-           "mgemm_version"]
+           "mgemm_version", "mgemm_moe_combine"]
 
 
 def _load():
@@ -110,6 +110,8 @@ def _load():
     lib.mgemm_round_tokens.argtypes = [i64, ctypes.c_int32]
     lib.mgemm_round_tokens.restype = i64
     lib.mgemm_version.restype = ctypes.c_char_p
+    lib.mgemm_moe_combine.argtypes = [vp, i64, i64, vp, vp, vp, i64, i64, ctypes.c_int32, i64, ctypes.c_int, vp]
+    lib.mgemm_moe_combine.restype = st
     return lib
 
 
@@ -228,6 +230,17 @@ def grouped_gemm_run(plan: Plan, A, B, D, row_offsets, workspace=None, workspace
     tensor of num_groups + 1 prefix sums."""
     _check(lib.grouped_gemm_run(plan.handle, _ptr(A), _ptr(B), _ptr(D), _ptr(row_offsets), _ptr(workspace),
                                 _nbytes(workspace, workspace_bytes), _stream(stream)), "grouped_gemm_run")
+
+
+def moe_combine(Z, pos, weights, Y, top_k: int, z_rows=None, stream=None):
+    """Enqueue Y[t] = sum_k weights[t, k] * Z[pos[t, k]] (fp32 accumulate,
+    one rounding).  Z: [z_rows, H] and Y: [T, H] 16-bit cuda tensors with
+    unit column stride; pos: int32 and weights: float32 cuda tensors of
+    T * top_k entries."""
+    T, H = Y.shape
+    z_rows = Z.shape[0] if z_rows is None else z_rows
+    _check(lib.mgemm_moe_combine(_ptr(Z), z_rows, Z.stride(0), _ptr(pos), _ptr(weights), _ptr(Y), Y.stride(0), T,
+                                 top_k, H, TORCH_DTYPE[Y.dtype], _stream(stream)), "mgemm_moe_combine")
 
 
 def tile_budget(M, N, K, BM, BN, BK, stages, elt_bytes) -> Budget:

@@ -195,6 +195,44 @@ extern "C" mgemm_status_t grouped_gemm_run(mgemm_plan_t plan, const void *A, con
     return MGEMM_OK;
 }
 
+extern "C" mgemm_status_t mgemm_moe_combine(const void *Z, int64_t z_rows, int64_t ldz, const int32_t *d_pos,
+                                            const float *d_weights, void *Y, int64_t ldy, int64_t T, int32_t top_k,
+                                            int64_t H, mgemm_dtype_t dtype, mgemm_stream_t stream)
+{
+    if (T < 0 || H < 0 || z_rows < 0 || top_k < 1 || top_k > 256 || T > INT32_MAX) {
+        set_error("mgemm_moe_combine: bad sizes (T=%lld H=%lld z_rows=%lld top_k=%d)", (long long)T, (long long)H,
+                  (long long)z_rows, top_k);
+        return MGEMM_ERR_INVALID_ARG;
+    }
+    if (dtype != MGEMM_BF16 && dtype != MGEMM_F16) {
+        set_error("mgemm_moe_combine: dtype must be BF16 or F16");
+        return MGEMM_ERR_UNSUPPORTED;
+    }
+    if (T == 0 || H == 0)
+        return MGEMM_OK;
+    if (ldz < H || ldy < H) {
+        set_error("mgemm_moe_combine: ldz=%lld and ldy=%lld must be >= H=%lld", (long long)ldz, (long long)ldy,
+                  (long long)H);
+        return MGEMM_ERR_INVALID_ARG;
+    }
+    if (!Z || !Y || !d_pos || !d_weights) {
+        set_error("mgemm_moe_combine: null pointer");
+        return MGEMM_ERR_INVALID_ARG;
+    }
+    if (H % 8 || ldz % 8 || ldy % 8 || !aligned16(Z) || !aligned16(Y)) {
+        set_error("mgemm_moe_combine: H, ldz, ldy must be multiples of 8 and Z, Y 16-byte aligned");
+        return MGEMM_ERR_UNSUPPORTED;
+    }
+    if ((uint64_t)z_rows * (uint64_t)ldz * 2u > (uint64_t)kMaxRecords) {
+        set_error("mgemm_moe_combine: Z spans more than %u bytes", kMaxRecords);
+        return MGEMM_ERR_UNSUPPORTED;
+    }
+    const int out = dtype == MGEMM_BF16 ? OUT_BF16 : OUT_F16;
+    return hip_status(launch_moe_combine(Z, z_rows, ldz, d_pos, d_weights, Y, ldy, T, top_k, H, out,
+                                         (hipStream_t)stream),
+                      "mgemm_moe_combine launch");
+}
+
 extern "C" const char *gemm_status_string(mgemm_status_t s)
 {
     switch (s) {

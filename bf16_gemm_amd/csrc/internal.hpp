@@ -60,6 +60,8 @@ MGEMM_DECLARE_TU(256x256dtl_f16)
 using EdgeFn = hipError_t (*)(const DenseArgs &, int a_kmajor, int b_kmajor, int n_first, hipStream_t);
 EdgeFn edge_fn(int in, int out);
 hipError_t launch_zero_fill(void *D, int rows, int cols, int64_t ld_bytes, int esize, hipStream_t s);
+hipError_t launch_moe_combine(const void *Z, int64_t z_rows, int64_t ldz, const int32_t *pos, const float *w,
+                              void *Y, int64_t ldy, int64_t T, int top_k, int64_t H, int out, hipStream_t s);
 // D[M x N] = sum over r < splits of W[r][M x N] (fp32, row pitch ldw, slabs
 // split_stride apart), added in increasing r and rounded once to D's type.
 hipError_t launch_reduce_splits(const float *W, void *D, int M, int N, int ldw, int64_t split_stride, int splits,

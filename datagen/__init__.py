@@ -181,6 +181,8 @@ class Routing:
     offsets: np.ndarray          # [E + 1] prefix sums (int32)
     token_of_row: np.ndarray     # [total_rows] source token of each routed row
     expert_of_row: np.ndarray = field(default=None)
+    pos: np.ndarray = field(default=None)     # [num_tokens, top_k] routed row of (token, choice)
+    weight: np.ndarray = field(default=None)  # [num_tokens, top_k] fp32 routing weight (softmax of the scores)
 
 
 def moe_routing(num_tokens: int, num_experts: int, top_k: int, alpha: float, seed: int) -> Routing:
@@ -200,8 +202,19 @@ def moe_routing(num_tokens: int, num_experts: int, top_k: int, alpha: float, see
         rows.append(toks)
         experts.append(np.full(toks.size, e, dtype=np.int32))
     token_of_row = np.concatenate(rows).astype(np.int64) if rows else np.zeros(0, np.int64)
+    # the row each (token, choice) was routed to: expert e's rows hold its
+    # tokens in ascending order
+    pos = np.empty(top.shape, dtype=np.int32)
+    for k in range(top_k):
+        e = top[:, k]
+        for ex in np.unique(e):
+            sel = np.nonzero(e == ex)[0]
+            pos[sel, k] = offsets[ex] + np.searchsorted(rows[ex], sel)
+    s = np.take_along_axis(score, top, axis=1)
+    s = np.exp(s - s.max(axis=1, keepdims=True))
+    weight = (s / s.sum(axis=1, keepdims=True)).astype(np.float32)
     return Routing(top=top, counts=counts, offsets=offsets, token_of_row=token_of_row,
-                   expert_of_row=np.concatenate(experts))
+                   expert_of_row=np.concatenate(experts), pos=pos, weight=weight)
 
 
 def moe_route(cfg: MoeConfig) -> Routing:

@@ -214,6 +214,25 @@ int64_t mgemm_group_working_set(int32_t group_m, int32_t group_n, int32_t BM, in
  * to a multiple of 16 before sizing the MMA). */
 int64_t mgemm_round_tokens(int64_t n, int32_t granule);
 
+/* MoE combine: every token's output row is the routing-weighted sum of the
+ * rows its top-k experts produced ("MegaMoE：Blackwell 与 Hopper 的融合算子解读",
+ * Blackwell section 13: a separate top-k reduce reads each branch and adds
+ * them into the token's output; Hopper section 09 for the routing weight p
+ * applied to an expert's output, p(hW2) = (ph)W2).
+ *   Y[t, j] = sum_{k < top_k} weights[t*top_k + k] * Z[pos[t*top_k + k], j]
+ * for t < T, j < H.  Z: 16-bit rows (the FC2 output in expert order),
+ * z_rows x H, row pitch ldz; Y: T x H of the same type, row pitch ldy; pos
+ * (int32) and weights (fp32): device arrays of T*top_k entries.  The terms
+ * are added in k order with fp32 fused multiply-adds, then rounded once
+ * (RNE) to the 16-bit type.  A position outside [0, z_rows) contributes
+ * nothing.  dtype: BF16 or F16.  H % 8 == 0, ldz and ldy multiples of 8 and
+ * >= H, Z and Y 16-byte aligned, z_rows * ldz * 2 <= 2^31 - 16 bytes,
+ * 1 <= top_k <= 256, otherwise MGEMM_ERR_UNSUPPORTED / _INVALID_ARG.
+ * T == 0 or H == 0: no-op.  Y must not overlap Z.  Asynchronous on stream. */
+mgemm_status_t mgemm_moe_combine(const void *Z, int64_t z_rows, int64_t ldz, const int32_t *d_pos,
+                                 const float *d_weights, void *Y, int64_t ldy, int64_t T, int32_t top_k, int64_t H,
+                                 mgemm_dtype_t dtype, mgemm_stream_t stream);
+
 /* Library version, e.g. "mgemm 0.1 gfx950". */
 const char *mgemm_version(void);
 

@@ -213,3 +213,26 @@ def moe_ref(A: np.ndarray, W1: np.ndarray, W2: np.ndarray, offsets):
     h_bits = encode(h_ref, "bf16")
     y_ref = grouped_ref(h_bits, W2, offsets)
     return h_ref, h_bits, y_ref
+
+
+def moe_combine_ref(Z: np.ndarray, pos, weights, dtype: str = "bf16") -> np.ndarray:
+    """Top-k combine of the expert outputs ("MegaMoE：Blackwell 与 Hopper 的融合
+    算子解读", Blackwell section 13: the top-k reduce reads every branch of a
+    token and adds them into its output; Hopper section 09: the routing
+    weight p scales an expert's contribution, p(hW2) = (ph)W2).
+
+    ``Z``: [rows][H] 16-bit bits (expert outputs in expert order); ``pos``:
+    [T][top_k] row of Z for each (token, choice); ``weights``: [T][top_k].
+    Returns y[t] = sum_k weights[t, k] * Z[pos[t, k]] (fp64, unrounded); a
+    position outside [0, rows) adds nothing.
+    """
+    z = decode(Z, dtype)
+    pos = np.asarray(pos)
+    w = np.asarray(weights, dtype=np.float64)
+    y = np.zeros((pos.shape[0], z.shape[1]), dtype=np.float64)
+    for k in range(pos.shape[1]):
+        p = pos[:, k]
+        ok = (p >= 0) & (p < z.shape[0])
+        y[ok] += w[ok, k][:, None] * z[p[ok]]
+    return y
+
