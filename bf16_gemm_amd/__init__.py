@@ -72,7 +72,7 @@ class Budget(ctypes.Structure):
 EXPORTS = ["gemm_plan", "grouped_gemm_plan", "gemm_plan_workspace_size", "gemm_run", "grouped_gemm_run",
            "gemm_plan_describe", "gemm_plan_info", "gemm_plan_destroy", "gemm_status_string",
            "gemm_last_error_message", "mgemm_tile_budget", "mgemm_group_working_set", "mgemm_round_tokens",
-           "mgemm_version", "mgemm_moe_combine"]
+           "mgemm_version", "mgemm_moe_combine", "grouped_gemm_run_gather"]
 
 
 def _load():
@@ -110,6 +110,8 @@ def _load():
     lib.mgemm_round_tokens.argtypes = [i64, ctypes.c_int32]
     lib.mgemm_round_tokens.restype = i64
     lib.mgemm_version.restype = ctypes.c_char_p
+    lib.grouped_gemm_run_gather.argtypes = [vp, vp, i64, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.grouped_gemm_run_gather.restype = st
     lib.mgemm_moe_combine.argtypes = [vp, i64, i64, vp, vp, vp, i64, i64, ctypes.c_int32, i64, ctypes.c_int, vp]
     lib.mgemm_moe_combine.restype = st
     return lib
@@ -230,6 +232,15 @@ def grouped_gemm_run(plan: Plan, A, B, D, row_offsets, workspace=None, workspace
     tensor of num_groups + 1 prefix sums."""
     _check(lib.grouped_gemm_run(plan.handle, _ptr(A), _ptr(B), _ptr(D), _ptr(row_offsets), _ptr(workspace),
                                 _nbytes(workspace, workspace_bytes), _stream(stream)), "grouped_gemm_run")
+
+
+def grouped_gemm_run_gather(plan: Plan, X, B, D, row_offsets, row_index, x_rows=None, stream=None):
+    """Enqueue the planned grouped product with A's routed row r read from
+    X[row_index[r]] (``row_index``: device int32 tensor, one entry per
+    routed row)."""
+    x_rows = X.shape[0] if x_rows is None else x_rows
+    _check(lib.grouped_gemm_run_gather(plan.handle, _ptr(X), x_rows, _ptr(B), _ptr(D), _ptr(row_offsets),
+                                       _ptr(row_index), None, 0, _stream(stream)), "grouped_gemm_run_gather")
 
 
 def moe_combine(Z, pos, weights, Y, top_k: int, z_rows=None, stream=None):

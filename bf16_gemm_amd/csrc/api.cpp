@@ -134,12 +134,11 @@ extern "C" mgemm_status_t gemm_run(mgemm_plan_t plan, const void *A, const void 
     return MGEMM_OK;
 }
 
-extern "C" mgemm_status_t grouped_gemm_run(mgemm_plan_t plan, const void *A, const void *B, void *D,
-                                           const int32_t *d_row_offsets, void *workspace, size_t workspace_bytes,
-                                           mgemm_stream_t stream)
+// row_index: nullptr, or the gathered form's index (x_rows rows of A exist).
+static mgemm_status_t grouped_run(mgemm_plan_t plan, const void *A, const void *B, void *D,
+                                  const int32_t *d_row_offsets, const int32_t *row_index, int64_t x_rows,
+                                  mgemm_stream_t stream)
 {
-    (void)workspace;
-    (void)workspace_bytes;
     if (!plan || plan->kind != PLAN_GROUPED) {
         set_error("grouped_gemm_run: null or non-grouped plan");
         return MGEMM_ERR_INVALID_ARG;
@@ -150,6 +149,21 @@ extern "C" mgemm_status_t grouped_gemm_run(mgemm_plan_t plan, const void *A, con
     if (!D || !d_row_offsets || (!plan->zero_fill && (!A || !B))) {
         set_error("grouped_gemm_run: null pointer");
         return MGEMM_ERR_INVALID_ARG;
+    }
+    if (row_index && !plan->zero_fill) {
+        if (x_rows < 0 || x_rows > INT32_MAX ||
+            (uint64_t)x_rows * (uint64_t)d.lda * 2u > (uint64_t)kMaxRecords) {
+            set_error("grouped_gemm_run_gather: x_rows=%lld out of range (x_rows * lda * 2 must be < 2^31)",
+                      (long long)x_rows);
+            return MGEMM_ERR_INVALID_ARG;
+        }
+        for (const GroupedLaunch &L : plan->launches) {
+            if (L.tile != TILE_32x256 && L.tile != TILE_256x256_DTL) {
+                set_error("grouped_gemm_run_gather: the planned tile %d does not take gathered rows (the default "
+                          "32x256 and direct-to-LDS 256x256 tiles do)", L.tile);
+                return MGEMM_ERR_UNSUPPORTED;
+            }
+        }
     }
     if (!aligned16(A) || !aligned16(B) || !aligned16(D)) {
         set_error("grouped_gemm_run: A, B and D must be 16-byte aligned");
@@ -184,6 +198,8 @@ extern "C" mgemm_status_t grouped_gemm_run(mgemm_plan_t plan, const void *A, con
         a.bucket_lo = L.lo;
         a.bucket_hi = L.hi;
         a.xcd_remap = plan->xcd_remap;
+        a.row_index = row_index;
+        a.x_rows = (int)x_rows;
         GroupedFn f = grouped_fn(L.tile, bk, in, out, epi);
         if (!f) {
             set_error("grouped_gemm_run: kernel missing for the planned variant");
@@ -193,6 +209,29 @@ extern "C" mgemm_status_t grouped_gemm_run(mgemm_plan_t plan, const void *A, con
             return st;
     }
     return MGEMM_OK;
+}
+
+extern "C" mgemm_status_t grouped_gemm_run(mgemm_plan_t plan, const void *A, const void *B, void *D,
+                                           const int32_t *d_row_offsets, void *workspace, size_t workspace_bytes,
+                                           mgemm_stream_t stream)
+{
+    (void)workspace;
+    (void)workspace_bytes;
+    return grouped_run(plan, A, B, D, d_row_offsets, nullptr, 0, stream);
+}
+
+extern "C" mgemm_status_t grouped_gemm_run_gather(mgemm_plan_t plan, const void *X, int64_t x_rows, const void *B,
+                                                  void *D, const int32_t *d_row_offsets,
+                                                  const int32_t *d_row_index, void *workspace,
+                                                  size_t workspace_bytes, mgemm_stream_t stream)
+{
+    (void)workspace;
+    (void)workspace_bytes;
+    if (!d_row_index) {
+        set_error("grouped_gemm_run_gather: null row index");
+        return MGEMM_ERR_INVALID_ARG;
+    }
+    return grouped_run(plan, X, B, D, d_row_offsets, d_row_index, x_rows, stream);
 }
 
 extern "C" mgemm_status_t mgemm_moe_combine(const void *Z, int64_t z_rows, int64_t ldz, const int32_t *d_pos,

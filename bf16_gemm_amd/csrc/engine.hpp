@@ -68,6 +68,24 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, ui
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)n, 0x00020000);
 }
 
+// Rows of A taken through an index (the MoE dispatch fused into the A
+// loads: "MegaMoE：Blackwell 与 Hopper 的融合算子解读", Hopper section 11, a
+// dispatch warp pulls the routed tokens' rows for the expert GEMM).  Tile
+// row r reads A row idx[r]; rows r >= valid, and indices outside
+// [0, limit), read as zeros.  idx == nullptr: tile row r is row r of the
+// tile's own block of A.
+struct RowGather {
+    const int32_t *idx = nullptr;
+    int valid = 0;
+    int limit = 0;
+    // byte offset of tile row r's source row (ld elements per row), or kOOB
+    __device__ __forceinline__ uint32_t row_offset(int r, int ld) const
+    {
+        const int src = r < valid ? idx[r] : -1;
+        return (src >= 0 && src < limit) ? (uint32_t)src * (uint32_t)ld * 2u : kOOB;
+    }
+};
+
 __device__ __forceinline__ u32x4_t bload16(__amdgpu_buffer_rsrc_t r, uint32_t off)
 {
     return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
@@ -126,6 +144,13 @@ struct Loader<R, NT, true> {
         kc = c * 8;
         lds_even = row * kRowBytes + ((c ^ swz(row)) << 4);
         lds_odd = (row + RSTEP) * kRowBytes + ((c ^ swz(row + RSTEP)) << 4) - RSTEP * kRowBytes;
+    }
+    // rows through an index (one chunk per lane only: NC == 1)
+    __device__ __forceinline__ void gather(int tid, int ld, const RowGather &g)
+    {
+        static_assert(NC == 1, "gathered rows need one row per lane");
+        const uint32_t ro = g.row_offset(tid >> 3, ld);
+        goff = ro == kOOB ? kOOB : ro + (uint32_t)(tid & 7) * 16u;
     }
     // k_left: k remaining from this step's first k (>= 64 means a full step)
     __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, int k_left)
@@ -358,7 +383,7 @@ struct Tile {
     // per-lane address arithmetic is not hoisted out of the persistent tile
     // loop and held in registers across it.
     __device__ __forceinline__ void mainloop(char *lds, const OperandSrc &sa, int lda, const OperandSrc &sb, int ldb,
-                                             int K, int tid)
+                                             int K, int tid, const RowGather &ga = RowGather{})
     {
         const int lane = tid & 63;
         const int wave = tid >> 6;
@@ -384,6 +409,12 @@ struct Tile {
         for (int s = 0; s < NS; ++s) {
             la[s].init(tid, lda);
             lb[s].init(tid, ldb);
+            if constexpr (A_KMAJOR) {
+                if constexpr (Loader<BM, NT, true>::NC == 1) {
+                    if (ga.idx)
+                        la[s].gather(tid, lda, ga);
+                }
+            }
         }
 
         // Fragment read offsets.  Lane l reads row (l & 31) of a 32-row
@@ -797,7 +828,7 @@ struct DtlTile {
     static constexpr int RB = BKM ? 4 : 8;   // LDS read instructions for the four B fragments
 
     __device__ __forceinline__ void mainloop(char *lds, const OperandSrc &sa, int lda, const OperandSrc &sb, int ldb,
-                                             int K, int tid)
+                                             int K, int tid, const RowGather &ga = RowGather{})
     {
         static_assert(LOADS % 2 == 0, "loads are issued in halves");
         constexpr int H = LOADS / 2;
@@ -813,6 +844,15 @@ struct DtlTile {
         if (ksteps <= 0)
             return;
         setup(lane, wave, wm0, wn0, lda, ldb);
+        if (ga.idx) {
+            // A's rows through the index: the same chunk of another row
+#pragma unroll
+            for (int j = 0; j < LOADS; ++j) {
+                const int row = (wave * LOADS + j) * 8 + (lane >> 3);
+                const uint32_t ro = ga.row_offset(row, lda);
+                va[j] = ro == kOOB ? kOOB : ro + (uint32_t)((lane & 7) ^ dswz(row)) * 16u;
+            }
+        }
         char *const A0 = lds;
         char *const B0 = lds + A_SLOTS * OPS;
         char *const D0 = DEEP_B ? B0 : A0;

@@ -36,7 +36,10 @@ struct GroupedArgs {
     int tiles_n;
     int bucket_lo, bucket_hi;  // only experts with bucket_lo <= rows < bucket_hi
     int xcd_remap;
+    const int32_t *row_index = nullptr;  // gathered A: routed row r reads A row row_index[r]
+    int x_rows = 0;                      // rows of A that exist when gathering
 };
+
 
 // Workgroup id -> logical id.  Workgroups are handed to the eight XCDs
 // round-robin, so id w runs on XCD w % 8.  Mapping w to
@@ -84,6 +87,20 @@ __device__ __forceinline__ OperandSrc operand_src(const uint16_t *tile_origin, i
         s.step_bytes = (uint32_t)kBK * (uint32_t)ld * 2u;
     }
     return s;
+}
+
+// Tile operand A of a grouped task: the tile's own block of rows, or (with
+// a row index) the whole of A, each tile row picked through the index.
+__device__ __forceinline__ OperandSrc grouped_a_src(const GroupedArgs &p, int m0, int m_valid, RowGather &g)
+{
+    const uint16_t *A = (const uint16_t *)p.A;
+    if (p.row_index) {
+        g.idx = p.row_index + m0;
+        g.valid = m_valid;
+        g.limit = p.x_rows;
+        return operand_src<true>(A, p.lda, p.x_rows, p.K);
+    }
+    return operand_src<true>(A + (int64_t)m0 * p.lda, p.lda, m_valid, p.K);
 }
 
 template <class T, bool A_KMAJOR, bool B_KMAJOR, int IN, int OUT>
@@ -160,7 +177,6 @@ __global__ void __launch_bounds__(T::NT) grouped_kernel(GroupedArgs p)
     T tile;
     const int grid = gridDim.x;
     const int L = logical_block(blockIdx.x, grid, p.xcd_remap);
-    const uint16_t *A = (const uint16_t *)p.A;
     const uint16_t *B = (const uint16_t *)p.B;
     constexpr int esize = out_size(OUT);
     for (int t = L; t < total; t += grid) {
@@ -181,12 +197,12 @@ __global__ void __launch_bounds__(T::NT) grouped_kernel(GroupedArgs p)
         const int mb = local % tm, nb = local / tm;
         const int m0 = rows0 + mb * T::BM, n0 = nb * T::BN;
         const int m_valid = min(T::BM, rows_e - mb * T::BM);
-        const uint16_t *At = A + (int64_t)m0 * p.lda;
         const uint16_t *Be = B + (int64_t)e * p.stride_b;
         const uint16_t *Bt = B_KMAJOR ? Be + (int64_t)n0 * p.ldb : Be + n0;
-        const OperandSrc sa = operand_src<true>(At, p.lda, m_valid, p.K);
+        RowGather ga;
+        const OperandSrc sa = grouped_a_src(p, m0, m_valid, ga);
         const OperandSrc sb = operand_src<B_KMAJOR>(Bt, p.ldb, p.N - n0, p.K);
-        tile.mainloop(lds, sa, p.lda, sb, p.ldb, p.K, opaque((int)threadIdx.x));
+        tile.mainloop(lds, sa, p.lda, sb, p.ldb, p.K, opaque((int)threadIdx.x), ga);
         const int dcol0 = EPI == EPI_SILU_GATE ? n0 / 2 : n0;
         char *Dt = (char *)p.D + ((int64_t)m0 * p.ldd + dcol0) * esize;
         tile_epilogue<T, EPI, OUT>(tile, lds, Dt, p.ldd, m_valid, min(T::BN, p.N - n0), opaque((int)threadIdx.x));
@@ -286,7 +302,6 @@ __global__ void __launch_bounds__(T::NT) grouped_kernel_wt(GroupedArgs p)
     T tile;
     const int grid = gridDim.x;
     const int L = logical_block(blockIdx.x, grid, p.xcd_remap);
-    const uint16_t *A = (const uint16_t *)p.A;
     const uint16_t *B = (const uint16_t *)p.B;
     constexpr int esize = out_size(OUT);
     for (int t = L; t < wt.total; t += grid) {
@@ -296,12 +311,12 @@ __global__ void __launch_bounds__(T::NT) grouped_kernel_wt(GroupedArgs p)
         const int mb = local % tm, nb = local / tm;
         const int m0 = rows0 + mb * T::BM, n0 = nb * T::BN;
         const int m_valid = min(T::BM, rows_e - mb * T::BM);
-        const uint16_t *At = A + (int64_t)m0 * p.lda;
         const uint16_t *Be = B + (int64_t)e * p.stride_b;
         const uint16_t *Bt = B_KMAJOR ? Be + (int64_t)n0 * p.ldb : Be + n0;
-        const OperandSrc sa = operand_src<true>(At, p.lda, m_valid, p.K);
+        RowGather ga;
+        const OperandSrc sa = grouped_a_src(p, m0, m_valid, ga);
         const OperandSrc sb = operand_src<B_KMAJOR>(Bt, p.ldb, p.N - n0, p.K);
-        tile.mainloop(lds, sa, p.lda, sb, p.ldb, p.K, opaque((int)threadIdx.x));
+        tile.mainloop(lds, sa, p.lda, sb, p.ldb, p.K, opaque((int)threadIdx.x), ga);
         const int dcol0 = EPI == EPI_SILU_GATE ? n0 / 2 : n0;
         char *Dt = (char *)p.D + ((int64_t)m0 * p.ldd + dcol0) * esize;
         tile_epilogue<T, EPI, OUT>(tile, lds, Dt, p.ldd, m_valid, min(T::BN, p.N - n0), opaque((int)threadIdx.x));

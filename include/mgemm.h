@@ -214,6 +214,21 @@ int64_t mgemm_group_working_set(int32_t group_m, int32_t group_n, int32_t BM, in
  * to a multiple of 16 before sizing the MMA). */
 int64_t mgemm_round_tokens(int64_t n, int32_t granule);
 
+/* The grouped product with A's rows gathered (the MoE dispatch fused into the
+ * A loads; "MegaMoE：Blackwell 与 Hopper 的融合算子解读", Hopper section 11, a
+ * dispatch warp pulls the routed tokens' rows for the expert GEMM): routed
+ * row r of the product reads row d_row_index[r] of X, a row-major
+ * [x_rows][K] matrix with the plan's lda, instead of row r of a gathered A.
+ * d_row_index: device int32, one entry per routed row (off[num_groups]
+ * entries); an entry outside [0, x_rows) reads as a row of zeros.
+ * Everything else is grouped_gemm_run's.  x_rows * lda * 2 must be below
+ * 2^31 (else MGEMM_ERR_INVALID_ARG).  Only plans whose launches use the
+ * default 32x256 and direct-to-LDS 256x256 tiles take gathered rows (a plan
+ * forced onto another tile returns MGEMM_ERR_UNSUPPORTED). */
+mgemm_status_t grouped_gemm_run_gather(mgemm_plan_t plan, const void *X, int64_t x_rows, const void *B, void *D,
+                                       const int32_t *d_row_offsets, const int32_t *d_row_index, void *workspace,
+                                       size_t workspace_bytes, mgemm_stream_t stream);
+
 /* MoE combine: every token's output row is the routing-weighted sum of the
  * rows its top-k experts produced ("MegaMoE：Blackwell 与 Hopper 的融合算子解读",
  * Blackwell section 13: a separate top-k reduce reads each branch and adds
