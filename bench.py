@@ -161,6 +161,47 @@ def moe_case(torch, mg, datagen):
     return step, info, None
 
 
+def moe_layer_case(torch, mg, datagen):
+    """The whole 64-expert layer: FC1 reading the routed rows of X through
+    the routing's row index (the dispatch fused into its A loads), FC2, and
+    the weighted top-k combine into each token's output row."""
+    import numpy as np
+    cfg = datagen.MOE["moe64"]
+    r, A, W1, W2 = datagen.moe_inputs_device(cfg, "cuda")
+    rows = int(r.offsets[-1])
+    H, I, E, T = cfg.hidden, cfg.inter, cfg.num_experts, cfg.num_tokens
+    first = np.full(T, -1, dtype=np.int64)
+    first[r.token_of_row[::-1]] = np.arange(rows)[::-1]   # a routed row of each token
+    X = A[torch.from_numpy(first).cuda()].contiguous()    # the token rows the dispatch reads
+    del A
+    offs = torch.from_numpy(r.offsets).cuda()
+    idx = torch.from_numpy(r.token_of_row.astype(np.int32)).cuda()
+    pos = torch.from_numpy(r.pos).cuda()
+    wts = torch.from_numpy(r.weight).cuda()
+    h = torch.empty((rows, I), dtype=torch.bfloat16, device="cuda")
+    z = torch.empty((rows, H), dtype=torch.bfloat16, device="cuda")
+    y = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+    p1 = mg.grouped_gemm_plan(E, rows, 2 * I, H, stride_b=H * 2 * I, epilogue=mg.EPI_SILU_GATE_I8)
+    p2 = mg.grouped_gemm_plan(E, rows, H, I, stride_b=I * H)
+
+    def step():
+        mg.grouped_gemm_run_gather(p1, X, W1, h, offs, idx)
+        mg.grouped_gemm_run(p2, h, W2, z, offs)
+        mg.moe_combine(z, pos, wts, y, cfg.top_k)
+
+    flops = 2.0 * rows * (2 * I) * H + 2.0 * rows * H * I
+    active = int((r.counts > 0).sum())
+    wbytes = active * (H * 2 * I + I * H) * 2
+    abytes = T * H * 2 + rows * I * 2 * 2 + rows * H * 2 * 2 + T * H * 2
+    info = dict(flops=flops, bytes=wbytes + abytes, plan=p1.describe() + " | " + p2.describe() + " | combine",
+                dtype="bf16",
+                config={"workload": "moe64_layer", "experts": E, "hidden": H, "inter": I, "tokens": T,
+                        "top_k": cfg.top_k, "routed_rows": rows, "active_experts": active,
+                        "stages": "gathered FC1 (SiLU gate) + FC2 + weighted top-k combine"},
+                launches_per_step=len(p1.describe().split("grid=")) - 1 + len(p2.describe().split("grid=")) - 1 + 1)
+    return step, info, None
+
+
 def cpu_baseline(case, target_s):
     """The oracle, as it stands, on the first R rows of the same product."""
     import numpy as np
@@ -207,6 +248,8 @@ def main():
 
     if args.workload == "moe64":
         step, info, case = moe_case(torch, mg, datagen)
+    elif args.workload == "moe64_layer":
+        step, info, case = moe_layer_case(torch, mg, datagen)
     else:
         step, info, case = dense_case(torch, mg, datagen, args.workload)
     print(f"# plan: {info['plan']}", file=sys.stderr, flush=True)
