@@ -69,6 +69,22 @@ def test_combine_against_oracle(dtype, variant):
         assert np.all(err <= bound(Zb, pos, w, dtype, ref)), f"max err {err.max():.3e}"
 
 
+def test_combine_strided_rows():
+    """Z rows longer than H (ldz = H + 24, the slack NaN): integer data, bit-exact."""
+    T, top_k, H, rows = 40, 4, 128, 90
+    rs = np.random.RandomState(13)
+    Zb = datagen.matrix((rows, H), ("int", 3), "bf16", rs)
+    Zw = np.full((rows, H + 24), 0x7FC1, dtype=np.uint16)
+    Zw[:, :H] = Zb
+    pos = rs.randint(0, rows, size=(T, top_k)).astype(np.int32)
+    w = (rs.randint(-4, 5, size=(T, top_k)) / 2.0).astype(np.float32)
+    Z = to_dev(Zw, "bf16")[:, :H]
+    Y = torch.empty(T, H, dtype=torch.bfloat16, device="cuda")
+    mg.moe_combine(Z, torch.from_numpy(pos).cuda(), torch.from_numpy(w).cuda(), Y, top_k)
+    torch.cuda.synchronize()
+    assert_bits_equal(from_dev_bits(Y), oracle.moe_combine_ref(Zb, pos, w.astype(np.float64)), "bf16", "strided Z")
+
+
 def test_combine_moe64_routing_sampled_tokens():
     """The 64-expert layer's routing (4096 tokens, top 8, hidden 7168) on
     routed rows of random data; 64 tokens checked against the oracle."""

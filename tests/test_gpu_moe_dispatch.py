@@ -73,6 +73,33 @@ def test_gather_against_oracle(tile, epi, variant):
         assert np.all(err <= tol), f"{plan.describe()}: max err {err.max():.3e}"
 
 
+@pytest.mark.parametrize("tile", ["auto", "256d"])
+def test_gather_column_major_weights_and_wide_lda(tile):
+    """Column-major expert weights ([N][K] per expert) and an X whose rows are
+    longer than K (lda = K + 40, the slack NaN): integer data, bit-exact."""
+    flags = {"auto": 0, "256d": mg.PLAN_FORCE_TILE_256x256_DTL}[tile]
+    counts = [3, 0, 140, 257, 60]
+    N, K, T = 256, 200, 300
+    log(f"case gather col-major weights tile={tile}")
+    rs = np.random.RandomState(31)
+    off = offsets(counts)
+    rows = int(off[-1])
+    idx = rs.randint(0, T, size=rows).astype(np.int32)
+    X = datagen.matrix((T, K), ("int", 2), "bf16", rs)
+    Wr = datagen.matrix((len(counts), K, N), ("int", 2), "bf16", rs)
+    Wc = np.ascontiguousarray(Wr.transpose(0, 2, 1))
+    lda = K + 40
+    Xw = np.full((T, lda), 0x7FC1, dtype=np.uint16)
+    Xw[:, :K] = X
+    D = torch.empty(rows, N, dtype=torch.bfloat16, device="cuda")
+    plan = mg.grouped_gemm_plan(len(counts), rows, N, K, b_layout="col", lda=lda, ldb=K, stride_b=N * K,
+                                flags=flags)
+    mg.grouped_gemm_run_gather(plan, to_dev(Xw, "bf16"), to_dev(Wc, "bf16"), D, dev_i32(off), dev_i32(idx))
+    torch.cuda.synchronize()
+    ref = oracle.grouped_ref(X[idx], Wc, off, w_layout="col")
+    assert_bits_equal(from_dev_bits(D), ref, "bf16", plan.describe())
+
+
 def test_gather_equals_pregathered_moe64():
     """The 64-expert layer's FC1 with the routing's row index gives exactly the
     bits of the same product on rows gathered beforehand."""
