@@ -135,6 +135,15 @@ def matrix(shape, dist, dtype: str, rs: np.random.RandomState) -> np.ndarray:
     return _to_bits(draw(rs, shape, dist), dtype)
 
 
+def matrix_e4m3(shape, dist, rs: np.random.RandomState) -> np.ndarray:
+    """uint8 E4M3 codes of float32 draws (RNE and saturation by torch's
+    float8_e4m3fn cast; draws beyond +-448 are clipped first)."""
+    import torch
+    x = np.clip(draw(rs, shape, dist), -448.0, 448.0)
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.float8_e4m3fn)
+    return t.view(torch.uint8).numpy().copy()
+
+
 def gemm_inputs(cfg: GemmConfig, variant: str = "random", M: Optional[int] = None,
                 N: Optional[int] = None, K: Optional[int] = None):
     """(A_storage, B_storage) uint16 bit arrays for a dense workload.

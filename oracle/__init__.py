@@ -18,6 +18,10 @@ and from which passage of the pages:
 * ``silu_gate`` -- up x SiLU(gate) (same page, section 七, "Gate／SwiGLU"),
   with gate/up interleaved in blocks of eight output columns, gate first
   ("MegaMoE：Blackwell 与 Hopper 的融合算子解读", Hopper section 10).
+* ``decode_e4m3`` / ``gemm_e4m3_ref`` -- the FP8 form with one scale per
+  tensor ("MegaMoE", Hopper section 04: per-tensor scales are applied once,
+  in the epilogue): scale_a x scale_b x the ascending-k double sum of the
+  decoded E4M3 products (E4M3 bits from the OCP 8-bit float layout).
 * ``grouped_ref`` / ``moe_ref`` -- the per-expert form: expert e owns rows
   [off[e], off[e+1]) of the routed activations and multiplies them by its
   own weight matrix ("MegaMoE", Recap 1 on the MoE stages: FC1 -> activation
@@ -76,6 +80,13 @@ def _load():
     lib.oracle_silu.restype = ctypes.c_double
     lib.oracle_silu_gate.argtypes = [i64, i64, i64, dp, dp]
     lib.oracle_num_threads.restype = i32
+    lib.oracle_e4m3_to_double.argtypes = [ctypes.c_uint8]
+    lib.oracle_e4m3_to_double.restype = ctypes.c_double
+    lib.oracle_decode_e4m3.argtypes = [vp, i64, dp]
+    lib.oracle_gemm_e4m3_ref.argtypes = [i64, i64, i64, vp, i64, vp, i64, ctypes.c_double, ctypes.c_double, dp]
+    lib.oracle_gemm_e4m3_ref.restype = i32
+    lib.oracle_gemm_e4m3_ref_sampled.argtypes = [i64, vp, i64, vp, i64, ctypes.c_double, ctypes.c_double,
+                                                 vp, vp, i64, dp]
     _lib = lib
     return lib
 
@@ -236,3 +247,51 @@ def moe_combine_ref(Z: np.ndarray, pos, weights, dtype: str = "bf16") -> np.ndar
         y[ok] += w[ok, k][:, None] * z[p[ok]]
     return y
 
+
+
+def _check_u8(x: np.ndarray, name: str):
+    if x.dtype != np.uint8 or x.ndim != 2:
+        raise TypeError(f"{name} must be a 2-D uint8 bit array, got {x.dtype} {x.shape}")
+
+
+def decode_e4m3(bits: np.ndarray) -> np.ndarray:
+    """Exact values (float64) of E4M3 bit patterns (NaN for 0x7F / 0xFF)."""
+    b = np.ascontiguousarray(bits, dtype=np.uint8)
+    out = np.empty(b.shape, dtype=np.float64)
+    _load().oracle_decode_e4m3(_p(b), b.size, _p(out))
+    return out
+
+
+def gemm_e4m3_ref(A: np.ndarray, B: np.ndarray, scale_a: float = 1.0, scale_b: float = 1.0) -> np.ndarray:
+    """Unrounded fp64 scale_a * scale_b * (A x B) of E4M3 operands.
+
+    ``A``: [M][K] uint8 (k contiguous); ``B``: [N][K] uint8, the K x N
+    operand stored column-major (k contiguous).  Returns M x N float64.
+    """
+    _check_u8(A, "A")
+    _check_u8(B, "B")
+    A = np.ascontiguousarray(A)
+    B = np.ascontiguousarray(B)
+    (M, K), (N, K2) = A.shape, B.shape
+    if K2 != K:
+        raise ValueError(f"inner dimensions differ: {K} vs {K2}")
+    ref = np.empty((M, N), dtype=np.float64)
+    rc = _load().oracle_gemm_e4m3_ref(M, N, K, _p(A), K, _p(B), K, float(scale_a), float(scale_b), _p(ref))
+    if rc != 0:
+        raise MemoryError("oracle_gemm_e4m3_ref could not allocate its temporaries")
+    return ref
+
+
+def gemm_e4m3_ref_sampled(A: np.ndarray, B: np.ndarray, rows, cols, scale_a: float = 1.0,
+                          scale_b: float = 1.0) -> np.ndarray:
+    """``gemm_e4m3_ref`` at the elements (rows[t], cols[t]) only."""
+    _check_u8(A, "A")
+    _check_u8(B, "B")
+    A = np.ascontiguousarray(A)
+    B = np.ascontiguousarray(B)
+    r = np.ascontiguousarray(rows, dtype=np.int64)
+    c = np.ascontiguousarray(cols, dtype=np.int64)
+    out = np.empty(r.shape, dtype=np.float64)
+    _load().oracle_gemm_e4m3_ref_sampled(A.shape[1], _p(A), A.shape[1], _p(B), B.shape[1], float(scale_a),
+                                         float(scale_b), _p(r), _p(c), r.size, _p(out))
+    return out

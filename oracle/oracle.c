@@ -304,3 +304,89 @@ int oracle_num_threads(void)
     }
     return n;
 }
+
+/* ------------------------------------------------------------------ */
+/* FP8 (E4M3) GEMM with per-tensor scales                              */
+/* ------------------------------------------------------------------ */
+
+/*
+ * The 8-bit input format, written out from the OCP 8-bit floating point
+ * specification's E4M3 layout (the pages use FP8 without defining its bits):
+ * 1 sign, 4 exponent bits with bias 7, 3 fraction bits; exponent field 0 is
+ * subnormal (fraction x 2^-9); there are no infinities, and only the two
+ * codes with every exponent and fraction bit set are NaN, so the largest
+ * finite magnitude is 1.75 x 2^8 = 448.
+ */
+double oracle_e4m3_to_double(uint8_t v)
+{
+    const int s = v >> 7, e = (v >> 3) & 15, f = v & 7;
+    double mag;
+    if (e == 15 && f == 7)
+        return NAN;
+    if (e == 0)
+        mag = ldexp((double)f, -9);
+    else
+        mag = ldexp(1.0 + f / 8.0, e - 7);
+    return s ? -mag : mag;
+}
+
+void oracle_decode_e4m3(const uint8_t *src, int64_t n, double *dst)
+{
+    for (int64_t i = 0; i < n; ++i)
+        dst[i] = oracle_e4m3_to_double(src[i]);
+}
+
+/*
+ * Per-tensor FP8 product ("MegaMoE：Blackwell 与 Hopper 的融合算子解读",
+ * Hopper section 04 on FP8 quantisation: with one scale per tensor the
+ * dequantisation happens once, in the epilogue): ref[i][j] = scale_a x
+ * scale_b x sum_k a(i,k) b(k,j).  A is stored [M][lda] (row i holds k
+ * contiguously), B is stored [N][ldb] (column j of the K x N operand holds k
+ * contiguously).  The sum is the same ascending-k double sum as
+ * oracle_gemm_ref (products of two E4M3 values are exact in double); the
+ * scales multiply the finished sum, scale_a first.
+ */
+int oracle_gemm_e4m3_ref(int64_t M, int64_t N, int64_t K, const uint8_t *A, int64_t lda, const uint8_t *B,
+                         int64_t ldb, double scale_a, double scale_b, double *ref)
+{
+    double *a = (double *)malloc(sizeof(double) * (size_t)(M * K > 0 ? M * K : 1));
+    double *b = (double *)malloc(sizeof(double) * (size_t)(N * K > 0 ? N * K : 1));
+    if (!a || !b) {
+        free(a);
+        free(b);
+        return -1;
+    }
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < M; ++i)
+        for (int64_t k = 0; k < K; ++k)
+            a[i * K + k] = oracle_e4m3_to_double(A[i * lda + k]);
+#pragma omp parallel for schedule(static)
+    for (int64_t j = 0; j < N; ++j)
+        for (int64_t k = 0; k < K; ++k)
+            b[j * K + k] = oracle_e4m3_to_double(B[j * ldb + k]);
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t i = 0; i < M; ++i)
+        for (int64_t j = 0; j < N; ++j) {
+            double acc = 0.0;
+            for (int64_t k = 0; k < K; ++k)
+                acc += a[i * K + k] * b[j * K + k];
+            ref[i * N + j] = scale_a * scale_b * acc;
+        }
+    free(a);
+    free(b);
+    return 0;
+}
+
+/* The same value at the elements (rows[t], cols[t]) only. */
+void oracle_gemm_e4m3_ref_sampled(int64_t K, const uint8_t *A, int64_t lda, const uint8_t *B, int64_t ldb,
+                                  double scale_a, double scale_b, const int64_t *rows, const int64_t *cols,
+                                  int64_t n, double *out)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < n; ++t) {
+        double acc = 0.0;
+        for (int64_t k = 0; k < K; ++k)
+            acc += oracle_e4m3_to_double(A[rows[t] * lda + k]) * oracle_e4m3_to_double(B[cols[t] * ldb + k]);
+        out[t] = scale_a * scale_b * acc;
+    }
+}

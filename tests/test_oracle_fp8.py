@@ -1,0 +1,97 @@
+"""CPU pins of the FP8 (E4M3) oracle: the decoder against the format's own
+constants and against torch's float8_e4m3fn conversion over all 256 codes,
+the per-tensor-scaled product against exact rational brute force, and the
+identities a transposed operand pair and the scales must satisfy."""
+import math
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import datagen
+import oracle
+
+torch = pytest.importorskip("torch")
+
+
+def test_decode_format_constants():
+    """Values fixed by the E4M3 layout (bias 7, 3 fraction bits, subnormals
+    below exponent field 1, no infinities, NaN only at S.1111.111)."""
+    want = {0x00: 0.0, 0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9, 0x08: 2.0 ** -6, 0x30: 0.5, 0x38: 1.0,
+            0x3C: 1.5, 0x40: 2.0, 0x44: 3.0, 0x4F: 7.5, 0x57: 15.0, 0x77: 240.0, 0x78: 256.0, 0x7E: 448.0,
+            0xB8: -1.0, 0xFE: -448.0}
+    got = oracle.decode_e4m3(np.array(list(want), dtype=np.uint8))
+    assert got.tolist() == list(want.values())
+    assert math.copysign(1.0, oracle.decode_e4m3(np.array([0x80], dtype=np.uint8))[0]) == -1.0
+    assert np.isnan(oracle.decode_e4m3(np.array([0x7F, 0xFF], dtype=np.uint8))).all()
+    assert np.isfinite(oracle.decode_e4m3(np.array([0x7E, 0xF8, 0x7D], dtype=np.uint8))).all()
+
+
+def test_decode_all_codes_match_torch():
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = oracle.decode_e4m3(codes)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+
+
+def finite_codes(shape, rs):
+    c = rs.randint(0, 256, size=shape).astype(np.uint8)
+    c[(c & 0x7F) == 0x7F] = 0x38
+    return c
+
+
+def test_product_against_rational_brute_force():
+    rs = np.random.RandomState(5)
+    M, N, K = 5, 4, 37
+    A, B = finite_codes((M, K), rs), finite_codes((N, K), rs)
+    sa, sb = 0.375, 1.0 / 1024
+    val = lambda c: Fraction(torch.tensor([int(c)], dtype=torch.uint8).view(torch.float8_e4m3fn)
+                             .to(torch.float64).item())
+    got = oracle.gemm_e4m3_ref(A, B, sa, sb)
+    for i in range(M):
+        for j in range(N):
+            exact = Fraction(sa) * Fraction(sb) * sum(val(A[i, k]) * val(B[j, k]) for k in range(K))
+            # the double sum of at most 37 products of 4-bit significands is exact
+            assert Fraction(got[i, j]) == exact, (i, j)
+
+
+def test_transpose_and_scale_identities():
+    rs = np.random.RandomState(9)
+    A, B = finite_codes((24, 50), rs), finite_codes((17, 50), rs)
+    base = oracle.gemm_e4m3_ref(A, B)
+    assert np.array_equal(oracle.gemm_e4m3_ref(B, A), base.T)
+    assert np.array_equal(oracle.gemm_e4m3_ref(A, B, 4.0, 0.125), base * 0.5)
+    # a code's sign bit flips the sign of its row of the product
+    An = A.copy()
+    An[3] ^= 0x80
+    neg = oracle.gemm_e4m3_ref(An, B)
+    assert np.array_equal(neg[3], -base[3]) and np.array_equal(np.delete(neg, 3, 0), np.delete(base, 3, 0))
+
+
+def test_special_case_identity_and_sampled():
+    """One code per row of A at position i (the rest zero) picks row i of B:
+    A x B = diag(values) selection; the sampled form agrees with the full one."""
+    rs = np.random.RandomState(2)
+    K = 16
+    A = np.zeros((K, K), dtype=np.uint8)
+    A[np.arange(K), np.arange(K)] = 0x38  # 1.0
+    B = finite_codes((7, K), rs)
+    got = oracle.gemm_e4m3_ref(A, B)
+    assert np.array_equal(got, oracle.decode_e4m3(B).T)
+    A2, B2 = finite_codes((33, 70), rs), finite_codes((29, 70), rs)
+    full = oracle.gemm_e4m3_ref(A2, B2, 2.0, 3.0)
+    r, c = rs.randint(0, 33, 40), rs.randint(0, 29, 40)
+    assert np.array_equal(oracle.gemm_e4m3_ref_sampled(A2, B2, r, c, 2.0, 3.0), full[r, c])
+
+
+def test_datagen_codes_are_finite_and_round_to_nearest():
+    rs = np.random.RandomState(1)
+    c = datagen.matrix_e4m3((64, 64), ("normal", 100.0), rs)
+    v = oracle.decode_e4m3(c)
+    assert np.isfinite(v).all() and np.abs(v).max() <= 448.0
+    ci = datagen.matrix_e4m3((8, 8), ("int", 3), np.random.RandomState(2))
+    vi = oracle.decode_e4m3(ci)
+    assert np.array_equal(vi, np.round(vi)) and np.abs(vi).max() <= 3
