@@ -29,7 +29,9 @@ sys.path.insert(0, ROOT)
 
 # MI355X dense MFMA peak for 16-bit inputs: 256 CUs x 2.4 GHz x 4096 FLOP per
 # clock per CU = 2516.6 TFLOP/s (AMD's "2.5 PFLOP/s" dense bf16/fp16 figure).
-PEAK_TFLOPS = {"bf16": 256 * 2.4e9 * 4096 / 1e12, "f16": 256 * 2.4e9 * 4096 / 1e12}
+PEAK_TFLOPS = {"bf16": 256 * 2.4e9 * 4096 / 1e12, "f16": 256 * 2.4e9 * 4096 / 1e12,
+               # E4M3 inputs: twice the FLOP per clock (AMD's "5.0 PFLOP/s" dense fp8 figure)
+               "e4m3": 256 * 2.4e9 * 8192 / 1e12}
 HBM_GBPS = 8000.0
 METRIC = "GEMM TFLOPS and % of MI355X bf16 dense peak at 4096^3/8192^3 (1 GPU)"
 DEFAULT_WORKLOAD = "gemm8192_bf16_bcol"
@@ -202,6 +204,51 @@ def moe_layer_case(torch, mg, datagen):
     return step, info, None
 
 
+# E4M3 workloads: per-tensor scales, B column-major, bf16 out
+E4M3 = {"gemm8192_e4m3": (8192, 8192, 8192)}
+
+
+def e4m3_case(torch, mg, datagen, name):
+    import numpy as np
+    M, N, K = E4M3[name]
+    rs = np.random.RandomState(8192)
+    # normal(0, 100) codes: a per-tensor-quantised tensor whose largest
+    # magnitudes (4.5 sigma) reach the format's 448; the scales undo the 100
+    a = datagen.matrix_e4m3((M, K), ("normal", 100.0), rs)
+    b = datagen.matrix_e4m3((N, K), ("normal", 100.0), rs)
+    A, B = torch.from_numpy(a).cuda(), torch.from_numpy(b).cuda()
+    sa = torch.tensor([0.01], dtype=torch.float32, device="cuda")
+    sb = torch.tensor([0.01], dtype=torch.float32, device="cuda")
+    D = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    plan = mg.gemm_plan(M, N, K, "e4m3", d_type="bf16", a_layout="row", b_layout="col")
+
+    def step():
+        mg.gemm_run_scaled(plan, A, B, D, sa, sb)
+
+    info = dict(flops=2.0 * M * N * K, bytes=M * K + N * K + 2 * M * N, plan=plan.describe(), dtype="e4m3",
+                config={"workload": name, "M": M, "N": N, "K": K, "in": "e4m3", "out": "bf16",
+                        "a_layout": "row", "b_layout": "col", "scales": "per-tensor"},
+                launches_per_step=1)
+    return step, info, ("e4m3", M, N, K, a, b)
+
+
+def cpu_baseline_e4m3(case, target_s):
+    import oracle
+    _, M, N, K, a, b = case
+
+    def timed(R):
+        t0 = time.perf_counter()
+        oracle.gemm_e4m3_ref(a[:R], b, 0.01, 0.01)
+        return time.perf_counter() - t0
+    r1, r2 = 4, 36
+    t1, t2 = timed(r1), timed(r2)
+    per_row = max((t2 - t1) / (r2 - r1), 1e-6)
+    R2 = int(min(M, max(r2, (target_s - max(t1 - r1 * per_row, 0.0)) / per_row)))
+    t = timed(R2)
+    return {"value": 2.0 * R2 * N * K / t / 1e12, "unit": "TFLOPS", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"first {R2} of {M} output rows (all {N} columns, full K={K}), {t:.1f} s incl. operand decode"}
+
+
 def cpu_baseline(case, target_s):
     """The oracle, as it stands, on the first R rows of the same product."""
     import numpy as np
@@ -209,6 +256,8 @@ def cpu_baseline(case, target_s):
     import oracle
     if case is None:
         return None
+    if case[0] == "e4m3":
+        return cpu_baseline_e4m3(case, target_s)
     cfg, a, b = case
     a_rows = (lambda R: a[:R]) if cfg.a_layout == "row" else (lambda R: np.ascontiguousarray(a[:, :R]))
     # two calibration runs give the fixed cost (decoding B) and the per-row
@@ -250,6 +299,8 @@ def main():
         step, info, case = moe_case(torch, mg, datagen)
     elif args.workload == "moe64_layer":
         step, info, case = moe_layer_case(torch, mg, datagen)
+    elif args.workload in E4M3:
+        step, info, case = e4m3_case(torch, mg, datagen, args.workload)
     else:
         step, info, case = dense_case(torch, mg, datagen, args.workload)
     print(f"# plan: {info['plan']}", file=sys.stderr, flush=True)

@@ -33,7 +33,8 @@ def PLAN_SPLIT_K(n: int) -> int:
     """Plan flag fixing the number of K ranges per output tile (1 = no split)."""
     return (int(n) & 0xFF) << 16
 
-DTYPE = {"f16": F16, "bf16": BF16, "f32": F32}
+E4M3 = 4
+DTYPE = {"f16": F16, "bf16": BF16, "f32": F32, "e4m3": E4M3}
 TORCH_DTYPE = {torch.float16: F16, torch.bfloat16: BF16, torch.float32: F32}
 LAYOUT = {"row": ROW_MAJOR, "col": COL_MAJOR}
 
@@ -69,7 +70,8 @@ class Budget(ctypes.Structure):
 
 
 #: every symbol include/mgemm.h declares
-EXPORTS = ["gemm_plan", "grouped_gemm_plan", "gemm_plan_workspace_size", "gemm_run", "grouped_gemm_run",
+EXPORTS = ["gemm_plan", "grouped_gemm_plan", "gemm_plan_workspace_size", "gemm_run", "gemm_run_scaled",
+           "grouped_gemm_run",
            "gemm_plan_describe", "gemm_plan_info", "gemm_plan_destroy", "gemm_status_string",
            "gemm_last_error_message", "mgemm_tile_budget", "mgemm_group_working_set", "mgemm_round_tokens",
            "mgemm_version", "mgemm_moe_combine", "grouped_gemm_run_gather"]
@@ -89,6 +91,8 @@ def _load():
     lib.gemm_plan_workspace_size.restype = st
     lib.gemm_run.argtypes = [vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.gemm_run.restype = st
+    lib.gemm_run_scaled.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.gemm_run_scaled.restype = st
     lib.grouped_gemm_run.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.grouped_gemm_run.restype = st
     lib.gemm_plan_describe.argtypes = [vp, ctypes.c_char_p, ctypes.c_size_t]
@@ -225,6 +229,15 @@ def gemm_run(plan: Plan, A, B, D, workspace=None, workspace_bytes: int = 0, stre
         workspace = workspace_for(plan, D.device)
     _check(lib.gemm_run(plan.handle, _ptr(A), _ptr(B), _ptr(D), _ptr(workspace), _nbytes(workspace, workspace_bytes),
                         _stream(stream)), "gemm_run")
+
+
+def gemm_run_scaled(plan: Plan, A, B, D, scale_a, scale_b, stream=None):
+    """Enqueue D = scale_a * scale_b * (A x B) for a plan with E4M3 inputs;
+    ``scale_a`` / ``scale_b``: device float32 tensors of one element (read by
+    the kernel when it runs).  A, B: uint8 (or float8_e4m3fn) device tensors
+    holding the E4M3 codes."""
+    _check(lib.gemm_run_scaled(plan.handle, _ptr(A), _ptr(B), _ptr(D), _ptr(scale_a), _ptr(scale_b), None, 0,
+                               _stream(stream)), "gemm_run_scaled")
 
 
 def grouped_gemm_run(plan: Plan, A, B, D, row_offsets, workspace=None, workspace_bytes: int = 0, stream=None):

@@ -41,13 +41,9 @@ static mgemm_status_t hip_status(hipError_t e, const char *what)
 
 using namespace mgemm;
 
-extern "C" mgemm_status_t gemm_run(mgemm_plan_t plan, const void *A, const void *B, void *D, void *workspace,
-                                   size_t workspace_bytes, mgemm_stream_t stream)
+static mgemm_status_t dense_run(mgemm_plan_t plan, const void *A, const void *B, void *D, const float *scale_a,
+                                const float *scale_b, void *workspace, size_t workspace_bytes, mgemm_stream_t stream)
 {
-    if (!plan || plan->kind != PLAN_DENSE) {
-        set_error("gemm_run: null or non-dense plan");
-        return MGEMM_ERR_INVALID_ARG;
-    }
     const mgemm_desc_t &d = plan->dense;
     if (plan->noop)
         return MGEMM_OK;
@@ -91,6 +87,8 @@ extern "C" mgemm_status_t gemm_run(mgemm_plan_t plan, const void *A, const void 
     a.splits = 1;
     a.kchunk = (int)d.K;
     a.split_stride = 0;
+    a.scale_a = scale_a;
+    a.scale_b = scale_b;
     if (split) {
         // every K range writes its fp32 partial tile into its own slab of
         // the workspace; the reduction adds the slabs into D
@@ -132,6 +130,35 @@ extern "C" mgemm_status_t gemm_run(mgemm_plan_t plan, const void *A, const void 
         return hip_status(ef(e, ak ? 1 : 0, bk ? 1 : 0, a.N, s), "gemm_run edge launch");
     }
     return MGEMM_OK;
+}
+
+extern "C" mgemm_status_t gemm_run(mgemm_plan_t plan, const void *A, const void *B, void *D, void *workspace,
+                                   size_t workspace_bytes, mgemm_stream_t stream)
+{
+    if (!plan || plan->kind != PLAN_DENSE) {
+        set_error("gemm_run: null or non-dense plan");
+        return MGEMM_ERR_INVALID_ARG;
+    }
+    return dense_run(plan, A, B, D, nullptr, nullptr, workspace, workspace_bytes, stream);
+}
+
+extern "C" mgemm_status_t gemm_run_scaled(mgemm_plan_t plan, const void *A, const void *B, void *D,
+                                          const float *d_scale_a, const float *d_scale_b, void *workspace,
+                                          size_t workspace_bytes, mgemm_stream_t stream)
+{
+    if (!plan || plan->kind != PLAN_DENSE) {
+        set_error("gemm_run_scaled: null or non-dense plan");
+        return MGEMM_ERR_INVALID_ARG;
+    }
+    if (plan->dense.a_type != MGEMM_E4M3) {
+        set_error("gemm_run_scaled: the plan's inputs are not E4M3");
+        return MGEMM_ERR_UNSUPPORTED;
+    }
+    if (!d_scale_a || !d_scale_b || ((uintptr_t)d_scale_a & 3) || ((uintptr_t)d_scale_b & 3)) {
+        set_error("gemm_run_scaled: scale pointers must be non-null and 4-byte aligned");
+        return MGEMM_ERR_INVALID_ARG;
+    }
+    return dense_run(plan, A, B, D, d_scale_a, d_scale_b, workspace, workspace_bytes, stream);
 }
 
 // row_index: nullptr, or the gathered form's index (x_rows rows of A exist).

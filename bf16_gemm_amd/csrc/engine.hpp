@@ -45,6 +45,7 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x8_t __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
@@ -53,7 +54,7 @@ constexpr int kRowBytes = kBK * 2;      // bytes of one tile row in LDS
 constexpr uint32_t kOOB = 0x80000000u;  // a buffer offset past every range
 constexpr uint32_t kMaxRecords = 0x7ffffff0u;
 
-enum InType { IN_BF16 = 0, IN_F16 = 1 };
+enum InType { IN_BF16 = 0, IN_F16 = 1, IN_E4M3 = 2 };
 enum OutType { OUT_F32 = 0, OUT_BF16 = 1, OUT_F16 = 2 };
 enum EpiKind { EPI_NONE = 0, EPI_SILU_GATE = 1 };
 
@@ -1298,6 +1299,244 @@ struct DtlTile4 {
     }
 };
 
+// acc += a . b over 128 k of E4M3 (OCP FP8, 1-4-3) on the matrix cores,
+// accumulator in AGPRs (same reasons as mfma16_agpr).  Operand lanes: lane l
+// holds row (l mod 16) and 32 of the 128 k; the same (lane, byte) -> k
+// assignment holds for both operands, so any one permutation of the 128 k
+// applied to both gives the same sum.
+__device__ __forceinline__ void mfma16_e4m3_agpr(f32x4_t &c, const u32x8_t &a, const u32x8_t &b)
+{
+    asm volatile("v_mfma_f32_16x16x128_f8f6f4 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+}
+
+// The four-wave 256 x 256 direct-to-LDS tile for E4M3 inputs, A and B both
+// k-contiguous ([M][K] and [N][K]).  A K step is 128 elements = 128 bytes of
+// each tile row, so the rings, the global-side swizzle, the load
+// assignment and the barrier placement are the 16-bit tile's (DtlTile4 with
+// a column-major B: B on the 3-slot ring, A on the 2-slot one).  What
+// differs is the MFMA: v_mfma_f32_16x16x128_f8f6f4 takes a whole step's
+// 128 k per block at once (32 bytes per lane: the lane's chunk q and chunk
+// q + 4 of the row, in both operands), so a step is one pass of 64 MFMAs
+// instead of two 32-k sub-steps.  The wave's fragments are four sets of
+// four blocks (A rows 0-63 / 64-127, B rows 0-63 / 64-127: Al, Ah, Bl, Bh;
+// 128 VGPRs in all, no second copy), and the step is four quarters, each
+// one set pair:
+//   even steps: Al.Bl, Al.Bh | barrier | Ah.Bh, Ah.Bl
+//   odd steps:  Al.Bh, Al.Bl | barrier | Ah.Bl, Ah.Bh
+// Each quarter reads, two halves per block, the set that the order leaves
+// free next: even steps read Bh and Ah of this step, then Al and Bh of the
+// next; odd steps Bl and Ah of this step, then Al and Bl of the next.  The
+// reads of a step end before its barrier and those of the next start after
+// it, as in the 16-bit tile, and every set is read a whole quarter before
+// the quarter that uses it; a quarter that uses a set read in the quarter
+// just before it runs through that set's blocks in the order they arrived.
+// Loads: the deep operand's step kt+2 four per quarter in the first half,
+// the shallow operand's step kt+2 four per quarter in the second.
+struct DtlTile4E4M3 {
+    using Base = DtlTile<IN_BF16, true>;
+    static constexpr int BM = 256, BN = 256, WM = 2, WN = 2;
+    static constexpr int MI = 16;
+    static constexpr int NT = 64 * WM * WN;
+    static constexpr int TM = BM / WM, TN = BN / WN, FM = TM / 16, FN = TN / 16;
+    static constexpr int KSTEP = kRowBytes;  // E4M3 elements per K step
+    static constexpr int OPS = Base::OPS;
+    static constexpr int A_SLOTS = Base::A_SLOTS, B_SLOTS = Base::B_SLOTS;
+    static_assert(A_SLOTS == 2 && B_SLOTS == 3, "B is the deep operand");
+    static constexpr int LDS_BYTES = Base::LDS_BYTES;
+    static constexpr int LOADS = 256 / 8 / (NT / 64);
+    static_assert(FM == 8 && FN == 8 && LOADS == 8, "the quarter rotation assumes 8 x 8 blocks per wave");
+    struct F8 {
+        u32x8_t v[4];
+    };
+
+    f32x4_t acc[FM][FN];
+    uint32_t va[LOADS], vb[LOADS];
+    int kc[LOADS];
+    int abase[2], bbase[2];
+    uint32_t a_sh[2][2];  // LDS addresses of the A fragment halves, per A slot
+
+    __device__ __forceinline__ void setup(int lane, int wave, int wm0, int wn0, int lda, int ldb)
+    {
+        const int r8 = lane >> 3;
+#pragma unroll
+        for (int j = 0; j < LOADS; ++j) {
+            const int row = (wave * LOADS + j) * 8 + r8;
+            const int c = (lane & 7) ^ Base::dswz(row);
+            kc[j] = c * 16;
+            va[j] = (uint32_t)row * (uint32_t)lda + (uint32_t)c * 16u;
+            vb[j] = (uint32_t)row * (uint32_t)ldb + (uint32_t)c * 16u;
+        }
+        const int r = lane & 15, q = lane >> 4;
+        const int c0 = q ^ Base::dswz(r);
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            abase[s] = (wm0 + r) * kRowBytes + ((c0 ^ (4 * s)) << 4);
+            bbase[s] = (wn0 + r) * kRowBytes + ((c0 ^ (4 * s)) << 4);
+        }
+    }
+    template <bool MASK>
+    __device__ __forceinline__ void load_a(__amdgpu_buffer_rsrc_t r, char *slot, int wave, int j, int k_left) const
+    {
+        const uint32_t off = !MASK || kc[j] < k_left ? va[j] : kOOB;
+        load_to_lds16(r, lds_addr(slot + (wave * LOADS + j) * 1024), off);
+    }
+    template <bool MASK>
+    __device__ __forceinline__ void load_b(__amdgpu_buffer_rsrc_t r, char *slot, int wave, int j, int k_left) const
+    {
+        const uint32_t off = !MASK || kc[j] < k_left ? vb[j] : kOOB;
+        load_to_lds16(r, lds_addr(slot + (wave * LOADS + j) * 1024), off);
+    }
+    // half h of block 4 H + b of A (from A slot Q, an LDS address held in a
+    // register plus an immediate) or of B (through the slot pointer)
+    template <int Q, int H>
+    __device__ __forceinline__ void rd_a(F8 &f, int i) const
+    {
+        typedef __attribute__((address_space(3))) u32x4_t lds_u32x4;
+        const int b = i >> 1, h = i & 1;
+        const u32x4_t v = *(const lds_u32x4 *)(uintptr_t)(a_sh[Q][h] + (4 * H + b) * 16 * kRowBytes);
+        if (h == 0)
+            f.v[b].lo = v;
+        else
+            f.v[b].hi = v;
+    }
+    template <int H>
+    __device__ __forceinline__ void rd_b(const char *bs, F8 &f, int i) const
+    {
+        const int b = i >> 1, h = i & 1;
+        const u32x4_t v = *(const u32x4_t *)(bs + bbase[h] + (4 * H + b) * 16 * kRowBytes);
+        if (h == 0)
+            f.v[b].lo = v;
+        else
+            f.v[b].hi = v;
+    }
+    // 16 MFMAs on m blocks 4 HM .. +3 x n blocks 4 HN .. +3, n outer (AO
+    // false) or m outer (AO true); read i (of 8) after MFMAs 0, 2, .., 14,
+    // load j (of 4) after MFMA 4 j + LOFF
+    static constexpr int LOFF = 1;
+    template <int HM, int HN, bool AO, class RD, class LD>
+    __device__ __forceinline__ void quarter(const F8 &a, const F8 &b, RD &&rd, LD &&ld)
+    {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int o = i / 4, n = i % 4;
+            const int ia = AO ? o : n, jb = AO ? n : o;
+            mfma16_e4m3_agpr(acc[4 * HM + ia][4 * HN + jb], b.v[jb], a.v[ia]);
+            if (i % 2 == 0)
+                rd(i / 2);
+            if (i % 4 == LOFF)
+                ld(i / 4);
+        }
+    }
+
+    __device__ __forceinline__ void mainloop(char *lds, const OperandSrc &sa, int lda, const OperandSrc &sb, int ldb,
+                                             int K, int tid)
+    {
+        const int lane = tid & 63;
+        const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+        const int wm0 = (wave / WN) * TM, wn0 = (wave % WN) * TN;
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+                acc[i][j] = f32x4_t{};
+        const int ksteps = (K + KSTEP - 1) / KSTEP;
+        if (ksteps <= 0)
+            return;
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+                asm volatile("" : "+a"(acc[i][j]));
+        setup(lane, wave, wm0, wn0, lda, ldb);
+        char *const A0 = lds;                  // 2 slots
+        char *const B0 = lds + A_SLOTS * OPS;  // 3 slots
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+                a_sh[q][h] = lds_addr(A0 + q * OPS) + (uint32_t)abase[h];
+        const OperandSrc ua = uniform_src(sa), ub = uniform_src(sb);
+        constexpr std::true_type masked{};
+        constexpr std::false_type unmasked{};
+        // prologue: steps 0 and 1 of both operands; wait for step 0
+        {
+            const auto ra0 = ua.at_step(0), rb0 = ub.at_step(0), ra1 = ua.at_step(1), rb1 = ub.at_step(1);
+#pragma unroll
+            for (int j = 0; j < LOADS; ++j) {
+                load_b<true>(rb0, B0, wave, j, K);
+                load_a<true>(ra0, A0, wave, j, K);
+            }
+#pragma unroll
+            for (int j = 0; j < LOADS; ++j)
+                load_b<true>(rb1, B0 + OPS, wave, j, K - KSTEP);
+#pragma unroll
+            for (int j = 0; j < LOADS; ++j)
+                load_a<true>(ra1, A0 + OPS, wave, j, K - KSTEP);
+            wait_vm<2 * LOADS>();
+        }
+        lds_barrier();
+        F8 Al, Ah, Bl, Bh;
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            rd_a<0, 0>(Al, i);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            rd_b<0>(B0, Bl, i);
+        mfma_drain();
+        int sb_cur = 0;  // B slot of step kt
+        // one K step; P = kt & 1 (the A slot and the quarter order)
+        auto step = [&](int kt, auto mask, auto par) {
+            constexpr int P = decltype(par)::value;
+            constexpr bool MASK = decltype(mask)::value;
+            const int sb_next = sb_cur == 2 ? 0 : sb_cur + 1;
+            const int sb_fill = sb_next == 2 ? 0 : sb_next + 1;
+            const char *bc = B0 + sb_cur * OPS;
+            const char *bn = B0 + sb_next * OPS;
+            const auto rB = MASK ? ub.at_step(kt + 2) : step_rsrc(ub, true, kt + 2);
+            const int kb = K - (kt + 2) * KSTEP;
+            char *const bw = B0 + sb_fill * OPS;
+            auto ldB = [&](int j) { load_b<MASK>(rB, bw, wave, j, kb); };
+            if constexpr (P == 0) {
+                quarter<0, 0, false>(Al, Bl, [&](int i) { rd_b<1>(bc, Bh, i); }, [&](int j) { ldB(j); });
+                quarter<0, 1, false>(Al, Bh, [&](int i) { rd_a<0, 1>(Ah, i); }, [&](int j) { ldB(4 + j); });
+            } else {
+                quarter<0, 1, false>(Al, Bh, [&](int i) { rd_b<0>(bc, Bl, i); }, [&](int j) { ldB(j); });
+                quarter<0, 0, false>(Al, Bl, [&](int i) { rd_a<1, 1>(Ah, i); }, [&](int j) { ldB(4 + j); });
+            }
+            wait_vm<LOADS>();
+            lds_barrier();
+            // A's step kt+2 into the slot step kt leaves
+            const auto rA = MASK ? ua.at_step(kt + 2) : step_rsrc(ua, true, kt + 2);
+            const int ka = K - (kt + 2) * KSTEP;
+            char *const aw = A0 + P * OPS;
+            auto ldA = [&](int j) { load_a<MASK>(rA, aw, wave, j, ka); };
+            if constexpr (P == 0) {
+                quarter<1, 1, true>(Ah, Bh, [&](int i) { rd_a<1, 0>(Al, i); }, [&](int j) { ldA(j); });
+                quarter<1, 0, false>(Ah, Bl, [&](int i) { rd_b<1>(bn, Bh, i); }, [&](int j) { ldA(4 + j); });
+            } else {
+                quarter<1, 0, true>(Ah, Bl, [&](int i) { rd_a<0, 0>(Al, i); }, [&](int j) { ldA(j); });
+                quarter<1, 1, false>(Ah, Bh, [&](int i) { rd_b<0>(bn, Bl, i); }, [&](int j) { ldA(4 + j); });
+            }
+            sb_cur = sb_next;
+        };
+        // Steps two at a time, the quarter order fixed per parity (a branch
+        // between the two orders would make the compiler move the
+        // accumulators where the paths meet).  An odd step count gets one
+        // more step whose loads were all past K: its slots hold zeros.
+        int kt = 0;
+        for (; kt + 1 < ksteps - 3; kt += 2) {
+            step(kt, unmasked, std::integral_constant<int, 0>{});
+            step(kt + 1, unmasked, std::integral_constant<int, 1>{});
+        }
+        for (; kt < ksteps; kt += 2) {
+            step(kt, masked, std::integral_constant<int, 0>{});
+            step(kt + 1, masked, std::integral_constant<int, 1>{});
+        }
+        wait_vm<0>();
+        mfma_drain();
+    }
+};
+
 // ---------------------------------------------------------------------------
 // Epilogue helpers
 // ---------------------------------------------------------------------------
@@ -1430,9 +1669,10 @@ __device__ __forceinline__ void epilogue(const T &t, void *D, int64_t ldd, int m
 // stores of one half need not complete before the next is staged); each wave
 // enters it with its own loads into the rings complete, so after the first
 // barrier nothing writes the rings any more.
-template <class T, int OUT>
+// SCALE: every output is first multiplied by `scale` (fp32).
+template <class T, int OUT, bool SCALE = false>
 __device__ __forceinline__ void epilogue_staged(const T &t, char *lds, void *D, int64_t ldd, int m_valid,
-                                                int n_valid, int tid)
+                                                int n_valid, int tid, float scale = 1.0f)
 {
     static_assert(T::MI == 16 && T::BN == 256 && T::WM == 2 && T::TM == 128 && T::LDS_BYTES >= 128 * 1024, "");
     constexpr int esize = out_size(OUT);
@@ -1461,7 +1701,9 @@ __device__ __forceinline__ void epilogue_staged(const T &t, char *lds, void *D, 
         lds_barrier();
 #pragma unroll 4
         for (int x = wave; x < 128; x += T::NT / 64) {
-            const f32x4_t v = *(const f32x4_t *)(lds + x * 1024 + ((lane ^ (x & 15)) << 4));
+            f32x4_t v = *(const f32x4_t *)(lds + x * 1024 + ((lane ^ (x & 15)) << 4));
+            if constexpr (SCALE)
+                v *= scale;
             const int m = (x >> 6) * T::TM + 64 * h + (x & 63);
             const uint32_t off = n < n_valid ? (uint32_t)m * row_bytes + (uint32_t)n * esize : kOOB;
             // whole rows, written once and not read again here: streaming

@@ -22,6 +22,8 @@ struct DenseArgs {
     int splits;       // K ranges per output tile (1: the whole K)
     int kchunk;       // elements of K per range, a multiple of 64
     int64_t split_stride;  // elements of D between the partial results of consecutive ranges
+    const float *scale_a = nullptr;  // E4M3 inputs: per-tensor scales (device, one float each; null = 1)
+    const float *scale_b = nullptr;
 };
 
 struct GroupedArgs {
@@ -131,6 +133,44 @@ __global__ void __launch_bounds__(T::NT) dense_kernel(DenseArgs p)
         char *Dt = (char *)p.D + ((int64_t)r * p.split_stride + (int64_t)m0 * p.ldd + n0) * esize;
         tile_epilogue<T, EPI_NONE, OUT>(tile, lds, Dt, p.ldd, min(T::BM, p.M - m0), min(T::BN, p.N - n0),
                                         opaque((int)threadIdx.x));
+    }
+}
+
+// D = scale_a x scale_b x (A x B) for E4M3 A ([M][K], lda) and B ([N][K],
+// ldb), both k-contiguous, on the four-wave direct-to-LDS tile; K is not
+// split.  With one scale per tensor the dequantisation is one multiply of
+// the finished fp32 sums, done in the epilogue ("MegaMoE：Blackwell 与 Hopper
+// 的融合算子解读", Hopper section 04).  Leading dimensions and offsets are
+// in elements = bytes.
+template <int OUT>
+__global__ void __launch_bounds__(DtlTile4E4M3::NT) dense_e4m3_kernel(DenseArgs p)
+{
+    using T = DtlTile4E4M3;
+    __shared__ __attribute__((aligned(16))) char lds[T::LDS_BYTES];
+    T tile;
+    const int grid = gridDim.x;
+    const int L = logical_block(blockIdx.x, grid, p.xcd_remap);
+    const char *A = (const char *)p.A;
+    const char *B = (const char *)p.B;
+    const float scale = (p.scale_a ? *p.scale_a : 1.0f) * (p.scale_b ? *p.scale_b : 1.0f);
+    constexpr int esize = out_size(OUT);
+    for (int t = L; t < p.tiles; t += grid) {
+        int mb, nb;
+        tile_coords(t, p.tiles_m, p.tiles_n, p.group_m, mb, nb);
+        const int m0 = mb * T::BM, n0 = nb * T::BN;
+        OperandSrc sa, sb;
+        sa.base = A + (int64_t)m0 * p.lda;
+        sa.bytes = (uint64_t)(p.M - m0) * (uint64_t)p.lda;
+        sa.step_bytes = T::KSTEP;
+        sb.base = B + (int64_t)n0 * p.ldb;
+        sb.bytes = (uint64_t)(p.N - n0) * (uint64_t)p.ldb;
+        sb.step_bytes = T::KSTEP;
+        tile.mainloop(lds, sa, p.lda, sb, p.ldb, p.K, opaque((int)threadIdx.x));
+        char *Dt = (char *)p.D + ((int64_t)m0 * p.ldd + n0) * esize;
+        epilogue_staged<T, OUT, true>(tile, lds, Dt, p.ldd, min(T::BM, p.M - m0), min(T::BN, p.N - n0),
+                                      opaque((int)threadIdx.x), scale);
+        // the next tile's loads are counted from zero (as in tile_epilogue)
+        wait_vm<0>();
     }
 }
 

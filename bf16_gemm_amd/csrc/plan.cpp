@@ -55,6 +55,8 @@ static const char *tile_name(int tile)
 
 DenseFn dense_fn(int tile, bool ak, bool bk, int in, int out)
 {
+    if (in == IN_E4M3)
+        return tile == TILE_256x256_DTL ? dense_fn_256x256dtl_e4m3(ak, bk, out) : nullptr;
     const bool bf = in == IN_BF16;
     switch (tile) {
     case TILE_256x256: return bf ? dense_fn_256x256_bf16(ak, bk, out) : dense_fn_256x256_f16(ak, bk, out);
@@ -68,6 +70,8 @@ DenseFn dense_fn(int tile, bool ak, bool bk, int in, int out)
 
 GroupedFn grouped_fn(int tile, bool bk, int in, int out, int epi)
 {
+    if (in == IN_E4M3)
+        return nullptr;
     const bool bf = in == IN_BF16;
     switch (tile) {
     case TILE_256x256: return bf ? grouped_fn_256x256_bf16(bk, out, epi) : grouped_fn_256x256_f16(bk, out, epi);
@@ -80,7 +84,7 @@ GroupedFn grouped_fn(int tile, bool bk, int in, int out, int epi)
     }
 }
 
-int in_code(mgemm_dtype_t t) { return t == MGEMM_BF16 ? IN_BF16 : IN_F16; }
+int in_code(mgemm_dtype_t t) { return t == MGEMM_BF16 ? IN_BF16 : (t == MGEMM_E4M3 ? IN_E4M3 : IN_F16); }
 int out_code(mgemm_dtype_t t) { return t == MGEMM_F32 ? OUT_F32 : (t == MGEMM_BF16 ? OUT_BF16 : OUT_F16); }
 int dtype_size(mgemm_dtype_t t) { return t == MGEMM_F32 ? 4 : 2; }
 
@@ -136,7 +140,8 @@ static double task_model_us(const TileShape &t, int64_t M, int64_t N, int64_t K,
     return us;
 }
 
-static bool is_in_type(mgemm_dtype_t t) { return t == MGEMM_F16 || t == MGEMM_BF16; }
+static bool is_in_type(mgemm_dtype_t t) { return t == MGEMM_F16 || t == MGEMM_BF16 || t == MGEMM_E4M3; }
+static const char *in_name(mgemm_dtype_t t) { return t == MGEMM_BF16 ? "bf16" : (t == MGEMM_E4M3 ? "e4m3" : "f16"); }
 static bool is_out_type(mgemm_dtype_t t) { return t == MGEMM_F16 || t == MGEMM_BF16 || t == MGEMM_F32; }
 static bool is_layout(mgemm_layout_t l) { return l == MGEMM_ROW_MAJOR || l == MGEMM_COL_MAJOR; }
 
@@ -153,7 +158,7 @@ static mgemm_status_t check_types(mgemm_dtype_t a, mgemm_dtype_t b, mgemm_dtype_
         set_error("a_type and b_type must match");
         return MGEMM_ERR_UNSUPPORTED;
     }
-    if (d != MGEMM_F32 && d != a) {
+    if (d != MGEMM_F32 && d != a && a != MGEMM_E4M3) {
         set_error("d_type must be F32 or the input type");
         return MGEMM_ERR_UNSUPPORTED;
     }
@@ -196,6 +201,19 @@ static mgemm_status_t plan_dense(const mgemm_desc_t *d, uint32_t flags, mgemm_pl
         set_error("K must be a multiple of 8 (got %lld)", (long long)d->K);
         return MGEMM_ERR_UNSUPPORTED;
     }
+    const bool e4m3 = d->a_type == MGEMM_E4M3;
+    if (e4m3) {
+        // one kernel: k-contiguous A and B, 16-byte rows, whole tile columns
+        // of four, no split of K
+        const int fs = (int)((flags >> 16) & 0xFF);
+        const int ft = forced_tile(flags);
+        if (d->a_layout != MGEMM_ROW_MAJOR || d->b_layout != MGEMM_COL_MAJOR || d->K % 16 || d->lda % 16 ||
+            d->ldb % 16 || d->N % 4 || fs > 1 || (ft >= 0 && ft != TILE_256x256_DTL)) {
+            set_error("E4M3 plans need row-major A, column-major B, K, lda, ldb multiples of 16, N a multiple "
+                      "of 4, no split of K and no tile but the 256x256 direct-to-LDS one");
+            return MGEMM_ERR_UNSUPPORTED;
+        }
+    }
     const int esz = dtype_size(d->d_type);
     if (d->lda % 8 || d->ldb % 8 || (d->ldd * esz) % 16) {
         set_error("leading dimensions must give 16-byte aligned rows (lda, ldb multiples of 8; ldd*%d %% 16 == 0)",
@@ -216,7 +234,7 @@ static mgemm_status_t plan_dense(const mgemm_desc_t *d, uint32_t flags, mgemm_pl
     const bool bk = d->b_layout == MGEMM_COL_MAJOR;
     const int in = in_code(d->a_type), out = out_code(d->d_type);
 
-    int tile = forced_tile(flags);
+    int tile = e4m3 ? TILE_256x256_DTL : forced_tile(flags);
     if (tile >= 0) {
         if (!dense_fn(tile, ak, bk, in, out)) {
             set_error("forced tile %s is not compiled for this layout/dtype", tile_name(tile));
@@ -252,7 +270,7 @@ static mgemm_status_t plan_dense(const mgemm_desc_t *d, uint32_t flags, mgemm_pl
     int splits = 1;
     if (forced_splits > 0) {
         splits = (int)std::min<int64_t>(forced_splits, std::max<int64_t>(ksteps, 1));
-    } else if (forced_tile(flags) < 0 && n_main > 0 && d->M > 0) {
+    } else if (!e4m3 && forced_tile(flags) < 0 && n_main > 0 && d->M > 0) {
         // Split K when the chosen tiles leave most compute units idle: the
         // tile and range count with the lowest modelled time wins if it beats
         // the unsplit plan by 10 %.
@@ -308,12 +326,12 @@ static mgemm_status_t plan_dense(const mgemm_desc_t *d, uint32_t flags, mgemm_pl
         snprintf(stages, sizeof stages, "%da/%db", a_slots, b_slots);
     char buf[256];
     snprintf(buf, sizeof buf,
-             "dense M=%lld N=%lld K=%lld %s%s->%s tile=%s waves=%dx%d bk=64 stages=%s tiles=%lld splits=%d "
+             "dense M=%lld N=%lld K=%lld %s%s->%s tile=%s waves=%dx%d bk=%d stages=%s tiles=%lld splits=%d "
              "grid=%d group_m=%d xcd_remap=%d edge_cols=%lld",
-             (long long)d->M, (long long)d->N, (long long)d->K, d->a_type == MGEMM_BF16 ? "bf16" : "f16",
+             (long long)d->M, (long long)d->N, (long long)d->K, in_name(d->a_type),
              ak ? (bk ? " NT" : " NN") : (bk ? " TT" : " TN"),
              d->d_type == MGEMM_F32 ? "f32" : (d->d_type == MGEMM_BF16 ? "bf16" : "f16"), tile_name(tile), wm, wn,
-             stages, (long long)p->tiles, p->splits, p->grid, p->group_m, p->xcd_remap, (long long)(d->N - n_main));
+             e4m3 ? 128 : 64, stages, (long long)p->tiles, p->splits, p->grid, p->group_m, p->xcd_remap, (long long)(d->N - n_main));
     p->description = buf;
     return MGEMM_OK;
 }
@@ -331,6 +349,10 @@ static mgemm_status_t plan_grouped(const mgemm_grouped_desc_t *d, uint32_t flags
     }
     if (mgemm_status_t s = check_types(d->a_type, d->b_type, d->d_type))
         return s;
+    if (d->a_type == MGEMM_E4M3) {
+        set_error("grouped plans take F16 or BF16 inputs");
+        return MGEMM_ERR_UNSUPPORTED;
+    }
     if (!is_layout(d->b_layout) || (d->epilogue != MGEMM_EPI_NONE && d->epilogue != MGEMM_EPI_SILU_GATE_I8)) {
         set_error("invalid layout or epilogue code");
         return MGEMM_ERR_INVALID_ARG;

@@ -73,6 +73,25 @@ DenseFn dense_dtl_table(bool ak, bool bk, int out)
                           : launch_dense_tile<DtlTile4<IN, false>, true, false, IN, same16<IN>()>;
 }
 
+// E4M3 inputs: A row-major and B column-major only (both k-contiguous).
+template <int OUT>
+hipError_t launch_dense_e4m3(const DenseArgs &a, int grid, hipStream_t s)
+{
+    hipLaunchKernelGGL((dense_e4m3_kernel<OUT>), dim3(grid), dim3(DtlTile4E4M3::NT), 0, s, a);
+    return hipGetLastError();
+}
+inline DenseFn dense_e4m3_table(bool ak, bool bk, int out)
+{
+    if (!ak || !bk)
+        return nullptr;
+    switch (out) {
+    case OUT_F32: return launch_dense_e4m3<OUT_F32>;
+    case OUT_BF16: return launch_dense_e4m3<OUT_BF16>;
+    case OUT_F16: return launch_dense_e4m3<OUT_F16>;
+    default: return nullptr;
+    }
+}
+
 // Grouped launches of the direct-to-LDS tile: its rings fill the LDS, so
 // the task list lives in registers (grouped_kernel_wt).
 template <bool BK, int IN, int OUT, int EPI>

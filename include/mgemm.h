@@ -45,7 +45,10 @@ extern "C" {
 struct ihipStream_t;
 typedef struct ihipStream_t *mgemm_stream_t;
 
-typedef enum { MGEMM_F16 = 1, MGEMM_BF16 = 2, MGEMM_F32 = 3 } mgemm_dtype_t;
+/* E4M3: the OCP 8-bit float with 1 sign, 4 exponent (bias 7) and 3 fraction
+ * bits, subnormals, no infinities, NaN = S.1111.111 (largest finite 448).
+ * An input type only (dense plans; see gemm_run_scaled). */
+typedef enum { MGEMM_F16 = 1, MGEMM_BF16 = 2, MGEMM_F32 = 3, MGEMM_E4M3 = 4 } mgemm_dtype_t;
 
 /* Storage of a logical rows x cols operand.  ROW_MAJOR: element (r,c) at
  * r*ld + c.  COL_MAJOR: element (r,c) at c*ld + r.  D is always row-major. */
@@ -72,7 +75,12 @@ typedef struct mgemm_plan *mgemm_plan_t;
 /* Dense problem.  Sizes and leading dimensions are in elements.
  *  - M, N, K >= 0.  M == 0 or N == 0: the run is a no-op.  K == 0: D is
  *    filled with zeros (the empty sum).
- *  - a_type == b_type, one of F16 / BF16.  d_type: F32, BF16 or F16.
+ *  - a_type == b_type, one of F16 / BF16 / E4M3.  d_type: F32 or the input
+ *    type (E4M3 inputs: F32, BF16 or F16).
+ *  - E4M3 inputs: A row-major and B column-major (both k-contiguous),
+ *    K, lda and ldb multiples of 16, N a multiple of 4, no split of K and
+ *    no forced tile but MGEMM_PLAN_FORCE_TILE_256x256_DTL; otherwise
+ *    MGEMM_ERR_UNSUPPORTED.  Grouped plans reject E4M3.
  *  - K % 8 == 0; A, B, D base addresses 16-byte aligned; lda, ldb a
  *    multiple of 8 elements; ldd * sizeof(d_type) a multiple of 16 bytes.
  *    Otherwise MGEMM_ERR_UNSUPPORTED.
@@ -149,6 +157,21 @@ mgemm_status_t gemm_plan_workspace_size(mgemm_plan_t plan, size_t *bytes);
  * missing, misaligned or smaller than gemm_plan_workspace_size. */
 mgemm_status_t gemm_run(mgemm_plan_t plan, const void *A, const void *B, void *D,
                         void *workspace, size_t workspace_bytes, mgemm_stream_t stream);
+
+/* Enqueue D = (scale_a x scale_b) x (A x B) on `stream` for a plan with
+ * E4M3 inputs, with one scale per tensor ("MegaMoE：Blackwell 与 Hopper 的融合
+ * 算子解读", Hopper section 04: with per-tensor scales the dequantisation is
+ * a single multiply in the epilogue).  d_scale_a and d_scale_b are device
+ * pointers to one fp32 value each, read by the kernel when it runs (so they
+ * may be produced on the device without a host synchronisation).  The
+ * products are accumulated in fp32; each finished sum is multiplied by the
+ * fp32 product scale_a x scale_b and rounded once to d_type.  gemm_run on an
+ * E4M3 plan is the same with both scales 1.  Errors: a non-E4M3 plan gives
+ * MGEMM_ERR_UNSUPPORTED; a null or misaligned scale pointer
+ * MGEMM_ERR_INVALID_ARG; otherwise as gemm_run.  K == 0 writes zeros. */
+mgemm_status_t gemm_run_scaled(mgemm_plan_t plan, const void *A, const void *B, void *D,
+                               const float *d_scale_a, const float *d_scale_b,
+                               void *workspace, size_t workspace_bytes, mgemm_stream_t stream);
 
 /* Enqueue the grouped product on `stream`.  d_row_offsets is a device array
  * of num_groups + 1 int32 prefix sums; it is read by the kernels only (no

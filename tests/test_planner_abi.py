@@ -207,3 +207,30 @@ def test_null_arguments_rejected():
     p = mg.gemm_plan(4, 8, 8, "bf16")
     assert mg.lib.gemm_run(p.handle, None, None, None, None, 0, None) == mg.ERR_INVALID_ARG
     assert mg.lib.gemm_status_string(mg.ERR_HIP) == b"MGEMM_ERR_HIP"
+
+
+def test_e4m3_plan_rules():
+    """E4M3 plans: k-contiguous A and B only, 16-element alignment, no split,
+    no grouped form; gemm_run_scaled checks the plan type and the scale
+    pointers before anything is launched."""
+    ok = mg.gemm_plan(512, 512, 256, a_type="e4m3", d_type="bf16", a_layout="row", b_layout="col")
+    assert "e4m3 NT->bf16 tile=256x256dtl" in ok.describe() and "bk=128" in ok.describe()
+    assert "splits=1" in ok.describe()
+    for kw in [dict(b_layout="row"), dict(a_layout="col", lda=512), dict(K=264), dict(N=514),
+               dict(flags=mg.PLAN_FORCE_TILE_128x128), dict(flags=mg.PLAN_SPLIT_K(4))]:
+        args = dict(M=512, N=512, K=256, a_type="e4m3", d_type="bf16", a_layout="row", b_layout="col")
+        args.update(kw)
+        with pytest.raises(mg.MgemmError) as e:
+            mg.gemm_plan(**args)
+        assert e.value.status == mg.ERR_UNSUPPORTED, kw
+    with pytest.raises(mg.MgemmError) as e:
+        mg.grouped_gemm_plan(4, 256, 256, 256, a_type="e4m3", d_type="bf16", b_layout="col")
+    assert e.value.status == mg.ERR_UNSUPPORTED
+    fake = 1 << 20
+    with pytest.raises(mg.MgemmError) as e:
+        mg.gemm_run_scaled(ok, fake, fake, fake, None, fake, stream=0)
+    assert e.value.status == mg.ERR_INVALID_ARG
+    bf = mg.gemm_plan(512, 512, 256, a_type="bf16", d_type="bf16")
+    with pytest.raises(mg.MgemmError) as e:
+        mg.gemm_run_scaled(bf, fake, fake, fake, fake, fake, stream=0)
+    assert e.value.status == mg.ERR_UNSUPPORTED
