@@ -1311,27 +1311,25 @@ __device__ __forceinline__ void mfma16_e4m3_agpr(f32x4_t &c, const u32x8_t &a, c
 
 // The four-wave 256 x 256 direct-to-LDS tile for E4M3 inputs, A and B both
 // k-contiguous ([M][K] and [N][K]).  A K step is 128 elements = 128 bytes of
-// each tile row, so the rings, the global-side swizzle, the load
-// assignment and the barrier placement are the 16-bit tile's (DtlTile4 with
-// a column-major B: B on the 3-slot ring, A on the 2-slot one).  What
-// differs is the MFMA: v_mfma_f32_16x16x128_f8f6f4 takes a whole step's
-// 128 k per block at once (32 bytes per lane: the lane's chunk q and chunk
-// q + 4 of the row, in both operands), so a step is one pass of 64 MFMAs
-// instead of two 32-k sub-steps.  The wave's fragments are four sets of
-// four blocks (A rows 0-63 / 64-127, B rows 0-63 / 64-127: Al, Ah, Bl, Bh;
-// 128 VGPRs in all, no second copy), and the step is four quarters, each
-// one set pair:
-//   even steps: Al.Bl, Al.Bh | barrier | Ah.Bh, Ah.Bl
-//   odd steps:  Al.Bh, Al.Bl | barrier | Ah.Bl, Ah.Bh
-// Each quarter reads, two halves per block, the set that the order leaves
-// free next: even steps read Bh and Ah of this step, then Al and Bh of the
-// next; odd steps Bl and Ah of this step, then Al and Bl of the next.  The
-// reads of a step end before its barrier and those of the next start after
-// it, as in the 16-bit tile, and every set is read a whole quarter before
-// the quarter that uses it; a quarter that uses a set read in the quarter
-// just before it runs through that set's blocks in the order they arrived.
-// Loads: the deep operand's step kt+2 four per quarter in the first half,
-// the shallow operand's step kt+2 four per quarter in the second.
+// each tile row, so the rings (A on two slots, B on three), the global-side
+// swizzle and the load assignment are the 16-bit tile's.  What differs is
+// the MFMA: v_mfma_f32_16x16x128_f8f6f4 takes a whole step's 128 k per
+// block at once (32 bytes per lane: the lane's chunk q and chunk q + 4 of
+// the row, in both operands), so a step is one pass of 64 MFMAs, in four
+// quarters of 16, each on one pair of fragment sets of four blocks (A rows
+// 0-63 / 64-127 and B rows 0-63 / 64-127 of the wave: Al, Ah, Bl, Bh):
+//   q0 Al.Bl  (reads Ah of this step)
+//   wait for step kt+1 in LDS, barrier
+//   q1 Al.Bh  (reads Bl of step kt+1 into a fifth set; loads A of kt+2)
+//   q2 Ah.Bh  (reads Al of step kt+1;                 loads A of kt+2)
+//   q3 Ah.Bl  (reads Bh of step kt+1;                 loads B of kt+3)
+// Every set is read two quarters before the quarter that first uses it:
+// with the loads writing the same LDS, a read issued one quarter ahead
+// arrived too late (the step ran at twice the time of the loop without
+// global loads, and of the loop without LDS reads).  Bl alternates between
+// two registers sets, so steps run in pairs.  After the barrier of step kt
+// no wave reads step kt's slots again: A's slot takes step kt+2 and B's
+// step kt+3 (B's ring runs two steps ahead, A's one).
 struct DtlTile4E4M3 {
     using Base = DtlTile<IN_BF16, true>;
     static constexpr int BM = 256, BN = 256, WM = 2, WN = 2;
@@ -1409,22 +1407,21 @@ struct DtlTile4E4M3 {
         else
             f.v[b].hi = v;
     }
-    // 16 MFMAs on m blocks 4 HM .. +3 x n blocks 4 HN .. +3, n outer (AO
-    // false) or m outer (AO true); read i (of 8) after MFMAs 0, 2, .., 14,
-    // load j (of 4) after MFMA 4 j + LOFF
-    static constexpr int LOFF = 1;
-    template <int HM, int HN, bool AO, class RD, class LD>
+    // 16 MFMAs on m blocks 4 HM .. +3 x n blocks 4 HN .. +3 (n outer); read
+    // i (of 8) after MFMAs 0, 2, .., 14, load j (of NL) after MFMA
+    // j * 16 / NL + 1
+    template <int HM, int HN, int NL, class RD, class LD>
     __device__ __forceinline__ void quarter(const F8 &a, const F8 &b, RD &&rd, LD &&ld)
     {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            const int o = i / 4, n = i % 4;
-            const int ia = AO ? o : n, jb = AO ? n : o;
-            mfma16_e4m3_agpr(acc[4 * HM + ia][4 * HN + jb], b.v[jb], a.v[ia]);
+            mfma16_e4m3_agpr(acc[4 * HM + i % 4][4 * HN + i / 4], b.v[i / 4], a.v[i % 4]);
             if (i % 2 == 0)
                 rd(i / 2);
-            if (i % 4 == LOFF)
-                ld(i / 4);
+            if constexpr (NL > 0) {
+                if (i % (16 / NL) == 1)
+                    ld(i / (16 / NL));
+            }
         }
     }
 
@@ -1448,8 +1445,8 @@ struct DtlTile4E4M3 {
             for (int j = 0; j < FN; ++j)
                 asm volatile("" : "+a"(acc[i][j]));
         setup(lane, wave, wm0, wn0, lda, ldb);
-        char *const A0 = lds;                  // 2 slots
-        char *const B0 = lds + A_SLOTS * OPS;  // 3 slots
+        char *const A0 = lds;                  // 2 slots: step s in slot s % 2
+        char *const B0 = lds + A_SLOTS * OPS;  // 3 slots: step s in slot s % 3
 #pragma unroll
         for (int q = 0; q < 2; ++q)
 #pragma unroll
@@ -1458,73 +1455,67 @@ struct DtlTile4E4M3 {
         const OperandSrc ua = uniform_src(sa), ub = uniform_src(sb);
         constexpr std::true_type masked{};
         constexpr std::false_type unmasked{};
-        // prologue: steps 0 and 1 of both operands; wait for step 0
+        // prologue: A of steps 0, 1 and B of steps 0, 1, 2; wait for all but
+        // B of step 2
         {
-            const auto ra0 = ua.at_step(0), rb0 = ub.at_step(0), ra1 = ua.at_step(1), rb1 = ub.at_step(1);
 #pragma unroll
-            for (int j = 0; j < LOADS; ++j) {
-                load_b<true>(rb0, B0, wave, j, K);
-                load_a<true>(ra0, A0, wave, j, K);
+            for (int s = 0; s < 2; ++s) {
+                const auto rb = ub.at_step(s), ra = ua.at_step(s);
+#pragma unroll
+                for (int j = 0; j < LOADS; ++j) {
+                    load_b<true>(rb, B0 + s * OPS, wave, j, K - s * KSTEP);
+                    load_a<true>(ra, A0 + s * OPS, wave, j, K - s * KSTEP);
+                }
             }
+            const auto rb2 = ub.at_step(2);
 #pragma unroll
             for (int j = 0; j < LOADS; ++j)
-                load_b<true>(rb1, B0 + OPS, wave, j, K - KSTEP);
-#pragma unroll
-            for (int j = 0; j < LOADS; ++j)
-                load_a<true>(ra1, A0 + OPS, wave, j, K - KSTEP);
-            wait_vm<2 * LOADS>();
+                load_b<true>(rb2, B0 + 2 * OPS, wave, j, K - 2 * KSTEP);
+            wait_vm<LOADS>();
         }
         lds_barrier();
-        F8 Al, Ah, Bl, Bh;
+        F8 Al, Ah, Bh, BlX, BlY;
 #pragma unroll
         for (int i = 0; i < 8; ++i)
             rd_a<0, 0>(Al, i);
 #pragma unroll
         for (int i = 0; i < 8; ++i)
-            rd_b<0>(B0, Bl, i);
+            rd_b<0>(B0, BlX, i);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            rd_b<1>(B0, Bh, i);
         mfma_drain();
         int sb_cur = 0;  // B slot of step kt
-        // one K step; P = kt & 1 (the A slot and the quarter order)
+        // one K step; P = kt & 1 (A's slot, and which of BlX / BlY is Bl)
         auto step = [&](int kt, auto mask, auto par) {
             constexpr int P = decltype(par)::value;
             constexpr bool MASK = decltype(mask)::value;
+            F8 &Bl = P == 0 ? BlX : BlY;
+            F8 &Bn = P == 0 ? BlY : BlX;
             const int sb_next = sb_cur == 2 ? 0 : sb_cur + 1;
-            const int sb_fill = sb_next == 2 ? 0 : sb_next + 1;
-            const char *bc = B0 + sb_cur * OPS;
             const char *bn = B0 + sb_next * OPS;
-            const auto rB = MASK ? ub.at_step(kt + 2) : step_rsrc(ub, true, kt + 2);
-            const int kb = K - (kt + 2) * KSTEP;
-            char *const bw = B0 + sb_fill * OPS;
-            auto ldB = [&](int j) { load_b<MASK>(rB, bw, wave, j, kb); };
-            if constexpr (P == 0) {
-                quarter<0, 0, false>(Al, Bl, [&](int i) { rd_b<1>(bc, Bh, i); }, [&](int j) { ldB(j); });
-                quarter<0, 1, false>(Al, Bh, [&](int i) { rd_a<0, 1>(Ah, i); }, [&](int j) { ldB(4 + j); });
-            } else {
-                quarter<0, 1, false>(Al, Bh, [&](int i) { rd_b<0>(bc, Bl, i); }, [&](int j) { ldB(j); });
-                quarter<0, 0, false>(Al, Bl, [&](int i) { rd_a<1, 1>(Ah, i); }, [&](int j) { ldB(4 + j); });
-            }
+            quarter<0, 0, 0>(Al, Bl, [&](int i) { rd_a<P, 1>(Ah, i); }, [](int) {});
             wait_vm<LOADS>();
             lds_barrier();
-            // A's step kt+2 into the slot step kt leaves
             const auto rA = MASK ? ua.at_step(kt + 2) : step_rsrc(ua, true, kt + 2);
             const int ka = K - (kt + 2) * KSTEP;
             char *const aw = A0 + P * OPS;
-            auto ldA = [&](int j) { load_a<MASK>(rA, aw, wave, j, ka); };
-            if constexpr (P == 0) {
-                quarter<1, 1, true>(Ah, Bh, [&](int i) { rd_a<1, 0>(Al, i); }, [&](int j) { ldA(j); });
-                quarter<1, 0, false>(Ah, Bl, [&](int i) { rd_b<1>(bn, Bh, i); }, [&](int j) { ldA(4 + j); });
-            } else {
-                quarter<1, 0, true>(Ah, Bl, [&](int i) { rd_a<0, 0>(Al, i); }, [&](int j) { ldA(j); });
-                quarter<1, 1, false>(Ah, Bh, [&](int i) { rd_b<0>(bn, Bl, i); }, [&](int j) { ldA(4 + j); });
-            }
+            const auto rB = MASK ? ub.at_step(kt + 3) : step_rsrc(ub, true, kt + 3);
+            const int kb = K - (kt + 3) * KSTEP;
+            char *const bw = B0 + sb_cur * OPS;
+            quarter<0, 1, 4>(Al, Bh, [&](int i) { rd_b<0>(bn, Bn, i); },
+                             [&](int j) { load_a<MASK>(rA, aw, wave, j, ka); });
+            quarter<1, 1, 4>(Ah, Bh, [&](int i) { rd_a<P ^ 1, 0>(Al, i); },
+                             [&](int j) { load_a<MASK>(rA, aw, wave, 4 + j, ka); });
+            quarter<1, 0, 8>(Ah, Bl, [&](int i) { rd_b<1>(bn, Bh, i); },
+                             [&](int j) { load_b<MASK>(rB, bw, wave, j, kb); });
             sb_cur = sb_next;
         };
-        // Steps two at a time, the quarter order fixed per parity (a branch
-        // between the two orders would make the compiler move the
-        // accumulators where the paths meet).  An odd step count gets one
-        // more step whose loads were all past K: its slots hold zeros.
+        // Steps two at a time while every load is of a whole step
+        // (kt + 4 <= ksteps - 2); the rest with the K mask.  An odd step
+        // count gets one more step, whose loads were all past K: zeros.
         int kt = 0;
-        for (; kt + 1 < ksteps - 3; kt += 2) {
+        for (; kt + 1 < ksteps - 4; kt += 2) {
             step(kt, unmasked, std::integral_constant<int, 0>{});
             step(kt + 1, unmasked, std::integral_constant<int, 1>{});
         }
