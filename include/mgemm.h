@@ -11,6 +11,9 @@
  * stages), and can fuse the SwiGLU gate, h = up x SiLU(gate), into the
  * epilogue (first page, section 七, "Gate／SwiGLU"; gate and up columns
  * interleaved in blocks of eight, gate first, MegaMoE Hopper section 10).
+ * The dense form also takes E4M3 (FP8) operands with one fp32 scale per
+ * tensor, multiplied into the finished sum (MegaMoE Hopper section 04;
+ * gemm_run_scaled).
  *
  * Launch semantics follow the execution-model page ("从 CUDA 代码到 GPU 执行",
  * the launch-configuration and Stream sections): a run call only enqueues
