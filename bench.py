@@ -47,7 +47,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle sample time")
     ap.add_argument("--no-secondary", action="store_true",
-                    help="skip the second square size the metric is quoted at (4096^3 next to 8192^3)")
+                    help="skip the second square size the metric is quoted at (4096^3 next to 8192^3) "
+                         "and the E4M3 8192^3 line")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a plain 256 MiB device copy (the reference kernel that scales the "
                          "FETCH_SIZE / WRITE_SIZE counters to bytes)")
@@ -307,6 +308,7 @@ def main():
     ms, warmup_done = time_steps(torch, step, args.steps, args.warmup)
     roof, tflops, peak = roofline(info, ms)
     secondary = []
+    e4m3_line = None
     if args.workload == DEFAULT_WORKLOAD and not args.no_secondary:
         # the metric is quoted at 4096^3 as well: same timing, reported beside
         del step
@@ -317,6 +319,17 @@ def main():
         secondary.append({"config": info2["config"], "value": round(tflops2, 2), "unit": "TFLOPS",
                           "ms_per_step": round(ms2, 5), "pct_of_peak": round(100 * tflops2 / peak2, 2),
                           "roofline": roof2})
+        # the E4M3 product of the same size (per-tensor scales), priced
+        # against the fp8 dense peak: reported beside, not the metric
+        del step2
+        step3, info3, _ = e4m3_case(torch, mg, datagen, "gemm8192_e4m3")
+        print(f"# plan: {info3['plan']}", file=sys.stderr, flush=True)
+        ms3, _ = time_steps(torch, step3, args.steps, args.warmup)
+        roof3, tflops3, peak3 = roofline(info3, ms3)
+        e4m3_line = {"config": info3["config"], "value": round(tflops3, 2), "unit": "TFLOPS",
+                     "ms_per_step": round(ms3, 5), "pct_of_fp8_peak": round(100 * tflops3 / peak3, 2),
+                     "roofline": roof3}
+        del step3
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(case, args.cpu_seconds)
@@ -327,6 +340,8 @@ def main():
             "roofline": roof, "cpu_baseline": cpu}
     if secondary:
         line["also"] = secondary
+    if e4m3_line:
+        line["e4m3"] = e4m3_line
     print(json.dumps(line), flush=True)
 
 
