@@ -71,7 +71,7 @@ class Budget(ctypes.Structure):
 
 #: every symbol include/mgemm.h declares
 EXPORTS = ["gemm_plan", "grouped_gemm_plan", "gemm_plan_workspace_size", "gemm_run", "gemm_run_scaled",
-           "grouped_gemm_run",
+           "grouped_gemm_run", "grouped_gemm_run_scaled",
            "gemm_plan_describe", "gemm_plan_info", "gemm_plan_destroy", "gemm_status_string",
            "gemm_last_error_message", "mgemm_tile_budget", "mgemm_group_working_set", "mgemm_round_tokens",
            "mgemm_version", "mgemm_moe_combine", "grouped_gemm_run_gather"]
@@ -93,6 +93,8 @@ def _load():
     lib.gemm_run.restype = st
     lib.gemm_run_scaled.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.gemm_run_scaled.restype = st
+    lib.grouped_gemm_run_scaled.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.grouped_gemm_run_scaled.restype = st
     lib.grouped_gemm_run.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.grouped_gemm_run.restype = st
     lib.gemm_plan_describe.argtypes = [vp, ctypes.c_char_p, ctypes.c_size_t]
@@ -238,6 +240,13 @@ def gemm_run_scaled(plan: Plan, A, B, D, scale_a, scale_b, stream=None):
     holding the E4M3 codes."""
     _check(lib.gemm_run_scaled(plan.handle, _ptr(A), _ptr(B), _ptr(D), _ptr(scale_a), _ptr(scale_b), None, 0,
                                _stream(stream)), "gemm_run_scaled")
+
+
+def grouped_gemm_run_scaled(plan: Plan, A, B, D, row_offsets, scale_a, scale_b, stream=None):
+    """Enqueue the grouped E4M3 product; ``scale_a``: device float32 tensor of
+    one element, ``scale_b``: one float32 per expert (device)."""
+    _check(lib.grouped_gemm_run_scaled(plan.handle, _ptr(A), _ptr(B), _ptr(D), _ptr(row_offsets), _ptr(scale_a),
+                                       _ptr(scale_b), None, 0, _stream(stream)), "grouped_gemm_run_scaled")
 
 
 def grouped_gemm_run(plan: Plan, A, B, D, row_offsets, workspace=None, workspace_bytes: int = 0, stream=None):

@@ -164,7 +164,8 @@ extern "C" mgemm_status_t gemm_run_scaled(mgemm_plan_t plan, const void *A, cons
 // row_index: nullptr, or the gathered form's index (x_rows rows of A exist).
 static mgemm_status_t grouped_run(mgemm_plan_t plan, const void *A, const void *B, void *D,
                                   const int32_t *d_row_offsets, const int32_t *row_index, int64_t x_rows,
-                                  mgemm_stream_t stream)
+                                  mgemm_stream_t stream, const float *scale_a = nullptr,
+                                  const float *scale_b = nullptr)
 {
     if (!plan || plan->kind != PLAN_GROUPED) {
         set_error("grouped_gemm_run: null or non-grouped plan");
@@ -224,6 +225,8 @@ static mgemm_status_t grouped_run(mgemm_plan_t plan, const void *A, const void *
         a.tiles_n = (int)((d.N + ts.bn - 1) / ts.bn);
         a.bucket_lo = L.lo;
         a.bucket_hi = L.hi;
+        a.scale_a = scale_a;
+        a.scale_b = scale_b;
         a.xcd_remap = plan->xcd_remap;
         a.row_index = row_index;
         a.x_rows = (int)x_rows;
@@ -259,6 +262,28 @@ extern "C" mgemm_status_t grouped_gemm_run_gather(mgemm_plan_t plan, const void 
         return MGEMM_ERR_INVALID_ARG;
     }
     return grouped_run(plan, X, B, D, d_row_offsets, d_row_index, x_rows, stream);
+}
+
+extern "C" mgemm_status_t grouped_gemm_run_scaled(mgemm_plan_t plan, const void *A, const void *B, void *D,
+                                                  const int32_t *d_row_offsets, const float *d_scale_a,
+                                                  const float *d_scale_b, void *workspace, size_t workspace_bytes,
+                                                  mgemm_stream_t stream)
+{
+    (void)workspace;
+    (void)workspace_bytes;
+    if (!plan || plan->kind != PLAN_GROUPED) {
+        set_error("grouped_gemm_run_scaled: null or non-grouped plan");
+        return MGEMM_ERR_INVALID_ARG;
+    }
+    if (plan->grouped.a_type != MGEMM_E4M3) {
+        set_error("grouped_gemm_run_scaled: the plan's inputs are not E4M3");
+        return MGEMM_ERR_UNSUPPORTED;
+    }
+    if (!d_scale_a || !d_scale_b || ((uintptr_t)d_scale_a & 3) || ((uintptr_t)d_scale_b & 3)) {
+        set_error("grouped_gemm_run_scaled: scale pointers must be non-null and 4-byte aligned");
+        return MGEMM_ERR_INVALID_ARG;
+    }
+    return grouped_run(plan, A, B, D, d_row_offsets, nullptr, 0, stream, d_scale_a, d_scale_b);
 }
 
 extern "C" mgemm_status_t mgemm_moe_combine(const void *Z, int64_t z_rows, int64_t ldz, const int32_t *d_pos,

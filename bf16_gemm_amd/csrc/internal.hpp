@@ -57,6 +57,7 @@ MGEMM_DECLARE_TU(256x256dtl_bf16)
 MGEMM_DECLARE_TU(256x256dtl_f16)
 #undef MGEMM_DECLARE_TU
 DenseFn dense_fn_256x256dtl_e4m3(bool ak, bool bk, int out);
+GroupedFn grouped_fn_256x256dtl_e4m3(bool bk, int out, int epi);
 
 using EdgeFn = hipError_t (*)(const DenseArgs &, int a_kmajor, int b_kmajor, int n_first, hipStream_t);
 EdgeFn edge_fn(int in, int out);

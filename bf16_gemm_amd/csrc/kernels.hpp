@@ -40,6 +40,8 @@ struct GroupedArgs {
     int xcd_remap;
     const int32_t *row_index = nullptr;  // gathered A: routed row r reads A row row_index[r]
     int x_rows = 0;                      // rows of A that exist when gathering
+    const float *scale_a = nullptr;      // E4M3: the activations' scale (device, one float; null = 1)
+    const float *scale_b = nullptr;      // E4M3: one weight scale per expert (device, G floats; null = 1)
 };
 
 
@@ -360,6 +362,49 @@ __global__ void __launch_bounds__(T::NT) grouped_kernel_wt(GroupedArgs p)
         const int dcol0 = EPI == EPI_SILU_GATE ? n0 / 2 : n0;
         char *Dt = (char *)p.D + ((int64_t)m0 * p.ldd + dcol0) * esize;
         tile_epilogue<T, EPI, OUT>(tile, lds, Dt, p.ldd, m_valid, min(T::BN, p.N - n0), opaque((int)threadIdx.x));
+    }
+}
+
+// The grouped product on E4M3 inputs (expert weights column-major, [N][K]
+// each) on the four-wave direct-to-LDS tile, task list in registers:
+// expert e's rows are multiplied by its weights and the finished sums by
+// scale_a x scale_b[e] -- one scale for the activations, one per expert for
+// the weights ("MegaMoE：Blackwell 与 Hopper 的融合算子解读", Hopper section 04,
+// the per-tensor path).
+template <int OUT>
+__global__ void __launch_bounds__(DtlTile4E4M3::NT) grouped_e4m3_kernel(GroupedArgs p)
+{
+    using T = DtlTile4E4M3;
+    __shared__ __attribute__((aligned(16))) char lds[T::LDS_BYTES];
+    WaveTasks wt;
+    wt.build(p, T::BM, (int)threadIdx.x & 63);
+    T tile;
+    const int grid = gridDim.x;
+    const int L = logical_block(blockIdx.x, grid, p.xcd_remap);
+    const char *A = (const char *)p.A;
+    const char *B = (const char *)p.B;
+    const float sa = p.scale_a ? *p.scale_a : 1.0f;
+    constexpr int esize = out_size(OUT);
+    for (int t = L; t < wt.total; t += grid) {
+        int e, local, rows0, rows_e;
+        wt.find(t, e, local, rows0, rows_e);
+        const int tm = (rows_e + T::BM - 1) / T::BM;
+        const int mb = local % tm, nb = local / tm;
+        const int m0 = rows0 + mb * T::BM, n0 = nb * T::BN;
+        const int m_valid = min(T::BM, rows_e - mb * T::BM);
+        OperandSrc sa_src, sb_src;
+        sa_src.base = A + (int64_t)m0 * p.lda;
+        sa_src.bytes = (uint64_t)m_valid * (uint64_t)p.lda;
+        sa_src.step_bytes = T::KSTEP;
+        sb_src.base = B + (int64_t)e * p.stride_b + (int64_t)n0 * p.ldb;
+        sb_src.bytes = (uint64_t)(p.N - n0) * (uint64_t)p.ldb;
+        sb_src.step_bytes = T::KSTEP;
+        tile.mainloop(lds, sa_src, p.lda, sb_src, p.ldb, p.K, opaque((int)threadIdx.x));
+        const float scale = sa * (p.scale_b ? p.scale_b[e] : 1.0f);
+        char *Dt = (char *)p.D + ((int64_t)m0 * p.ldd + n0) * esize;
+        epilogue_staged<T, OUT, true>(tile, lds, Dt, p.ldd, m_valid, min(T::BN, p.N - n0),
+                                      opaque((int)threadIdx.x), scale);
+        wait_vm<0>();
     }
 }
 

@@ -71,7 +71,7 @@ DenseFn dense_fn(int tile, bool ak, bool bk, int in, int out)
 GroupedFn grouped_fn(int tile, bool bk, int in, int out, int epi)
 {
     if (in == IN_E4M3)
-        return nullptr;
+        return tile == TILE_256x256_DTL ? grouped_fn_256x256dtl_e4m3(bk, out, epi) : nullptr;
     const bool bf = in == IN_BF16;
     switch (tile) {
     case TILE_256x256: return bf ? grouped_fn_256x256_bf16(bk, out, epi) : grouped_fn_256x256_f16(bk, out, epi);
@@ -349,10 +349,6 @@ static mgemm_status_t plan_grouped(const mgemm_grouped_desc_t *d, uint32_t flags
     }
     if (mgemm_status_t s = check_types(d->a_type, d->b_type, d->d_type))
         return s;
-    if (d->a_type == MGEMM_E4M3) {
-        set_error("grouped plans take F16 or BF16 inputs");
-        return MGEMM_ERR_UNSUPPORTED;
-    }
     if (!is_layout(d->b_layout) || (d->epilogue != MGEMM_EPI_NONE && d->epilogue != MGEMM_EPI_SILU_GATE_I8)) {
         set_error("invalid layout or epilogue code");
         return MGEMM_ERR_INVALID_ARG;
@@ -384,6 +380,13 @@ static mgemm_status_t plan_grouped(const mgemm_grouped_desc_t *d, uint32_t flags
         set_error("leading dimensions above 2^20 elements are not supported");
         return MGEMM_ERR_UNSUPPORTED;
     }
+    const bool e4m3 = d->a_type == MGEMM_E4M3;
+    if (e4m3 && (d->b_layout != MGEMM_COL_MAJOR || silu || d->K % 16 || d->lda % 16 || d->ldb % 16 ||
+                 d->stride_b % 16 || (forced_tile(flags) >= 0 && forced_tile(flags) != TILE_256x256_DTL))) {
+        set_error("grouped E4M3 plans need column-major expert weights, no epilogue, K, lda, ldb and stride_b "
+                  "multiples of 16, and no tile but the 256x256 direct-to-LDS one");
+        return MGEMM_ERR_UNSUPPORTED;
+    }
     p->kind = PLAN_GROUPED;
     p->grouped = *d;
     p->flags = flags;
@@ -406,7 +409,7 @@ static mgemm_status_t plan_grouped(const mgemm_grouped_desc_t *d, uint32_t flags
     struct B { int tile, lo, hi; };
     B buckets[2] = {{TILE_32x256, 1, 129}, {TILE_256x256_DTL, 129, 1 << 30}};
     int nb = 2;
-    const int ft = forced_tile(flags);
+    const int ft = e4m3 ? TILE_256x256_DTL : forced_tile(flags);
     if (ft >= 0) {
         buckets[0] = {ft, 1, 1 << 30};
         nb = 1;
@@ -415,7 +418,7 @@ static mgemm_status_t plan_grouped(const mgemm_grouped_desc_t *d, uint32_t flags
     std::string desc;
     char buf[256];
     snprintf(buf, sizeof buf, "grouped G=%d rows<=%lld N=%lld K=%lld %s%s->%s epi=%s", d->num_groups,
-             (long long)d->max_total_rows, (long long)d->N, (long long)d->K, d->a_type == MGEMM_BF16 ? "bf16" : "f16",
+             (long long)d->max_total_rows, (long long)d->N, (long long)d->K, in_name(d->a_type),
              bk ? " NT" : " NN", d->d_type == MGEMM_F32 ? "f32" : (d->d_type == MGEMM_BF16 ? "bf16" : "f16"),
              silu ? "silu_gate_i8" : "none");
     desc = buf;

@@ -92,6 +92,24 @@ inline DenseFn dense_e4m3_table(bool ak, bool bk, int out)
     }
 }
 
+template <int OUT>
+hipError_t launch_grouped_e4m3(const GroupedArgs &a, int grid, hipStream_t s)
+{
+    hipLaunchKernelGGL((grouped_e4m3_kernel<OUT>), dim3(grid), dim3(DtlTile4E4M3::NT), 0, s, a);
+    return hipGetLastError();
+}
+inline GroupedFn grouped_e4m3_table(bool bk, int out, int epi)
+{
+    if (!bk || epi != EPI_NONE)
+        return nullptr;
+    switch (out) {
+    case OUT_F32: return launch_grouped_e4m3<OUT_F32>;
+    case OUT_BF16: return launch_grouped_e4m3<OUT_BF16>;
+    case OUT_F16: return launch_grouped_e4m3<OUT_F16>;
+    default: return nullptr;
+    }
+}
+
 // Grouped launches of the direct-to-LDS tile: its rings fill the LDS, so
 // the task list lives in registers (grouped_kernel_wt).
 template <bool BK, int IN, int OUT, int EPI>

@@ -83,7 +83,7 @@ typedef struct mgemm_plan *mgemm_plan_t;
  *  - E4M3 inputs: A row-major and B column-major (both k-contiguous),
  *    K, lda and ldb multiples of 16, N a multiple of 4, no split of K and
  *    no forced tile but MGEMM_PLAN_FORCE_TILE_256x256_DTL; otherwise
- *    MGEMM_ERR_UNSUPPORTED.  Grouped plans reject E4M3.
+ *    MGEMM_ERR_UNSUPPORTED.  Grouped E4M3: see grouped_gemm_run_scaled.
  *  - K % 8 == 0; A, B, D base addresses 16-byte aligned; lda, ldb a
  *    multiple of 8 elements; ldd * sizeof(d_type) a multiple of 16 bytes.
  *    Otherwise MGEMM_ERR_UNSUPPORTED.
@@ -175,6 +175,22 @@ mgemm_status_t gemm_run(mgemm_plan_t plan, const void *A, const void *B, void *D
 mgemm_status_t gemm_run_scaled(mgemm_plan_t plan, const void *A, const void *B, void *D,
                                const float *d_scale_a, const float *d_scale_b,
                                void *workspace, size_t workspace_bytes, mgemm_stream_t stream);
+
+/* Enqueue the grouped product of a plan with E4M3 inputs: expert e's rows
+ * times its weights, each finished fp32 sum multiplied by the fp32 product
+ * scale_a x scale_b[e] and rounded once to d_type (one scale for the
+ * activations and one per expert for the weights: "MegaMoE：Blackwell 与
+ * Hopper 的融合算子解读", Hopper section 04, the per-tensor path).
+ * d_scale_a: device pointer to one float; d_scale_b: device pointer to
+ * num_groups floats; both read by the kernel when it runs.  Grouped E4M3
+ * plans need column-major expert weights, MGEMM_EPI_NONE, K, lda, ldb and
+ * stride_b multiples of 16.  grouped_gemm_run on such a plan uses scales 1.
+ * Errors: a non-E4M3 plan gives MGEMM_ERR_UNSUPPORTED, a null or misaligned
+ * scale pointer MGEMM_ERR_INVALID_ARG, otherwise as grouped_gemm_run. */
+mgemm_status_t grouped_gemm_run_scaled(mgemm_plan_t plan, const void *A, const void *B, void *D,
+                                       const int32_t *d_row_offsets, const float *d_scale_a,
+                                       const float *d_scale_b, void *workspace, size_t workspace_bytes,
+                                       mgemm_stream_t stream);
 
 /* Enqueue the grouped product on `stream`.  d_row_offsets is a device array
  * of num_groups + 1 int32 prefix sums; it is read by the kernels only (no

@@ -295,3 +295,21 @@ def gemm_e4m3_ref_sampled(A: np.ndarray, B: np.ndarray, rows, cols, scale_a: flo
     _load().oracle_gemm_e4m3_ref_sampled(A.shape[1], _p(A), A.shape[1], _p(B), B.shape[1], float(scale_a),
                                          float(scale_b), _p(r), _p(c), r.size, _p(out))
     return out
+
+
+def grouped_e4m3_ref(A: np.ndarray, W: np.ndarray, offsets, scale_a: float, scale_b) -> np.ndarray:
+    """The per-expert E4M3 product ("MegaMoE", Recap 1: expert e multiplies its
+    rows [off[e], off[e+1]) by its own weights; Hopper section 04: one scale
+    for the activations, one per expert for the weights).  ``A``: [rows][K]
+    uint8; ``W``: [G][N][K] uint8 (each expert's K x N weight column-major);
+    ``scale_b``: G floats.  Returns [rows][N] float64; rows past off[G] stay
+    NaN (not produced)."""
+    off = np.asarray(offsets, dtype=np.int64)
+    G, N, K = W.shape
+    out = np.full((A.shape[0], N), np.nan)
+    for e in range(G):
+        lo, hi = int(off[e]), int(off[e + 1])
+        if hi > lo:
+            out[lo:hi] = gemm_e4m3_ref(np.ascontiguousarray(A[lo:hi]), np.ascontiguousarray(W[e]),
+                                       scale_a, float(scale_b[e]))
+    return out

@@ -95,3 +95,23 @@ def test_datagen_codes_are_finite_and_round_to_nearest():
     ci = datagen.matrix_e4m3((8, 8), ("int", 3), np.random.RandomState(2))
     vi = oracle.decode_e4m3(ci)
     assert np.array_equal(vi, np.round(vi)) and np.abs(vi).max() <= 3
+
+
+def test_grouped_is_the_per_expert_product():
+    """Each expert's rows equal the dense product of those rows and that
+    expert's weights with its own scale; empty experts produce nothing and a
+    one-row expert is one row of the dense product."""
+    rs = np.random.RandomState(4)
+    counts = [0, 1, 7, 0, 12]
+    off = np.concatenate([[0], np.cumsum(counts)])
+    K, N = 48, 20
+    A = finite_codes((int(off[-1]) + 3, K), rs)
+    W = finite_codes((len(counts), N, K), rs)
+    sb = np.array([1.0, 0.5, 2.0, 4.0, 0.25])
+    got = oracle.gemm_e4m3_ref  # the dense form, pinned above
+    g = oracle.grouped_e4m3_ref(A, W, off, 0.75, sb)
+    assert np.isnan(g[int(off[-1]):]).all()
+    dense_all = {e: got(A, W[e]) for e in range(len(counts))}
+    for e in range(len(counts)):
+        lo, hi = off[e], off[e + 1]
+        assert np.array_equal(g[lo:hi], dense_all[e][lo:hi] * (0.75 * sb[e]))

@@ -213,6 +213,7 @@ def test_e4m3_plan_rules():
     """E4M3 plans: k-contiguous A and B only, 16-element alignment, no split,
     no grouped form; gemm_run_scaled checks the plan type and the scale
     pointers before anything is launched."""
+    fake = 1 << 20
     ok = mg.gemm_plan(512, 512, 256, a_type="e4m3", d_type="bf16", a_layout="row", b_layout="col")
     assert "e4m3 NT->bf16 tile=256x256dtl" in ok.describe() and "bk=128" in ok.describe()
     assert "splits=1" in ok.describe()
@@ -223,9 +224,16 @@ def test_e4m3_plan_rules():
         with pytest.raises(mg.MgemmError) as e:
             mg.gemm_plan(**args)
         assert e.value.status == mg.ERR_UNSUPPORTED, kw
+    g = mg.grouped_gemm_plan(4, 256, 256, 256, a_type="e4m3", d_type="bf16", b_layout="col")
+    assert "e4m3 NT->bf16" in g.describe() and "256x256dtl" in g.describe()
+    for kw in [dict(b_layout="row"), dict(b_layout="col", epilogue=mg.EPI_SILU_GATE_I8),
+               dict(b_layout="col", stride_b=256 * 256 + 8)]:
+        with pytest.raises(mg.MgemmError) as e:
+            mg.grouped_gemm_plan(4, 256, 256, 256, a_type="e4m3", d_type="bf16", **kw)
+        assert e.value.status == mg.ERR_UNSUPPORTED, kw
     with pytest.raises(mg.MgemmError) as e:
-        mg.grouped_gemm_plan(4, 256, 256, 256, a_type="e4m3", d_type="bf16", b_layout="col")
-    assert e.value.status == mg.ERR_UNSUPPORTED
+        mg.grouped_gemm_run_scaled(g, fake, fake, fake, fake, fake, None, stream=0)
+    assert e.value.status == mg.ERR_INVALID_ARG
     fake = 1 << 20
     with pytest.raises(mg.MgemmError) as e:
         mg.gemm_run_scaled(ok, fake, fake, fake, None, fake, stream=0)
