@@ -178,6 +178,12 @@ static mgemm_status_t grouped_run(mgemm_plan_t plan, const void *A, const void *
         set_error("grouped_gemm_run: null pointer");
         return MGEMM_ERR_INVALID_ARG;
     }
+    if (row_index && d.a_type == MGEMM_E4M3) {
+        // the E4M3 grouped kernel reads A's rows in place; it has no gathered form
+        set_error("grouped_gemm_run_gather: E4M3 plans take no gathered rows (gather the rows first and use "
+                  "grouped_gemm_run_scaled)");
+        return MGEMM_ERR_UNSUPPORTED;
+    }
     if (row_index && !plan->zero_fill) {
         if (x_rows < 0 || x_rows > INT32_MAX ||
             (uint64_t)x_rows * (uint64_t)d.lda * 2u > (uint64_t)kMaxRecords) {

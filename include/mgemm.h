@@ -50,7 +50,8 @@ typedef struct ihipStream_t *mgemm_stream_t;
 
 /* E4M3: the OCP 8-bit float with 1 sign, 4 exponent (bias 7) and 3 fraction
  * bits, subnormals, no infinities, NaN = S.1111.111 (largest finite 448).
- * An input type only (dense plans; see gemm_run_scaled). */
+ * An input type only, of dense and grouped plans (gemm_run_scaled,
+ * grouped_gemm_run_scaled). */
 typedef enum { MGEMM_F16 = 1, MGEMM_BF16 = 2, MGEMM_F32 = 3, MGEMM_E4M3 = 4 } mgemm_dtype_t;
 
 /* Storage of a logical rows x cols operand.  ROW_MAJOR: element (r,c) at
@@ -168,7 +169,8 @@ mgemm_status_t gemm_run(mgemm_plan_t plan, const void *A, const void *B, void *D
  * pointers to one fp32 value each, read by the kernel when it runs (so they
  * may be produced on the device without a host synchronisation).  The
  * products are accumulated in fp32; each finished sum is multiplied by the
- * fp32 product scale_a x scale_b and rounded once to d_type.  gemm_run on an
+ * fp32 product scale_a x scale_b (each output is fl(fl(scale_a * scale_b) *
+ * acc), an fp32 multiply) and that is rounded once to d_type.  gemm_run on an
  * E4M3 plan is the same with both scales 1.  Errors: a non-E4M3 plan gives
  * MGEMM_ERR_UNSUPPORTED; a null or misaligned scale pointer
  * MGEMM_ERR_INVALID_ARG; otherwise as gemm_run.  K == 0 writes zeros. */
@@ -178,9 +180,11 @@ mgemm_status_t gemm_run_scaled(mgemm_plan_t plan, const void *A, const void *B, 
 
 /* Enqueue the grouped product of a plan with E4M3 inputs: expert e's rows
  * times its weights, each finished fp32 sum multiplied by the fp32 product
- * scale_a x scale_b[e] and rounded once to d_type (one scale for the
- * activations and one per expert for the weights: "MegaMoE：Blackwell 与
- * Hopper 的融合算子解读", Hopper section 04, the per-tensor path).
+ * scale_a x scale_b[e] -- fl(fl(scale_a * scale_b[e]) * acc) -- and that
+ * rounded once to d_type (one scale for the activations and one per expert
+ * for the weights: "MegaMoE：Blackwell 与 Hopper 的融合算子解读", Hopper
+ * section 04, the per-tensor path).  No gathered form (see
+ * grouped_gemm_run_gather).
  * d_scale_a: device pointer to one float; d_scale_b: device pointer to
  * num_groups floats; both read by the kernel when it runs.  Grouped E4M3
  * plans need column-major expert weights, MGEMM_EPI_NONE, K, lda, ldb and
@@ -264,9 +268,10 @@ int64_t mgemm_round_tokens(int64_t n, int32_t granule);
  * d_row_index: device int32, one entry per routed row (off[num_groups]
  * entries); an entry outside [0, x_rows) reads as a row of zeros.
  * Everything else is grouped_gemm_run's.  x_rows * lda * 2 must be below
- * 2^31 (else MGEMM_ERR_INVALID_ARG).  Only plans whose launches use the
- * default 32x256 and direct-to-LDS 256x256 tiles take gathered rows (a plan
- * forced onto another tile returns MGEMM_ERR_UNSUPPORTED). */
+ * 2^31 (else MGEMM_ERR_INVALID_ARG).  Only 16-bit plans whose launches use
+ * the default 32x256 and direct-to-LDS 256x256 tiles take gathered rows: a
+ * plan forced onto another tile, and any E4M3 plan, returns
+ * MGEMM_ERR_UNSUPPORTED before anything is launched. */
 mgemm_status_t grouped_gemm_run_gather(mgemm_plan_t plan, const void *X, int64_t x_rows, const void *B, void *D,
                                        const int32_t *d_row_offsets, const int32_t *d_row_index, void *workspace,
                                        size_t workspace_bytes, mgemm_stream_t stream);

@@ -344,7 +344,7 @@ void oracle_decode_e4m3(const uint8_t *src, int64_t n, double *dst)
  * contiguously), B is stored [N][ldb] (column j of the K x N operand holds k
  * contiguously).  The sum is the same ascending-k double sum as
  * oracle_gemm_ref (products of two E4M3 values are exact in double); the
- * scales multiply the finished sum, scale_a first.
+ * product (scale_a x scale_b), formed first, multiplies the finished sum.
  */
 int oracle_gemm_e4m3_ref(int64_t M, int64_t N, int64_t K, const uint8_t *A, int64_t lda, const uint8_t *B,
                          int64_t ldb, double scale_a, double scale_b, double *ref)

@@ -5,13 +5,21 @@ output type.
 
 Integer-valued codes with power-of-two scales make every sum exact in fp32
 (and in any accumulator of 24 bits or more), so those cases are bit-exact.
-Random codes are held to a bound in the sum of absolute products: the
-matrix instruction reduces its 128 products internally, not as a chain of
-IEEE fp32 additions (at K = 128, one instruction per output, the error of
-normal(0, 100) codes reached 2^-15.7 of scale * sum|a b|, far above one fp32
-rounding of the result), so the bound allows 2^-13 of scale * sum|a b| for
-the products and the fp32 accumulation together, plus the final rounding to
-the output type taken as 2^-22 (f32), 2^-8 (bf16) or 2^-10 (f16) of |ref|.
+Random codes are held to a bound in the sum of absolute products, in two
+parts:
+  * each v_mfma_f32_16x16x128_f8f6f4 reduces its (up to) 128 exact products
+    internally; the ISA documentation states the result (the sum added to
+    the accumulator) but not the order, width or rounding of that
+    reduction, so this part can only be bounded empirically: INSTR = 2^-13
+    of scale * sum|a b| (the worst seen is 2^-15.2, at K = 16, one
+    instruction with 16 nonzero products -- far above one fp32 rounding, so
+    the reduction is narrower than an fp32 chain);
+  * the ceil(K/128) instruction results are then added into the fp32
+    accumulator, each addition rounding once: at most ceil(K/128) * 2^-24
+    of scale * sum|a b| (the n*u bound of a recursive sum);
+plus the final rounding to the output type, 2^-22 (f32: the scale multiply
+and the store), 2^-8 (bf16) or 2^-10 (f16) of |ref|.  Every random case
+logs its worst err / (scale * sum|a b|) and err / tolerance.
 """
 import sys
 
@@ -61,13 +69,18 @@ def run(A, B, M, N, K, out, sa, sb, lda=None, ldb=None, flags=0):
     return plan, from_dev_bits(D[:, :N].contiguous())
 
 
-ABS = 2.0 ** -13
+INSTR = 2.0 ** -13     # one matrix instruction's internal reduction (empirical)
+
+
+def rel_sum(K):
+    """Bound on |err| / (scale * sum|a b|) before the output rounding."""
+    return INSTR + -(-K // 128) * 2.0 ** -24
 
 
 def bound(A, B, ref, out, s):
     """(tolerance, scale * sum|a b|)"""
     absum = abs(s) * oracle.gemm_e4m3_ref(A & 0x7F, B & 0x7F)
-    return ABS * absum + REL[out] * np.abs(ref) + 1e-30, absum
+    return rel_sum(A.shape[1]) * absum + REL[out] * np.abs(ref) + 1e-30, absum
 
 
 def inputs(M, N, K, variant, seed):
@@ -95,7 +108,8 @@ def test_against_oracle(shape, out, variant):
     else:
         err = np.abs(values(got, out) - ref)
         tol, absum = bound(A, B, ref, out, s)
-        log(f"  max err / (scale * sum|ab|) = 2^{np.log2((err / absum).max() + 1e-300):.1f}")
+        log(f"  K={K}: max err / (scale * sum|ab|) = 2^{np.log2((err / absum).max() + 1e-300):.1f}, "
+            f"max err / tol = {(err / tol).max():.3f}")
         assert np.all(err <= tol), f"{plan.describe()}: max err {err.max():.3e}, worst ratio {(err / tol).max():.3f}"
 
 
@@ -155,9 +169,10 @@ def test_full_size_8192_sampled(out):
     fa, fb = float(np.float32(sa)), float(np.float32(sb))
     ref = oracle.gemm_e4m3_ref_sampled(A, B, r, c, fa, fb)
     absum = abs(fa * fb) * oracle.gemm_e4m3_ref_sampled(A & 0x7F, B & 0x7F, r, c)
-    tol = ABS * absum + REL[out] * np.abs(ref)
+    tol = rel_sum(K) * absum + REL[out] * np.abs(ref)
     err = np.abs(values(got[r, c], out) - ref)
-    log(f"  max err / (scale * sum|ab|) = 2^{np.log2((err / absum).max() + 1e-300):.1f}")
+    log(f"  K={K}: max err / (scale * sum|ab|) = 2^{np.log2((err / absum).max() + 1e-300):.1f}, "
+        f"max err / tol = {(err / tol).max():.3f}")
     assert np.all(err <= tol), f"max err {err.max():.3e}, worst ratio {(err / tol).max():.3f}"
     # every output was written (no NaN fill left)
     assert not np.isnan(values(got, out)).any()

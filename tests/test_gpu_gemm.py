@@ -8,6 +8,7 @@ meet the acceptance rule in helpers.py.
 """
 import math
 import sys
+import zlib
 
 import numpy as np
 import pytest
@@ -319,6 +320,24 @@ def test_direct_to_lds_long_k_ragged_tail(K, bl):
     assert_close(got, oracle.gemm_ref(a, b, "bf16", "bf16", "row", bl), K, "f32", plan.describe())
 
 
+@pytest.mark.parametrize("bl,out_t", [("col", "f32"), ("row", "bf16")])
+def test_direct_to_lds_steady_state_second_tile_full(bl, out_t):
+    """The paired-step steady-state loop (unmasked loads, the 2-slot
+    operand's slot fixed per step of a pair) on a workgroup's second tile:
+    4352 x 4352 gives 17 x 17 = 289 tiles of 256 x 256 on 256 workgroups,
+    K = 1024 gives 16 steps, 12 of them in unmasked pairs.  Every output
+    element against the oracle, integer inputs, bit-exact."""
+    M = N = 4352
+    K = 1024
+    log(f"case dtl steady-state second tile M={M} N={N} K={K} B {bl} -> {out_t}")
+    cfg = datagen.GemmConfig("t", M, N, K, "bf16", out_t, "row", bl, seed=41, int_seed=43 + (bl == "row"))
+    a, b = datagen.gemm_inputs(cfg, "int")
+    got, plan = run_dense(a, b, M, N, K, "bf16", out_t, "row", bl, TILES["256d"])
+    d = plan.describe()
+    assert "256x256dtl" in d and "tiles=289" in d and "grid=256" in d and "splits=1" in d, d
+    assert_bits_equal(got, oracle.gemm_ref(a, b, "bf16", "bf16", "row", bl), out_t, d)
+
+
 # --------------------------------------------------------------- full size
 
 FULL = ["gemm512_f16", "gemm4096_bf16", "gemm8192_bf16_bcol", "ts16384x2048x7168", "decode128x7168x2048"]
@@ -345,7 +364,9 @@ def test_full_size_workloads(name, flags, variant):
         g = got
     else:
         inf = plan.info()
-        r, c = sample_positions(cfg.M, cfg.N, 3000, (inf.block_m, inf.block_n), seed=hash(name) % 1000)
+        seed = zlib.crc32(name.encode()) % 1000   # fixed per workload: a failure replays
+        log(f"  sample seed {seed}")
+        r, c = sample_positions(cfg.M, cfg.N, 3000, (inf.block_m, inf.block_n), seed=seed)
         ref = oracle.gemm_ref_sampled(a, b, r, c, cfg.in_dtype, cfg.in_dtype, cfg.a_layout, cfg.b_layout)
         g = got[r, c]
     if variant == "int":

@@ -279,6 +279,64 @@ def test_moe_integer_chain_exact():
         assert np.array_equal(y[lo:hi], (Hi[lo:hi] @ W).astype(np.float64))
 
 
+def test_moe_ref_closed_form_with_saturated_gate():
+    """moe_ref (FC1 -> SiLU gate -> bf16 h -> FC2 per expert) against a
+    closed form worked out with Python integers.  Every routed row has
+    A[r, 0] = 1 and every gate column of W1 is 64 at k = 0 and 0 elsewhere,
+    so each gate sum is exactly 64; SiLU(64) = 64 / (1 + e^-64) is 64.0 in
+    fp64 (e^-64 is below half an ulp of 1), so h = 64 * up, an integer that
+    bf16 holds exactly (|up| <= 64 has at most 7 significant bits), and
+    y = h . W2 is exact.  One row's first up sum is forced to 259, so its h
+    (64 * 259) needs nine significant bits and bf16 must round it to nearest
+    (64 * 260; truncation would give 64 * 258), and FC2 must take the
+    rounded value.  Gate and up
+    columns follow the interleave of eight columns, gate first.  A swapped
+    gate/up order, a wrong expert's weights, an unrounded h fed to FC2, or a
+    mis-walked (or empty) expert fails."""
+    rs = np.random.RandomState(7)
+    K1, I, H = 16, 16, 24          # hidden in, intermediate, hidden out
+    offsets = [0, 3, 3, 7]         # three experts, the second empty
+    G, rows = len(offsets) - 1, offsets[-1]
+    A = rs.randint(-2, 3, (rows, K1))
+    A[:, 0] = 1
+    W1 = rs.randint(-2, 3, (G, K1, 2 * I))
+    W2 = rs.randint(-2, 3, (G, I, H))
+    for c in range(I):             # gate column of output c: 16 (c // 8) + c % 8
+        jg = 16 * (c // 8) + c % 8
+        W1[:, :, jg] = 0
+        W1[:, 0, jg] = 64
+    # row 0 (expert 0): up sum of output column 0 is 259
+    ju0 = 8
+    A[0, 1] = 1
+    W1[0, :, ju0] = 0
+    W1[0, 0, ju0], W1[0, 1, ju0] = 256, 3
+
+    def bf16_int(v):
+        """v rounded to 8 significant bits, ties to even (bf16 on integers)."""
+        m, sign = abs(v), (-1 if v < 0 else 1)
+        sh = max(m.bit_length() - 8, 0)
+        q, rem = divmod(m, 1 << sh)
+        half = 1 << sh >> 1
+        if sh and (rem > half or (rem == half and q & 1)):
+            q += 1
+        return sign * (q << sh)
+
+    bits = lambda x: (np.asarray(x, dtype=np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    assert np.all((np.abs(W1) < 256) | (W1 == 256))   # every weight is exact in bf16
+    h_ref, h_bits, y_ref = oracle.moe_ref(bits(A), bits(W1), bits(W2), offsets)
+    for e in range(G):
+        for r in range(offsets[e], offsets[e + 1]):
+            up = [sum(int(A[r, k]) * int(W1[e, k, 16 * (c // 8) + c % 8 + 8]) for k in range(K1)) for c in range(I)]
+            h = [64 * u for u in up]
+            hb = [bf16_int(v) for v in h]
+            y = [sum(hb[c] * int(W2[e, c, j]) for c in range(I)) for j in range(H)]
+            assert h_ref[r].tolist() == [float(v) for v in h]
+            assert oracle.decode(h_bits[r], "bf16").tolist() == [float(v) for v in hb]
+            assert y_ref[r].tolist() == [float(v) for v in y]
+    assert h_ref.shape == (rows, I) and y_ref.shape == (rows, H)
+    assert h_ref[0, 0] == 64 * 259 and oracle.decode(h_bits[0, :1], "bf16")[0] == 64 * 260
+
+
 def test_routing_pinned_counts():
     """The 64-expert routing reproduces the pinned seed-0 counts."""
     golden = np.loadtxt(datagen_golden("moe64_counts_seed0.txt"), dtype=np.int64)

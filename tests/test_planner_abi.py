@@ -210,9 +210,11 @@ def test_null_arguments_rejected():
 
 
 def test_e4m3_plan_rules():
-    """E4M3 plans: k-contiguous A and B only, 16-element alignment, no split,
-    no grouped form; gemm_run_scaled checks the plan type and the scale
-    pointers before anything is launched."""
+    """E4M3 plans: k-contiguous A and B only, 16-element alignment, no split
+    of K; the grouped form takes column-major expert weights and no
+    epilogue, and no gathered rows.  The run calls check the plan type, the
+    scale pointers and the gather before anything is launched (the fake
+    device addresses below are never touched: the calls return first)."""
     fake = 1 << 20
     ok = mg.gemm_plan(512, 512, 256, a_type="e4m3", d_type="bf16", a_layout="row", b_layout="col")
     assert "e4m3 NT->bf16 tile=256x256dtl" in ok.describe() and "bk=128" in ok.describe()
@@ -234,6 +236,11 @@ def test_e4m3_plan_rules():
     with pytest.raises(mg.MgemmError) as e:
         mg.grouped_gemm_run_scaled(g, fake, fake, fake, fake, fake, None, stream=0)
     assert e.value.status == mg.ERR_INVALID_ARG
+    # the E4M3 grouped kernel reads A in place: a gathered run is refused
+    with pytest.raises(mg.MgemmError) as e:
+        mg.grouped_gemm_run_gather(g, fake, fake, fake, fake, fake, x_rows=64, stream=0)
+    assert e.value.status == mg.ERR_UNSUPPORTED
+    assert "E4M3" in mg.lib.gemm_last_error_message().decode()
     fake = 1 << 20
     with pytest.raises(mg.MgemmError) as e:
         mg.gemm_run_scaled(ok, fake, fake, fake, None, fake, stream=0)
