@@ -4,11 +4,25 @@
 
 A step is one pass of the hot path over the workload's inputs, which are
 resident in HBM before timing starts: for a dense workload one gemm_run, for
-the MoE workload FC1 (SiLU-gated) plus FC2 over all experts.  W untimed
-steps (without --warmup: as many as fill a quarter second, so that the
-clocks have settled), then K steps bracketed by device synchronisation;
-events recorded on the stream the kernels are launched on give the average
-step duration.
+the MoE workload FC1 (SiLU-gated) plus FC2 over all experts.
+
+Timing protocol ("B200 的 2CTA 怎样调优" section 十: warm up separately,
+repeat, report the spread; hot and rotating input buffers):
+  * warm-up: at least W untimed steps, and at least WARMUP_SECONDS of them.
+    The engine clock idles near 150 MHz and takes tens of milliseconds of
+    load to reach its settled ~2.1 GHz, so five steps of 8192^3 (4 ms)
+    would time the clock's ramp, not the kernel; the line reports the W
+    asked for and the steps actually run;
+  * then exactly K steps, bracketed by device synchronisation, split into
+    (up to) ten windows by events recorded on the stream the kernels are
+    launched on: the value is K steps over the whole bracket, the windows
+    give median / min / max per step;
+  * the engine and memory clocks are sampled from sysfs while the timed
+    steps run, and the clock-adjusted MFMA peak is reported beside the
+    nominal 2.4 GHz one;
+  * workloads whose operands fit the 256 MB MALL (the decode shape) are also
+    timed over rotating copies of their buffers (more bytes than the MALL
+    holds), so every step reads its weights from HBM.
 
 Prints one JSON line: the metric (TFLOPS of algorithmic work, 2*M*N*K per
 GEMM, no padding), the roofline of the dominant kernel against MI355X's
@@ -115,18 +129,23 @@ def dev16(torch, bits, dt):
         torch.bfloat16 if dt == "bf16" else torch.float16)
 
 
-def dense_case(torch, mg, datagen, name):
+def dense_case(torch, mg, datagen, name, copies=1):
+    """The workload's step; with copies > 1 a list of steps, one per copy of
+    A, B and D (the rotating-buffer regime)."""
     cfg = datagen.DENSE[name]
     a, b = datagen.gemm_inputs(cfg, "random")
     A, B = dev16(torch, a, cfg.in_dtype), dev16(torch, b, cfg.in_dtype)
     out = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[cfg.out_dtype]
-    D = torch.empty((cfg.M, cfg.N), dtype=out, device="cuda")
     plan = mg.gemm_plan(cfg.M, cfg.N, cfg.K, cfg.in_dtype, d_type=cfg.out_dtype, a_layout=cfg.a_layout,
                         b_layout=cfg.b_layout)
     ws = mg.workspace_for(plan)      # split-K scratch, allocated before timing
+    sets = [(A, B, torch.empty((cfg.M, cfg.N), dtype=out, device="cuda"))]
+    for _ in range(copies - 1):
+        sets.append((A.clone(), B.clone(), torch.empty((cfg.M, cfg.N), dtype=out, device="cuda")))
 
-    def step():
-        mg.gemm_run(plan, A, B, D, workspace=ws)
+    def make(Ai, Bi, Di):
+        return lambda: mg.gemm_run(plan, Ai, Bi, Di, workspace=ws)
+    step = make(*sets[0]) if copies == 1 else [make(*x) for x in sets]
 
     esz = 4 if cfg.out_dtype == "f32" else 2
     inf = plan.info()
@@ -247,6 +266,7 @@ def cpu_baseline_e4m3(case, target_s):
     R2 = int(min(M, max(r2, (target_s - max(t1 - r1 * per_row, 0.0)) / per_row)))
     t = timed(R2)
     return {"value": 2.0 * R2 * N * K / t / 1e12, "unit": "TFLOPS", "cores": oracle.num_threads(), "kind": "oracle",
+            "cpu": cpu_model(),
             "sample": f"first {R2} of {M} output rows (all {N} columns, full K={K}), {t:.1f} s incl. operand decode"}
 
 
@@ -276,8 +296,20 @@ def cpu_baseline(case, target_s):
     t = time.perf_counter() - t0
     flops = 2.0 * R2 * cfg.N * cfg.K
     return {"value": flops / t / 1e12, "unit": "TFLOPS", "cores": oracle.num_threads(), "kind": "oracle",
+            "cpu": cpu_model(),
             "sample": f"first {R2} of {cfg.M} output rows (all {cfg.N} columns, full K={cfg.K}), "
                       f"{t:.1f} s incl. operand decode"}
+
+
+# Last-level (MALL) cache of MI355X: a workload whose bytes fit in it is
+# also timed over enough rotating copies of its buffers to exceed it.
+MALL_BYTES = 256 << 20
+
+
+def sub_line(info, t, tflops, peak, roof, pct_key="pct_of_peak"):
+    return {"config": info["config"], "value": round(tflops, 2), "unit": "TFLOPS", "ms_per_step": round(t["ms"], 5),
+            pct_key: round(100 * tflops / peak, 2), "windows": window_stats(t),
+            "clocks": clock_report(t, tflops, info["dtype"]), "roofline": roof}
 
 
 def main():
@@ -305,8 +337,22 @@ def main():
     else:
         step, info, case = dense_case(torch, mg, datagen, args.workload)
     print(f"# plan: {info['plan']}", file=sys.stderr, flush=True)
-    ms, warmup_done = time_steps(torch, step, args.steps, args.warmup)
-    roof, tflops, peak = roofline(info, ms)
+    t = time_steps(torch, step, args.steps, args.warmup)
+    roof, tflops, peak = roofline(info, t["ms"])
+    hot = None
+    if args.workload in datagen.DENSE and info["bytes"] < MALL_BYTES:
+        # every step's buffers fit the MALL: the line's value is the
+        # rotating regime (each step reads its own copy, from HBM), the hot
+        # one is reported beside it
+        del step
+        copies = -(-(MALL_BYTES * 5 // 4) // info["bytes"])
+        hot = sub_line(info, t, tflops, peak, roof)
+        hot["regime"] = "hot (one set of buffers, MALL-resident)"
+        step, info, _ = dense_case(torch, mg, datagen, args.workload, copies=copies)
+        info["config"] = dict(info["config"], buffers=f"rotating x{copies}")
+        print(f"# rotating over {copies} copies of A, B, D", file=sys.stderr, flush=True)
+        t = time_steps(torch, step, args.steps, args.warmup)
+        roof, tflops, peak = roofline(info, t["ms"])
     secondary = []
     e4m3_line = None
     if args.workload == DEFAULT_WORKLOAD and not args.no_secondary:
@@ -314,30 +360,32 @@ def main():
         del step
         step2, info2, _ = dense_case(torch, mg, datagen, "gemm4096_bf16")
         print(f"# plan: {info2['plan']}", file=sys.stderr, flush=True)
-        ms2, _ = time_steps(torch, step2, args.steps, args.warmup)
-        roof2, tflops2, peak2 = roofline(info2, ms2)
-        secondary.append({"config": info2["config"], "value": round(tflops2, 2), "unit": "TFLOPS",
-                          "ms_per_step": round(ms2, 5), "pct_of_peak": round(100 * tflops2 / peak2, 2),
-                          "roofline": roof2})
+        t2 = time_steps(torch, step2, args.steps, args.warmup)
+        roof2, tflops2, peak2 = roofline(info2, t2["ms"])
+        secondary.append(sub_line(info2, t2, tflops2, peak2, roof2))
         # the E4M3 product of the same size (per-tensor scales), priced
         # against the fp8 dense peak: reported beside, not the metric
         del step2
         step3, info3, _ = e4m3_case(torch, mg, datagen, "gemm8192_e4m3")
         print(f"# plan: {info3['plan']}", file=sys.stderr, flush=True)
-        ms3, _ = time_steps(torch, step3, args.steps, args.warmup)
-        roof3, tflops3, peak3 = roofline(info3, ms3)
-        e4m3_line = {"config": info3["config"], "value": round(tflops3, 2), "unit": "TFLOPS",
-                     "ms_per_step": round(ms3, 5), "pct_of_fp8_peak": round(100 * tflops3 / peak3, 2),
-                     "roofline": roof3}
+        t3 = time_steps(torch, step3, args.steps, args.warmup)
+        roof3, tflops3, peak3 = roofline(info3, t3["ms"])
+        e4m3_line = sub_line(info3, t3, tflops3, peak3, roof3, "pct_of_fp8_peak")
         del step3
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(case, args.cpu_seconds)
     line = {"metric": METRIC, "value": round(tflops, 2), "unit": "TFLOPS", "n_gpus": 1, "steps": args.steps,
-            "warmup": warmup_done, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
-            "vs_baseline": None, "dtype": info["dtype"], "data": "synthetic",
+            "warmup": t["warmup_asked"], "ms_per_step": round(t["ms"], 5), "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": info["dtype"], "data": "synthetic",
             "config": info["config"], "pct_of_peak": round(100 * tflops / peak, 2),
-            "roofline": roof, "cpu_baseline": cpu}
+            "roofline": roof, "cpu_baseline": cpu,
+            "warmup_run": {"steps": t["warmup_run"], "seconds": round(t["warmup_s"], 3),
+                           "rule": f"at least --warmup steps and at least {WARMUP_SECONDS} s"},
+            "windows": window_stats(t), "clocks": clock_report(t, tflops, info["dtype"]),
+            "versions": versions(torch)}
+    if hot:
+        line["hot"] = hot
     if secondary:
         line["also"] = secondary
     if e4m3_line:
@@ -345,43 +393,177 @@ def main():
     print(json.dumps(line), flush=True)
 
 
+def versions(torch):
+    v = {"torch": torch.__version__, "hip": getattr(torch.version, "hip", None)}
+    try:
+        with open("/opt/rocm/.info/version") as f:
+            v["rocm"] = f.read().strip()
+    except OSError:
+        pass
+    return v
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 # MI355X's clocks take tens of milliseconds of load to settle: 4096^3 runs
 # at ~121 us per step after 10 warmup steps and ~98 us after 400 (8192^3:
-# 793 against 768 us after 100).  Without --warmup the untimed steps
-# therefore fill at least this much time (and number at least 10).
+# 793 against 768 us after 100).  The untimed steps therefore fill at least
+# this much time, and number at least --warmup (default 10).
 WARMUP_SECONDS = 0.25
+WINDOWS = 10
+
+
+class ClockSampler:
+    """Engine (sclk) and memory (mclk) clocks read from the GPU's sysfs
+    performance-level files every ~2 ms in a background thread (the level
+    marked current); None where the files are not visible."""
+
+    def __init__(self):
+        self.card = self._find_card()
+        self.samples = []
+        self._stop = None
+        self._thread = None
+
+    @staticmethod
+    def _find_card():
+        import glob
+        cards = sorted(os.path.dirname(p) for p in glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+        if len(cards) == 1:
+            return cards[0]
+        try:   # several visible: the one on torch's device 0's PCI bus
+            import torch
+            bus = torch.cuda.get_device_properties(0).pci_bus_id
+            for c in cards:
+                slot = os.path.basename(os.path.realpath(c))   # e.g. 0000:75:00.0
+                if int(slot.split(":")[1], 16) == bus:
+                    return c
+        except Exception:
+            pass
+        return None
+
+    @staticmethod
+    def _current_mhz(path):
+        try:
+            with open(path) as f:
+                for line in f:
+                    if "*" in line:
+                        return float(line.split(":")[1].strip().split("Mhz")[0].strip("( )"))
+        except (OSError, ValueError, IndexError):
+            return None
+        return None
+
+    def read(self):
+        if not self.card:
+            return None, None
+        return (self._current_mhz(os.path.join(self.card, "pp_dpm_sclk")),
+                self._current_mhz(os.path.join(self.card, "pp_dpm_mclk")))
+
+    def start(self):
+        import threading
+        if not self.card:
+            return self
+        self.samples = []
+        self._stop = threading.Event()
+
+        def run():
+            while not self._stop.is_set():
+                sc, mc = self.read()
+                if sc is not None:
+                    self.samples.append((sc, mc))
+                self._stop.wait(0.002)
+        self._thread = threading.Thread(target=run, daemon=True)
+        self._thread.start()
+        return self
+
+    def stop(self):
+        if self._thread:
+            self._stop.set()
+            self._thread.join()
+        return self
+
+    def summary(self):
+        if not self.samples:
+            return None
+        sc = sorted(x[0] for x in self.samples)
+        mc = sorted(x[1] for x in self.samples if x[1] is not None)
+        return {"sclk_mhz": {"median": sc[len(sc) // 2], "min": sc[0], "max": sc[-1]},
+                "mclk_mhz": mc[len(mc) // 2] if mc else None, "samples": len(sc)}
 
 
 def time_steps(torch, step, steps, warmup):
-    """(average step time in ms, warmup steps run): events on the stream the
-    launches go to, bracketed by device synchronisation.  warmup None: run
-    untimed steps until WARMUP_SECONDS have passed (at least 10)."""
-    if warmup is None:
-        n, t_end = 0, time.perf_counter() + WARMUP_SECONDS
-        while n < 10 or time.perf_counter() < t_end:
-            step()
-            n += 1
-            if n % 10 == 0:
-                torch.cuda.synchronize()
-        warmup = n
-    else:
-        for _ in range(warmup):
-            step()
+    """Warm up, then time exactly `steps` steps (see the module docstring).
+    `step` is a callable, or a list of callables run in rotation (one per
+    copy of the buffers).  Returns a dict: ms (per step over the whole
+    bracket), windows (per-step ms of each window), warmup_asked,
+    warmup_run, warmup_s, clocks."""
+    fns = step if isinstance(step, (list, tuple)) else [step]
+    clk = ClockSampler()
+    idle = clk.read()
+    asked = 10 if warmup is None else warmup
+    n, t0 = 0, time.perf_counter()
+    t_end = t0 + WARMUP_SECONDS
+    while n < asked or time.perf_counter() < t_end:
+        fns[n % len(fns)]()
+        n += 1
+        if n % 10 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
+    warm_s = time.perf_counter() - t0
     stream = torch.cuda.current_stream()     # the stream every launch goes to
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
+    nwin = min(WINDOWS, steps)
+    bounds = [round(i * steps / nwin) for i in range(nwin + 1)]
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(nwin + 1)]
+    clk.start()
     t0 = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(steps):
-        step()
-    ev1.record(stream)
+    ev[0].record(stream)
+    for w in range(nwin):
+        for i in range(bounds[w], bounds[w + 1]):
+            fns[i % len(fns)]()
+        ev[w + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms = ev0.elapsed_time(ev1) / steps
-    print(f"# {steps} steps after {warmup} warmup steps: {ms * 1e3:.1f} us/step (events), "
-          f"wall {wall * 1e6 / steps:.1f} us/step", file=sys.stderr, flush=True)
-    return ms, warmup
+    clk.stop()
+    ms = ev[0].elapsed_time(ev[nwin]) / steps
+    win = [ev[w].elapsed_time(ev[w + 1]) / (bounds[w + 1] - bounds[w]) for w in range(nwin)]
+    clocks = clk.summary()
+    if clocks is not None:
+        clocks["idle_before_mhz"] = {"sclk": idle[0], "mclk": idle[1]}
+    ws = sorted(win)
+    print(f"# {steps} steps in {nwin} windows after {n} warmup steps ({warm_s:.2f} s): {ms * 1e3:.1f} us/step "
+          f"(events; windows median {ws[len(ws) // 2] * 1e3:.1f}, min {ws[0] * 1e3:.1f}, max {ws[-1] * 1e3:.1f}), "
+          f"wall {wall * 1e6 / steps:.1f} us/step; clocks {clocks}", file=sys.stderr, flush=True)
+    return {"ms": ms, "windows": win, "warmup_asked": asked, "warmup_run": n, "warmup_s": warm_s,
+            "clocks": clocks}
+
+
+def window_stats(t):
+    ws = sorted(t["windows"])
+    return {"n": len(ws), "median_ms": round(ws[len(ws) // 2], 5), "min_ms": round(ws[0], 5),
+            "max_ms": round(ws[-1], 5)}
+
+
+def clock_report(t, tflops, dtype):
+    """Clocks seen while the timed steps ran, and the MFMA peak at that
+    engine clock (the nominal peak scaled by sclk / 2400 MHz)."""
+    c = t["clocks"]
+    if not c:
+        return None
+    out = dict(c)
+    sclk = c["sclk_mhz"]["median"]
+    if sclk:
+        adj = PEAK_TFLOPS[dtype] * sclk / 2400.0
+        out["adjusted_peak_tflops"] = round(adj, 1)
+        out["frac_of_adjusted_peak"] = round(tflops / adj, 4)
+    return out
 
 
 def roofline(info, ms):
