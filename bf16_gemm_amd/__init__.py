@@ -74,7 +74,7 @@ EXPORTS = ["gemm_plan", "grouped_gemm_plan", "gemm_plan_workspace_size", "gemm_r
            "grouped_gemm_run", "grouped_gemm_run_scaled",
            "gemm_plan_describe", "gemm_plan_info", "gemm_plan_destroy", "gemm_status_string",
            "gemm_last_error_message", "mgemm_tile_budget", "mgemm_group_working_set", "mgemm_round_tokens",
-           "mgemm_version", "mgemm_moe_combine", "grouped_gemm_run_gather"]
+           "mgemm_version", "mgemm_moe_combine", "grouped_gemm_run_gather", "gemm_run_noalloc"]
 
 
 def _load():
@@ -91,6 +91,8 @@ def _load():
     lib.gemm_plan_workspace_size.restype = st
     lib.gemm_run.argtypes = [vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.gemm_run.restype = st
+    lib.gemm_run_noalloc.argtypes = [vp, vp, vp, vp, vp]
+    lib.gemm_run_noalloc.restype = st
     lib.gemm_run_scaled.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.gemm_run_scaled.restype = st
     lib.grouped_gemm_run_scaled.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
@@ -231,6 +233,17 @@ def gemm_run(plan: Plan, A, B, D, workspace=None, workspace_bytes: int = 0, stre
         workspace = workspace_for(plan, D.device)
     _check(lib.gemm_run(plan.handle, _ptr(A), _ptr(B), _ptr(D), _ptr(workspace), _nbytes(workspace, workspace_bytes),
                         _stream(stream)), "gemm_run")
+
+
+#: scratch bytes per device behind gemm_run_noalloc (MGEMM_NOALLOC_SCRATCH_BYTES)
+NOALLOC_SCRATCH_BYTES = 32 << 20
+
+
+def gemm_run_noalloc(plan: Plan, A, B, D, stream=None):
+    """Enqueue the planned product without a workspace: a plan's scratch
+    comes from the library's own per-device array (no allocation).  Calls
+    that overlap on one GPU race."""
+    _check(lib.gemm_run_noalloc(plan.handle, _ptr(A), _ptr(B), _ptr(D), _stream(stream)), "gemm_run_noalloc")
 
 
 def gemm_run_scaled(plan: Plan, A, B, D, scale_a, scale_b, stream=None):

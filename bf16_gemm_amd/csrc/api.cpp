@@ -41,7 +41,7 @@ static mgemm_status_t hip_status(hipError_t e, const char *what)
 
 using namespace mgemm;
 
-static mgemm_status_t dense_run(mgemm_plan_t plan, const void *A, const void *B, void *D, const float *scale_a,
+mgemm_status_t mgemm::dense_run(mgemm_plan_t plan, const void *A, const void *B, void *D, const float *scale_a,
                                 const float *scale_b, void *workspace, size_t workspace_bytes, mgemm_stream_t stream)
 {
     const mgemm_desc_t &d = plan->dense;

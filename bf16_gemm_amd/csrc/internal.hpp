@@ -79,6 +79,14 @@ struct GroupedLaunch {
 
 enum PlanKind { PLAN_DENSE = 1, PLAN_GROUPED = 2 };
 
+void set_error(const char *fmt, ...);
+
+// Enqueue a dense plan's kernels (gemm_run, gemm_run_scaled and
+// gemm_run_noalloc all end here); workspace: the plan's scratch, or null
+// when it needs none.
+mgemm_status_t dense_run(mgemm_plan_t plan, const void *A, const void *B, void *D, const float *scale_a,
+                         const float *scale_b, void *workspace, size_t workspace_bytes, mgemm_stream_t stream);
+
 }  // namespace mgemm
 
 struct mgemm_plan {

@@ -162,6 +162,23 @@ mgemm_status_t gemm_plan_workspace_size(mgemm_plan_t plan, size_t *bytes);
 mgemm_status_t gemm_run(mgemm_plan_t plan, const void *A, const void *B, void *D,
                         void *workspace, size_t workspace_bytes, mgemm_stream_t stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): gemm_run
+ * without a workspace argument.  The scratch a plan needs (the fp32 partial
+ * sums of a plan that splits K) comes from a device array the library
+ * holds, MGEMM_NOALLOC_SCRATCH_BYTES per device, kept by every GPU the
+ * library has run on until the process ends; its address is looked up on
+ * the first call with a device current.  The call allocates nothing.  A
+ * plan whose gemm_plan_workspace_size exceeds MGEMM_NOALLOC_SCRATCH_BYTES
+ * returns MGEMM_ERR_WORKSPACE and launches nothing.  Every call on one GPU
+ * shares that GPU's array and leaves its last contents there: calls that
+ * overlap on one GPU (on different streams, or from different threads)
+ * race and give undefined results; serialise them.  Otherwise the same
+ * semantics, results and errors as gemm_run (bit for bit the same output). */
+#define MGEMM_NOALLOC_SCRATCH_BYTES (32u << 20)
+mgemm_status_t gemm_run_noalloc(mgemm_plan_t plan, const void *A, const void *B, void *D,
+                                mgemm_stream_t stream);
+
 /* Enqueue D = (scale_a x scale_b) x (A x B) on `stream` for a plan with
  * E4M3 inputs, with one scale per tensor ("MegaMoE：Blackwell 与 Hopper 的融合
  * 算子解读", Hopper section 04: with per-tensor scales the dequantisation is

@@ -1,0 +1,82 @@
+"""gemm_run_noalloc (the dense run whose scratch is the library's own
+per-device array, for callers that cannot allocate) against gemm_run with a
+caller-owned workspace, through the C ABI.
+
+Both run the same kernels in the same order, so their outputs must be equal
+bit for bit; each is also held to the oracle (random inputs within the
+tolerance, integer inputs bit-exact).  Two calls in a row, the second with a
+smaller problem, so the second finds the first one's partial sums left in
+the array; and a plan without a split, which needs no scratch at all.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+
+import datagen
+import oracle
+from helpers import assert_bits_equal, assert_close, from_dev_bits, to_dev
+
+torch = pytest.importorskip("torch")
+mg = pytest.importorskip("bf16_gemm_amd")
+
+pytestmark = pytest.mark.gpu
+
+
+def log(*a):
+    print(*a, flush=True, file=sys.stderr)
+
+
+def run_both(M, N, K, bl, splits, variant, seed):
+    cfg = datagen.GemmConfig("noalloc", M, N, K, "bf16", "bf16", "row", bl, ("normal", 1.0), ("normal", 0.02),
+                             seed=seed, int_seed=seed + 1)
+    a, b = datagen.gemm_inputs(cfg, variant)
+    A, B = to_dev(a, "bf16"), to_dev(b, "bf16")
+    flags = mg.PLAN_SPLIT_K(splits) if splits else 0
+    ldd = -(-N // 8) * 8                  # 16-byte output rows
+    plan = mg.gemm_plan(M, N, K, "bf16", d_type="bf16", b_layout=bl, ldd=ldd, flags=flags)
+    log(f"case noalloc {M}x{N}x{K} B {bl} {variant}: {plan.describe()}")
+    ws_bytes = plan.workspace_size()
+    assert ws_bytes <= mg.NOALLOC_SCRATCH_BYTES
+    ws = torch.full((max(ws_bytes, 16),), 0xFF, dtype=torch.uint8, device="cuda")   # NaN bytes
+    D_ref = torch.full((M, ldd), float("nan"), dtype=torch.bfloat16, device="cuda")
+    D_new = torch.full((M, ldd), float("nan"), dtype=torch.bfloat16, device="cuda")
+    mg.gemm_run(plan, A, B, D_ref, workspace=ws)
+    mg.gemm_run_noalloc(plan, A, B, D_new)
+    torch.cuda.synchronize()
+    assert torch.isnan(D_new[:, N:].float()).all(), "padding columns written"
+    got_ref, got_new = from_dev_bits(D_ref[:, :N]), from_dev_bits(D_new[:, :N])
+    assert np.array_equal(got_new, got_ref), f"{plan.describe()}: gemm_run_noalloc differs from gemm_run"
+    ref = oracle.gemm_ref(a, b, "bf16", "bf16", "row", bl)
+    if variant == "int":
+        assert_bits_equal(got_new, ref, "bf16", plan.describe())
+    else:
+        assert_close(got_new, ref, K, "bf16", plan.describe())
+    return plan
+
+
+@pytest.mark.parametrize("variant", ["random", "int"])
+def test_noalloc_matches_gemm_run_two_calls_second_smaller(variant):
+    # first: the decode shape split in four (14.7 MB of partial sums)
+    p1 = run_both(128, 7168, 2048, "row", 4, variant, seed=71)
+    assert p1.workspace_size() == 4 * 128 * 7168 * 4
+    # second, smaller: ragged N (an edge column), column-major B, three ranges;
+    # the array still holds the first call's partial sums
+    p2 = run_both(40, 1002, 1024, "col", 3, variant, seed=72)
+    assert 0 < p2.workspace_size() < p1.workspace_size()
+
+
+def test_noalloc_without_split_needs_no_scratch():
+    p = run_both(300, 520, 392, "row", 1, "int", seed=73)
+    assert p.workspace_size() == 0
+
+
+def test_noalloc_rejects_plans_beyond_the_array():
+    plan = mg.gemm_plan(4096, 4096, 65536, "bf16", d_type="bf16", flags=mg.PLAN_SPLIT_K(8))
+    assert plan.workspace_size() > mg.NOALLOC_SCRATCH_BYTES
+    D = torch.zeros(16, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(mg.MgemmError) as e:
+        mg.gemm_run_noalloc(plan, D, D, D)
+    assert e.value.status == mg.ERR_WORKSPACE
+    assert (D == 0).all()
