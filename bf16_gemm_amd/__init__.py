@@ -26,6 +26,9 @@ PLAN_FORCE_TILE_128x128 = 0x2
 PLAN_FORCE_TILE_32x256 = 0x4
 PLAN_FORCE_TILE_64x256 = 0x8
 PLAN_FORCE_TILE_256x256_DTL = 0x10
+PLAN_FORCE_TILE_NARROW = 0x20
+PLAN_FORCE_TILE_NARROW64 = 0x40
+PLAN_FORCE_TILE_NARROW32 = 0x80
 PLAN_NO_XCD_REMAP = 0x100
 
 

@@ -11,9 +11,23 @@
 
 #include "internal.hpp"
 
+#include <atomic>
+
 namespace mgemm {
 
 static thread_local char g_err[512];
+
+// A tag per run for the split arrival counters: process-wide, never 0 or
+// ~0 (the values of a zeroed or 0xFF-filled workspace).
+static uint32_t next_run_tag()
+{
+    static std::atomic<uint32_t> counter{0};
+    uint32_t t;
+    do {
+        t = counter.fetch_add(1, std::memory_order_relaxed) + 1;
+    } while (t == 0 || t == 0xFFFFFFFFu);
+    return t;
+}
 
 void set_error(const char *fmt, ...)
 {
@@ -89,7 +103,23 @@ mgemm_status_t mgemm::dense_run(mgemm_plan_t plan, const void *A, const void *B,
     a.split_stride = 0;
     a.scale_a = scale_a;
     a.scale_b = scale_b;
-    if (split) {
+    if (is_narrow(plan->tile) && a.tiles > 0) {
+        // one launch: a split's last range adds the ranges' partials itself
+        DenseArgs w = a;
+        w.splits = plan->splits;
+        w.kchunk = plan->kchunk;
+        w.tiles = a.tiles * plan->splits;
+        w.ws = split ? (char *)workspace : nullptr;
+        w.slab_offset = plan->slab_offset;
+        w.tag = split ? next_run_tag() : 0;
+        DenseFn f = dense_fn(plan->tile, ak, bk, in, out);
+        if (!f) {
+            set_error("gemm_run: kernel missing for the planned variant");
+            return MGEMM_ERR_UNSUPPORTED;
+        }
+        if (mgemm_status_t st = hip_status(f(w, plan->grid, s), "gemm_run launch"))
+            return st;
+    } else if (split) {
         // every K range writes its fp32 partial tile into its own slab of
         // the workspace; the reduction adds the slabs into D
         DenseArgs w = a;
@@ -192,9 +222,9 @@ static mgemm_status_t grouped_run(mgemm_plan_t plan, const void *A, const void *
             return MGEMM_ERR_INVALID_ARG;
         }
         for (const GroupedLaunch &L : plan->launches) {
-            if (L.tile != TILE_32x256 && L.tile != TILE_256x256_DTL) {
+            if (L.tile != TILE_32x256 && L.tile != TILE_256x256_DTL && !is_narrow(L.tile)) {
                 set_error("grouped_gemm_run_gather: the planned tile %d does not take gathered rows (the default "
-                          "32x256 and direct-to-LDS 256x256 tiles do)", L.tile);
+                          "narrow, 32x256 and direct-to-LDS 256x256 tiles do)", L.tile);
                 return MGEMM_ERR_UNSUPPORTED;
             }
         }

@@ -23,8 +23,13 @@ enum TileId {
     TILE_32x256 = 2,
     TILE_64x256 = 3,
     TILE_256x256_DTL = 4,  // 256 x 256 with direct-to-LDS loads (k-contiguous A and B only)
-    NUM_TILES = 5
+    TILE_NARROW = 5,       // up to 128 tokens x 128 columns, token blocks sized at run time (row-major A)
+    TILE_NARROW64 = 6,     // the same, 64 columns
+    TILE_NARROW32 = 7,     // the same, 32 columns (two waves)
+    NUM_TILES = 8
 };
+
+inline bool is_narrow(int tile) { return tile == TILE_NARROW || tile == TILE_NARROW64 || tile == TILE_NARROW32; }
 
 struct TileShape {
     int bm, bn, wm, wn;
@@ -55,6 +60,12 @@ MGEMM_DECLARE_TU(64x256_bf16)
 MGEMM_DECLARE_TU(64x256_f16)
 MGEMM_DECLARE_TU(256x256dtl_bf16)
 MGEMM_DECLARE_TU(256x256dtl_f16)
+MGEMM_DECLARE_TU(narrow128_bf16)
+MGEMM_DECLARE_TU(narrow128_f16)
+MGEMM_DECLARE_TU(narrow64_bf16)
+MGEMM_DECLARE_TU(narrow64_f16)
+MGEMM_DECLARE_TU(narrow32_bf16)
+MGEMM_DECLARE_TU(narrow32_f16)
 #undef MGEMM_DECLARE_TU
 DenseFn dense_fn_256x256dtl_e4m3(bool ak, bool bk, int out);
 GroupedFn grouped_fn_256x256dtl_e4m3(bool bk, int out, int epi);
@@ -103,6 +114,7 @@ struct mgemm_plan {
     int xcd_remap;
     int splits;      // K ranges per output tile; > 1 writes fp32 partials to the workspace
     int kchunk;      // elements of K per range
+    int64_t slab_offset;  // narrow tile split: bytes of arrival counters before the partial slabs
     size_t workspace_bytes;
     bool zero_fill;  // K == 0
     bool noop;       // M == 0 or N == 0

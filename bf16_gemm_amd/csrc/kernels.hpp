@@ -6,6 +6,7 @@
 #include <stdint.h>
 
 #include "engine.hpp"
+#include "narrow.hpp"
 
 namespace mgemm {
 
@@ -24,6 +25,9 @@ struct DenseArgs {
     int64_t split_stride;  // elements of D between the partial results of consecutive ranges
     const float *scale_a = nullptr;  // E4M3 inputs: per-tensor scales (device, one float each; null = 1)
     const float *scale_b = nullptr;
+    char *ws = nullptr;               // narrow tile split over K: arrival counters, then partial slabs
+    int64_t slab_offset = 0;          // bytes from ws to the first slab
+    uint32_t tag = 0;                 // this run's tag for the arrival counters (never 0 or ~0)
 };
 
 struct GroupedArgs {
@@ -404,6 +408,157 @@ __global__ void __launch_bounds__(DtlTile4E4M3::NT) grouped_e4m3_kernel(GroupedA
         char *Dt = (char *)p.D + ((int64_t)m0 * p.ldd + n0) * esize;
         epilogue_staged<T, OUT, true>(tile, lds, Dt, p.ldd, m_valid, min(T::BN, p.N - n0),
                                       opaque((int)threadIdx.x), scale);
+        wait_vm<0>();
+    }
+}
+
+// Dense product on the few-token tile: output tile t / splits, K range
+// t % splits (consecutive tasks -- one XCD with the remap -- are the ranges
+// of one tile).  Unsplit, a task stores its tile.  Split, every range
+// writes its fp32 partial tile to its slab of the workspace, publishes it
+// (release fence, then an arrival on the tile's counter), and the range
+// that arrives last adds all ranges' partials in increasing range order
+// (its own from registers) and stores the tile: the reduction of "B200 的
+// 2CTA 怎样调优" (section 八: a K split pays for its reduction) inside the
+// same launch, with a result that does not depend on which range finishes
+// last.  No range waits for another, so the grid needs no co-residency.
+template <bool BKM, int IN, int OUT, int BN>
+__global__ void __launch_bounds__((NarrowTile<IN, BKM, BN>::NT)) narrow_dense_kernel(DenseArgs p)
+{
+    using T = NarrowTile<IN, BKM, BN>;
+    constexpr int SLAB = narrow_slab_bytes(BN);   // bytes of one partial tile
+    constexpr uint32_t BSTRIDE = T::NT * 16;       // bytes between its blocks
+    __shared__ __attribute__((aligned(16))) char lds[T::LDS_BYTES];
+    // the arrival count is passed to every wave through the ring's last slot:
+    // the next tile's prologue fills the other slots, and this one only
+    // after the next tile's first barrier, which every wave reaches after
+    // reading the count
+    uint32_t *arrived = (uint32_t *)(lds + (T::NST - 1) * T::SLOT);
+    T tile;
+    const int tid = threadIdx.x;
+    const int grid = gridDim.x;
+    const int L = logical_block(blockIdx.x, grid, p.xcd_remap);
+    const uint16_t *A = (const uint16_t *)p.A;
+    const uint16_t *B = (const uint16_t *)p.B;
+    constexpr int esize = out_size(OUT);
+    for (int t = L; t < p.tiles; t += grid) {
+        const int tile_id = t / p.splits;
+        const int r = t - tile_id * p.splits;
+        int mb, nb;
+        tile_coords(tile_id, p.tiles_m, p.tiles_n, p.group_m, mb, nb);
+        const int m0 = mb * T::BM, n0 = nb * T::BN;
+        const int m_valid = min(T::BM, p.M - m0);
+        const int ntb = (m_valid + 15) >> 4;     // tokens rounded up to 16
+        const int k0 = r * p.kchunk;
+        const int klen = min(p.kchunk, p.K - k0);
+        const uint16_t *At = A + (int64_t)m0 * p.lda + k0;
+        const uint16_t *Bt = BKM ? B + (int64_t)n0 * p.ldb + k0 : B + (int64_t)k0 * p.ldb + n0;
+        const OperandSrc sa = operand_src<true>(At, p.lda, m_valid, klen);
+        const OperandSrc sb = operand_src<BKM>(Bt, p.ldb, p.N - n0, klen);
+        tile.mainloop(lds, sa, p.lda, sb, p.ldb, klen, ntb, opaque(tid));
+        f32x4_t v[T::NTB][T::NB];
+        tile.values(v, ntb);
+        if (p.splits > 1) {
+            // the slabs of all tasks (tile-major), device-scope stores and loads
+            const __amdgpu_buffer_rsrc_t slabs =
+                make_rsrc(p.ws + p.slab_offset, (uint64_t)p.tiles * (uint64_t)SLAB);
+            uint64_t *counter = (uint64_t *)p.ws + tile_id;
+            const uint32_t mine = (uint32_t)t * (uint32_t)SLAB + (uint32_t)tid * 16u;
+#pragma unroll
+            for (int tb = 0; tb < T::NTB; ++tb) {
+                if (tb < ntb) {
+#pragma unroll
+                    for (int j = 0; j < T::NB; ++j)
+                        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v[tb][j]), slabs,
+                                                               mine + (uint32_t)(tb * T::NB + j) * BSTRIDE, 0,
+                                                               kDeviceScope);
+                }
+            }
+            wait_vm<0>();         // this range's partial has reached the shared level
+            __syncthreads();
+            if (tid == 0)
+                *arrived = split_arrive(counter, p.tag);
+            __syncthreads();
+            if (*arrived != (uint32_t)p.splits)
+                continue;         // another range arrives later and stores the tile
+            if (tid == 0)
+                split_reset(counter, p.tag);
+            // sum = P0 + P1 + ... in range order, this range's own partial
+            // from registers; one range's blocks are loaded together
+            const uint32_t first = (uint32_t)(t - r) * (uint32_t)SLAB + (uint32_t)tid * 16u;
+            f32x4_t sum[T::NTB][T::NB];
+            for (int rr = 0; rr < p.splits; ++rr) {
+                f32x4_t x[T::NTB][T::NB];
+                if (rr == r) {
+#pragma unroll
+                    for (int tb = 0; tb < T::NTB; ++tb)
+#pragma unroll
+                        for (int j = 0; j < T::NB; ++j)
+                            x[tb][j] = v[tb][j];
+                } else {
+                    const uint32_t base = first + (uint32_t)rr * (uint32_t)SLAB;
+#pragma unroll
+                    for (int tb = 0; tb < T::NTB; ++tb)
+#pragma unroll
+                        for (int j = 0; j < T::NB; ++j)
+                            x[tb][j] = tb < ntb ? __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                                                    slabs, base + (uint32_t)(tb * T::NB + j) * BSTRIDE,
+                                                                    0, kDeviceScope))
+                                                : f32x4_t{};
+                }
+#pragma unroll
+                for (int tb = 0; tb < T::NTB; ++tb)
+#pragma unroll
+                    for (int j = 0; j < T::NB; ++j)
+                        sum[tb][j] = rr == 0 ? x[tb][j] : sum[tb][j] + x[tb][j];
+            }
+#pragma unroll
+            for (int tb = 0; tb < T::NTB; ++tb)
+#pragma unroll
+                for (int j = 0; j < T::NB; ++j)
+                    v[tb][j] = sum[tb][j];
+        }
+        char *Dt = (char *)p.D + ((int64_t)m0 * p.ldd + n0) * esize;
+        narrow_store<EPI_NONE, OUT>(v, Dt, p.ldd, m_valid, min(T::BN, p.N - n0), ntb, tid);
+        wait_vm<0>();
+    }
+}
+
+// Grouped product on the few-token tile (experts with at most 128 rows):
+// task list in registers, each task one expert's rows against 128 of its
+// weight columns, its token blocks sized to the expert's row count.
+template <bool BKM, int IN, int OUT, int EPI, int BN>
+__global__ void __launch_bounds__((NarrowTile<IN, BKM, BN>::NT)) narrow_grouped_kernel(GroupedArgs p)
+{
+    using T = NarrowTile<IN, BKM, BN>;
+    __shared__ __attribute__((aligned(16))) char lds[T::LDS_BYTES];
+    const int tid = threadIdx.x;
+    WaveTasks wt;
+    wt.build(p, T::BM, tid & 63);
+    T tile;
+    const int grid = gridDim.x;
+    const int L = logical_block(blockIdx.x, grid, p.xcd_remap);
+    const uint16_t *B = (const uint16_t *)p.B;
+    constexpr int esize = out_size(OUT);
+    for (int t = L; t < wt.total; t += grid) {
+        int e, local, rows0, rows_e;
+        wt.find(t, e, local, rows0, rows_e);
+        const int tm = (rows_e + T::BM - 1) / T::BM;
+        const int mb = local % tm, nb = local / tm;
+        const int m0 = rows0 + mb * T::BM, n0 = nb * T::BN;
+        const int m_valid = min(T::BM, rows_e - mb * T::BM);
+        const int ntb = (m_valid + 15) >> 4;
+        const uint16_t *Be = B + (int64_t)e * p.stride_b;
+        const uint16_t *Bt = BKM ? Be + (int64_t)n0 * p.ldb : Be + n0;
+        RowGather ga;
+        const OperandSrc sa = grouped_a_src(p, m0, m_valid, ga);
+        const OperandSrc sb = operand_src<BKM>(Bt, p.ldb, p.N - n0, p.K);
+        tile.mainloop(lds, sa, p.lda, sb, p.ldb, p.K, ntb, opaque(tid), ga);
+        f32x4_t v[T::NTB][T::NB];
+        tile.values(v, ntb);
+        const int dcol0 = EPI == EPI_SILU_GATE ? n0 / 2 : n0;
+        char *Dt = (char *)p.D + ((int64_t)m0 * p.ldd + dcol0) * esize;
+        narrow_store<EPI, OUT>(v, Dt, p.ldd, m_valid, min(T::BN, p.N - n0), ntb, tid);
         wait_vm<0>();
     }
 }

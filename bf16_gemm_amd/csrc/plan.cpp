@@ -26,6 +26,9 @@ static const TileShape kTiles[NUM_TILES] = {
     /* 32x256     */ {32, 256, 1, 4, 2 * (32 + 256) * 128, 2, 0.55, true, false},
     /* 64x256     */ {64, 256, 1, 4, 2 * (64 + 256) * 128, 1, 0.70, true, false},
     /* 256x256dtl */ {256, 256, 2, 4, (3 + 2) * 256 * 128, 1, 1.00, false, true},
+    /* narrow     */ {128, 128, 1, 4, 5 * (128 * 128 + 64 * 256), 1, 0.50, true, true},
+    /* narrow64   */ {128, 64, 1, 4, 6 * (128 * 128 + 64 * 128), 1, 0.50, true, true},
+    /* narrow32   */ {128, 32, 1, 2, 7 * (128 * 128 + 64 * 64), 1, 0.50, true, true},
 };
 
 const TileShape &tile_shape(int tile) { return kTiles[tile]; }
@@ -45,11 +48,18 @@ static void dense_waves(int tile, bool bk, int &wm, int &wn, int &a_slots, int &
         a_slots = bk ? 2 : 3;
         b_slots = bk ? 3 : 2;
     }
+    if (tile == TILE_NARROW)
+        a_slots = b_slots = 5;
+    if (tile == TILE_NARROW64)
+        a_slots = b_slots = 6;
+    if (tile == TILE_NARROW32)
+        a_slots = b_slots = 7;
 }
 
 static const char *tile_name(int tile)
 {
-    static const char *n[NUM_TILES] = {"256x256", "128x128", "32x256", "64x256", "256x256dtl"};
+    static const char *n[NUM_TILES] = {"256x256", "128x128", "32x256", "64x256", "256x256dtl", "narrow128",
+                                       "narrow64", "narrow32"};
     return n[tile];
 }
 
@@ -64,6 +74,9 @@ DenseFn dense_fn(int tile, bool ak, bool bk, int in, int out)
     case TILE_32x256: return bf ? dense_fn_32x256_bf16(ak, bk, out) : dense_fn_32x256_f16(ak, bk, out);
     case TILE_64x256: return bf ? dense_fn_64x256_bf16(ak, bk, out) : dense_fn_64x256_f16(ak, bk, out);
     case TILE_256x256_DTL: return bf ? dense_fn_256x256dtl_bf16(ak, bk, out) : dense_fn_256x256dtl_f16(ak, bk, out);
+    case TILE_NARROW: return bf ? dense_fn_narrow128_bf16(ak, bk, out) : dense_fn_narrow128_f16(ak, bk, out);
+    case TILE_NARROW64: return bf ? dense_fn_narrow64_bf16(ak, bk, out) : dense_fn_narrow64_f16(ak, bk, out);
+    case TILE_NARROW32: return bf ? dense_fn_narrow32_bf16(ak, bk, out) : dense_fn_narrow32_f16(ak, bk, out);
     default: return nullptr;
     }
 }
@@ -80,6 +93,9 @@ GroupedFn grouped_fn(int tile, bool bk, int in, int out, int epi)
     case TILE_64x256: return bf ? grouped_fn_64x256_bf16(bk, out, epi) : grouped_fn_64x256_f16(bk, out, epi);
     case TILE_256x256_DTL:
         return bf ? grouped_fn_256x256dtl_bf16(bk, out, epi) : grouped_fn_256x256dtl_f16(bk, out, epi);
+    case TILE_NARROW: return bf ? grouped_fn_narrow128_bf16(bk, out, epi) : grouped_fn_narrow128_f16(bk, out, epi);
+    case TILE_NARROW64: return bf ? grouped_fn_narrow64_bf16(bk, out, epi) : grouped_fn_narrow64_f16(bk, out, epi);
+    case TILE_NARROW32: return bf ? grouped_fn_narrow32_bf16(bk, out, epi) : grouped_fn_narrow32_f16(bk, out, epi);
     default: return nullptr;
     }
 }
@@ -140,6 +156,28 @@ static double task_model_us(const TileShape &t, int64_t M, int64_t N, int64_t K,
     return us;
 }
 
+// Time model (microseconds) of a few-token plan: width `bn`, `splits` K
+// ranges.  Fitted to MI355X runs of the tile on decode-sized products
+// (16-128 tokens, N 2048-7168, K 2048-7168): ~2.5 us until the first K
+// step's operands have landed, then each task streams its token rows and
+// weight columns at ~45 GB/s per CU; a split then costs ~3 us of device-
+// scope round trips (partial stored, arrival, partials read) plus its
+// partial tiles moved at the same rate (every range writes one, the last
+// reads the others).  Tasks beyond one per CU run in further rounds.
+static double narrow_model_us(int64_t M, int64_t N, int64_t K, int bn, int splits, int cus)
+{
+    const double rate = 45e3;   // bytes per microsecond per CU
+    const int64_t tokens = std::min<int64_t>(mgemm_round_tokens(std::min<int64_t>(M, 128), 16), 128);
+    const int64_t tiles = cdiv(M, 128) * cdiv(N, bn);
+    const int64_t tasks = tiles * splits;
+    const double kr = (double)cdiv(K, splits);
+    const double task_bytes = kr * 2.0 * (double)(tokens + bn);
+    double us = 2.5 + (double)cdiv(tasks, cus) * task_bytes / rate;
+    if (splits > 1)
+        us += 3.0 + (double)splits * (double)(tokens * bn * 4) / rate;
+    return us;
+}
+
 static bool is_in_type(mgemm_dtype_t t) { return t == MGEMM_F16 || t == MGEMM_BF16 || t == MGEMM_E4M3; }
 static const char *in_name(mgemm_dtype_t t) { return t == MGEMM_BF16 ? "bf16" : (t == MGEMM_E4M3 ? "e4m3" : "f16"); }
 static bool is_out_type(mgemm_dtype_t t) { return t == MGEMM_F16 || t == MGEMM_BF16 || t == MGEMM_F32; }
@@ -172,6 +210,9 @@ static int forced_tile(uint32_t flags)
     if (flags & MGEMM_PLAN_FORCE_TILE_32x256) return TILE_32x256;
     if (flags & MGEMM_PLAN_FORCE_TILE_64x256) return TILE_64x256;
     if (flags & MGEMM_PLAN_FORCE_TILE_256x256_DTL) return TILE_256x256_DTL;
+    if (flags & MGEMM_PLAN_FORCE_TILE_NARROW) return TILE_NARROW;
+    if (flags & MGEMM_PLAN_FORCE_TILE_NARROW64) return TILE_NARROW64;
+    if (flags & MGEMM_PLAN_FORCE_TILE_NARROW32) return TILE_NARROW32;
     return -1;
 }
 
@@ -256,6 +297,35 @@ static mgemm_status_t plan_dense(const mgemm_desc_t *d, uint32_t flags, mgemm_pl
         set_error("no kernel compiled for this layout/dtype combination");
         return MGEMM_ERR_UNSUPPORTED;
     }
+    // Few tokens (M up to one narrow tile): the tokens go on the MFMA's narrow
+    // side and the tile computes only their 16-row blocks ("MegaMoE", Blackwell
+    // section 04: dynamic N = valid tokens rounded up to 16).
+    const int64_t n_main_all = d->N & ~(int64_t)3;
+    const bool narrow_rule = !e4m3 && forced_tile(flags) < 0 && d->M <= kTiles[TILE_NARROW].bm && n_main_all > 0 &&
+                             dense_fn(TILE_NARROW, ak, bk, in, out) != nullptr;
+    int narrow_splits = 0;
+    if (narrow_rule) {
+        // width and K split by the time model: 128 or 64 columns (32 is
+        // left to the FORCE flag: two waves, measured slower), every split
+        // count whose tasks fit one round of CUs
+        const int64_t ks = std::max<int64_t>(cdiv(d->K, kBK), 1);
+        double best = 0;
+        for (int t : {TILE_NARROW, TILE_NARROW64}) {
+            if (!dense_fn(t, ak, bk, in, out))
+                continue;
+            const int64_t tl = cdiv(d->M, 128) * cdiv(n_main_all, kTiles[t].bn);
+            for (int sp = 1; sp <= 16; ++sp) {
+                if (sp > 1 && (tl * sp > p->num_cus || cdiv(ks, sp) < 2))
+                    break;
+                const double c = narrow_model_us(d->M, n_main_all, d->K, kTiles[t].bn, sp, p->num_cus);
+                if (narrow_splits == 0 || c < best) {
+                    best = c;
+                    tile = t;
+                    narrow_splits = sp;
+                }
+            }
+        }
+    }
     // the 256 x 256 tile with both operands k-contiguous runs on the
     // direct-to-LDS engine (eight waves, no staging registers)
     if (tile == TILE_256x256 && forced_tile(flags) < 0 && dense_fn(TILE_256x256_DTL, ak, bk, in, out))
@@ -270,6 +340,14 @@ static mgemm_status_t plan_dense(const mgemm_desc_t *d, uint32_t flags, mgemm_pl
     int splits = 1;
     if (forced_splits > 0) {
         splits = (int)std::min<int64_t>(forced_splits, std::max<int64_t>(ksteps, 1));
+    } else if (narrow_splits > 0) {
+        splits = narrow_splits;   // the time model's choice (each range streams its own part of the weights)
+    } else if (is_narrow(tile)) {
+        // forced width: split K so that the tasks fill the CUs; the last
+        // range of a tile adds the others' partials in the same launch
+        const int64_t tl = cdiv(d->M, kTiles[tile].bm) * cdiv(n_main, kTiles[tile].bn);
+        if (tl * 2 <= p->num_cus && ksteps >= 8)
+            splits = (int)std::max<int64_t>(1, std::min<int64_t>({(int64_t)p->num_cus / tl, ksteps / 4, 16}));
     } else if (!e4m3 && forced_tile(flags) < 0 && n_main > 0 && d->M > 0) {
         // Split K when the chosen tiles leave most compute units idle: the
         // tile and range count with the lowest modelled time wins if it beats
@@ -308,6 +386,18 @@ static mgemm_status_t plan_dense(const mgemm_desc_t *d, uint32_t flags, mgemm_pl
         return MGEMM_ERR_UNSUPPORTED;
     }
     p->workspace_bytes = p->splits > 1 ? (size_t)p->splits * (size_t)d->M * (size_t)n_main * 4u : 0;
+    p->slab_offset = 0;
+    if (is_narrow(tile) && p->splits > 1) {
+        // counters, then one partial slab per (tile, range)
+        p->slab_offset = narrow_counter_bytes(p->tiles);
+        const int64_t slabs = (int64_t)p->tiles * p->splits * narrow_slab_bytes(ts.bn);
+        if (slabs >= ((int64_t)1 << 31)) {
+            set_error("the K split needs %lld bytes of partial tiles, more than the kernel addresses (2^31); use "
+                      "fewer K ranges", (long long)slabs);
+            return MGEMM_ERR_UNSUPPORTED;
+        }
+        p->workspace_bytes = (size_t)p->slab_offset + (size_t)slabs;
+    }
     const int64_t tasks = p->tiles * p->splits;
     const int64_t slots = (int64_t)p->num_cus * ts.occupancy;
     p->grid = (int)std::max<int64_t>(1, std::min<int64_t>(tasks, slots));
@@ -324,13 +414,17 @@ static mgemm_status_t plan_dense(const mgemm_desc_t *d, uint32_t flags, mgemm_pl
         snprintf(stages, sizeof stages, "%d", a_slots);
     else
         snprintf(stages, sizeof stages, "%da/%db", a_slots, b_slots);
-    char buf[256];
+    char tokens[48] = "";
+    if (is_narrow(tile))
+        snprintf(tokens, sizeof tokens, " tokens=%lld",
+                 (long long)mgemm_round_tokens(std::min<int64_t>(d->M, kTiles[TILE_NARROW].bm), 16));
+    char buf[320];
     snprintf(buf, sizeof buf,
-             "dense M=%lld N=%lld K=%lld %s%s->%s tile=%s waves=%dx%d bk=%d stages=%s tiles=%lld splits=%d "
+             "dense M=%lld N=%lld K=%lld %s%s->%s tile=%s%s waves=%dx%d bk=%d stages=%s tiles=%lld splits=%d "
              "grid=%d group_m=%d xcd_remap=%d edge_cols=%lld",
              (long long)d->M, (long long)d->N, (long long)d->K, in_name(d->a_type),
              ak ? (bk ? " NT" : " NN") : (bk ? " TT" : " TN"),
-             d->d_type == MGEMM_F32 ? "f32" : (d->d_type == MGEMM_BF16 ? "bf16" : "f16"), tile_name(tile), wm, wn,
+             d->d_type == MGEMM_F32 ? "f32" : (d->d_type == MGEMM_BF16 ? "bf16" : "f16"), tile_name(tile), tokens, wm, wn,
              e4m3 ? 128 : 64, stages, (long long)p->tiles, p->splits, p->grid, p->group_m, p->xcd_remap, (long long)(d->N - n_main));
     p->description = buf;
     return MGEMM_OK;
@@ -407,7 +501,7 @@ static mgemm_status_t plan_grouped(const mgemm_grouped_desc_t *d, uint32_t flags
     // layer: 3.32 ms against 3.61 ms with 32/64/128-row classes; boundaries
     // at 97 or 193 rows and a third 128x128 class were slower).
     struct B { int tile, lo, hi; };
-    B buckets[2] = {{TILE_32x256, 1, 129}, {TILE_256x256_DTL, 129, 1 << 30}};
+    B buckets[2] = {{TILE_NARROW, 1, 129}, {TILE_256x256_DTL, 129, 1 << 30}};
     int nb = 2;
     const int ft = e4m3 ? TILE_256x256_DTL : forced_tile(flags);
     if (ft >= 0) {
@@ -555,6 +649,8 @@ extern "C" mgemm_status_t gemm_plan_info(mgemm_plan_t plan, mgemm_plan_info_t *i
     info->waves_m = ts.wm;
     info->waves_n = ts.wn;
     info->stages = plan->tile == TILE_256x256_DTL ? 3 : 2;   // the deeper ring's slots
+    if (is_narrow(plan->tile))
+        info->stages = ts.lds_bytes / ((ts.bm + ts.bn) * 128);   // 128 token rows and 64 k x BN weights per slot
     if (plan->kind == PLAN_DENSE) {
         int a_slots, b_slots;
         dense_waves(plan->tile, plan->dense.b_layout == MGEMM_COL_MAJOR, info->waves_m, info->waves_n, a_slots,

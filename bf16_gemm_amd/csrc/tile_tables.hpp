@@ -134,6 +134,43 @@ GroupedFn grouped_dtl_table(bool bk, int out, int epi)
 #undef MG_G
 }
 
+// The few-token tile (BN columns): row-major (k-contiguous) A, B either way.
+template <bool BK, int IN, int OUT, int BN>
+hipError_t launch_dense_narrow(const DenseArgs &a, int grid, hipStream_t s)
+{
+    hipLaunchKernelGGL((narrow_dense_kernel<BK, IN, OUT, BN>), dim3(grid), dim3(NarrowTile<IN, BK, BN>::NT), 0, s, a);
+    return hipGetLastError();
+}
+template <int IN, int BN>
+DenseFn dense_narrow_table(bool ak, bool bk, int out)
+{
+    if (!ak || (out != OUT_F32 && out != same16<IN>()))
+        return nullptr;
+    if (bk)
+        return out == OUT_F32 ? launch_dense_narrow<true, IN, OUT_F32, BN> : launch_dense_narrow<true, IN, same16<IN>(), BN>;
+    return out == OUT_F32 ? launch_dense_narrow<false, IN, OUT_F32, BN> : launch_dense_narrow<false, IN, same16<IN>(), BN>;
+}
+template <bool BK, int IN, int OUT, int EPI, int BN>
+hipError_t launch_grouped_narrow(const GroupedArgs &a, int grid, hipStream_t s)
+{
+    hipLaunchKernelGGL((narrow_grouped_kernel<BK, IN, OUT, EPI, BN>), dim3(grid), dim3(NarrowTile<IN, BK, BN>::NT), 0, s,
+                       a);
+    return hipGetLastError();
+}
+template <int IN, int BN>
+GroupedFn grouped_narrow_table(bool bk, int out, int epi)
+{
+    if (out != OUT_F32 && out != same16<IN>())
+        return nullptr;
+    const bool f32 = out == OUT_F32;
+#define MG_G(BKV, OUTV) (epi == EPI_NONE ? launch_grouped_narrow<BKV, IN, OUTV, EPI_NONE, BN> \
+                                         : launch_grouped_narrow<BKV, IN, OUTV, EPI_SILU_GATE, BN>)
+    if (bk)
+        return f32 ? MG_G(true, OUT_F32) : MG_G(true, same16<IN>());
+    return f32 ? MG_G(false, OUT_F32) : MG_G(false, same16<IN>());
+#undef MG_G
+}
+
 template <int BM, int BN, int WM, int WN, int IN>
 GroupedFn grouped_table(bool bk, int out, int epi)
 {

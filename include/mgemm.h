@@ -130,6 +130,15 @@ typedef struct {
  * rows or more.  In both, MGEMM_PLAN_FORCE_TILE_256x256 selects the
  * register-staged 256x256 engine instead. */
 #define MGEMM_PLAN_FORCE_TILE_256x256_DTL 0x10u
+/* The few-token tile: up to 128 rows of A (tokens) x 128 columns, each
+ * tile computing only its valid tokens rounded up to 16 (row-major A only,
+ * else UNSUPPORTED).  The planner uses it for dense plans with M <= 128 and
+ * for the grouped experts of 1..128 rows. */
+#define MGEMM_PLAN_FORCE_TILE_NARROW  0x20u
+/* The same tile 64 and 32 columns wide (more tiles for the same N, so a
+ * decode-sized product fills the CUs with fewer or no K splits). */
+#define MGEMM_PLAN_FORCE_TILE_NARROW64 0x40u
+#define MGEMM_PLAN_FORCE_TILE_NARROW32 0x80u
 #define MGEMM_PLAN_NO_XCD_REMAP       0x100u /* plain tile order        */
 /* Dense plans: fix the number of K ranges per output tile (1..64; 1 turns
  * splitting off).  Without it the planner splits K only when the output

@@ -24,11 +24,11 @@ pytestmark = pytest.mark.gpu
 
 TILES = {"auto": 0, "256": mg.PLAN_FORCE_TILE_256x256, "128": mg.PLAN_FORCE_TILE_128x128,
          "32n": mg.PLAN_FORCE_TILE_32x256, "64n": mg.PLAN_FORCE_TILE_64x256,
-         "256d": mg.PLAN_FORCE_TILE_256x256_DTL}
+         "256d": mg.PLAN_FORCE_TILE_256x256_DTL, "nrw": mg.PLAN_FORCE_TILE_NARROW}
 
 
 def tile_skip(tile, al, bl):
-    if tile in ("32n", "64n") and al == "col":
+    if tile in ("32n", "64n", "nrw") and al == "col":
         pytest.skip("narrow-M tiles take a k-contiguous A only")
     if tile == "256d" and al != "row":
         pytest.skip("the direct-to-LDS tile takes a row-major (k-contiguous) A only")
@@ -88,7 +88,7 @@ LAYOUTS = [("row", "row"), ("row", "col"), ("col", "row"), ("col", "col")]
 
 @pytest.mark.parametrize("in_t,out_t", COMBOS)
 @pytest.mark.parametrize("al,bl", LAYOUTS)
-@pytest.mark.parametrize("tile", ["256", "128", "32n", "64n", "256d"])
+@pytest.mark.parametrize("tile", ["256", "128", "32n", "64n", "256d", "nrw"])
 def test_ragged_random_and_integer(in_t, out_t, al, bl, tile):
     tile_skip(tile, al, bl)
     M, N, K = 300, 520, 200   # several tiles, ragged in M, N and K
@@ -201,10 +201,12 @@ def test_run_errors():
 
 @pytest.mark.parametrize("in_t,out_t", [("bf16", "bf16"), ("f16", "f32")])
 @pytest.mark.parametrize("al,bl", LAYOUTS)
-@pytest.mark.parametrize("tile", ["256", "128", "32n", "64n", "256d"])
+@pytest.mark.parametrize("tile", ["256", "128", "32n", "64n", "256d", "nrw"])
 def test_split_k_random_and_integer(in_t, out_t, al, bl, tile):
     """K split into ranges whose fp32 partial tiles are added by the
-    reduction: ragged M, N (two edge columns) and K (a short last step)."""
+    reduction (a second kernel; on the few-token tile, the last range in
+    the same launch, with two m tiles of it here): ragged M, N (two edge
+    columns) and K (a short last step); the workspace starts full of 0xFF."""
     tile_skip(tile, al, bl)
     M, N, K = 150, 302, 1000
     cfg = datagen.GemmConfig("t", M, N, K, in_t, out_t, al, bl, ("uniform", 1.0), ("normal", 1.0), seed=17,
@@ -223,9 +225,10 @@ def test_split_k_random_and_integer(in_t, out_t, al, bl, tile):
 
 def test_split_k_workspace_checked_before_launch():
     log("case split-K workspace errors")
-    plan = mg.gemm_plan(64, 256, 1024, "bf16", d_type="bf16", flags=mg.PLAN_SPLIT_K(4))
+    plan = mg.gemm_plan(64, 256, 1024, "bf16", d_type="bf16", flags=mg.PLAN_SPLIT_K(4) | mg.PLAN_FORCE_TILE_NARROW)
     need = plan.workspace_size()
-    assert need == 4 * 64 * 256 * 4
+    # few-token tile: 2 output tiles (counters padded to 256 B), 4 slabs each
+    assert "narrow128" in plan.describe() and need == 256 + 2 * 4 * 65536
     A = torch.zeros((64, 1024), dtype=torch.bfloat16, device="cuda")
     B = torch.zeros((1024, 256), dtype=torch.bfloat16, device="cuda")
     D = torch.full((64, 256), -1.0, dtype=torch.bfloat16, device="cuda")
@@ -260,7 +263,7 @@ def embed(x: np.ndarray, cols: int, fill: int) -> np.ndarray:
 
 
 @pytest.mark.parametrize("al,bl", LAYOUTS)
-@pytest.mark.parametrize("tile", ["auto", "256", "128", "32n", "64n", "256d"])
+@pytest.mark.parametrize("tile", ["auto", "256", "128", "32n", "64n", "256d", "nrw"])
 def test_wide_leading_dimensions(tile, al, bl):
     """Leading dimensions well past the matrix (lda = K+24 etc., in elements
     of the stored rows), the slack holding NaN bit patterns: any read of it

@@ -62,7 +62,7 @@ BUCKET_COUNTS = [0, 1, 5, 31, 32, 33, 64, 65, 100, 128, 129, 200, 256, 257, 300,
 
 GROUPED_TILES = {"auto": 0, "256": mg.PLAN_FORCE_TILE_256x256, "128": mg.PLAN_FORCE_TILE_128x128,
                  "32n": mg.PLAN_FORCE_TILE_32x256, "64n": mg.PLAN_FORCE_TILE_64x256,
-                 "256d": mg.PLAN_FORCE_TILE_256x256_DTL}
+                 "256d": mg.PLAN_FORCE_TILE_256x256_DTL, "nrw": mg.PLAN_FORCE_TILE_NARROW}
 
 
 @pytest.mark.parametrize("tile", list(GROUPED_TILES))
@@ -141,7 +141,7 @@ def test_grouped_256_experts(tile):
     assert_bits_equal(from_dev_bits(D[:rows]), ref, "bf16", plan.describe())
 
 
-@pytest.mark.parametrize("tile", ["auto", "256"])
+@pytest.mark.parametrize("tile", ["auto", "256", "nrw"])
 @pytest.mark.parametrize("variant", ["random", "int"])
 def test_grouped_silu_gate_small_moe(variant, tile):
     """FC1 with the SiLU gate and FC2, planner buckets (large experts on the

@@ -34,7 +34,7 @@ def test_header_constants_match_binding():
                                "MGEMM_ERR_NO_MEMORY", "MGEMM_ERR_HIP")] == [mg.OK, mg.ERR_INVALID_ARG,
                                                                             mg.ERR_UNSUPPORTED, mg.ERR_WORKSPACE,
                                                                             mg.ERR_NO_MEMORY, mg.ERR_HIP]
-    assert len(flags) == 6
+    assert len(flags) == 9
     for name, value in flags.items():
         assert getattr(mg, name[len("MGEMM_"):]) == value, name
     assert "((((uint32_t)(n)) & 0xFFu) << 16)" in text and mg.PLAN_SPLIT_K(5) == 5 << 16
@@ -96,15 +96,25 @@ def test_plan_choices_for_workloads():
     assert (i.block_m, i.block_n, i.block_k) == (256, 256, 64)
     assert i.tiles == 1024 and i.coverage == 1.0 and i.lds_bytes <= 160 * 1024
     assert i.grid == min(1024, i.num_cus)
-    # the decode shape: 128 rows cannot fill the chip with output tiles, so
-    # K is split (each range a task) instead of narrowing the tile further
+    # the decode shape: 128 tokens on the few-token tile; the planner's time
+    # model takes 64 columns and two K ranges (112 tiles x 2 = 224 tasks)
     p = mg.gemm_plan(128, 7168, 2048, "bf16", d_type="bf16")
     i = p.info()
-    assert i.block_m <= 128 and i.splits > 1 and i.tiles * i.splits <= 2 * i.num_cus, p.describe()
+    assert "tile=narrow64 tokens=128" in p.describe() and (i.block_m, i.block_n) == (128, 64), p.describe()
+    assert i.splits == 2 and i.tiles == 112 and i.grid == 224 and i.stages == 6, p.describe()
     p = mg.gemm_plan(128, 7168, 2048, "bf16", d_type="bf16", flags=mg.PLAN_SPLIT_K(1))
-    assert p.info().block_m <= 64 and p.info().splits == 1, p.describe()   # narrow-M tile when unsplit
+    assert "narrow" in p.describe() and p.info().splits == 1 and p.workspace_size() == 0, p.describe()
+    # forced widths: 128 columns (five slots), 32 columns (two waves, seven slots)
+    p = mg.gemm_plan(128, 7168, 2048, "bf16", d_type="bf16", flags=mg.PLAN_FORCE_TILE_NARROW)
+    assert "tile=narrow128" in p.describe() and p.info().stages == 5 and p.info().splits == 4, p.describe()
+    p = mg.gemm_plan(128, 7168, 2048, "bf16", d_type="bf16", flags=mg.PLAN_FORCE_TILE_NARROW32)
+    assert "tile=narrow32" in p.describe() and "waves=1x2" in p.describe() and p.info().stages == 7
+    # the token width is the row count rounded up to 16 (mgemm_round_tokens)
+    for M, w in [(1, 16), (16, 16), (17, 32), (100, 112), (128, 128)]:
+        assert f"tokens={w} " in mg.gemm_plan(M, 4096, 1024, "bf16", d_type="bf16").describe()
+    assert "narrow" not in mg.gemm_plan(129, 4096, 1024, "bf16", d_type="bf16").describe()
     p = mg.grouped_gemm_plan(64, 32768, 4096, 7168, epilogue=mg.EPI_SILU_GATE_I8)
-    assert "32x256" in p.describe() and "256x256" in p.describe()
+    assert "[1,129)->narrow128" in p.describe() and "[129,inf)->256x256dtl" in p.describe()
 
 
 def test_split_k_plans():
@@ -112,13 +122,19 @@ def test_split_k_plans():
     for (M, N, K) in [(8192, 8192, 8192), (4096, 4096, 4096), (16384, 2048, 7168), (512, 512, 512)]:
         p = mg.gemm_plan(M, N, K, "bf16", d_type="bf16")
         assert p.info().splits == 1 and p.workspace_size() == 0 and "splits=1" in p.describe(), p.describe()
-    # a split plan needs splits partial slabs of M x (N rounded down to 4) fp32
+    # a split plan on the few-token tile needs one 8-byte arrival counter per
+    # output tile (rounded up to 256 bytes), then a 64 KiB partial slab per
+    # (tile, range)
+    # (128 x block_n x 4 bytes)
     p = mg.gemm_plan(128, 7170, 2048, "bf16", d_type="bf16", ldb=7176, ldd=7176)
     i = p.info()
-    assert i.splits > 1 and f"splits={i.splits}" in p.describe()
-    assert p.workspace_size() == i.splits * 128 * 7168 * 4
+    assert i.splits > 1 and f"splits={i.splits}" in p.describe() and i.tiles == 112
+    assert p.workspace_size() == 1024 + 112 * i.splits * 128 * 64 * 4
     # forced counts: K = 2048 is 32 steps; 3 ranges of 11 steps
-    p = mg.gemm_plan(128, 7168, 2048, "bf16", d_type="bf16", flags=mg.PLAN_SPLIT_K(3))
+    p = mg.gemm_plan(128, 7168, 2048, "bf16", d_type="bf16", flags=mg.PLAN_SPLIT_K(3) | mg.PLAN_FORCE_TILE_NARROW)
+    assert p.info().splits == 3 and p.workspace_size() == 512 + 56 * 3 * 65536
+    # other tiles split with fp32 slabs of M x (N rounded down to 4), added by a second kernel
+    p = mg.gemm_plan(128, 7168, 2048, "bf16", d_type="bf16", flags=mg.PLAN_SPLIT_K(3) | mg.PLAN_FORCE_TILE_128x128)
     assert p.info().splits == 3 and p.workspace_size() == 3 * 128 * 7168 * 4
     p = mg.gemm_plan(64, 64, 128, "bf16", d_type="f32", flags=mg.PLAN_SPLIT_K(16))
     assert p.info().splits == 2   # never more ranges than K steps
@@ -158,7 +174,11 @@ def test_direct_to_lds_tile_choice():
     # grouped: the large-expert bucket runs on the direct-to-LDS tile (task
     # list in registers); forcing the 256x256 tile keeps the register engine
     g = mg.grouped_gemm_plan(64, 32768, 4096, 7168)
-    assert "[129,inf)->256x256dtl" in g.describe() and "[1,129)->32x256" in g.describe()
+    assert "[129,inf)->256x256dtl" in g.describe() and "[1,129)->narrow128" in g.describe()
+    # the few-token tile takes a row-major A only
+    with pytest.raises(mg.MgemmError) as e:
+        mg.gemm_plan(64, 512, 512, "bf16", a_layout="col", flags=mg.PLAN_FORCE_TILE_NARROW)
+    assert e.value.status == mg.ERR_UNSUPPORTED
     for bl in ("row", "col"):
         g = mg.grouped_gemm_plan(4, 64, 256, 128, b_layout=bl, flags=mg.PLAN_FORCE_TILE_256x256_DTL)
         assert "->256x256dtl" in g.describe()

@@ -28,12 +28,12 @@ def log(*a):
     print(*a, flush=True, file=sys.stderr)
 
 
-def run_both(M, N, K, bl, splits, variant, seed):
+def run_both(M, N, K, bl, splits, variant, seed, tile_flags=0):
     cfg = datagen.GemmConfig("noalloc", M, N, K, "bf16", "bf16", "row", bl, ("normal", 1.0), ("normal", 0.02),
                              seed=seed, int_seed=seed + 1)
     a, b = datagen.gemm_inputs(cfg, variant)
     A, B = to_dev(a, "bf16"), to_dev(b, "bf16")
-    flags = mg.PLAN_SPLIT_K(splits) if splits else 0
+    flags = (mg.PLAN_SPLIT_K(splits) if splits else 0) | tile_flags
     ldd = -(-N // 8) * 8                  # 16-byte output rows
     plan = mg.gemm_plan(M, N, K, "bf16", d_type="bf16", b_layout=bl, ldd=ldd, flags=flags)
     log(f"case noalloc {M}x{N}x{K} B {bl} {variant}: {plan.describe()}")
@@ -58,13 +58,17 @@ def run_both(M, N, K, bl, splits, variant, seed):
 
 @pytest.mark.parametrize("variant", ["random", "int"])
 def test_noalloc_matches_gemm_run_two_calls_second_smaller(variant):
-    # first: the decode shape split in four (14.7 MB of partial sums)
-    p1 = run_both(128, 7168, 2048, "row", 4, variant, seed=71)
-    assert p1.workspace_size() == 4 * 128 * 7168 * 4
-    # second, smaller: ragged N (an edge column), column-major B, three ranges;
-    # the array still holds the first call's partial sums
+    # first: the decode shape on the few-token tile (128 columns) split in
+    # four: 56 arrival counters and 224 partial slabs of 64 KiB, 14.7 MB
+    p1 = run_both(128, 7168, 2048, "row", 4, variant, seed=71, tile_flags=mg.PLAN_FORCE_TILE_NARROW)
+    assert "narrow128" in p1.describe() and p1.workspace_size() == 512 + 56 * 4 * 65536
+    # second, smaller: ragged N (an edge column), column-major B, three
+    # ranges; the array still holds the first call's counters and partials
     p2 = run_both(40, 1002, 1024, "col", 3, variant, seed=72)
     assert 0 < p2.workspace_size() < p1.workspace_size()
+    # and a split whose partial slabs a second kernel adds (128x128 tile)
+    p3 = run_both(64, 512, 1024, "row", 4, variant, seed=74, tile_flags=mg.PLAN_FORCE_TILE_128x128)
+    assert "tile=128x128" in p3.describe() and p3.workspace_size() == 4 * 64 * 512 * 4
 
 
 def test_noalloc_without_split_needs_no_scratch():
