@@ -103,7 +103,23 @@ mgemm_status_t mgemm::dense_run(mgemm_plan_t plan, const void *A, const void *B,
     a.split_stride = 0;
     a.scale_a = scale_a;
     a.scale_b = scale_b;
-    if (is_narrow(plan->tile) && a.tiles > 0) {
+    if (plan->sk_tiles > 0 && a.tiles > 0) {
+        // stream-K: whole tiles and the cut tiles' ranges in one launch
+        DenseArgs w = a;
+        w.splits = plan->splits;
+        w.kchunk = plan->kchunk;
+        w.sk_tiles = plan->sk_tiles;
+        w.ws = (char *)workspace;
+        w.slab_offset = plan->slab_offset;
+        w.tag = next_run_tag();
+        DenseFn f = in == IN_BF16 ? dense_sk_fn_256x256dtl_bf16(bk, out) : dense_sk_fn_256x256dtl_f16(bk, out);
+        if (!f) {
+            set_error("gemm_run: stream-K kernel missing for the planned variant");
+            return MGEMM_ERR_UNSUPPORTED;
+        }
+        if (mgemm_status_t st = hip_status(f(w, plan->grid, s), "gemm_run launch"))
+            return st;
+    } else if (is_narrow(plan->tile) && a.tiles > 0) {
         // one launch: a split's last range adds the ranges' partials itself
         DenseArgs w = a;
         w.splits = plan->splits;

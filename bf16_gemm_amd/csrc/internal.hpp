@@ -68,6 +68,9 @@ MGEMM_DECLARE_TU(narrow32_bf16)
 MGEMM_DECLARE_TU(narrow32_f16)
 #undef MGEMM_DECLARE_TU
 DenseFn dense_fn_256x256dtl_e4m3(bool ak, bool bk, int out);
+// stream-K launch of the four-wave direct-to-LDS tile (row-major A)
+DenseFn dense_sk_fn_256x256dtl_bf16(bool bk, int out);
+DenseFn dense_sk_fn_256x256dtl_f16(bool bk, int out);
 GroupedFn grouped_fn_256x256dtl_e4m3(bool bk, int out, int epi);
 
 using EdgeFn = hipError_t (*)(const DenseArgs &, int a_kmajor, int b_kmajor, int n_first, hipStream_t);
@@ -114,7 +117,8 @@ struct mgemm_plan {
     int xcd_remap;
     int splits;      // K ranges per output tile; > 1 writes fp32 partials to the workspace
     int kchunk;      // elements of K per range
-    int64_t slab_offset;  // narrow tile split: bytes of arrival counters before the partial slabs
+    int64_t slab_offset;  // split reduced in the launch: bytes of arrival counters before the partial slabs
+    int sk_tiles;         // stream-K: tiles cut into `splits` K ranges (the rest run whole), else 0
     size_t workspace_bytes;
     bool zero_fill;  // K == 0
     bool noop;       // M == 0 or N == 0

@@ -25,9 +25,10 @@ struct DenseArgs {
     int64_t split_stride;  // elements of D between the partial results of consecutive ranges
     const float *scale_a = nullptr;  // E4M3 inputs: per-tensor scales (device, one float each; null = 1)
     const float *scale_b = nullptr;
-    char *ws = nullptr;               // narrow tile split over K: arrival counters, then partial slabs
+    char *ws = nullptr;               // split reduced in the launch: arrival counters, then partial slabs
     int64_t slab_offset = 0;          // bytes from ws to the first slab
     uint32_t tag = 0;                 // this run's tag for the arrival counters (never 0 or ~0)
+    int sk_tiles = 0;                 // stream-K: the last sk_tiles tiles are cut into `splits` K ranges
 };
 
 struct GroupedArgs {
@@ -139,6 +140,124 @@ __global__ void __launch_bounds__(T::NT) dense_kernel(DenseArgs p)
         char *Dt = (char *)p.D + ((int64_t)r * p.split_stride + (int64_t)m0 * p.ldd + n0) * esize;
         tile_epilogue<T, EPI_NONE, OUT>(tile, lds, Dt, p.ldd, min(T::BM, p.M - m0), min(T::BN, p.N - n0),
                                         opaque((int)threadIdx.x));
+    }
+}
+
+// Stream-K tail balancing on the four-wave 256 x 256 tile.  When the
+// output tiles leave the last round of the persistent grid partly idle
+// ("B200 的 2CTA 怎样调优", section 十: uneven SM use makes a long tail),
+// the plan keeps the first tiles whole (data-parallel) and cuts the last
+// sk_tiles tiles into `splits` K ranges, so every CU gets the same number
+// of K steps to within one range.  Ranges run first (tasks 0 ..
+// sk_tiles * splits - 1), then the whole tiles.  A range stores its fp32
+// partial tile (256 x 256, in the accumulators' lane order) and arrives on
+// its tile's counter (split_arrive: tagged, needs no initial value); the
+// last range to arrive adds the partials in range order (its own from its
+// accumulators) and stores the tile through the usual epilogue.  Nothing
+// waits for another workgroup.
+template <class T, bool BKM, int IN, int OUT>
+__global__ void __launch_bounds__(T::NT) dense_sk_kernel(DenseArgs p)
+{
+    static_assert(T::FM == 8 && T::FN == 8 && T::NT == 256, "the four-wave 256 x 256 tile");
+    constexpr uint32_t SLAB = 256 * 256 * 4;   // bytes of one partial tile
+    constexpr uint32_t BLK = T::NT * 16;       // bytes between its 16-byte blocks
+    __shared__ __attribute__((aligned(16))) char lds[T::LDS_BYTES];
+    // the arrival count goes to every wave through the deep ring's third
+    // slot, which the next task's prologue does not fill (its loads go out
+    // after the first barrier of that task, and the epilogue's staging meets
+    // the other waves at a barrier before writing LDS)
+    uint32_t *arrived = (uint32_t *)(lds + (T::DEEP_B ? T::A_SLOTS * T::OPS : 0) + 2 * T::OPS);
+    T tile;
+    const int tid = threadIdx.x;
+    const int grid = gridDim.x;
+    const int L = logical_block(blockIdx.x, grid, p.xcd_remap);
+    const uint16_t *A = (const uint16_t *)p.A;
+    const uint16_t *B = (const uint16_t *)p.B;
+    constexpr int esize = out_size(OUT);
+    const int tiles = p.tiles_m * p.tiles_n;
+    const int dp_tiles = tiles - p.sk_tiles;
+    const int sk_tasks = p.sk_tiles * p.splits;
+    const int total = sk_tasks + dp_tiles;
+    const __amdgpu_buffer_rsrc_t slabs = make_rsrc(p.ws + p.slab_offset, (uint64_t)sk_tasks * SLAB);
+    for (int t = L; t < total; t += grid) {
+        const bool sk = t < sk_tasks;
+        const int tile_id = sk ? dp_tiles + t / p.splits : t - sk_tasks;
+        const int r = sk ? t % p.splits : 0;
+        const int k0 = r * p.kchunk;
+        const int klen = sk ? min(p.kchunk, p.K - k0) : p.K;
+        int mb, nb;
+        tile_coords(tile_id, p.tiles_m, p.tiles_n, p.group_m, mb, nb);
+        const int m0 = mb * T::BM, n0 = nb * T::BN;
+        const uint16_t *At = A + (int64_t)m0 * p.lda + k0;
+        const uint16_t *Bt = BKM ? B + (int64_t)n0 * p.ldb + k0 : B + (int64_t)k0 * p.ldb + n0;
+        const OperandSrc sa = operand_src<true>(At, p.lda, p.M - m0, klen);
+        const OperandSrc sb = operand_src<BKM>(Bt, p.ldb, p.N - n0, klen);
+        tile.mainloop(lds, sa, p.lda, sb, p.ldb, klen, opaque(tid));
+        if (sk) {
+            // one row of 8 blocks at a time (the scheduling barriers keep
+            // the accumulators' copies to 32 registers)
+            const uint32_t mine = (uint32_t)t * SLAB + (uint32_t)tid * 16u;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, tile.acc[i][j]), slabs,
+                                                           mine + (uint32_t)(i * 8 + j) * BLK, 0, kDeviceScope);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            wait_vm<0>();
+            __syncthreads();
+            if (tid == 0)
+                *arrived = split_arrive((uint64_t *)p.ws + (tile_id - dp_tiles), p.tag);
+            __syncthreads();
+            if (*arrived != (uint32_t)p.splits)
+                continue;
+            if (tid == 0)
+                split_reset((uint64_t *)p.ws + (tile_id - dp_tiles), p.tag);
+            // sum = P0 + P1 + ... in range order, one row of blocks at a time
+            // with every other range's blocks of that row in flight together;
+            // x[q] holds the q-th other range (q, or q + 1 from this range on),
+            // so range rr != r is x[rr] below r and x[rr - 1] above: a select
+            // between two fixed registers, no indexing at run time
+            const uint32_t first = (uint32_t)(t - r) * SLAB + (uint32_t)tid * 16u;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                f32x4_t x[kSkMaxSplits - 1][8];
+#pragma unroll
+                for (int q = 0; q < kSkMaxSplits - 1; ++q) {
+                    const int rr = q < r ? q : q + 1;
+                    if (rr < p.splits) {
+#pragma unroll
+                        for (int j = 0; j < 8; ++j)
+                            x[q][j] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                                                      slabs, first + (uint32_t)rr * SLAB +
+                                                                                 (uint32_t)(i * 8 + j) * BLK,
+                                                                      0, kDeviceScope));
+                    } else {
+#pragma unroll
+                        for (int j = 0; j < 8; ++j)
+                            x[q][j] = f32x4_t{};
+                    }
+                }
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const f32x4_t own = tile.acc[i][j];
+                    f32x4_t s = r == 0 ? own : x[0][j];
+#pragma unroll
+                    for (int rr = 1; rr < kSkMaxSplits; ++rr) {
+                        const f32x4_t below = x[rr < kSkMaxSplits - 1 ? rr : kSkMaxSplits - 2][j];
+                        const f32x4_t other = rr < r ? below : x[rr - 1][j];
+                        if (rr < p.splits)
+                            s += rr == r ? own : other;
+                    }
+                    tile.acc[i][j] = s;
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        char *Dt = (char *)p.D + ((int64_t)m0 * p.ldd + n0) * esize;
+        epilogue_staged<T, OUT>(tile, lds, Dt, p.ldd, min(T::BM, p.M - m0), min(T::BN, p.N - n0), opaque(tid));
+        wait_vm<0>();
     }
 }
 

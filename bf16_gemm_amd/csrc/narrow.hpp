@@ -80,6 +80,10 @@ __device__ __forceinline__ uint32_t split_arrive(uint64_t *word, uint32_t tag)
 // Cache-policy bits of a buffer access: sc1, device scope.
 constexpr int kDeviceScope = 16;
 
+// Most K ranges a stream-K tile is cut into (the fixup keeps the other
+// ranges' blocks of one row in registers).
+constexpr int kSkMaxSplits = 4;
+
 __device__ __forceinline__ void split_reset(uint64_t *word, uint32_t tag)
 {
     __hip_atomic_store(word, (uint64_t)tag << 32, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

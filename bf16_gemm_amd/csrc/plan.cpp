@@ -128,10 +128,15 @@ static int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // ceil(tiles / CUs) tiles, each bound by its MFMA work at the shape's
 // efficiency or by the operand bytes it stages (about 64 B per clock per CU
 // from L2), whichever is larger.
-static double tile_cost(const TileShape &t, int64_t M, int64_t N, int64_t K, int cus)
+// sk: the tile can balance a partial last round with stream-K (then the
+// busiest CU runs tiles / CUs tiles, plus a tenth of one for the fixup).
+static double tile_cost(const TileShape &t, int64_t M, int64_t N, int64_t K, int cus, bool sk = false)
 {
     const int64_t tiles = cdiv(M, t.bm) * cdiv(N, t.bn);
-    const double per_cu = (double)cdiv(tiles, cus);
+    const int64_t rem = tiles % cus;
+    double per_cu = (double)cdiv(tiles, cus);
+    if (sk && tiles > cus && rem > 0 && rem * 2 <= cus && cdiv(K, kBK) >= 48)
+        per_cu = (double)tiles / cus + 0.1;
     const double flops = 2.0 * t.bm * t.bn * (double)std::max<int64_t>(K, 64);
     const double mfma_clk = flops / (4096.0 * t.eff);
     const double load_clk = (double)(t.bm + t.bn) * 2.0 * (double)std::max<int64_t>(K, 64) / 64.0;
@@ -286,7 +291,10 @@ static mgemm_status_t plan_dense(const mgemm_desc_t *d, uint32_t flags, mgemm_pl
         for (int t = 0; t < NUM_TILES; ++t) {
             if (kTiles[t].forced_only || !dense_fn(t, ak, bk, in, out))
                 continue;
-            const double c = tile_cost(kTiles[t], d->M, d->N & ~(int64_t)3, d->K, p->num_cus);
+            // the 256 x 256 tile runs on the direct-to-LDS engine where it can (stream-K tails included)
+            const bool sk = t == TILE_256x256 && !e4m3 && (flags >> 16 & 0xFF) == 0 &&
+                            dense_fn(TILE_256x256_DTL, ak, bk, in, out) != nullptr;
+            const double c = tile_cost(kTiles[t], d->M, d->N & ~(int64_t)3, d->K, p->num_cus, sk);
             if (tile < 0 || c < best * 0.999) {
                 best = c;
                 tile = t;
@@ -379,6 +387,22 @@ static mgemm_status_t plan_dense(const mgemm_desc_t *d, uint32_t flags, mgemm_pl
     p->tiles_m = cdiv(d->M, ts.bm);
     p->tiles_n = cdiv(n_main, ts.bn);
     p->tiles = p->tiles_m * p->tiles_n;
+    // Stream-K tail: the four-wave tile's last round of tiles leaves at most
+    // half the CUs busy; cut those tiles into K ranges so every CU gets the
+    // same K steps to within one range ("B200 的 2CTA 怎样调优", section 十:
+    // uneven SM use, long tail).  Worth it when a tile is long enough that
+    // the steps saved outweigh the fixup (partials written and read, ~3
+    // device-scope round trips): 48 steps and more.
+    p->sk_tiles = 0;
+    const int64_t rem = p->tiles % p->num_cus;
+    if (tile == TILE_256x256_DTL && !e4m3 && forced_splits == 0 && p->tiles > p->num_cus && rem > 0 &&
+        rem * 2 <= p->num_cus && ksteps >= 48) {
+        const int64_t sk = std::min<int64_t>({(int64_t)kSkMaxSplits, p->num_cus / rem, ksteps / 16});
+        if (sk >= 2 && (in == IN_BF16 ? dense_sk_fn_256x256dtl_bf16(bk, out) : dense_sk_fn_256x256dtl_f16(bk, out))) {
+            p->sk_tiles = (int)rem;
+            splits = (int)sk;
+        }
+    }
     p->kchunk = (int)(cdiv(ksteps, splits) * kBK);
     p->splits = splits > 1 ? (int)cdiv(d->K, p->kchunk) : 1;
     if (p->splits > 1 && !dense_fn(tile, ak, bk, in, OUT_F32)) {
@@ -387,6 +411,11 @@ static mgemm_status_t plan_dense(const mgemm_desc_t *d, uint32_t flags, mgemm_pl
     }
     p->workspace_bytes = p->splits > 1 ? (size_t)p->splits * (size_t)d->M * (size_t)n_main * 4u : 0;
     p->slab_offset = 0;
+    if (p->sk_tiles > 0) {
+        // counters of the cut tiles, then one 256 x 256 fp32 partial per range
+        p->slab_offset = narrow_counter_bytes(p->sk_tiles);
+        p->workspace_bytes = (size_t)p->slab_offset + (size_t)p->sk_tiles * (size_t)p->splits * 256u * 256u * 4u;
+    }
     if (is_narrow(tile) && p->splits > 1) {
         // counters, then one partial slab per (tile, range)
         p->slab_offset = narrow_counter_bytes(p->tiles);
@@ -398,7 +427,8 @@ static mgemm_status_t plan_dense(const mgemm_desc_t *d, uint32_t flags, mgemm_pl
         }
         p->workspace_bytes = (size_t)p->slab_offset + (size_t)slabs;
     }
-    const int64_t tasks = p->tiles * p->splits;
+    const int64_t tasks = p->sk_tiles > 0 ? p->tiles - p->sk_tiles + (int64_t)p->sk_tiles * p->splits
+                                          : p->tiles * p->splits;
     const int64_t slots = (int64_t)p->num_cus * ts.occupancy;
     p->grid = (int)std::max<int64_t>(1, std::min<int64_t>(tasks, slots));
     // Tiles are issued in groups of group_m tile rows, m fastest; with the XCD
@@ -418,14 +448,18 @@ static mgemm_status_t plan_dense(const mgemm_desc_t *d, uint32_t flags, mgemm_pl
     if (is_narrow(tile))
         snprintf(tokens, sizeof tokens, " tokens=%lld",
                  (long long)mgemm_round_tokens(std::min<int64_t>(d->M, kTiles[TILE_NARROW].bm), 16));
-    char buf[320];
+    char sk_desc[64] = "";
+    if (p->sk_tiles > 0)
+        snprintf(sk_desc, sizeof sk_desc, " stream_k_tiles=%d", p->sk_tiles);
+    char buf[384];
     snprintf(buf, sizeof buf,
              "dense M=%lld N=%lld K=%lld %s%s->%s tile=%s%s waves=%dx%d bk=%d stages=%s tiles=%lld splits=%d "
-             "grid=%d group_m=%d xcd_remap=%d edge_cols=%lld",
+             "grid=%d group_m=%d xcd_remap=%d edge_cols=%lld%s",
              (long long)d->M, (long long)d->N, (long long)d->K, in_name(d->a_type),
              ak ? (bk ? " NT" : " NN") : (bk ? " TT" : " TN"),
              d->d_type == MGEMM_F32 ? "f32" : (d->d_type == MGEMM_BF16 ? "bf16" : "f16"), tile_name(tile), tokens, wm, wn,
-             e4m3 ? 128 : 64, stages, (long long)p->tiles, p->splits, p->grid, p->group_m, p->xcd_remap, (long long)(d->N - n_main));
+             e4m3 ? 128 : 64, stages, (long long)p->tiles, p->splits, p->grid, p->group_m, p->xcd_remap, (long long)(d->N - n_main),
+             sk_desc);
     p->description = buf;
     return MGEMM_OK;
 }

@@ -73,6 +73,24 @@ DenseFn dense_dtl_table(bool ak, bool bk, int out)
                           : launch_dense_tile<DtlTile4<IN, false>, true, false, IN, same16<IN>()>;
 }
 
+// Stream-K launch of the four-wave direct-to-LDS tile (row-major A).
+template <bool BK, int IN, int OUT>
+hipError_t launch_dense_sk(const DenseArgs &a, int grid, hipStream_t s)
+{
+    using T = DtlTile4<IN, BK>;
+    hipLaunchKernelGGL((dense_sk_kernel<T, BK, IN, OUT>), dim3(grid), dim3(T::NT), 0, s, a);
+    return hipGetLastError();
+}
+template <int IN>
+DenseFn dense_sk_table(bool bk, int out)
+{
+    if (out != OUT_F32 && out != same16<IN>())
+        return nullptr;
+    if (bk)
+        return out == OUT_F32 ? launch_dense_sk<true, IN, OUT_F32> : launch_dense_sk<true, IN, same16<IN>()>;
+    return out == OUT_F32 ? launch_dense_sk<false, IN, OUT_F32> : launch_dense_sk<false, IN, same16<IN>()>;
+}
+
 // E4M3 inputs: A row-major and B column-major only (both k-contiguous).
 template <int OUT>
 hipError_t launch_dense_e4m3(const DenseArgs &a, int grid, hipStream_t s)

@@ -148,6 +148,25 @@ def test_split_k_plans():
     assert mg.gemm_plan(0, 8, 64, "bf16", flags=mg.PLAN_SPLIT_K(4)).workspace_size() == 0
 
 
+def test_stream_k_plans():
+    """A partial last round of 256 x 256 tiles (at most half the CUs) with a
+    long K is balanced by stream-K: the last tiles are cut into K ranges
+    (at most four), the rest run whole; its workspace holds one 8-byte
+    counter per cut tile (256-byte rounded) and one 256 x 256 fp32 partial
+    per range."""
+    p = mg.gemm_plan(5120, 4096, 8192, "bf16", d_type="bf16", b_layout="col")
+    d = p.describe()
+    assert "tile=256x256dtl" in d and "tiles=320" in d and "stream_k_tiles=64" in d and "splits=4" in d, d
+    assert p.info().grid == 256 and p.workspace_size() == 512 + 64 * 4 * 256 * 256 * 4
+    p = mg.gemm_plan(4352, 4352, 4096, "bf16", d_type="bf16")
+    assert "stream_k_tiles=33" in p.describe() and p.workspace_size() == 512 + 33 * 4 * 256 * 256 * 4
+    # whole rounds, short K, a mostly full last round, or a fixed split: no stream-K
+    for (M, N, K, fl) in [(8192, 8192, 8192, 0), (4352, 4352, 1024, 0), (7936, 8192, 4096, 0),
+                          (5120, 4096, 8192, mg.PLAN_SPLIT_K(1))]:
+        p = mg.gemm_plan(M, N, K, "bf16", d_type="bf16", flags=fl)
+        assert "stream_k" not in p.describe(), p.describe()
+
+
 def test_direct_to_lds_tile_choice():
     # k-contiguous A and B: the planner's 256x256 tile runs on the direct-to-LDS engine
     p = mg.gemm_plan(8192, 8192, 8192, "bf16", d_type="f32", b_layout="col")
