@@ -72,6 +72,7 @@ def parse():
 # the kernels and the planner that picks their launch (tile, grid, tile order):
 # a change to any of them makes stored traffic counts stale
 KERNEL_SOURCES = ["bf16_gemm_amd/csrc/engine.hpp", "bf16_gemm_amd/csrc/kernels.hpp",
+                  "bf16_gemm_amd/csrc/narrow.hpp", "bf16_gemm_amd/csrc/moe_fused.hpp",
                   "bf16_gemm_amd/csrc/tile_tables.hpp", "bf16_gemm_amd/csrc/plan.cpp"]
 
 
@@ -180,6 +181,34 @@ def moe_case(torch, mg, datagen):
                 config={"workload": "moe64", "experts": E, "hidden": H, "inter": I, "tokens": cfg.num_tokens,
                         "top_k": cfg.top_k, "routed_rows": rows, "active_experts": active},
                 launches_per_step=len(p1.describe().split("grid=")) - 1 + len(p2.describe().split("grid=")) - 1)
+    return step, info, None
+
+
+def moe_fused_case(torch, mg, datagen):
+    """The 64-expert layer's FC1 (SiLU gate) and FC2 in one persistent
+    launch (moe_fused_run), on the same inputs as the moe64 workload."""
+    cfg = datagen.MOE["moe64"]
+    r, A, W1, W2 = datagen.moe_inputs_device(cfg, "cuda")
+    rows = int(r.offsets[-1])
+    H, I, E = cfg.hidden, cfg.inter, cfg.num_experts
+    offs = torch.from_numpy(r.offsets).cuda()
+    h = torch.empty((rows, I), dtype=torch.bfloat16, device="cuda")
+    y = torch.empty((rows, H), dtype=torch.bfloat16, device="cuda")
+    plan = mg.moe_fused_plan(E, rows, H, I)
+    ws = mg.workspace_for(plan)
+
+    def step():
+        mg.moe_fused_run(plan, A, W1, W2, h, y, offs, workspace=ws)
+
+    flops = 2.0 * rows * (2 * I) * H + 2.0 * rows * H * I
+    active = int((r.counts > 0).sum())
+    wbytes = active * (H * 2 * I + I * H) * 2
+    abytes = rows * H * 2 + rows * I * 2 * 2 + rows * H * 2
+    info = dict(flops=flops, bytes=wbytes + abytes, plan=plan.describe(), dtype="bf16",
+                config={"workload": "moe64_fused", "experts": E, "hidden": H, "inter": I,
+                        "tokens": cfg.num_tokens, "top_k": cfg.top_k, "routed_rows": rows,
+                        "active_experts": active},
+                launches_per_step=2)
     return step, info, None
 
 
@@ -330,6 +359,8 @@ def main():
 
     if args.workload == "moe64":
         step, info, case = moe_case(torch, mg, datagen)
+    elif args.workload == "moe64_fused":
+        step, info, case = moe_fused_case(torch, mg, datagen)
     elif args.workload == "moe64_layer":
         step, info, case = moe_layer_case(torch, mg, datagen)
     elif args.workload in E4M3:

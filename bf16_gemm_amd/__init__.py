@@ -58,6 +58,14 @@ class GroupedDesc(ctypes.Structure):
                 ("ldd", ctypes.c_int64), ("epilogue", ctypes.c_int)]
 
 
+class MoeDesc(ctypes.Structure):
+    _fields_ = [("num_experts", ctypes.c_int32), ("max_total_rows", ctypes.c_int64),
+                ("hidden", ctypes.c_int64), ("inter", ctypes.c_int64), ("dtype", ctypes.c_int),
+                ("lda", ctypes.c_int64), ("ldw1", ctypes.c_int64), ("stride_w1", ctypes.c_int64),
+                ("ldw2", ctypes.c_int64), ("stride_w2", ctypes.c_int64),
+                ("ldh", ctypes.c_int64), ("ldy", ctypes.c_int64)]
+
+
 class PlanInfo(ctypes.Structure):
     _fields_ = [("block_m", ctypes.c_int32), ("block_n", ctypes.c_int32), ("block_k", ctypes.c_int32),
                 ("waves_m", ctypes.c_int32), ("waves_n", ctypes.c_int32), ("stages", ctypes.c_int32),
@@ -77,7 +85,8 @@ EXPORTS = ["gemm_plan", "grouped_gemm_plan", "gemm_plan_workspace_size", "gemm_r
            "grouped_gemm_run", "grouped_gemm_run_scaled",
            "gemm_plan_describe", "gemm_plan_info", "gemm_plan_destroy", "gemm_status_string",
            "gemm_last_error_message", "mgemm_tile_budget", "mgemm_group_working_set", "mgemm_round_tokens",
-           "mgemm_version", "mgemm_moe_combine", "grouped_gemm_run_gather", "gemm_run_noalloc"]
+           "mgemm_version", "mgemm_moe_combine", "grouped_gemm_run_gather", "gemm_run_noalloc",
+           "moe_fused_plan", "moe_fused_run"]
 
 
 def _load():
@@ -123,6 +132,10 @@ def _load():
     lib.mgemm_version.restype = ctypes.c_char_p
     lib.grouped_gemm_run_gather.argtypes = [vp, vp, i64, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.grouped_gemm_run_gather.restype = st
+    lib.moe_fused_plan.argtypes = [ctypes.POINTER(MoeDesc), u32, ctypes.POINTER(vp)]
+    lib.moe_fused_plan.restype = st
+    lib.moe_fused_run.argtypes = [vp, vp, i64, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.moe_fused_run.restype = st
     lib.mgemm_moe_combine.argtypes = [vp, i64, i64, vp, vp, vp, i64, i64, ctypes.c_int32, i64, ctypes.c_int, vp]
     lib.mgemm_moe_combine.restype = st
     return lib
@@ -279,6 +292,36 @@ def grouped_gemm_run_gather(plan: Plan, X, B, D, row_offsets, row_index, x_rows=
     x_rows = X.shape[0] if x_rows is None else x_rows
     _check(lib.grouped_gemm_run_gather(plan.handle, _ptr(X), x_rows, _ptr(B), _ptr(D), _ptr(row_offsets),
                                        _ptr(row_index), None, 0, _stream(stream)), "grouped_gemm_run_gather")
+
+
+def moe_fused_plan(num_experts, max_total_rows, hidden, inter, dtype="bf16", lda=None, ldw1=None,
+                   stride_w1=None, ldw2=None, stride_w2=None, ldh=None, ldy=None, flags: int = 0) -> Plan:
+    """Plan the fused MoE layer (FC1 with the SiLU gate, then FC2, one
+    launch).  Leading dimensions default to the packed ones."""
+    ldw1 = ldw1 if ldw1 is not None else 2 * inter
+    ldw2 = ldw2 if ldw2 is not None else hidden
+    d = MoeDesc(num_experts, max_total_rows, hidden, inter, DTYPE[dtype], lda if lda is not None else hidden,
+                ldw1, stride_w1 if stride_w1 is not None else hidden * ldw1,
+                ldw2, stride_w2 if stride_w2 is not None else inter * ldw2,
+                ldh if ldh is not None else inter, ldy if ldy is not None else hidden)
+    h = ctypes.c_void_p()
+    _check(lib.moe_fused_plan(ctypes.byref(d), flags, ctypes.byref(h)), "moe_fused_plan")
+    return Plan(h.value, d)
+
+
+def moe_fused_run(plan: Plan, X, W1, W2, H, Y, row_offsets, workspace=None, row_index=None, x_rows=None,
+                  workspace_bytes: int = 0, stream=None):
+    """Enqueue the fused layer.  X: routed rows (or, with ``row_index``, the
+    token rows that routed row r reads as X[row_index[r]]); H receives h and
+    Y the FC2 output.  Without a workspace one is taken from torch's
+    allocator on Y's device."""
+    if workspace is None and isinstance(Y, torch.Tensor):
+        workspace = workspace_for(plan, Y.device)
+    if row_index is not None and x_rows is None:
+        x_rows = X.shape[0]
+    _check(lib.moe_fused_run(plan.handle, _ptr(X), x_rows or 0, _ptr(row_index), _ptr(W1), _ptr(W2), _ptr(H),
+                             _ptr(Y), _ptr(row_offsets), _ptr(workspace), _nbytes(workspace, workspace_bytes),
+                             _stream(stream)), "moe_fused_run")
 
 
 def moe_combine(Z, pos, weights, Y, top_k: int, z_rows=None, stream=None):

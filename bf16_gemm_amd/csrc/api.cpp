@@ -293,6 +293,64 @@ static mgemm_status_t grouped_run(mgemm_plan_t plan, const void *A, const void *
     return MGEMM_OK;
 }
 
+extern "C" mgemm_status_t moe_fused_run(mgemm_plan_t plan, const void *X, int64_t x_rows, const int32_t *d_row_index,
+                                        const void *W1, const void *W2, void *H, void *Y,
+                                        const int32_t *d_row_offsets, void *workspace, size_t workspace_bytes,
+                                        mgemm_stream_t stream)
+{
+    if (!plan || plan->kind != PLAN_MOE) {
+        set_error("moe_fused_run: null or non-MoE plan");
+        return MGEMM_ERR_INVALID_ARG;
+    }
+    const mgemm_moe_desc_t &d = plan->moe;
+    if (plan->noop)
+        return MGEMM_OK;
+    if (!X || !W1 || !W2 || !H || !Y || !d_row_offsets) {
+        set_error("moe_fused_run: null pointer");
+        return MGEMM_ERR_INVALID_ARG;
+    }
+    if (d_row_index && (x_rows < 0 || x_rows > INT32_MAX ||
+                        (uint64_t)x_rows * (uint64_t)d.lda * 2u > (uint64_t)kMaxRecords)) {
+        set_error("moe_fused_run: x_rows=%lld out of range (x_rows * lda * 2 must be < 2^31)", (long long)x_rows);
+        return MGEMM_ERR_INVALID_ARG;
+    }
+    if (!aligned16(X) || !aligned16(W1) || !aligned16(W2) || !aligned16(Y) || ((uintptr_t)H & 127u)) {
+        set_error("moe_fused_run: X, W1, W2 and Y must be 16-byte aligned, H 128-byte aligned");
+        return MGEMM_ERR_UNSUPPORTED;
+    }
+    if (!workspace || workspace_bytes < plan->workspace_bytes || !aligned16(workspace)) {
+        set_error("moe_fused_run: needs a 16-byte aligned workspace of %zu bytes (got %zu at %p)",
+                  plan->workspace_bytes, workspace_bytes, workspace);
+        return MGEMM_ERR_WORKSPACE;
+    }
+    MoeArgs a;
+    a.X = X;
+    a.row_index = d_row_index;
+    a.x_rows = d_row_index ? (int)x_rows : 0;
+    a.W1 = W1;
+    a.W2 = W2;
+    a.H = H;
+    a.Y = Y;
+    a.offs = d_row_offsets;
+    a.G = d.num_experts;
+    a.hidden = (int)d.hidden;
+    a.inter = (int)d.inter;
+    a.max_rows = (int)d.max_total_rows;
+    a.lda = (int)d.lda;
+    a.ldw1 = (int)d.ldw1;
+    a.ldw2 = (int)d.ldw2;
+    a.ldh = (int)d.ldh;
+    a.ldy = (int)d.ldy;
+    a.stride_w1 = d.stride_w1;
+    a.stride_w2 = d.stride_w2;
+    a.ws = (char *)workspace;
+    a.max_slots = (int)plan->moe_slots;
+    // about four seconds of polling before an FC2 task gives up; with valid
+    // offsets every count completes long before
+    a.spin_limit = 1u << 22;
+    return hip_status(launch_moe_fused(a, in_code(d.dtype), plan->grid, (hipStream_t)stream), "moe_fused_run launch");
+}
+
 extern "C" mgemm_status_t grouped_gemm_run(mgemm_plan_t plan, const void *A, const void *B, void *D,
                                            const int32_t *d_row_offsets, void *workspace, size_t workspace_bytes,
                                            mgemm_stream_t stream)

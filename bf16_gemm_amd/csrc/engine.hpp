@@ -1577,7 +1577,10 @@ constexpr int out_size(int out) { return out == OUT_F32 ? 4 : 2; }
 // resource and are dropped by the hardware, column groups past n_valid get
 // an out-of-range offset.  No branches, so accumulators are read out one
 // fragment at a time.
-template <class T, int EPI, int OUT>
+// AUX: the stores' cache-policy bits (kDeviceScope: written through to the
+// level every XCD shares, for outputs another workgroup reads in the same
+// launch).
+template <class T, int EPI, int OUT, int AUX = 0>
 __device__ __forceinline__ void epilogue(const T &t, void *D, int64_t ldd, int m_valid, int n_valid, int tid)
 {
     constexpr int esize = out_size(OUT);
@@ -1603,7 +1606,7 @@ __device__ __forceinline__ void epilogue(const T &t, void *D, int64_t ldd, int m
                 const int n = wn0 + 16 * j + 4 * (lane >> 4);
                 if constexpr (EPI == EPI_NONE) {
                     const uint32_t off = n < n_valid ? rowoff + (uint32_t)n * esize : kOOB;
-                    bstore4<OUT>(r, off, a[0], a[1], a[2], a[3]);
+                    bstore4<OUT, AUX>(r, off, a[0], a[1], a[2], a[3]);
                 } else {
                     // gate: columns 0-7 of the block (lanes 0-31); up: 8-15,
                     // 32 lanes further on
@@ -1611,7 +1614,7 @@ __device__ __forceinline__ void epilogue(const T &t, void *D, int64_t ldd, int m
                     const float u2 = __shfl_xor(a[2], 32, 64), u3 = __shfl_xor(a[3], 32, 64);
                     const int hc = (n >> 4) * 8 + (n & 15);
                     const uint32_t off = (lane < 32 && n < n_valid) ? rowoff + (uint32_t)hc * esize : kOOB;
-                    bstore4<OUT>(r, off, silu_mul(a[0], u0), silu_mul(a[1], u1), silu_mul(a[2], u2),
+                    bstore4<OUT, AUX>(r, off, silu_mul(a[0], u0), silu_mul(a[1], u1), silu_mul(a[2], u2),
                                  silu_mul(a[3], u3));
                 }
             }
@@ -1629,7 +1632,7 @@ __device__ __forceinline__ void epilogue(const T &t, void *D, int64_t ldd, int m
                     for (int rg = 0; rg < 4; ++rg) {
                         const int n = wn0 + 32 * j + 8 * rg + 4 * (lane >> 5);
                         const uint32_t off = n < n_valid ? rowoff + (uint32_t)n * esize : kOOB;
-                        bstore4<OUT>(r, off, a[4 * rg], a[4 * rg + 1], a[4 * rg + 2], a[4 * rg + 3]);
+                        bstore4<OUT, AUX>(r, off, a[4 * rg], a[4 * rg + 1], a[4 * rg + 2], a[4 * rg + 3]);
                     }
                 } else {
                     // columns 8*rg..8*rg+7 of a 32-wide block are gate for rg
@@ -1639,7 +1642,7 @@ __device__ __forceinline__ void epilogue(const T &t, void *D, int64_t ldd, int m
                         const int n = wn0 + 32 * j + 8 * rg + 4 * (lane >> 5);
                         const int hc = (n >> 4) * 8 + (n & 15);
                         const uint32_t off = n < n_valid ? rowoff + (uint32_t)hc * esize : kOOB;
-                        bstore4<OUT>(r, off, silu_mul(a[4 * rg + 0], a[4 * rg + 4]), silu_mul(a[4 * rg + 1], a[4 * rg + 5]),
+                        bstore4<OUT, AUX>(r, off, silu_mul(a[4 * rg + 0], a[4 * rg + 4]), silu_mul(a[4 * rg + 1], a[4 * rg + 5]),
                                      silu_mul(a[4 * rg + 2], a[4 * rg + 6]), silu_mul(a[4 * rg + 3], a[4 * rg + 7]));
                     }
                 }

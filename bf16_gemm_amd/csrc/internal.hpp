@@ -76,6 +76,8 @@ GroupedFn grouped_fn_256x256dtl_e4m3(bool bk, int out, int epi);
 using EdgeFn = hipError_t (*)(const DenseArgs &, int a_kmajor, int b_kmajor, int n_first, hipStream_t);
 EdgeFn edge_fn(int in, int out);
 hipError_t launch_zero_fill(void *D, int rows, int cols, int64_t ld_bytes, int esize, hipStream_t s);
+// the fused MoE layer: the prepare kernel, then the persistent kernel on `grid` workgroups
+hipError_t launch_moe_fused(const MoeArgs &a, int in, int grid, hipStream_t s);
 hipError_t launch_moe_combine(const void *Z, int64_t z_rows, int64_t ldz, const int32_t *pos, const float *w,
                               void *Y, int64_t ldy, int64_t T, int top_k, int64_t H, int out, hipStream_t s);
 // D[M x N] = sum over r < splits of W[r][M x N] (fp32, row pitch ldw, slabs
@@ -91,7 +93,7 @@ struct GroupedLaunch {
     int grid;
 };
 
-enum PlanKind { PLAN_DENSE = 1, PLAN_GROUPED = 2 };
+enum PlanKind { PLAN_DENSE = 1, PLAN_GROUPED = 2, PLAN_MOE = 3 };
 
 void set_error(const char *fmt, ...);
 
@@ -107,6 +109,7 @@ struct mgemm_plan {
     int kind;
     mgemm_desc_t dense;
     mgemm_grouped_desc_t grouped;
+    mgemm_moe_desc_t moe;
     uint32_t flags;
     int num_cus;
     // dense
@@ -124,5 +127,7 @@ struct mgemm_plan {
     bool noop;       // M == 0 or N == 0
     // grouped
     std::vector<mgemm::GroupedLaunch> launches;
+    // fused MoE layer: row blocks its counter array holds
+    int64_t moe_slots;
     std::string description;
 };

@@ -50,6 +50,56 @@ struct GroupedArgs {
 };
 
 
+// The fused MoE expert layer (moe_fused.hpp).
+struct MoeArgs {
+    const void *X;                       // FC1 A: routed rows [rows][hidden], or token rows with row_index
+    const int32_t *row_index = nullptr;  // gathered A: routed row r reads X row row_index[r]
+    int x_rows = 0;
+    const void *W1;                      // [G][hidden][2 inter] row-major, gate / up interleaved by 8
+    const void *W2;                      // [G][inter][hidden] row-major
+    void *H;                             // [rows][inter]
+    void *Y;                             // [rows][hidden]
+    const int32_t *offs;                 // [G + 1] device prefix sums
+    int G, hidden, inter, max_rows;
+    int lda, ldw1, ldw2, ldh, ldy;
+    int64_t stride_w1, stride_w2;
+    char *ws;                            // schedule and counters (moe_ws_bytes)
+    int max_slots;                       // row blocks the counter array holds
+    uint32_t spin_limit;                 // polls before an FC2 task gives up (status 1)
+};
+
+// Workspace layout (bytes):
+//   0    int32 ticket counter
+//   4    int32 FC1 tasks, 8: FC2 tasks (written by the prepare kernel)
+//   12   int32 status: 0 = fine; 1 = an FC2 task stopped waiting (never for
+//        valid offsets); 2 = offsets gave more row blocks than the counter
+//        array holds (nothing computed)
+//   256  per position p < 256 (experts by rows, largest first): int32 x 4
+//        {expert, first row, rows, first counter}
+//   4352 int32 [256] first FC1 ticket of each position (INT32_MAX past G)
+//   5376 int32 [256] first FC2 ticket of each position (counted from T1)
+//   6400 int32 [max_slots] completion counters, one per (expert, row block)
+constexpr int kMoeTicket = 0, kMoeT1 = 4, kMoeT2 = 8, kMoeStatus = 12;
+constexpr int kMoeEntries = 256, kMoeStart1 = 4352, kMoeStart2 = 5376, kMoeCounters = 6400;
+__host__ __device__ constexpr int64_t moe_ws_bytes(int64_t max_slots)
+{
+    return (kMoeCounters + max_slots * 4 + 255) / 256 * 256;
+}
+
+// Row blocks of an expert: blocks of 256 rows on the eight-wave 256 x 256
+// tile, or (at most 128 rows) one block on the few-token tile.  Column
+// tiles: 256 wide on the big tile, 128 on the few-token tile.
+constexpr int kMoeNarrowRows = 128;
+__host__ __device__ constexpr int moe_blocks(int rows)
+{
+    return rows <= 0 ? 0 : (rows <= kMoeNarrowRows ? 1 : (rows + 255) / 256);
+}
+__host__ __device__ constexpr int moe_tasks(int rows, int n)
+{
+    return rows <= 0 ? 0 : (rows <= kMoeNarrowRows ? (n + 127) / 128 : (rows + 255) / 256 * ((n + 255) / 256));
+}
+
+
 // Workgroup id -> logical id.  Workgroups are handed to the eight XCDs
 // round-robin, so id w runs on XCD w % 8.  Mapping w to
 // (w % 8) * (grid / 8) + w / 8 gives every XCD a contiguous block of logical

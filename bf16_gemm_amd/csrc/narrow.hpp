@@ -16,10 +16,13 @@
 // and every token block, so each wave's MFMA count scales with the token
 // count.  The weights stream from HBM once; the kernel is bound by that
 // stream, so operands go straight from global memory to LDS
-// (buffer_load ... lds) through a five-slot ring (32 KiB per 64-k step: up
-// to 128 token rows of 128 bytes, and the step's 64 x 128 weight block),
-// four steps ahead of the MFMAs.  Every step waits for its own slot, meets
-// the other waves at one barrier, refills the slot the previous step freed,
+// (buffer_load ... lds) through a ring of slots, one 64-k step each: the
+// tile's token rows that exist (16 per token block, 128 bytes each) and the
+// step's 64 x 128 weight block.  A tile with fewer tokens has smaller slots
+// and more of them (five with 128 tokens, eight with 16): its loads run
+// further ahead of the MFMAs, and a stream's rate is the bytes in flight
+// over the memory latency.  Every step waits for its own slot, meets the
+// other waves at one barrier, refills the slot the previous step freed,
 // then reads its fragments and issues its MFMAs.
 //
 // Swizzles.  Token rows (and k-contiguous weight rows, [n][k]) use the
@@ -97,41 +100,63 @@ __host__ __device__ constexpr int narrow_slab_bytes(int bn) { return 128 * bn * 
 
 // BN_: columns per tile, 128, 64 or 32.  128 and 64: four waves, each with
 // BN / 4 columns (two blocks of 16, or one); 32: two waves of 16 columns.
+// NW_ > 0 sets the wave count instead (eight waves of 16 columns at 128, for
+// a kernel whose workgroup also runs the eight-wave 256 x 256 tile).
+// AGPR_: accumulators in AGPRs through inline assembly (a kernel of its own)
+// or, false, in whatever registers the compiler picks (a kernel that also
+// holds the eight-wave tile's accumulators in VGPRs).
 // Every wave computes every token block of its columns.
-template <int IN, bool BKM, int BN_ = 128>
+template <int IN, bool BKM, int BN_ = 128, int NW_ = 0, bool AGPR_ = true>
 struct NarrowTile {
     static constexpr int TMAX = 128;              // tokens per tile
     static constexpr int NTB = TMAX / 16;         // token blocks
     static constexpr int BM = TMAX, BN = BN_;
     static_assert(BN == 128 || BN == 64 || BN == 32, "");
-    static constexpr int NW = BN >= 64 ? 4 : 2;   // waves
+    static constexpr int NW = NW_ > 0 ? NW_ : (BN >= 64 ? 4 : 2);   // waves
     static constexpr int WM = 1, WN = NW;
     static constexpr int MI = 16;
     static constexpr int NT = 64 * NW;
     static constexpr int NB = BN / 16 / NW;       // column blocks per wave
-    static constexpr int A_BYTES = TMAX * kRowBytes;   // token rows, 128 B each
     static constexpr int B_BYTES = 64 * BN * 2;        // one step of weights
-    static constexpr int SLOT = A_BYTES + B_BYTES;
-    static constexpr int LA = A_BYTES / 1024 / NW;     // loads per wave and step
-    static constexpr int LB = B_BYTES / 1024 / NW;
-    static constexpr int LOADS = LA + LB;
-    // ring slots: as many as the LDS holds, with at most 63 loads per wave
-    // in flight (the NST - 1 steps ahead), the most s_waitcnt vmcnt counts:
-    // 5, 6 and 7 slots for 128, 64 and 32 columns
-    static constexpr int NST = (160 * 1024) / SLOT < 63 / LOADS + 1 ? (160 * 1024) / SLOT : 63 / LOADS + 1;
-    static_assert((NST - 1) * LOADS <= 63, "loads in flight beyond the vmcnt range");
-    static constexpr int LDS_BYTES = NST * SLOT;
+    static constexpr int LB = B_BYTES / 1024 / NW;     // weight loads per wave and step
+    // The ring for NV token blocks (1..8): a slot holds one 64-k step, the
+    // 16 NV token rows that exist (128 B each) then the weights, so a tile
+    // with few tokens keeps more weight steps in flight -- its rate is the
+    // bytes in flight over the memory latency.  Token loads (1 KiB = 8 rows
+    // each, 2 NV per step) go round the waves; every wave issues LA(NV) of
+    // them, those past the tile's rows into a 1 KiB scratch area (offset
+    // out of range: zeros, no memory traffic), so that every wave counts the
+    // same loads per step.  Slots: as many as fit beside the scratch, with
+    // at most 63 loads per wave in flight (NST - 1 steps ahead), the most
+    // s_waitcnt vmcnt counts.
+    static constexpr int LDS_BYTES = 160 * 1024;
+    static constexpr int SCRATCH = LDS_BYTES - 1024;
+    template <int NV>
+    struct Ring {
+        static constexpr int A_BYTES = NV * 16 * kRowBytes;
+        static constexpr int SLOT = A_BYTES + B_BYTES;
+        static constexpr int LA = (2 * NV + NW - 1) / NW;
+        static constexpr int LOADS = LA + LB;
+        static constexpr bool DUMMY = LA * NW != 2 * NV;   // some token loads go to the scratch area
+        static constexpr int FIT = (DUMMY ? SCRATCH : LDS_BYTES) / SLOT;
+        static constexpr int NST = FIT < 63 / LOADS + 1 ? FIT : 63 / LOADS + 1;
+        static_assert(NST >= 3 && (NST - 1) * LOADS <= 63, "");
+    };
+    static constexpr int LA_MAX = Ring<NTB>::LA;
+    // the ring of a full tile (8 token blocks): its last slot is free once
+    // the K loop is done
+    static constexpr int NST = Ring<NTB>::NST, SLOT = Ring<NTB>::SLOT;
     static constexpr int BROW = BN * 2;           // bytes of a k row of a row-major weight step
     static constexpr int RPL = 1024 / BROW;       // k rows per (1 KiB) load of a row-major weight step
     static constexpr int LG_R = BN == 128 ? 0 : (BN == 64 ? 1 : 2);   // log2 of k rows per 256 bytes
-    static_assert(NB >= 1 && LA >= 1 && LB >= 1, "");
+    static_assert(NB >= 1 && LB >= 1, "");
 
     f32x4_t acc[NTB][NB];
-    uint32_t va[LA], vb[LB];   // per-lane global byte offsets within a step
-    int kca[LA], kcb[LB];      // k of this lane's 16-byte chunk (k-contiguous operands)
+    uint32_t va[LA_MAX], vb[LB];   // per-lane global byte offsets within a step
+    int kca[LA_MAX], kcb[LB];      // k of this lane's 16-byte chunk (k-contiguous operands)
     int afr[2];                // A fragment of token block 0, sub-step s (LDS offset in a slot)
-    int bfr[NB][2];            // k-contiguous B: fragment of column block nb, sub-step s
-    int btr[NB];               // row-major B: transpose-read piece of column block nb (k row 0)
+    int bfr[NB][2];            // k-contiguous B: fragment of column block nb, sub-step s (from the weights)
+    int btr[NB];               // row-major B: transpose-read piece of column block nb (k row 0, from the weights)
 
     // Row-major weight steps: 32-byte segment s of k row k is stored at
     // s ^ bseg(k).  One ds_read_b64_tr_b16 of a 16-lane group covers k rows
@@ -145,15 +170,23 @@ struct NarrowTile {
         return ((k & 3) >> LG_R) | (((k >> 3) & 1) << (2 - LG_R));
     }
 
+    // Per-lane load offsets and fragment addresses for NV token blocks.
+    template <int NV>
     __device__ __forceinline__ void setup(int lane, int wave, int lda, int ldb, const RowGather &ga)
     {
-        // A: load j of wave w fills token rows 8 (LA w + j) .. +7
+        using R = Ring<NV>;
+        // A: load j of wave w fills token rows 8 (LA w + j) .. +7 when they
+        // exist, else the scratch area
 #pragma unroll
-        for (int j = 0; j < LA; ++j) {
-            const int row = (wave * LA + j) * 8 + (lane >> 3);
+        for (int j = 0; j < R::LA; ++j) {
+            const int blk = wave * R::LA + j;
+            const int row = blk * 8 + (lane >> 3);
             const int c = (lane & 7) ^ DtlTile<IN, true>::dswz(row);
+            const bool real = blk < 2 * NV;
             kca[j] = c * 8;
-            if (ga.idx) {
+            if (!real) {
+                va[j] = kOOB;
+            } else if (ga.idx) {
                 const uint32_t ro = ga.row_offset(row, lda);
                 va[j] = ro == kOOB ? kOOB : ro + (uint32_t)c * 16u;
             } else {
@@ -191,46 +224,52 @@ struct NarrowTile {
             if constexpr (BKM) {
 #pragma unroll
                 for (int s = 0; s < 2; ++s)
-                    bfr[nb][s] = A_BYTES + (wn0 + 16 * nb + r) * kRowBytes + ((c0 ^ (4 * s)) << 4);
+                    bfr[nb][s] = (wn0 + 16 * nb + r) * kRowBytes + ((c0 ^ (4 * s)) << 4);
             } else {
                 // lane 4 j + qq of group q points at k row 8 q + j (+ 32 s + 4 hi),
                 // columns 4 qq .. 4 qq + 3 of the block's logical segment
                 // (bseg of those rows does not depend on s or hi)
                 const int j = r >> 2, qq = r & 3;
                 const int seg = (wn0 >> 4) + nb;
-                btr[nb] = A_BYTES + (8 * q + j) * BROW + ((seg ^ bseg(8 * q + j)) * 32) + 8 * qq;
+                btr[nb] = (8 * q + j) * BROW + ((seg ^ bseg(8 * q + j)) * 32) + 8 * qq;
             }
         }
     }
 
     // the loads of one K step into slot `slot`; ra / rb point at the step,
     // k_left = K minus the step's first k (<= 0: a step past K, all zeros)
-    __device__ __forceinline__ void load_step(char *slot, int wave, __amdgpu_buffer_rsrc_t ra,
+    template <int NV>
+    __device__ __forceinline__ void load_step(char *lds, char *slot, int wave, __amdgpu_buffer_rsrc_t ra,
                                               __amdgpu_buffer_rsrc_t rb, int k_left) const
     {
+        using R = Ring<NV>;
 #pragma unroll
-        for (int j = 0; j < LA; ++j)
-            load_to_lds16(ra, lds_addr(slot + (wave * LA + j) * 1024), kca[j] < k_left ? va[j] : kOOB);
+        for (int j = 0; j < R::LA; ++j) {
+            // wave-uniform: a token block of the slot, or the scratch area
+            const int blk = wave * R::LA + j;
+            load_to_lds16(ra, lds_addr(blk < 2 * NV ? slot + blk * 1024 : lds + SCRATCH),
+                          kca[j] < k_left ? va[j] : kOOB);
+        }
 #pragma unroll
         for (int j = 0; j < LB; ++j) {
             uint32_t off = vb[j];
             if constexpr (BKM)
                 off = kcb[j] < k_left ? off : kOOB;
-            load_to_lds16(rb, lds_addr(slot + A_BYTES + (wave * LB + j) * 1024), off);
+            load_to_lds16(rb, lds_addr(slot + R::A_BYTES + (wave * LB + j) * 1024), off);
         }
     }
 
-    // B fragments of sub-step s
+    // B fragments of sub-step s; wts = the slot's weights
     template <int S>
-    __device__ __forceinline__ void read_b(const char *slot, u32x4_t (&b)[NB]) const
+    __device__ __forceinline__ void read_b(const char *wts, u32x4_t (&b)[NB]) const
     {
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
             if constexpr (BKM) {
-                b[nb] = *(const u32x4_t *)(slot + bfr[nb][S]);
+                b[nb] = *(const u32x4_t *)(wts + bfr[nb][S]);
             } else {
                 typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
-                const char *p = slot + btr[nb] + 32 * S * BROW;
+                const char *p = wts + btr[nb] + 32 * S * BROW;
                 const u32x2_t lo = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)p));
                 const u32x2_t hi =
                     __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(p + 4 * BROW)));
@@ -239,14 +278,22 @@ struct NarrowTile {
         }
     }
 
+    static __device__ __forceinline__ void mma(f32x4_t &c, const u32x4_t &a, const u32x4_t &b)
+    {
+        if constexpr (AGPR_)
+            mfma16_agpr<IN>(c, a, b);
+        else
+            c = mfma16<IN>(a, b, c);
+    }
+
     // One K step on slot `slot`: both sub-steps' fragments first, then the
-    // MFMAs of the NV token blocks that exist.
+    // MFMAs of the NV token blocks.
     template <int NV>
     __device__ __forceinline__ void compute(const char *slot)
     {
         u32x4_t b0[NB], b1[NB], a0[NV], a1[NV];
-        read_b<0>(slot, b0);
-        read_b<1>(slot, b1);
+        read_b<0>(slot + Ring<NV>::A_BYTES, b0);
+        read_b<1>(slot + Ring<NV>::A_BYTES, b1);
 #pragma unroll
         for (int tb = 0; tb < NV; ++tb) {
             a0[tb] = *(const u32x4_t *)(slot + afr[0] + tb * 16 * kRowBytes);
@@ -256,31 +303,40 @@ struct NarrowTile {
         for (int tb = 0; tb < NV; ++tb)
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb)
-                mfma16_agpr<IN>(acc[tb][nb], b0[nb], a0[tb]);
+                mma(acc[tb][nb], b0[nb], a0[tb]);
 #pragma unroll
         for (int tb = 0; tb < NV; ++tb)
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb)
-                mfma16_agpr<IN>(acc[tb][nb], b1[nb], a1[tb]);
+                mma(acc[tb][nb], b1[nb], a1[tb]);
     }
 
-    // The K loop for NV token blocks.  Step kt: this wave's loads of step kt
-    // have landed (only the NST - 2 later steps' may be in flight); after
-    // the barrier every wave's have, and every wave is done with step
-    // kt - 1, whose slot takes step kt + NST - 1.
+    // The K loop for NV token blocks on its ring.  Step kt: this wave's
+    // loads of step kt have landed (only the NST - 2 later steps' may be in
+    // flight); after the barrier every wave's have, and every wave is done
+    // with step kt - 1, whose slot takes step kt + NST - 1.
     template <int NV>
-    __device__ __forceinline__ void kloop(char *lds, const OperandSrc &ua, const OperandSrc &ub, int K, int ksteps,
-                                          int wave)
+    __device__ __forceinline__ void kloop(char *lds, const OperandSrc &sa, const OperandSrc &sb, int lda, int ldb,
+                                          int K, int ksteps, int lane, int wave, const RowGather &ga)
     {
-        int slot = 0, fill = NST - 1;
+        using R = Ring<NV>;
+        setup<NV>(lane, wave, lda, ldb, ga);
+        const OperandSrc ua = uniform_src(sa), ub = uniform_src(sb);
+        // prologue: steps 0 .. NST-2 (a loop: unrolled, the deep rings'
+        // buffer descriptors would all be live at once)
+#pragma unroll 1
+        for (int s = 0; s < R::NST - 1; ++s)
+            load_step<NV>(lds, lds + s * R::SLOT, wave, ua.at_step(s), ub.at_step(s), K - s * kBK);
+        mfma_drain();
+        int slot = 0, fill = R::NST - 1;
         for (int kt = 0; kt < ksteps; ++kt) {
-            wait_vm<(NST - 2) * LOADS>();
+            wait_vm<(R::NST - 2) * R::LOADS>();
             lds_barrier();
-            load_step(lds + fill * SLOT, wave, ua.at_step(kt + NST - 1), ub.at_step(kt + NST - 1),
-                      K - (kt + NST - 1) * kBK);
-            compute<NV>(lds + slot * SLOT);
-            slot = slot == NST - 1 ? 0 : slot + 1;
-            fill = fill == NST - 1 ? 0 : fill + 1;
+            load_step<NV>(lds, lds + fill * R::SLOT, wave, ua.at_step(kt + R::NST - 1), ub.at_step(kt + R::NST - 1),
+                          K - (kt + R::NST - 1) * kBK);
+            compute<NV>(lds + slot * R::SLOT);
+            slot = slot == R::NST - 1 ? 0 : slot + 1;
+            fill = fill == R::NST - 1 ? 0 : fill + 1;
         }
     }
 
@@ -300,27 +356,22 @@ struct NarrowTile {
         const int ksteps = (K + kBK - 1) / kBK;
         if (ksteps <= 0)
             return;
+        if constexpr (AGPR_) {
 #pragma unroll
-        for (int i = 0; i < NTB; ++i)
+            for (int i = 0; i < NTB; ++i)
 #pragma unroll
-            for (int j = 0; j < NB; ++j)
-                asm volatile("" : "+a"(acc[i][j]));
-        setup(lane, wave, lda, ldb, ga);
-        const OperandSrc ua = uniform_src(sa), ub = uniform_src(sb);
-        // prologue: steps 0 .. NST-2
-#pragma unroll
-        for (int s = 0; s < NST - 1; ++s)
-            load_step(lds + s * SLOT, wave, ua.at_step(s), ub.at_step(s), K - s * kBK);
-        mfma_drain();
+                for (int j = 0; j < NB; ++j)
+                    asm volatile("" : "+a"(acc[i][j]));
+        }
         switch (__builtin_amdgcn_readfirstlane(ntb)) {
-        case 1: kloop<1>(lds, ua, ub, K, ksteps, wave); break;
-        case 2: kloop<2>(lds, ua, ub, K, ksteps, wave); break;
-        case 3: kloop<3>(lds, ua, ub, K, ksteps, wave); break;
-        case 4: kloop<4>(lds, ua, ub, K, ksteps, wave); break;
-        case 5: kloop<5>(lds, ua, ub, K, ksteps, wave); break;
-        case 6: kloop<6>(lds, ua, ub, K, ksteps, wave); break;
-        case 7: kloop<7>(lds, ua, ub, K, ksteps, wave); break;
-        default: kloop<8>(lds, ua, ub, K, ksteps, wave); break;
+        case 1: kloop<1>(lds, sa, sb, lda, ldb, K, ksteps, lane, wave, ga); break;
+        case 2: kloop<2>(lds, sa, sb, lda, ldb, K, ksteps, lane, wave, ga); break;
+        case 3: kloop<3>(lds, sa, sb, lda, ldb, K, ksteps, lane, wave, ga); break;
+        case 4: kloop<4>(lds, sa, sb, lda, ldb, K, ksteps, lane, wave, ga); break;
+        case 5: kloop<5>(lds, sa, sb, lda, ldb, K, ksteps, lane, wave, ga); break;
+        case 6: kloop<6>(lds, sa, sb, lda, ldb, K, ksteps, lane, wave, ga); break;
+        case 7: kloop<7>(lds, sa, sb, lda, ldb, K, ksteps, lane, wave, ga); break;
+        default: kloop<8>(lds, sa, sb, lda, ldb, K, ksteps, lane, wave, ga); break;
         }
         // the trailing loads (all past K) have landed, every wave is done
         // with the ring (the next tile's prologue refills it), and the last
@@ -347,7 +398,8 @@ struct NarrowTile {
 // n_valid: tokens and GEMM columns of the tile that exist (n_valid a
 // multiple of 4).  Rows past m_valid fall past the resource; column groups
 // past n_valid take an out-of-range offset.
-template <int EPI, int OUT, int NTB, int NB>
+// AUX: the stores' cache-policy bits.
+template <int EPI, int OUT, int NTB, int NB, int AUX = 0>
 __device__ __forceinline__ void narrow_store(const f32x4_t (&v)[NTB][NB], void *D, int64_t ldd, int m_valid,
                                              int n_valid, int ntb, int tid)
 {
@@ -371,14 +423,14 @@ __device__ __forceinline__ void narrow_store(const f32x4_t (&v)[NTB][NB], void *
             const int n = wave * NB * 16 + 16 * nb + 4 * (lane >> 4);
             if constexpr (EPI == EPI_NONE) {
                 const uint32_t off = n < n_valid ? rowoff + (uint32_t)n * esize : kOOB;
-                bstore4<OUT>(r, off, a[0], a[1], a[2], a[3]);
+                bstore4<OUT, AUX>(r, off, a[0], a[1], a[2], a[3]);
             } else {
                 // gate: columns 0-7 of the block (lanes 0-31); up: 8-15, 32 lanes on
                 const float u0 = __shfl_xor(a[0], 32, 64), u1 = __shfl_xor(a[1], 32, 64);
                 const float u2 = __shfl_xor(a[2], 32, 64), u3 = __shfl_xor(a[3], 32, 64);
                 const int hc = (n >> 4) * 8 + (n & 15);
                 const uint32_t off = (lane < 32 && n < n_valid) ? rowoff + (uint32_t)hc * esize : kOOB;
-                bstore4<OUT>(r, off, silu_mul(a[0], u0), silu_mul(a[1], u1), silu_mul(a[2], u2), silu_mul(a[3], u3));
+                bstore4<OUT, AUX>(r, off, silu_mul(a[0], u0), silu_mul(a[1], u1), silu_mul(a[2], u2), silu_mul(a[3], u3));
             }
         }
     }

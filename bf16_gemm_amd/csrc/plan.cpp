@@ -588,6 +588,81 @@ static mgemm_status_t plan_grouped(const mgemm_grouped_desc_t *d, uint32_t flags
     return MGEMM_OK;
 }
 
+// The fused MoE layer: one persistent launch over all experts (the
+// eight-wave 256 x 256 tile for experts of more than 128 rows, the
+// few-token tile for the others), one workgroup per compute unit (each
+// takes the whole LDS).
+static mgemm_status_t plan_moe(const mgemm_moe_desc_t *d, uint32_t flags, mgemm_plan *p)
+{
+    if (flags) {
+        set_error("moe_fused_plan takes no flags");
+        return MGEMM_ERR_UNSUPPORTED;
+    }
+    if (d->num_experts < 1 || d->num_experts > 256) {
+        set_error("num_experts must lie in [1, 256] (got %d)", d->num_experts);
+        return d->num_experts < 1 ? MGEMM_ERR_INVALID_ARG : MGEMM_ERR_UNSUPPORTED;
+    }
+    if (d->max_total_rows < 0 || d->hidden <= 0 || d->inter <= 0 || d->max_total_rows >= kMaxDim ||
+        d->hidden >= kMaxDim || d->inter >= kMaxDim || d->stride_w1 < 0 || d->stride_w2 < 0) {
+        set_error("sizes must lie in [0, 2^30) and hidden, inter be positive");
+        return MGEMM_ERR_INVALID_ARG;
+    }
+    if (d->dtype != MGEMM_BF16 && d->dtype != MGEMM_F16) {
+        set_error("the fused MoE layer takes BF16 or F16 operands");
+        return (d->dtype == MGEMM_F32 || d->dtype == MGEMM_E4M3) ? MGEMM_ERR_UNSUPPORTED : MGEMM_ERR_INVALID_ARG;
+    }
+    const int64_t N1 = 2 * d->inter;
+    if (d->lda < d->hidden || d->ldw1 < N1 || d->ldw2 < d->hidden || d->ldh < d->inter || d->ldy < d->hidden) {
+        set_error("leading dimension too small");
+        return MGEMM_ERR_INVALID_ARG;
+    }
+    const int64_t w1 = (d->hidden - 1) * d->ldw1 + N1, w2 = (d->inter - 1) * d->ldw2 + d->hidden;
+    if (d->num_experts > 1 && (d->stride_w1 < w1 || d->stride_w2 < w2)) {
+        set_error("stride_w1 / stride_w2 smaller than one expert's weight matrix");
+        return MGEMM_ERR_INVALID_ARG;
+    }
+    if (d->hidden % 16 || d->inter % 64) {
+        set_error("the fused MoE layer needs hidden %% 16 == 0 and inter %% 64 == 0");
+        return MGEMM_ERR_UNSUPPORTED;
+    }
+    if (d->lda % 8 || d->ldw1 % 8 || d->ldw2 % 8 || d->ldy % 8 || d->stride_w1 % 8 || d->stride_w2 % 8 ||
+        d->ldh % 64) {
+        set_error("lda, ldw1, ldw2, ldy and the expert strides must be multiples of 8, ldh of 64");
+        return MGEMM_ERR_UNSUPPORTED;
+    }
+    if (d->lda > kMaxLd || d->ldw1 > kMaxLd || d->ldw2 > kMaxLd || d->ldh > kMaxLd || d->ldy > kMaxLd) {
+        set_error("leading dimensions above 2^20 elements are not supported");
+        return MGEMM_ERR_UNSUPPORTED;
+    }
+    if (w1 >= kMaxDim || w2 >= kMaxDim) {
+        set_error("one expert's W1 or W2 must hold fewer than 2^30 elements");
+        return MGEMM_ERR_UNSUPPORTED;
+    }
+    p->kind = PLAN_MOE;
+    p->moe = *d;
+    p->flags = flags;
+    p->num_cus = device_cus();
+    p->noop = d->max_total_rows == 0;
+    p->zero_fill = false;
+    p->tile = TILE_256x256_DTL;
+    p->tiles_m = p->tiles_n = p->tiles = 0;
+    p->group_m = 1;
+    p->xcd_remap = 0;
+    p->splits = 1;
+    // counters: sum over experts of their row blocks <= rows / 256 + experts
+    p->moe_slots = cdiv(d->max_total_rows, 256) + d->num_experts;
+    p->workspace_bytes = (size_t)moe_ws_bytes(p->moe_slots);
+    p->grid = p->num_cus;
+    char buf[320];
+    snprintf(buf, sizeof buf,
+             "moe_fused G=%d rows<=%lld hidden=%lld inter=%lld %s fc1+fc2 one launch: [129,inf)->256x256dtl "
+             "[1,129)->narrow128 (8 waves) order=largest-first grid=%d ws=%zu",
+             d->num_experts, (long long)d->max_total_rows, (long long)d->hidden, (long long)d->inter,
+             in_name(d->dtype), p->grid, p->workspace_bytes);
+    p->description = buf;
+    return MGEMM_OK;
+}
+
 }  // namespace mgemm
 
 using namespace mgemm;
@@ -646,13 +721,40 @@ extern "C" mgemm_status_t grouped_gemm_plan(const mgemm_grouped_desc_t *desc, ui
     return MGEMM_OK;
 }
 
+extern "C" mgemm_status_t moe_fused_plan(const mgemm_moe_desc_t *desc, uint32_t flags, mgemm_plan_t *out)
+{
+    if (!desc || !out) {
+        set_error("moe_fused_plan: null argument");
+        return MGEMM_ERR_INVALID_ARG;
+    }
+    *out = nullptr;
+    mgemm_plan *p = new (std::nothrow) mgemm_plan();
+    if (!p) {
+        set_error("moe_fused_plan: out of host memory");
+        return MGEMM_ERR_NO_MEMORY;
+    }
+    mgemm_status_t s;
+    try {
+        s = plan_moe(desc, flags, p);
+    } catch (...) {
+        s = MGEMM_ERR_NO_MEMORY;
+        set_error("moe_fused_plan: exception while planning");
+    }
+    if (s != MGEMM_OK) {
+        delete p;
+        return s;
+    }
+    *out = p;
+    return MGEMM_OK;
+}
+
 extern "C" mgemm_status_t gemm_plan_workspace_size(mgemm_plan_t plan, size_t *bytes)
 {
     if (!plan || !bytes) {
         set_error("gemm_plan_workspace_size: null argument");
         return MGEMM_ERR_INVALID_ARG;
     }
-    *bytes = plan->kind == PLAN_DENSE ? plan->workspace_bytes : 0;
+    *bytes = plan->kind == PLAN_GROUPED ? 0 : plan->workspace_bytes;
     return MGEMM_OK;
 }
 
@@ -695,7 +797,8 @@ extern "C" mgemm_status_t gemm_plan_info(mgemm_plan_t plan, mgemm_plan_info_t *i
     info->tiles_m = plan->tiles_m;
     info->tiles_n = plan->tiles_n;
     info->tiles = plan->tiles;
-    const int64_t K = plan->kind == PLAN_DENSE ? plan->dense.K : plan->grouped.K;
+    const int64_t K = plan->kind == PLAN_DENSE ? plan->dense.K
+                      : plan->kind == PLAN_GROUPED ? plan->grouped.K : plan->moe.hidden;
     info->k_steps = cdiv(K, kBK);
     if (plan->kind == PLAN_DENSE && plan->tiles > 0)
         info->coverage = (double)plan->dense.M * (double)(plan->dense.N & ~(int64_t)3) /

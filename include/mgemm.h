@@ -159,8 +159,8 @@ mgemm_status_t gemm_plan(const mgemm_desc_t *desc, uint32_t flags, mgemm_plan_t 
 mgemm_status_t grouped_gemm_plan(const mgemm_grouped_desc_t *desc, uint32_t flags, mgemm_plan_t *out);
 
 /* Device workspace in bytes that run calls with this plan need (may be 0):
- * splits * M * (N rounded down to a multiple of 4) * 4 for a split dense
- * plan, else 0.  The workspace is scratch owned by the caller; it must be
+ * a split dense plan's counters and fp32 partial sums, a fused MoE plan's
+ * schedule and counters (moe_fused_plan), else 0.  The workspace is scratch owned by the caller; it must be
  * 16-byte aligned, and two runs in flight at once must not share it. */
 mgemm_status_t gemm_plan_workspace_size(mgemm_plan_t plan, size_t *bytes);
 
@@ -320,6 +320,67 @@ mgemm_status_t grouped_gemm_run_gather(mgemm_plan_t plan, const void *X, int64_t
 mgemm_status_t mgemm_moe_combine(const void *Z, int64_t z_rows, int64_t ldz, const int32_t *d_pos,
                                  const float *d_weights, void *Y, int64_t ldy, int64_t T, int32_t top_k, int64_t H,
                                  mgemm_dtype_t dtype, mgemm_stream_t stream);
+
+/* The MoE expert layer's two GEMMs in one persistent launch ("MegaMoE：
+ * Blackwell 与 Hopper 的融合算子解读", Hopper section 01 on the resident
+ * FC1 -> SwiGLU -> FC2 pipeline and its fc1_done counters, Blackwell section
+ * 06 on publishing a finished tile through a counter, Hopper sections 13 and
+ * 15 on when to publish and how to order the tasks).  For every expert e with
+ * rows [off[e], off[e+1]):
+ *   FC1: H[r, :] = SiLU(gate) * up of row r of X times W1_e, the SILU_GATE_I8
+ *        epilogue of grouped_gemm_run (gate and up columns of W1_e
+ *        interleaved in blocks of 8, gate first), each h rounded once to dtype;
+ *   FC2: Y[r, :] = H[r, :] x W2_e, accumulated in fp32, rounded once.
+ * H is both an output and FC2's input: FC2 reads the rounded h, so Y equals
+ * what grouped_gemm_run of FC1 then of FC2 gives, bit for bit.
+ *
+ * Shapes (elements):
+ *  - num_experts in [1, 256]; max_total_rows < 2^30: rows of H and Y (and of
+ *    X when not gathering) that exist;
+ *  - hidden: FC1's K and FC2's N, a multiple of 16; inter: the h width,
+ *    FC1's N is 2 * inter and FC2's K is inter, a multiple of 64;
+ *  - X row-major [rows][lda], lda >= hidden; W1_e at W1 + e * stride_w1,
+ *    row-major [hidden][2 * inter] with ldw1 >= 2 * inter; W2_e at W2 + e *
+ *    stride_w2, row-major [inter][hidden] with ldw2 >= hidden; H row-major
+ *    with ldh >= inter and ldh a multiple of 64; Y row-major, ldy >= hidden;
+ *  - lda, ldw1, ldw2, ldy, stride_w1 and stride_w2 multiples of 8, leading
+ *    dimensions at most 2^20, one expert's W1 or W2 below 2^30 elements;
+ *  - dtype BF16 or F16 for every operand.
+ * Other values: MGEMM_ERR_INVALID_ARG (inconsistent) or _UNSUPPORTED. */
+typedef struct {
+    int32_t num_experts;
+    int64_t max_total_rows;
+    int64_t hidden, inter;
+    mgemm_dtype_t dtype;
+    int64_t lda;
+    int64_t ldw1, stride_w1;
+    int64_t ldw2, stride_w2;
+    int64_t ldh, ldy;
+} mgemm_moe_desc_t;
+
+/* Make a plan for the fused layer (flags must be 0).  Its workspace
+ * (gemm_plan_workspace_size) holds the task schedule and the per-(expert,
+ * row block) counters: 6400 + 4 * (ceil(max_total_rows / 256) + num_experts)
+ * bytes rounded up to 256. */
+mgemm_status_t moe_fused_plan(const mgemm_moe_desc_t *desc, uint32_t flags, mgemm_plan_t *out);
+
+/* Enqueue the fused layer on `stream`: a one-workgroup kernel that orders
+ * the experts (largest first) and clears the counters, then the persistent
+ * kernel.  d_row_offsets: device int32 prefix sums as for grouped_gemm_run.
+ * d_row_index: NULL (row r of FC1 reads row r of X, which has
+ * max_total_rows rows), or a device int32 array with one entry per routed
+ * row, row r reading X row d_row_index[r] of x_rows rows (entries outside
+ * [0, x_rows) read as zeros; x_rows * lda * 2 < 2^31).  X, W1, W2, Y and
+ * the workspace must be 16-byte aligned, H 128-byte aligned (each h row block
+ * is written on one compute unit and read on others in the same launch, so
+ * no two row blocks may share a 128-byte line), else MGEMM_ERR_UNSUPPORTED.
+ * The workspace must not be shared by runs in flight at once; a missing or
+ * short one gives MGEMM_ERR_WORKSPACE.  H and Y must not overlap each other
+ * or the inputs.  Offsets that break the rules give undefined results but
+ * no access outside the buffers. */
+mgemm_status_t moe_fused_run(mgemm_plan_t plan, const void *X, int64_t x_rows, const int32_t *d_row_index,
+                             const void *W1, const void *W2, void *H, void *Y, const int32_t *d_row_offsets,
+                             void *workspace, size_t workspace_bytes, mgemm_stream_t stream);
 
 /* Library version, e.g. "mgemm 0.1 gfx950". */
 const char *mgemm_version(void);

@@ -16,7 +16,7 @@ HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "mg
 def test_exports_match_header():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)      # drop comments
-    declared = set(re.findall(r"\b((?:gemm|grouped_gemm|mgemm)_\w+)\s*\(", text))
+    declared = set(re.findall(r"\b((?:gemm|grouped_gemm|mgemm|moe)_\w+)\s*\(", text))
     assert declared == set(mg.EXPORTS), declared ^ set(mg.EXPORTS)
     for name in declared:
         assert hasattr(mg.lib, name), name
@@ -288,3 +288,63 @@ def test_e4m3_plan_rules():
     with pytest.raises(mg.MgemmError) as e:
         mg.gemm_run_scaled(bf, fake, fake, fake, fake, fake, stream=0)
     assert e.value.status == mg.ERR_UNSUPPORTED
+
+
+def test_moe_fused_plan_rules():
+    """The fused MoE plan: shape and alignment rules, its workspace formula
+    (6400 bytes of schedule, then one int32 counter per possible row block:
+    ceil(rows / 256) + experts), and the run call's checks before any
+    launch (the fake device addresses are never touched)."""
+    p = mg.moe_fused_plan(64, 32768, 7168, 2048)
+    assert p.workspace_size() == (6400 + 4 * (128 + 64) + 255) // 256 * 256
+    assert "moe_fused G=64" in p.describe() and "largest-first" in p.describe()
+    assert p.info().grid == p.info().num_cus
+    q = mg.moe_fused_plan(8, 384, 256, 128, dtype="f16")
+    assert q.workspace_size() == (6400 + 4 * (2 + 8) + 255) // 256 * 256
+    bad = [
+        (dict(num_experts=0), mg.ERR_INVALID_ARG),
+        (dict(num_experts=257), mg.ERR_UNSUPPORTED),
+        (dict(hidden=0), mg.ERR_INVALID_ARG),
+        (dict(hidden=264), mg.ERR_UNSUPPORTED),        # hidden % 16
+        (dict(inter=96), mg.ERR_UNSUPPORTED),          # inter % 64
+        (dict(ldh=160), mg.ERR_UNSUPPORTED),           # ldh % 64
+        (dict(lda=200), mg.ERR_INVALID_ARG),           # lda < hidden
+        (dict(ldw1=200), mg.ERR_INVALID_ARG),          # ldw1 < 2 inter
+        (dict(stride_w1=8), mg.ERR_INVALID_ARG),
+        (dict(dtype="f32"), mg.ERR_UNSUPPORTED),
+        (dict(flags=mg.PLAN_FORCE_TILE_NARROW), mg.ERR_UNSUPPORTED),
+    ]
+    for kw, status in bad:
+        args = dict(num_experts=8, max_total_rows=384, hidden=256, inter=128)
+        args.update(kw)
+        with pytest.raises(mg.MgemmError) as e:
+            mg.moe_fused_plan(**args)
+        assert e.value.status == status, kw
+    fake = 1 << 20
+    ws_n = q.workspace_size()
+    # no workspace, a short one, a misaligned H, a non-MoE plan, a null pointer
+    with pytest.raises(mg.MgemmError) as e:
+        mg.moe_fused_run(q, fake, fake, fake, fake, fake, fake, workspace=None, stream=0)
+    assert e.value.status == mg.ERR_WORKSPACE
+    with pytest.raises(mg.MgemmError) as e:
+        mg.moe_fused_run(q, fake, fake, fake, fake, fake, fake, workspace=fake, workspace_bytes=ws_n - 256,
+                         stream=0)
+    assert e.value.status == mg.ERR_WORKSPACE
+    with pytest.raises(mg.MgemmError) as e:
+        mg.moe_fused_run(q, fake, fake, fake, fake + 64, fake, fake, workspace=fake, workspace_bytes=ws_n,
+                         stream=0)
+    assert e.value.status == mg.ERR_UNSUPPORTED
+    with pytest.raises(mg.MgemmError) as e:
+        mg.moe_fused_run(mg.gemm_plan(4, 8, 8, "bf16"), fake, fake, fake, fake, fake, fake, workspace=fake,
+                         workspace_bytes=ws_n, stream=0)
+    assert e.value.status == mg.ERR_INVALID_ARG
+    with pytest.raises(mg.MgemmError) as e:
+        mg.moe_fused_run(q, fake, fake, None, fake, fake, fake, workspace=fake, workspace_bytes=ws_n, stream=0)
+    assert e.value.status == mg.ERR_INVALID_ARG
+    with pytest.raises(mg.MgemmError) as e:
+        mg.moe_fused_run(q, fake, fake, fake, fake, fake, fake, workspace=fake, workspace_bytes=ws_n,
+                         row_index=fake, x_rows=1 << 23, stream=0)
+    assert e.value.status == mg.ERR_INVALID_ARG
+    # no rows: nothing to do, nothing touched
+    mg.moe_fused_run(mg.moe_fused_plan(8, 0, 256, 128), fake, fake, fake, fake, fake, fake, workspace=None,
+                     stream=0)
