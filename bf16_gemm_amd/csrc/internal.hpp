@@ -122,6 +122,7 @@ struct mgemm_plan {
     int kchunk;      // elements of K per range
     int64_t slab_offset;  // split reduced in the launch: bytes of arrival counters before the partial slabs
     int sk_tiles;         // stream-K: tiles cut into `splits` K ranges (the rest run whole), else 0
+    int64_t lds_bytes;    // the tile's ring (dense plans), from the stage budget
     size_t workspace_bytes;
     bool zero_fill;  // K == 0
     bool noop;       // M == 0 or N == 0

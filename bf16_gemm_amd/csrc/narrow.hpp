@@ -322,11 +322,18 @@ struct NarrowTile {
         using R = Ring<NV>;
         setup<NV>(lane, wave, lda, ldb, ga);
         const OperandSrc ua = uniform_src(sa), ub = uniform_src(sb);
-        // prologue: steps 0 .. NST-2 (a loop: unrolled, the deep rings'
-        // buffer descriptors would all be live at once)
+        // prologue: steps 0 .. NST-2 (unrolled for the shallow rings; a loop
+        // for the deep ones, whose unrolled buffer descriptors would all be
+        // live at once)
+        if constexpr (R::NST <= 7) {
+#pragma unroll
+            for (int s = 0; s < R::NST - 1; ++s)
+                load_step<NV>(lds, lds + s * R::SLOT, wave, ua.at_step(s), ub.at_step(s), K - s * kBK);
+        } else {
 #pragma unroll 1
-        for (int s = 0; s < R::NST - 1; ++s)
-            load_step<NV>(lds, lds + s * R::SLOT, wave, ua.at_step(s), ub.at_step(s), K - s * kBK);
+            for (int s = 0; s < R::NST - 1; ++s)
+                load_step<NV>(lds, lds + s * R::SLOT, wave, ua.at_step(s), ub.at_step(s), K - s * kBK);
+        }
         mfma_drain();
         int slot = 0, fill = R::NST - 1;
         for (int kt = 0; kt < ksteps; ++kt) {

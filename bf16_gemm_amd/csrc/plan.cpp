@@ -33,6 +33,24 @@ static const TileShape kTiles[NUM_TILES] = {
 
 const TileShape &tile_shape(int tile) { return kTiles[tile]; }
 
+// LDS of one CU on gfx950.
+constexpr int64_t kLdsPerCu = 160 * 1024;
+
+// Bytes of one operand's ring: `slots` stages of rows x bk elements.  The
+// stage budget of "B200 的 2CTA 怎样调优" (section 三, the tile calculator:
+// stages x (BM x BK + BK x BN) x element bytes) is this for A plus this for
+// B with equal stage counts (mgemm_tile_budget); the planner applies it per
+// operand, since the direct-to-LDS tile gives one operand a deeper ring.
+static int64_t operand_ring_bytes(int64_t rows, int64_t bk, int64_t slots, int64_t elt)
+{
+    return slots * rows * bk * elt;
+}
+
+static int64_t ring_lds_bytes(const TileShape &t, int a_slots, int b_slots)
+{
+    return operand_ring_bytes(t.bm, kBK, a_slots, 2) + operand_ring_bytes(t.bn, kBK, b_slots, 2);
+}
+
 // Wave layout and ring depths of a dense plan's tile: the direct-to-LDS
 // tile runs dense plans on four waves of 128 x 128 (the tile table's 2x4 is
 // its grouped launches' layout), with the 3-slot ring on B when B is
@@ -221,6 +239,31 @@ static int forced_tile(uint32_t flags)
     return -1;
 }
 
+// Tile rows per L2 group.  Tiles are issued m fastest inside groups of
+// group_m tile rows, and with the XCD remap each XCD takes a run of
+// consecutive tiles, so the tiles one XCD runs at once (its CUs times the
+// workgroups per CU) form a group_m x group_n block sharing its L2.  Of the
+// power-of-two shapes the one whose operand rows and columns --
+// mgemm_group_working_set, the super-tile working set of "GEMM优化（三）"
+// section 3.4 -- are fewest is taken, the one with fewer rows on a tie: 4 x 8
+// for the 256 x 256 tile on 32 CUs, which measured fastest at 8192^3 (2, 8,
+// 16 and 32 rows were 3-20 % slower).
+static int pick_group_m(const TileShape &t, int64_t tiles_m, int cus, int occ, int64_t K)
+{
+    const int conc = std::max(1, cus / 8 * occ);
+    int best = 1;
+    int64_t best_ws = INT64_MAX;
+    for (int gm = 1; gm <= conc && gm <= tiles_m; gm *= 2) {
+        const int gn = (conc + gm - 1) / gm;
+        const int64_t ws = mgemm_group_working_set(gm, gn, t.bm, t.bn, std::max<int64_t>(K, 1), 2);
+        if (ws < best_ws) {
+            best_ws = ws;
+            best = gm;
+        }
+    }
+    return best;
+}
+
 static mgemm_status_t plan_dense(const mgemm_desc_t *d, uint32_t flags, mgemm_plan *p)
 {
     if (d->M < 0 || d->N < 0 || d->K < 0 || d->M >= kMaxDim || d->N >= kMaxDim || d->K >= kMaxDim) {
@@ -291,6 +334,10 @@ static mgemm_status_t plan_dense(const mgemm_desc_t *d, uint32_t flags, mgemm_pl
         for (int t = 0; t < NUM_TILES; ++t) {
             if (kTiles[t].forced_only || !dense_fn(t, ak, bk, in, out))
                 continue;
+            int cw, cn, ca, cb;
+            dense_waves(t, bk, cw, cn, ca, cb);
+            if (ring_lds_bytes(kTiles[t], ca, cb) > kLdsPerCu)
+                continue;   // its ring does not fit a CU's LDS
             // the 256 x 256 tile runs on the direct-to-LDS engine where it can (stream-K tails included)
             const bool sk = t == TILE_256x256 && !e4m3 && (flags >> 16 & 0xFF) == 0 &&
                             dense_fn(TILE_256x256_DTL, ak, bk, in, out) != nullptr;
@@ -429,16 +476,21 @@ static mgemm_status_t plan_dense(const mgemm_desc_t *d, uint32_t flags, mgemm_pl
     }
     const int64_t tasks = p->sk_tiles > 0 ? p->tiles - p->sk_tiles + (int64_t)p->sk_tiles * p->splits
                                           : p->tiles * p->splits;
-    const int64_t slots = (int64_t)p->num_cus * ts.occupancy;
-    p->grid = (int)std::max<int64_t>(1, std::min<int64_t>(tasks, slots));
-    // Tiles are issued in groups of group_m tile rows, m fastest; with the XCD
-    // remap each XCD takes a run of consecutive tiles, so group_m sets the
-    // shape of the tile block that shares one XCD's L2.  Four rows measured
-    // fastest on the 256x256 tile at 8192^3 (2, 8, 16 and 32 were 3-20% slower).
-    p->group_m = (int)std::max<int64_t>(1, std::min<int64_t>(4, p->tiles_m));
-    p->xcd_remap = (flags & MGEMM_PLAN_NO_XCD_REMAP) ? 0 : (p->grid % 8 == 0 ? 1 : 0);
     int wm, wn, a_slots, b_slots;
     dense_waves(tile, bk, wm, wn, a_slots, b_slots);
+    // the ring must fit the LDS, and as many workgroups per CU as the tile
+    // assumes must fit beside each other, else fewer
+    p->lds_bytes = ring_lds_bytes(ts, a_slots, b_slots);
+    if (p->lds_bytes > kLdsPerCu) {
+        set_error("the %s tile's ring (%d + %d stages) needs %lld bytes of LDS, more than a CU's %lld",
+                  tile_name(tile), a_slots, b_slots, (long long)p->lds_bytes, (long long)kLdsPerCu);
+        return MGEMM_ERR_UNSUPPORTED;
+    }
+    const int occ = (int)std::min<int64_t>(ts.occupancy, kLdsPerCu / p->lds_bytes);
+    const int64_t slots = (int64_t)p->num_cus * occ;
+    p->grid = (int)std::max<int64_t>(1, std::min<int64_t>(tasks, slots));
+    p->group_m = pick_group_m(ts, p->tiles_m, p->num_cus, occ, d->K);
+    p->xcd_remap = (flags & MGEMM_PLAN_NO_XCD_REMAP) ? 0 : (p->grid % 8 == 0 ? 1 : 0);
     char stages[16];
     if (a_slots == b_slots)
         snprintf(stages, sizeof stages, "%d", a_slots);
@@ -793,7 +845,7 @@ extern "C" mgemm_status_t gemm_plan_info(mgemm_plan_t plan, mgemm_plan_info_t *i
                     b_slots);
         info->stages = std::max(a_slots, b_slots);
     }
-    info->lds_bytes = ts.lds_bytes;
+    info->lds_bytes = plan->kind == PLAN_DENSE ? (int32_t)plan->lds_bytes : ts.lds_bytes;
     info->tiles_m = plan->tiles_m;
     info->tiles_n = plan->tiles_n;
     info->tiles = plan->tiles;
@@ -822,7 +874,7 @@ extern "C" mgemm_status_t mgemm_tile_budget(int64_t M, int64_t N, int64_t K, int
     }
     out->tiles = cdiv(M, BM) * cdiv(N, BN);
     out->coverage = out->tiles > 0 ? (double)M * (double)N / ((double)out->tiles * BM * BN) : 0.0;
-    out->lds_bytes = (int64_t)stages * ((int64_t)BM * BK + (int64_t)BK * BN) * elt_bytes;
+    out->lds_bytes = operand_ring_bytes(BM, BK, stages, elt_bytes) + operand_ring_bytes(BN, BK, stages, elt_bytes);
     out->k_steps = cdiv(K, BK);
     return MGEMM_OK;
 }

@@ -206,9 +206,44 @@ def test_direct_to_lds_tile_choice():
 
 
 def test_lds_budget_rejects_three_stage_macro_tile():
-    # three 256x256x64 bf16 stages would need 192 KiB: more than a CU's 160 KiB
+    """The planner sizes each plan's ring with the stage budget and keeps it
+    within a CU's 160 KiB: three stages of both 256x256 operands (192 KiB)
+    do not fit, so the 256x256 plans give the deeper third stage to one
+    operand only (3 + 2 stages = 160 KiB), A when B is row-major, B when it
+    is column-major; two-stage tiles fit twice per CU."""
     assert mg.tile_budget(256, 256, 64, 256, 256, 64, 3, 2).lds_bytes == 192 * 1024 > 160 * 1024
-    assert mg.tile_budget(256, 256, 64, 256, 256, 64, 2, 2).lds_bytes == 128 * 1024
+    half = mg.tile_budget(256, 256, 64, 256, 256, 64, 1, 2).lds_bytes // 2   # one operand's stage
+    for bl, deep in (("row", "3a/2b"), ("col", "2a/3b")):
+        p = mg.gemm_plan(8192, 8192, 8192, "bf16", d_type="bf16", b_layout=bl)
+        inf = p.info()
+        assert "tile=256x256dtl" in p.describe() and f"stages={deep}" in p.describe()
+        assert inf.stages == 3 and inf.lds_bytes == 5 * half == 160 * 1024
+    p = mg.gemm_plan(2048, 2048, 512, "bf16")
+    assert "tile=128x128" in p.describe()
+    assert p.info().lds_bytes == mg.tile_budget(2048, 2048, 512, 128, 128, 64, 2, 2).lds_bytes == 64 * 1024
+    assert p.info().grid == min(p.info().tiles, 2 * p.info().num_cus)   # two rings per CU
+
+
+def test_group_m_from_working_set():
+    """group_m: of the power-of-two blocks of tiles one XCD runs at once
+    (its CUs x workgroups per CU), the one whose super-tile working set is
+    smallest, fewer rows on a tie -- 4 x 8 for the 256x256 tile."""
+    def expect(p, BM, BN, occ):
+        inf = p.info()
+        conc = inf.num_cus // 8 * occ
+        best, best_ws, gm = 1, None, 1
+        while gm <= conc and gm <= inf.tiles_m:
+            ws = mg.group_working_set(gm, -(-conc // gm), BM, BN, p.desc.K, 2)
+            if best_ws is None or ws < best_ws:
+                best, best_ws = gm, ws
+            gm *= 2
+        return best
+    p = mg.gemm_plan(8192, 8192, 8192, "bf16", d_type="bf16")
+    assert p.info().group_m == expect(p, 256, 256, 1) == 4
+    p = mg.gemm_plan(2048, 2048, 512, "bf16")
+    assert p.info().group_m == expect(p, 128, 128, 2) == 8
+    p = mg.gemm_plan(128, 7168, 2048, "bf16", d_type="bf16")
+    assert p.info().group_m == 1   # one tile row
 
 
 @pytest.mark.parametrize("kw,status", [
