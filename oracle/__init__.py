@@ -22,6 +22,11 @@ and from which passage of the pages:
   tensor ("MegaMoE", Hopper section 04: per-tensor scales are applied once,
   in the epilogue): scale_a x scale_b x the ascending-k double sum of the
   decoded E4M3 products (E4M3 bits from the OCP 8-bit float layout).
+* ``e8m0`` / ``gemm_e4m3_block_ref`` -- the blockwise FP8 form ("MegaMoE",
+  Hopper section 04: activation scales per token and per 128-k block,
+  weight scales per 128 x 128 block, each K block's partial product scaled
+  before it is added): scales are E8M0 bytes (2^(v - 127), 255 NaN), the
+  power-of-two scale format the pages name for MXFP8 blocks.
 * ``grouped_ref`` / ``moe_ref`` -- the per-expert form: expert e owns rows
   [off[e], off[e+1]) of the routed activations and multiplies them by its
   own weight matrix ("MegaMoE", Recap 1 on the MoE stages: FC1 -> activation
@@ -85,6 +90,10 @@ def _load():
     lib.oracle_decode_e4m3.argtypes = [vp, i64, dp]
     lib.oracle_gemm_e4m3_ref.argtypes = [i64, i64, i64, vp, i64, vp, i64, ctypes.c_double, ctypes.c_double, dp]
     lib.oracle_gemm_e4m3_ref.restype = i32
+    lib.oracle_e8m0_to_double.argtypes = [ctypes.c_uint8]
+    lib.oracle_e8m0_to_double.restype = ctypes.c_double
+    lib.oracle_gemm_e4m3_block_ref.argtypes = [i64, i64, i64, vp, i64, vp, i64, vp, i64, vp, i64, dp]
+    lib.oracle_gemm_e4m3_block_ref.restype = i32
     lib.oracle_gemm_e4m3_ref_sampled.argtypes = [i64, vp, i64, vp, i64, ctypes.c_double, ctypes.c_double,
                                                  vp, vp, i64, dp]
     _lib = lib
@@ -279,6 +288,38 @@ def gemm_e4m3_ref(A: np.ndarray, B: np.ndarray, scale_a: float = 1.0, scale_b: f
     rc = _load().oracle_gemm_e4m3_ref(M, N, K, _p(A), K, _p(B), K, float(scale_a), float(scale_b), _p(ref))
     if rc != 0:
         raise MemoryError("oracle_gemm_e4m3_ref could not allocate its temporaries")
+    return ref
+
+
+def e8m0(v) -> float:
+    """Value of an E8M0 scale byte: 2^(v - 127), NaN for 255."""
+    return _load().oracle_e8m0_to_double(int(v))
+
+
+def gemm_e4m3_block_ref(A: np.ndarray, B: np.ndarray, sa: np.ndarray, sb: np.ndarray) -> np.ndarray:
+    """Unrounded fp64 blockwise-scaled product of E4M3 operands ("MegaMoE：
+    Blackwell 与 Hopper 的融合算子解读", Hopper section 04, the blockwise path).
+
+    ``A``: [M][K] uint8; ``B``: [N][K] uint8 (the K x N operand, k
+    contiguous); ``sa``: [M][ceil(K/128)] E8M0 bytes, one per row and 128-k
+    block; ``sb``: [ceil(N/128)][ceil(K/128)] E8M0 bytes, one per 128 output
+    columns and 128-k block.  Returns M x N float64:
+    sum over blocks b of e8m0(sa[i,b]) e8m0(sb[j//128,b]) sum_{k in b} a b.
+    """
+    for x, n in ((A, "A"), (B, "B"), (sa, "sa"), (sb, "sb")):
+        _check_u8(x, n)
+    A, B, sa, sb = (np.ascontiguousarray(x) for x in (A, B, sa, sb))
+    (M, K), (N, K2) = A.shape, B.shape
+    if K2 != K:
+        raise ValueError(f"inner dimensions differ: {K} vs {K2}")
+    kb, nb = -(-K // 128), -(-N // 128)
+    if sa.shape[0] != M or sa.shape[1] < kb or sb.shape[0] < nb or sb.shape[1] < kb:
+        raise ValueError(f"scale shapes {sa.shape}, {sb.shape} do not cover M={M}, N={N}, K={K}")
+    ref = np.empty((M, N), dtype=np.float64)
+    rc = _load().oracle_gemm_e4m3_block_ref(M, N, K, _p(A), K, _p(B), K, _p(sa), sa.shape[1], _p(sb),
+                                            sb.shape[1], _p(ref))
+    if rc != 0:
+        raise MemoryError("oracle_gemm_e4m3_block_ref could not allocate its temporaries")
     return ref
 
 

@@ -378,6 +378,69 @@ int oracle_gemm_e4m3_ref(int64_t M, int64_t N, int64_t K, const uint8_t *A, int6
 }
 
 /* The same value at the elements (rows[t], cols[t]) only. */
+/*
+ * Block scales in E8M0, the OCP microscaling scale format (the pages name it
+ * for MXFP8 data, one scale per block, in "MegaMoE：Blackwell 与 Hopper 的融合
+ * 算子解读", the quantised-dispatch formats table): an unsigned 8-bit
+ * exponent, value 2^(v - 127); 255 is NaN.
+ */
+double oracle_e8m0_to_double(uint8_t v)
+{
+    return v == 255 ? NAN : ldexp(1.0, (int)v - 127);
+}
+
+/*
+ * Blockwise-scaled FP8 product (MegaMoE, Hopper section 04, the blockwise
+ * path: activations scaled per token and per 128-element block of K,
+ * weights per 128 x 128 block, and the dequantisation inside the K loop:
+ * each K block's partial product is scaled before it joins the total).  A
+ * is stored [M][lda], B [N][ldb] (k contiguous, as in oracle_gemm_e4m3_ref);
+ * sa is [M][lds_a] bytes, sa[i][b] scaling row i of A over k in
+ * [128 b, 128 b + 128); sb is [ceil(N / 128)][lds_b] bytes, sb[c][b]
+ * scaling output columns [128 c, 128 c + 128) over the same k block:
+ *   ref[i][j] = sum over b < ceil(K / 128) of
+ *               e8m0(sa[i][b]) x e8m0(sb[j / 128][b]) x sum_{k in block b} a(i,k) b(k,j).
+ * Each block's sum is exact in double; the scales are powers of two.
+ */
+int oracle_gemm_e4m3_block_ref(int64_t M, int64_t N, int64_t K, const uint8_t *A, int64_t lda, const uint8_t *B,
+                               int64_t ldb, const uint8_t *sa, int64_t lds_a, const uint8_t *sb, int64_t lds_b,
+                               double *ref)
+{
+    const int64_t nblk = (K + 127) / 128;
+    double *a = (double *)malloc(sizeof(double) * (size_t)(M * K > 0 ? M * K : 1));
+    double *b = (double *)malloc(sizeof(double) * (size_t)(N * K > 0 ? N * K : 1));
+    if (!a || !b) {
+        free(a);
+        free(b);
+        return -1;
+    }
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < M; ++i)
+        for (int64_t k = 0; k < K; ++k)
+            a[i * K + k] = oracle_e4m3_to_double(A[i * lda + k]);
+#pragma omp parallel for schedule(static)
+    for (int64_t j = 0; j < N; ++j)
+        for (int64_t k = 0; k < K; ++k)
+            b[j * K + k] = oracle_e4m3_to_double(B[j * ldb + k]);
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t i = 0; i < M; ++i)
+        for (int64_t j = 0; j < N; ++j) {
+            double total = 0.0;
+            for (int64_t blk = 0; blk < nblk; ++blk) {
+                const int64_t k1 = (blk + 1) * 128 < K ? (blk + 1) * 128 : K;
+                double part = 0.0;
+                for (int64_t k = blk * 128; k < k1; ++k)
+                    part += a[i * K + k] * b[j * K + k];
+                total += oracle_e8m0_to_double(sa[i * lds_a + blk]) *
+                         oracle_e8m0_to_double(sb[(j / 128) * lds_b + blk]) * part;
+            }
+            ref[i * N + j] = total;
+        }
+    free(a);
+    free(b);
+    return 0;
+}
+
 void oracle_gemm_e4m3_ref_sampled(int64_t K, const uint8_t *A, int64_t lda, const uint8_t *B, int64_t ldb,
                                   double scale_a, double scale_b, const int64_t *rows, const int64_t *cols,
                                   int64_t n, double *out)

@@ -115,3 +115,119 @@ def test_grouped_is_the_per_expert_product():
     for e in range(len(counts)):
         lo, hi = off[e], off[e + 1]
         assert np.array_equal(g[lo:hi], dense_all[e][lo:hi] * (0.75 * sb[e]))
+
+
+# --- blockwise scales (E8M0 bytes: one per row of A and 128-k block, one per
+# 128 output columns and 128-k block) ---
+
+def test_e8m0_all_codes_match_torch():
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e8m0fnu).to(torch.float64).numpy()
+    got = np.array([oracle.e8m0(c) for c in codes])
+    assert np.isnan(got[255]) and np.isnan(ref[255])
+    assert np.array_equal(got[:255], ref[:255])
+    assert (oracle.e8m0(127), oracle.e8m0(128), oracle.e8m0(126)) == (1.0, 2.0, 0.5)
+
+
+def unit_scales(M, N, K):
+    return (np.full((M, -(-K // 128)), 127, np.uint8), np.full((-(-N // 128), -(-K // 128)), 127, np.uint8))
+
+
+def test_block_unit_scales_are_the_per_tensor_product():
+    rs = np.random.RandomState(11)
+    M, N, K = 9, 200, 300   # two column blocks, three k blocks (the last one 44 long)
+    A, B = finite_codes((M, K), rs), finite_codes((N, K), rs)
+    sa, sb = unit_scales(M, N, K)
+    assert np.array_equal(oracle.gemm_e4m3_block_ref(A, B, sa, sb), oracle.gemm_e4m3_ref(A, B))
+
+
+def test_block_closed_form_all_ones():
+    """A = B = 1.0 everywhere: block b's partial product is its length, so
+    D[i, j] = sum_b len_b 2^(ea[i,b] + eb[j//128, b]) with len = 128, 128, 128, 72."""
+    M, N, K = 6, 300, 456
+    A = np.full((M, K), 0x38, np.uint8)
+    B = np.full((N, K), 0x38, np.uint8)
+    ea = np.array([[(i + b) % 3 - 1 for b in range(4)] for i in range(M)])
+    eb = np.array([[(c + 2 * b) % 2 for b in range(4)] for c in range(3)])
+    sa, sb = (ea + 127).astype(np.uint8), (eb + 127).astype(np.uint8)
+    got = oracle.gemm_e4m3_block_ref(A, B, sa, sb)
+    lens = [128, 128, 128, 72]
+    for i in range(M):
+        for j in range(N):
+            assert got[i, j] == sum(lens[b] * 2.0 ** (ea[i, b] + eb[j // 128, b]) for b in range(4)), (i, j)
+
+
+def test_block_rational_brute_force():
+    """Exact rational arithmetic on torch's own decoders of both formats."""
+    rs = np.random.RandomState(12)
+    M, N, K = 3, 130, 150
+    A, B = finite_codes((M, K), rs), finite_codes((N, K), rs)
+    sa = rs.randint(120, 135, size=(M, 2)).astype(np.uint8)
+    sb = rs.randint(120, 135, size=(2, 2)).astype(np.uint8)
+    f8 = lambda c: Fraction(torch.tensor([int(c)], dtype=torch.uint8).view(torch.float8_e4m3fn)
+                            .to(torch.float64).item())
+    e8 = lambda c: Fraction(torch.tensor([int(c)], dtype=torch.uint8).view(torch.float8_e8m0fnu)
+                            .to(torch.float64).item())
+    got = oracle.gemm_e4m3_block_ref(A, B, sa, sb)
+    for i in range(M):
+        for j in (0, 1, 64, 127, 128, 129):
+            exact = Fraction(0)
+            for k in range(K):
+                exact += e8(sa[i, k // 128]) * e8(sb[j // 128, k // 128]) * f8(A[i, k]) * f8(B[j, k])
+            assert Fraction(got[i, j]) == exact, (i, j)
+
+
+def test_block_scale_pairs_with_its_own_block():
+    """Raising scale (i, b) by one power of two equals doubling row i's codes
+    in k block b (codes with exponent field <= 13 double exactly); raising
+    (c, b) of B's scales changes only output columns [128 c, 128 c + 128)."""
+    rs = np.random.RandomState(13)
+    M, N, K = 5, 260, 330
+    A = finite_codes((M, K), rs)
+    A[((A >> 3) & 15) > 13] &= 0x87     # exponent field <= 13 everywhere (doubling stays finite)
+    B = finite_codes((N, K), rs)
+    sa = rs.randint(124, 131, size=(M, 3)).astype(np.uint8)
+    sb = rs.randint(124, 131, size=(3, 3)).astype(np.uint8)
+    base = oracle.gemm_e4m3_block_ref(A, B, sa, sb)
+    for i, b in ((0, 0), (3, 2), (4, 1)):
+        s2 = sa.copy()
+        s2[i, b] += 1
+        A2 = A.copy()
+        ks = slice(128 * b, min(128 * b + 128, K))
+        nz = (A2[i, ks] & 0x7F) != 0
+        seg = A2[i, ks].copy()
+        # doubling a code: exponent field + 1 (normal codes); subnormal codes
+        # double by doubling their fraction when it stays below 8, else they
+        # become the normal code with exponent 1
+        out = []
+        for c in seg:
+            s, e, f = c & 0x80, (c >> 3) & 15, c & 7
+            if e > 0:
+                out.append(s | ((e + 1) << 3) | f)
+            elif f < 4:
+                out.append(s | (f * 2))
+            else:
+                out.append(s | (1 << 3) | ((f * 2 - 8)))
+        A2[i, ks] = np.array(out, dtype=np.uint8)
+        assert np.array_equal(oracle.decode_e4m3(A2[i, ks])[nz], 2 * oracle.decode_e4m3(seg)[nz])
+        assert np.array_equal(oracle.gemm_e4m3_block_ref(A, B, s2, sb), oracle.gemm_e4m3_block_ref(A2, B, sa, sb))
+    s3 = sb.copy()
+    s3[1, 2] += 2
+    moved = oracle.gemm_e4m3_block_ref(A, B, sa, s3)
+    cols = np.arange(N)
+    inside = (cols >= 128) & (cols < 256)
+    assert np.array_equal(moved[:, ~inside], base[:, ~inside])
+    assert not np.array_equal(moved[:, inside], base[:, inside])
+
+
+def test_block_nan_scale():
+    rs = np.random.RandomState(14)
+    M, N, K = 4, 140, 200
+    A, B = finite_codes((M, K), rs), finite_codes((N, K), rs)
+    sa, sb = unit_scales(M, N, K)
+    sa[2, 1] = 255
+    sb[1, 0] = 255
+    got = oracle.gemm_e4m3_block_ref(A, B, sa, sb)
+    assert np.isnan(got[2]).all()
+    assert np.isnan(got[:, 128:]).all()
+    assert np.isfinite(np.delete(got, 2, 0)[:, :128]).all()
