@@ -254,7 +254,7 @@ def moe_layer_case(torch, mg, datagen):
 
 
 # E4M3 workloads: per-tensor scales, B column-major, bf16 out
-E4M3 = {"gemm8192_e4m3": (8192, 8192, 8192)}
+E4M3 = {"gemm8192_e4m3": (8192, 8192, 8192), "gemm8192_e4m3_block": (8192, 8192, 8192)}
 
 
 def e4m3_case(torch, mg, datagen, name):
@@ -270,13 +270,26 @@ def e4m3_case(torch, mg, datagen, name):
     sb = torch.tensor([0.01], dtype=torch.float32, device="cuda")
     D = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
     plan = mg.gemm_plan(M, N, K, "e4m3", d_type="bf16", a_layout="row", b_layout="col")
+    block = name.endswith("_block")
+    if block:
+        # E8M0 block scales 2^-9 .. 2^-5 (one per row and 128-k block, one
+        # per 128 x 128 weight block)
+        kb = -(-K // 128)
+        bsa = torch.from_numpy(rs.randint(118, 123, size=(M, kb + (kb & 1))).astype(np.uint8)).cuda()
+        bsb = torch.from_numpy(rs.randint(118, 123, size=(-(-N // 128), kb + (kb & 1))).astype(np.uint8)).cuda()
 
-    def step():
-        mg.gemm_run_scaled(plan, A, B, D, sa, sb)
+        def step():
+            mg.gemm_run_blockscaled(plan, A, B, D, bsa, bsb)
+    else:
+        def step():
+            mg.gemm_run_scaled(plan, A, B, D, sa, sb)
 
-    info = dict(flops=2.0 * M * N * K, bytes=M * K + N * K + 2 * M * N, plan=plan.describe(), dtype="e4m3",
+    scale_bytes = (M + -(-N // 128)) * -(-K // 128) if block else 8
+    info = dict(flops=2.0 * M * N * K, bytes=M * K + N * K + 2 * M * N + scale_bytes, plan=plan.describe(),
+                dtype="e4m3",
                 config={"workload": name, "M": M, "N": N, "K": K, "in": "e4m3", "out": "bf16",
-                        "a_layout": "row", "b_layout": "col", "scales": "per-tensor"},
+                        "a_layout": "row", "b_layout": "col",
+                        "scales": "E8M0 per (row, 128-k) and per 128x128 weight block" if block else "per-tensor"},
                 launches_per_step=1)
     return step, info, ("e4m3", M, N, K, a, b)
 
@@ -385,7 +398,7 @@ def main():
         t = time_steps(torch, step, args.steps, args.warmup)
         roof, tflops, peak = roofline(info, t["ms"])
     secondary = []
-    e4m3_line = None
+    e4m3_line = e4m3_block_line = None
     if args.workload == DEFAULT_WORKLOAD and not args.no_secondary:
         # the metric is quoted at 4096^3 as well: same timing, reported beside
         del step
@@ -403,6 +416,13 @@ def main():
         roof3, tflops3, peak3 = roofline(info3, t3["ms"])
         e4m3_line = sub_line(info3, t3, tflops3, peak3, roof3, "pct_of_fp8_peak")
         del step3
+        # the same product with E8M0 block scales (the blockwise FP8 path)
+        step4, info4, _ = e4m3_case(torch, mg, datagen, "gemm8192_e4m3_block")
+        print(f"# plan: {info4['plan']} (block scales)", file=sys.stderr, flush=True)
+        t4 = time_steps(torch, step4, args.steps, args.warmup)
+        roof4, tflops4, peak4 = roofline(info4, t4["ms"])
+        e4m3_block_line = sub_line(info4, t4, tflops4, peak4, roof4, "pct_of_fp8_peak")
+        del step4
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(case, args.cpu_seconds)
@@ -421,6 +441,7 @@ def main():
         line["also"] = secondary
     if e4m3_line:
         line["e4m3"] = e4m3_line
+        line["e4m3_block"] = e4m3_block_line
     print(json.dumps(line), flush=True)
 
 

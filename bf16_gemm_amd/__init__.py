@@ -86,7 +86,7 @@ EXPORTS = ["gemm_plan", "grouped_gemm_plan", "gemm_plan_workspace_size", "gemm_r
            "gemm_plan_describe", "gemm_plan_info", "gemm_plan_destroy", "gemm_status_string",
            "gemm_last_error_message", "mgemm_tile_budget", "mgemm_group_working_set", "mgemm_round_tokens",
            "mgemm_version", "mgemm_moe_combine", "grouped_gemm_run_gather", "gemm_run_noalloc",
-           "moe_fused_plan", "moe_fused_run"]
+           "moe_fused_plan", "moe_fused_run", "gemm_run_blockscaled"]
 
 
 def _load():
@@ -132,6 +132,8 @@ def _load():
     lib.mgemm_version.restype = ctypes.c_char_p
     lib.grouped_gemm_run_gather.argtypes = [vp, vp, i64, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.grouped_gemm_run_gather.restype = st
+    lib.gemm_run_blockscaled.argtypes = [vp, vp, vp, vp, vp, i64, vp, i64, vp, ctypes.c_size_t, vp]
+    lib.gemm_run_blockscaled.restype = st
     lib.moe_fused_plan.argtypes = [ctypes.POINTER(MoeDesc), u32, ctypes.POINTER(vp)]
     lib.moe_fused_plan.restype = st
     lib.moe_fused_run.argtypes = [vp, vp, i64, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
@@ -269,6 +271,16 @@ def gemm_run_scaled(plan: Plan, A, B, D, scale_a, scale_b, stream=None):
     holding the E4M3 codes."""
     _check(lib.gemm_run_scaled(plan.handle, _ptr(A), _ptr(B), _ptr(D), _ptr(scale_a), _ptr(scale_b), None, 0,
                                _stream(stream)), "gemm_run_scaled")
+
+
+def gemm_run_blockscaled(plan: Plan, A, B, D, scale_a, scale_b, stream=None):
+    """Enqueue the blockwise-scaled E4M3 product: ``scale_a`` a uint8 device
+    tensor [M, >= ceil(K/128)] of E8M0 bytes (one per row and 128-k block),
+    ``scale_b`` [ceil(N/128), >= ceil(K/128)] (one per 128 columns and 128-k
+    block); their row pitches are taken from the tensors' strides."""
+    _check(lib.gemm_run_blockscaled(plan.handle, _ptr(A), _ptr(B), _ptr(D), _ptr(scale_a), scale_a.stride(0),
+                                    _ptr(scale_b), scale_b.stride(0), None, 0, _stream(stream)),
+           "gemm_run_blockscaled")
 
 
 def grouped_gemm_run_scaled(plan: Plan, A, B, D, row_offsets, scale_a, scale_b, stream=None):

@@ -56,7 +56,9 @@ static mgemm_status_t hip_status(hipError_t e, const char *what)
 using namespace mgemm;
 
 mgemm_status_t mgemm::dense_run(mgemm_plan_t plan, const void *A, const void *B, void *D, const float *scale_a,
-                                const float *scale_b, void *workspace, size_t workspace_bytes, mgemm_stream_t stream)
+                                const float *scale_b, void *workspace, size_t workspace_bytes, mgemm_stream_t stream,
+                                const uint8_t *block_sa, int64_t block_lda, const uint8_t *block_sb,
+                                int64_t block_ldb)
 {
     const mgemm_desc_t &d = plan->dense;
     if (plan->noop)
@@ -103,6 +105,19 @@ mgemm_status_t mgemm::dense_run(mgemm_plan_t plan, const void *A, const void *B,
     a.split_stride = 0;
     a.scale_a = scale_a;
     a.scale_b = scale_b;
+    a.block_sa = block_sa;
+    a.block_sb = block_sb;
+    a.block_lda = (int)block_lda;
+    a.block_ldb = (int)block_ldb;
+    if (block_sa && a.tiles > 0) {
+        // E8M0 block scales: the plan's tile with the scaled matrix instruction
+        DenseFn f = dense_block_fn_256x256dtl_e4m3(ak, bk, out);
+        if (!f) {
+            set_error("gemm_run_blockscaled: kernel missing for the planned variant");
+            return MGEMM_ERR_UNSUPPORTED;
+        }
+        return hip_status(f(a, plan->grid, s), "gemm_run_blockscaled launch");
+    }
     if (plan->sk_tiles > 0 && a.tiles > 0) {
         // stream-K: whole tiles and the cut tiles' ranges in one launch
         DenseArgs w = a;
@@ -205,6 +220,39 @@ extern "C" mgemm_status_t gemm_run_scaled(mgemm_plan_t plan, const void *A, cons
         return MGEMM_ERR_INVALID_ARG;
     }
     return dense_run(plan, A, B, D, d_scale_a, d_scale_b, workspace, workspace_bytes, stream);
+}
+
+extern "C" mgemm_status_t gemm_run_blockscaled(mgemm_plan_t plan, const void *A, const void *B, void *D,
+                                               const uint8_t *d_scale_a, int64_t lds_a, const uint8_t *d_scale_b,
+                                               int64_t lds_b, void *workspace, size_t workspace_bytes,
+                                               mgemm_stream_t stream)
+{
+    if (!plan || plan->kind != PLAN_DENSE) {
+        set_error("gemm_run_blockscaled: null or non-dense plan");
+        return MGEMM_ERR_INVALID_ARG;
+    }
+    const mgemm_desc_t &d = plan->dense;
+    if (d.a_type != MGEMM_E4M3) {
+        set_error("gemm_run_blockscaled: the plan's inputs are not E4M3");
+        return MGEMM_ERR_UNSUPPORTED;
+    }
+    const int64_t kb = (d.K + 127) / 128, nb = (d.N + 127) / 128;
+    if (!d_scale_a || !d_scale_b || lds_a < kb || lds_b < kb || lds_a < 1 || lds_b < 1) {
+        set_error("gemm_run_blockscaled: scale pointers must be non-null and lds_a, lds_b >= ceil(K / 128) (= %lld)",
+                  (long long)kb);
+        return MGEMM_ERR_INVALID_ARG;
+    }
+    if ((lds_a | lds_b) & 1) {
+        set_error("gemm_run_blockscaled: lds_a and lds_b must be even (two k blocks' scales are read at once)");
+        return MGEMM_ERR_UNSUPPORTED;
+    }
+    if ((uint64_t)d.M * (uint64_t)lds_a > (uint64_t)kMaxRecords ||
+        (uint64_t)nb * (uint64_t)lds_b > (uint64_t)kMaxRecords) {
+        set_error("gemm_run_blockscaled: each scale array must span less than 2^31 bytes");
+        return MGEMM_ERR_INVALID_ARG;
+    }
+    return dense_run(plan, A, B, D, nullptr, nullptr, workspace, workspace_bytes, stream, d_scale_a, lds_a,
+                     d_scale_b, lds_b);
 }
 
 // row_index: nullptr, or the gathered form's index (x_rows rows of A exist).

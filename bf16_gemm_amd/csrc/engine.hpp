@@ -1309,6 +1309,58 @@ __device__ __forceinline__ void mfma16_e4m3_agpr(f32x4_t &c, const u32x8_t &a, c
     asm volatile("v_mfma_f32_16x16x128_f8f6f4 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
 }
 
+// The same with E8M0 block scales applied inside the instruction
+// (v_mfma_scale_f32_16x16x128_f8f6f4): every lane's scale register scales
+// the 32 k of its own row that the lane holds, for each operand (measured:
+// a probe of distinct powers of two per lane recovers exactly this
+// pairing), and BYTE selects which byte of each scale register is read.
+template <int BYTE>
+__device__ __forceinline__ void mfma16_e4m3_scaled_agpr(f32x4_t &c, const u32x8_t &a, const u32x8_t &b,
+                                                        uint32_t scale_a, uint32_t scale_b)
+{
+    static_assert(BYTE == 0 || BYTE == 1, "");
+    if constexpr (BYTE == 0)
+        asm volatile("v_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel_hi:[0,0,0]"
+                     : "+a"(c)
+                     : "v"(a), "v"(b), "v"(scale_a), "v"(scale_b));
+    else
+        asm volatile("v_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel:[1,1,0] op_sel_hi:[0,0,0]"
+                     : "+a"(c)
+                     : "v"(a), "v"(b), "v"(scale_a), "v"(scale_b));
+}
+
+// Two consecutive E8M0 scale bytes (two K steps) into bytes 0 and 1 of a
+// register (buffer_load_ushort, the rest zero; the whole byte offset is in
+// the per-lane offset, none in soffset, so the resource's range check
+// covers all of it).  Written as assembly, like the direct-to-LDS loads, so
+// that the compiler's wait insertion does not wait for every outstanding
+// load before the register is read; the loops that use it count its
+// completion themselves, and nothing may read the register before that.
+__device__ __forceinline__ void load_scale_pair(uint32_t &reg, __amdgpu_buffer_rsrc_t r, uint32_t voff)
+{
+    asm volatile("buffer_load_ushort %0, %1, %2, 0 offen" : "=v"(reg) : "v"(voff), "s"(r));
+}
+
+// Keep byte 0 only (the second step of the pair lies past K): after the
+// load has been counted complete; two wait states before a matrix
+// instruction reads the register.
+__device__ __forceinline__ void keep_low_scale(uint32_t &reg)
+{
+    asm volatile("v_and_b32 %0, 0xff, %0\n\ts_nop 1" : "+v"(reg));
+}
+
+// Where a tile's block scales live (the blockwise E4M3 product): A's, one
+// byte per (row, 128-k block), rows of lds_a bytes from the tile's first
+// row; B's, one per (128 output columns, 128-k block), rows of lds_b bytes.
+struct BlockScaleSrc {
+    __amdgpu_buffer_rsrc_t ra;   // A scales from the tile's row 0 (rows past M out of range)
+    __amdgpu_buffer_rsrc_t rb;   // B scales, all column blocks
+    int lds_a;
+    int lds_b;
+    int nblk0;                   // column block of the tile's first column (n0 / 128)
+    int kb;                      // k blocks (ceil(K / 128))
+};
+
 // The four-wave 256 x 256 direct-to-LDS tile for E4M3 inputs, A and B both
 // k-contiguous ([M][K] and [N][K]).  A K step is 128 elements = 128 bytes of
 // each tile row, so the rings (A on two slots, B on three), the global-side
@@ -1330,7 +1382,8 @@ __device__ __forceinline__ void mfma16_e4m3_agpr(f32x4_t &c, const u32x8_t &a, c
 // two registers sets, so steps run in pairs.  After the barrier of step kt
 // no wave reads step kt's slots again: A's slot takes step kt+2 and B's
 // step kt+3 (B's ring runs two steps ahead, A's one).
-struct DtlTile4E4M3 {
+template <bool BS>
+struct DtlTile4E4M3X {
     using Base = DtlTile<IN_BF16, true>;
     static constexpr int BM = 256, BN = 256, WM = 2, WN = 2;
     static constexpr int MI = 16;
@@ -1352,6 +1405,13 @@ struct DtlTile4E4M3 {
     int kc[LOADS];
     int abase[2], bbase[2];
     uint32_t a_sh[2][2];  // LDS addresses of the A fragment halves, per A slot
+    // Block-scaled form: two register sets of scales, one per pair of K
+    // steps (set p % 2 for steps 2p, 2p + 1): sca[set][b] holds A's scale of
+    // the lane's row in row block b, step 2p in byte 0 and step 2p + 1 in
+    // byte 1; scb[set] B's scale of the wave's 128 columns, same bytes.
+    uint32_t sca[2][8], scb[2];
+    uint32_t sc_lane;     // byte offset of the lane's row of A scales in row block 0
+    int sc_brow;          // byte offset of the wave's row of B scales
 
     __device__ __forceinline__ void setup(int lane, int wave, int wm0, int wn0, int lda, int ldb)
     {
@@ -1410,12 +1470,41 @@ struct DtlTile4E4M3 {
     // 16 MFMAs on m blocks 4 HM .. +3 x n blocks 4 HN .. +3 (n outer); read
     // i (of 8) after MFMAs 0, 2, .., 14, load j (of NL) after MFMA
     // j * 16 / NL + 1
-    template <int HM, int HN, int NL, class RD, class LD>
+    // The scales of step pair p into set SET: A's for the lane's row of each
+    // row block, then B's, two bytes (steps 2p and 2p + 1) per load (the
+    // scale rows' pitches are even, so both bytes lie in the row); a pair
+    // at or past the last k block, and rows past M, read as zeros through an
+    // out-of-range offset.  9 loads.
+    template <int SET>
+    __device__ __forceinline__ void load_scales(const BlockScaleSrc &bs, int p)
+    {
+        const bool in_k = 2 * p < bs.kb;
+#pragma unroll
+        for (int b = 0; b < 8; ++b)
+            load_scale_pair(sca[SET][b], bs.ra, in_k ? sc_lane + (uint32_t)(16 * b * bs.lds_a + 2 * p) : kOOB);
+        load_scale_pair(scb[SET], bs.rb, in_k ? (uint32_t)(sc_brow + 2 * p) : kOOB);
+    }
+    // A pair whose second step lies past the last k block read a byte past
+    // the scales (padding): keep only the first step's.
+    template <int SET>
+    __device__ __forceinline__ void trim_scales()
+    {
+#pragma unroll
+        for (int b = 0; b < 8; ++b)
+            keep_low_scale(sca[SET][b]);
+        keep_low_scale(scb[SET]);
+    }
+
+    template <int HM, int HN, int NL, int SET, int P, class RD, class LD>
     __device__ __forceinline__ void quarter(const F8 &a, const F8 &b, RD &&rd, LD &&ld)
     {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            mfma16_e4m3_agpr(acc[4 * HM + i % 4][4 * HN + i / 4], b.v[i / 4], a.v[i % 4]);
+            if constexpr (BS)
+                mfma16_e4m3_scaled_agpr<P>(acc[4 * HM + i % 4][4 * HN + i / 4], b.v[i / 4], a.v[i % 4],
+                                               scb[SET], sca[SET][4 * HM + i % 4]);
+            else
+                mfma16_e4m3_agpr(acc[4 * HM + i % 4][4 * HN + i / 4], b.v[i / 4], a.v[i % 4]);
             if (i % 2 == 0)
                 rd(i / 2);
             if constexpr (NL > 0) {
@@ -1426,7 +1515,7 @@ struct DtlTile4E4M3 {
     }
 
     __device__ __forceinline__ void mainloop(char *lds, const OperandSrc &sa, int lda, const OperandSrc &sb, int ldb,
-                                             int K, int tid)
+                                             int K, int tid, const BlockScaleSrc &bs = BlockScaleSrc{})
     {
         const int lane = tid & 63;
         const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1436,6 +1525,12 @@ struct DtlTile4E4M3 {
 #pragma unroll
             for (int j = 0; j < FN; ++j)
                 acc[i][j] = f32x4_t{};
+        if constexpr (BS) {
+            // the wave's 128 columns are one scale block (TN == 128)
+            static_assert(TN == 128, "");
+            sc_lane = (uint32_t)((wm0 + (lane & 15)) * bs.lds_a);
+            sc_brow = (bs.nblk0 + wn0 / 128) * bs.lds_b;
+        }
         const int ksteps = (K + KSTEP - 1) / KSTEP;
         if (ksteps <= 0)
             return;
@@ -1455,9 +1550,11 @@ struct DtlTile4E4M3 {
         const OperandSrc ua = uniform_src(sa), ub = uniform_src(sb);
         constexpr std::true_type masked{};
         constexpr std::false_type unmasked{};
-        // prologue: A of steps 0, 1 and B of steps 0, 1, 2; wait for all but
-        // B of step 2
+        // prologue: (the scales of steps 0 and 1,) A of steps 0, 1 and B of
+        // steps 0, 1, 2; wait for all but B of step 2
         {
+            if constexpr (BS)
+                load_scales<0>(bs, 0);
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
                 const auto rb = ub.at_step(s), ra = ua.at_step(s);
@@ -1486,47 +1583,92 @@ struct DtlTile4E4M3 {
             rd_b<1>(B0, Bh, i);
         mfma_drain();
         int sb_cur = 0;  // B slot of step kt
-        // one K step; P = kt & 1 (A's slot, and which of BlX / BlY is Bl)
-        auto step = [&](int kt, auto mask, auto par) {
+        // one K step; P = kt & 1 (A's slot, and which of BlX / BlY is Bl);
+        // SET = (kt / 2) & 1, the scale set of the step pair (block-scaled
+        // form: the first step of pair p loads pair p + 1's scales into the
+        // other set, right after its barrier; they are counted complete by
+        // the next step's wait, which leaves only the last quarter's B loads
+        // outstanding)
+        auto step = [&](int kt, auto mask, auto par, auto set) {
             constexpr int P = decltype(par)::value;
+            constexpr int SET = decltype(set)::value;
             constexpr bool MASK = decltype(mask)::value;
             F8 &Bl = P == 0 ? BlX : BlY;
             F8 &Bn = P == 0 ? BlY : BlX;
+            // the pair's scales have been counted complete (previous step's
+            // wait); a pair ending past K drops its second step's byte
+            if constexpr (BS && MASK && P == 0) {
+                if (kt + 1 >= bs.kb)
+                    trim_scales<SET>();
+            }
             const int sb_next = sb_cur == 2 ? 0 : sb_cur + 1;
             const char *bn = B0 + sb_next * OPS;
-            quarter<0, 0, 0>(Al, Bl, [&](int i) { rd_a<P, 1>(Ah, i); }, [](int) {});
+            quarter<0, 0, 0, SET, P>(Al, Bl, [&](int i) { rd_a<P, 1>(Ah, i); }, [](int) {});
             wait_vm<LOADS>();
             lds_barrier();
+            if constexpr (BS && P == 0)
+                load_scales<SET ^ 1>(bs, (kt >> 1) + 1);
             const auto rA = MASK ? ua.at_step(kt + 2) : step_rsrc(ua, true, kt + 2);
             const int ka = K - (kt + 2) * KSTEP;
             char *const aw = A0 + P * OPS;
             const auto rB = MASK ? ub.at_step(kt + 3) : step_rsrc(ub, true, kt + 3);
             const int kb = K - (kt + 3) * KSTEP;
             char *const bw = B0 + sb_cur * OPS;
-            quarter<0, 1, 4>(Al, Bh, [&](int i) { rd_b<0>(bn, Bn, i); },
-                             [&](int j) { load_a<MASK>(rA, aw, wave, j, ka); });
-            quarter<1, 1, 4>(Ah, Bh, [&](int i) { rd_a<P ^ 1, 0>(Al, i); },
-                             [&](int j) { load_a<MASK>(rA, aw, wave, 4 + j, ka); });
-            quarter<1, 0, 8>(Ah, Bl, [&](int i) { rd_b<1>(bn, Bh, i); },
-                             [&](int j) { load_b<MASK>(rB, bw, wave, j, kb); });
+            quarter<0, 1, 4, SET, P>(Al, Bh, [&](int i) { rd_b<0>(bn, Bn, i); },
+                                     [&](int j) { load_a<MASK>(rA, aw, wave, j, ka); });
+            quarter<1, 1, 4, SET, P>(Ah, Bh, [&](int i) { rd_a<P ^ 1, 0>(Al, i); },
+                                     [&](int j) { load_a<MASK>(rA, aw, wave, 4 + j, ka); });
+            quarter<1, 0, 8, SET, P>(Ah, Bl, [&](int i) { rd_b<1>(bn, Bh, i); },
+                                     [&](int j) { load_b<MASK>(rB, bw, wave, j, kb); });
             sb_cur = sb_next;
         };
         // Steps two at a time while every load is of a whole step
         // (kt + 4 <= ksteps - 2); the rest with the K mask.  An odd step
         // count gets one more step, whose loads were all past K: zeros.
+        constexpr std::integral_constant<int, 0> p0{}, s0{};
+        constexpr std::integral_constant<int, 1> p1{}, s1{};
+        auto pair = [&](int kt, auto mask, auto set) {
+            step(kt, mask, p0, set);
+            step(kt + 1, mask, p1, set);
+        };
         int kt = 0;
-        for (; kt + 1 < ksteps - 4; kt += 2) {
-            step(kt, unmasked, std::integral_constant<int, 0>{});
-            step(kt + 1, unmasked, std::integral_constant<int, 1>{});
-        }
-        for (; kt < ksteps; kt += 2) {
-            step(kt, masked, std::integral_constant<int, 0>{});
-            step(kt + 1, masked, std::integral_constant<int, 1>{});
+        if constexpr (!BS) {
+            for (; kt + 1 < ksteps - 4; kt += 2)
+                pair(kt, unmasked, s0);
+            for (; kt < ksteps; kt += 2)
+                pair(kt, masked, s0);
+        } else {
+            // two pairs per iteration, so that each uses its own scale set
+            // without a branch (a branch on the pair's parity made the
+            // compiler spill ~1700 registers); the last iteration may run up
+            // to three steps past K, on zeros
+            for (; kt + 3 < ksteps - 4; kt += 4) {
+                pair(kt, unmasked, s0);
+                pair(kt + 2, unmasked, s1);
+            }
+            for (; kt < ksteps; kt += 4) {
+                pair(kt, masked, s0);
+                pair(kt + 2, masked, s1);
+            }
         }
         wait_vm<0>();
+        if constexpr (BS) {
+            // every scale load has landed: only now may the compiler reuse
+            // their registers (the last pair's loads are never read, and
+            // the compiler must not hand their registers to other values
+            // while those loads are in flight)
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+#pragma unroll
+                for (int b = 0; b < 8; ++b)
+                    asm volatile("" ::"v"(sca[q][b]));
+                asm volatile("" ::"v"(scb[q]));
+            }
+        }
         mfma_drain();
     }
 };
+using DtlTile4E4M3 = DtlTile4E4M3X<false>;
 
 // ---------------------------------------------------------------------------
 // Epilogue helpers

@@ -68,6 +68,8 @@ MGEMM_DECLARE_TU(narrow32_bf16)
 MGEMM_DECLARE_TU(narrow32_f16)
 #undef MGEMM_DECLARE_TU
 DenseFn dense_fn_256x256dtl_e4m3(bool ak, bool bk, int out);
+// the E4M3 product with E8M0 block scales
+DenseFn dense_block_fn_256x256dtl_e4m3(bool ak, bool bk, int out);
 // stream-K launch of the four-wave direct-to-LDS tile (row-major A)
 DenseFn dense_sk_fn_256x256dtl_bf16(bool bk, int out);
 DenseFn dense_sk_fn_256x256dtl_f16(bool bk, int out);
@@ -100,8 +102,11 @@ void set_error(const char *fmt, ...);
 // Enqueue a dense plan's kernels (gemm_run, gemm_run_scaled and
 // gemm_run_noalloc all end here); workspace: the plan's scratch, or null
 // when it needs none.
+// block_sa / block_sb: E8M0 block scales of an E4M3 plan (gemm_run_blockscaled), else null.
 mgemm_status_t dense_run(mgemm_plan_t plan, const void *A, const void *B, void *D, const float *scale_a,
-                         const float *scale_b, void *workspace, size_t workspace_bytes, mgemm_stream_t stream);
+                         const float *scale_b, void *workspace, size_t workspace_bytes, mgemm_stream_t stream,
+                         const uint8_t *block_sa = nullptr, int64_t block_lda = 0,
+                         const uint8_t *block_sb = nullptr, int64_t block_ldb = 0);
 
 }  // namespace mgemm
 

@@ -29,6 +29,9 @@ struct DenseArgs {
     int64_t slab_offset = 0;          // bytes from ws to the first slab
     uint32_t tag = 0;                 // this run's tag for the arrival counters (never 0 or ~0)
     int sk_tiles = 0;                 // stream-K: the last sk_tiles tiles are cut into `splits` K ranges
+    const uint8_t *block_sa = nullptr;  // E4M3 block scales (E8M0): [M][block_lda], one per (row, 128-k block)
+    const uint8_t *block_sb = nullptr;  // [ceil(N / 128)][block_ldb], one per (128 columns, 128-k block)
+    int block_lda = 0, block_ldb = 0;
 };
 
 struct GroupedArgs {
@@ -317,6 +320,48 @@ __global__ void __launch_bounds__(T::NT) dense_sk_kernel(DenseArgs p)
 // the finished fp32 sums, done in the epilogue ("MegaMoE：Blackwell 与 Hopper
 // 的融合算子解读", Hopper section 04).  Leading dimensions and offsets are
 // in elements = bytes.
+// The blockwise-scaled E4M3 product ("MegaMoE：Blackwell 与 Hopper 的融合算子
+// 解读", Hopper section 04, the blockwise path: the scales change along K, so
+// each K block's product is scaled inside the K loop before it joins the
+// sum): here the matrix instruction applies the E8M0 scales itself
+// (v_mfma_scale_f32_16x16x128_f8f6f4), one K step = one 128-k block.
+template <int OUT>
+__global__ void __launch_bounds__(DtlTile4E4M3::NT) dense_e4m3_block_kernel(DenseArgs p)
+{
+    using T = DtlTile4E4M3X<true>;
+    __shared__ __attribute__((aligned(16))) char lds[T::LDS_BYTES];
+    T tile;
+    const int grid = gridDim.x;
+    const int L = logical_block(blockIdx.x, grid, p.xcd_remap);
+    const char *A = (const char *)p.A;
+    const char *B = (const char *)p.B;
+    constexpr int esize = out_size(OUT);
+    BlockScaleSrc bs;
+    bs.kb = (p.K + T::KSTEP - 1) / T::KSTEP;
+    bs.lds_a = p.block_lda;
+    bs.lds_b = p.block_ldb;
+    bs.rb = make_rsrc(p.block_sb, (uint64_t)((p.N + 127) / 128) * (uint64_t)p.block_ldb);
+    for (int t = L; t < p.tiles; t += grid) {
+        int mb, nb;
+        tile_coords(t, p.tiles_m, p.tiles_n, p.group_m, mb, nb);
+        const int m0 = mb * T::BM, n0 = nb * T::BN;
+        OperandSrc sa, sb;
+        sa.base = A + (int64_t)m0 * p.lda;
+        sa.bytes = (uint64_t)(p.M - m0) * (uint64_t)p.lda;
+        sa.step_bytes = T::KSTEP;
+        sb.base = B + (int64_t)n0 * p.ldb;
+        sb.bytes = (uint64_t)(p.N - n0) * (uint64_t)p.ldb;
+        sb.step_bytes = T::KSTEP;
+        bs.ra = make_rsrc(p.block_sa + (int64_t)m0 * p.block_lda, (uint64_t)(p.M - m0) * (uint64_t)p.block_lda);
+        bs.nblk0 = n0 / 128;
+        tile.mainloop(lds, sa, p.lda, sb, p.ldb, p.K, opaque((int)threadIdx.x), bs);
+        char *Dt = (char *)p.D + ((int64_t)m0 * p.ldd + n0) * esize;
+        epilogue_staged<T, OUT>(tile, lds, Dt, p.ldd, min(T::BM, p.M - m0), min(T::BN, p.N - n0),
+                                opaque((int)threadIdx.x));
+        wait_vm<0>();
+    }
+}
+
 template <int OUT>
 __global__ void __launch_bounds__(DtlTile4E4M3::NT) dense_e4m3_kernel(DenseArgs p)
 {

@@ -110,6 +110,25 @@ inline DenseFn dense_e4m3_table(bool ak, bool bk, int out)
     }
 }
 
+// The blockwise-scaled E4M3 product (E8M0 block scales in DenseArgs).
+template <int OUT>
+hipError_t launch_dense_e4m3_block(const DenseArgs &a, int grid, hipStream_t s)
+{
+    hipLaunchKernelGGL((dense_e4m3_block_kernel<OUT>), dim3(grid), dim3(DtlTile4E4M3::NT), 0, s, a);
+    return hipGetLastError();
+}
+inline DenseFn dense_e4m3_block_table(bool ak, bool bk, int out)
+{
+    if (!ak || !bk)
+        return nullptr;
+    switch (out) {
+    case OUT_F32: return launch_dense_e4m3_block<OUT_F32>;
+    case OUT_BF16: return launch_dense_e4m3_block<OUT_BF16>;
+    case OUT_F16: return launch_dense_e4m3_block<OUT_F16>;
+    default: return nullptr;
+    }
+}
+
 template <int OUT>
 hipError_t launch_grouped_e4m3(const GroupedArgs &a, int grid, hipStream_t s)
 {

@@ -204,6 +204,27 @@ mgemm_status_t gemm_run_scaled(mgemm_plan_t plan, const void *A, const void *B, 
                                const float *d_scale_a, const float *d_scale_b,
                                void *workspace, size_t workspace_bytes, mgemm_stream_t stream);
 
+/* Enqueue the blockwise-scaled product of a plan with E4M3 inputs
+ * ("MegaMoE：Blackwell 与 Hopper 的融合算子解读", Hopper section 04, the
+ * blockwise path: activation scales per token and per 128-element block of
+ * K, weight scales per 128 x 128 block, each K block's partial product
+ * scaled before it joins the sum):
+ *   D[i,j] = sum over k blocks b of sa[i][b] x sb[j / 128][b] x
+ *            sum_{k in [128 b, 128 b + 128) and < K} A[i,k] B[k,j]
+ * accumulated in fp32 and rounded once to d_type.  Scales are E8M0 bytes
+ * (value 2^(v - 127); 255 is NaN), the power-of-two scale format of the
+ * OCP microscaling blocks, applied by the matrix instruction itself.
+ * d_scale_a: device bytes [M][lds_a], sa[i][b] at i * lds_a + b; d_scale_b:
+ * device bytes [ceil(N / 128)][lds_b]; lds_a, lds_b >= ceil(K / 128), and
+ * each array below 2^31 bytes (else MGEMM_ERR_INVALID_ARG); lds_a and lds_b
+ * even (else MGEMM_ERR_UNSUPPORTED).  Bytes past ceil(K / 128) in a row are
+ * padding: they may be read, never used.  Same operand
+ * rules, workspace and errors as gemm_run_scaled; a non-E4M3 plan gives
+ * MGEMM_ERR_UNSUPPORTED.  K == 0 writes zeros. */
+mgemm_status_t gemm_run_blockscaled(mgemm_plan_t plan, const void *A, const void *B, void *D,
+                                    const uint8_t *d_scale_a, int64_t lds_a, const uint8_t *d_scale_b,
+                                    int64_t lds_b, void *workspace, size_t workspace_bytes, mgemm_stream_t stream);
+
 /* Enqueue the grouped product of a plan with E4M3 inputs: expert e's rows
  * times its weights, each finished fp32 sum multiplied by the fp32 product
  * scale_a x scale_b[e] -- fl(fl(scale_a * scale_b[e]) * acc) -- and that
