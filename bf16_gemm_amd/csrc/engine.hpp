@@ -197,21 +197,19 @@ struct Loader<R, NT, true> {
     }
 };
 
-// Two 16-bit halves from two dwords: lo16(a) | lo16(b) << 16 (sel 0x05040100)
-// or hi16(a) | hi16(b) << 16 (sel 0x07060302).
-__device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x05040100u); }
-__device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x07060302u); }
-
 // Row-contiguous storage ([k][row], rows contiguous): each thread loads KB
 // consecutive k of 8 consecutive rows (KB x 16 B), transposes the KB x 8
-// block in registers and writes 8 LDS rows of KB k each.  Lanes of a wave
-// take consecutive 8-row groups, so every load instruction reads whole
-// contiguous segments of a k row.
+// block in registers and writes 8 LDS rows of KB k each.  When KB < 8 a
+// 16-byte LDS chunk (8 k of one row) holds S = 8 / KB threads' pieces; the
+// S threads of one chunk are adjacent lanes, and the lanes above them take
+// consecutive 8-row groups, so every load instruction still reads whole
+// 128-byte segments of a k row.
 template <int R, int NT>
 struct Loader<R, NT, false> {
     static constexpr int NGR = R / 8;                                             // 8-row groups
     static constexpr int KB = (NGR * 8 >= NT) ? 8 : ((NGR * 16 >= NT) ? 4 : 2);   // k per block
     static constexpr int NKG = kBK / KB;                                           // k groups
+    static constexpr int S = 8 / KB;                                               // pieces per chunk
     static_assert(R % 8 == 0 && NGR * NKG == NT, "transposing loader: one block per thread");
     u32x4_t v[KB];
     uint32_t goff;   // byte offset of this lane's first k row segment
@@ -220,8 +218,8 @@ struct Loader<R, NT, false> {
 
     __device__ __forceinline__ void init(int tid, int ld)
     {
-        g = tid % NGR;
-        kg = tid / NGR;
+        g = (tid / S) % NGR;
+        kg = (tid / S) / NGR * S + tid % S;
         goff = (uint32_t)(kg * KB) * (uint32_t)ld * 2u + (uint32_t)g * 16u;
         gstep = (uint32_t)ld * 2u;
     }
@@ -233,30 +231,49 @@ struct Loader<R, NT, false> {
         for (int i = 0; i < KB; ++i)
             v[i] = bload16(r, base + (uint32_t)i * gstep);
     }
-    // LDS rows g*8 + j for j in [J0, J1)
+    // Bank order of the LDS writes.  The LDS serves a 64-lane write in
+    // groups of 128 bytes (16 lanes of 8 bytes) on 32 banks; a tile row is
+    // 128 bytes.  The lane mapping above puts the S pieces of each chunk in
+    // one group, and the swizzle (j ^ g) & 7 sends the group's 8 row groups
+    // to distinct chunks, so no group conflicts.  (With every 16-lane group on
+    // one k piece the 128 x 128 tile's writes were two-way conflicts:
+    // 294,912 cycles per 2048 x 2048 x 512 launch.)  Writing the group's
+    // rows in the order j ^ flip, flip one lane bit above the groups of
+    // 16, also keeps the writes free of conflicts where 32 lanes are served
+    // at once on 64 banks, since each such set then writes both row parities
+    // (both halves of the banks).
+    __device__ __forceinline__ int flip() const { return KB == 2 ? (kg >> 2) & 1 : (g >> 3) & 1; }
+
+    // LDS rows g*8 + (j ^ flip) for j in [J0, J1)
     template <int J0, int J1>
     __device__ __forceinline__ void store_rows(char *lds) const
     {
+        const int f = flip();
 #pragma unroll
         for (int j = J0; j < J1; ++j) {
-            const int row = g * 8 + j;
-            const int d = j >> 1;
-            // swz(8g + j) = (j ^ g) & 7
+            const int jj = j ^ f;
+            const int row = g * 8 + jj;
+            const int d = j >> 1;   // = jj >> 1
+            // the row's 16-bit halves of two k rows: lo16(a) | lo16(b) << 16
+            // for even rows, hi16(a) | hi16(b) << 16 for odd rows
+            const uint32_t sel = (jj & 1) ? 0x07060302u : 0x05040100u;
+            auto pk = [&](uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, sel); };
+            // swz(8g + jj) = (jj ^ g) & 7
             if constexpr (KB == 8) {
                 u32x4_t o;
 #pragma unroll
                 for (int p = 0; p < 4; ++p)
-                    o[p] = (j & 1) ? pack_hi(v[2 * p][d], v[2 * p + 1][d]) : pack_lo(v[2 * p][d], v[2 * p + 1][d]);
+                    o[p] = pk(v[2 * p][d], v[2 * p + 1][d]);
                 *(u32x4_t *)(lds + row * kRowBytes + ((kg ^ swz(row)) << 4)) = o;
             } else if constexpr (KB == 4) {
                 u32x2_t o;
 #pragma unroll
                 for (int p = 0; p < 2; ++p)
-                    o[p] = (j & 1) ? pack_hi(v[2 * p][d], v[2 * p + 1][d]) : pack_lo(v[2 * p][d], v[2 * p + 1][d]);
+                    o[p] = pk(v[2 * p][d], v[2 * p + 1][d]);
                 const int chunk = kg >> 1, sub = (kg & 1) * 8;
                 *(u32x2_t *)(lds + row * kRowBytes + ((chunk ^ swz(row)) << 4) + sub) = o;
             } else {
-                const uint32_t o = (j & 1) ? pack_hi(v[0][d], v[1][d]) : pack_lo(v[0][d], v[1][d]);
+                const uint32_t o = pk(v[0][d], v[1][d]);
                 const int chunk = kg >> 2, sub = (kg & 3) * 4;
                 *(uint32_t *)(lds + row * kRowBytes + ((chunk ^ swz(row)) << 4) + sub) = o;
             }
