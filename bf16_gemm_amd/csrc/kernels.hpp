@@ -643,11 +643,9 @@ __global__ void __launch_bounds__((NarrowTile<IN, BKM, BN>::NT)) narrow_dense_ke
     constexpr int SLAB = narrow_slab_bytes(BN);   // bytes of one partial tile
     constexpr uint32_t BSTRIDE = T::NT * 16;       // bytes between its blocks
     __shared__ __attribute__((aligned(16))) char lds[T::LDS_BYTES];
-    // the arrival count is passed to every wave through the ring's last slot:
-    // the next tile's prologue fills the other slots, and this one only
-    // after the next tile's first barrier, which every wave reaches after
-    // reading the count
-    uint32_t *arrived = (uint32_t *)(lds + (T::NST - 1) * T::SLOT);
+    // the arrival count is passed to every wave through a word that no load
+    // of the rings writes
+    uint32_t *arrived = (uint32_t *)(lds + T::WORDS);
     T tile;
     const int tid = threadIdx.x;
     const int grid = gridDim.x;

@@ -155,8 +155,10 @@ __global__ void __launch_bounds__(512) moe_fused_kernel(MoeArgs p)
     __shared__ __attribute__((aligned(16))) char lds[LDS];
     constexpr int OUT = IN == IN_BF16 ? OUT_BF16 : OUT_F16;
     constexpr int esize = 2;
-    // the ticket hand-over word: the ring's last bytes, used only while every
-    // wave is between tasks
+    // the ticket hand-over word: among the narrow tile's words that no load
+    // writes (the eight-wave tile's ring may cover it: it is used only while
+    // every wave is between tasks)
+    static_assert(LDS - 16 >= Nar::WORDS, "");
     int *const handover = (int *)(lds + LDS - 16);
 
     const int tid = threadIdx.x;

@@ -16,14 +16,15 @@
 // and every token block, so each wave's MFMA count scales with the token
 // count.  The weights stream from HBM once; the kernel is bound by that
 // stream, so operands go straight from global memory to LDS
-// (buffer_load ... lds) through a ring of slots, one 64-k step each: the
-// tile's token rows that exist (16 per token block, 128 bytes each) and the
-// step's 64 x 128 weight block.  A tile with fewer tokens has smaller slots
-// and more of them (five with 128 tokens, eight with 16): its loads run
-// further ahead of the MFMAs, and a stream's rate is the bytes in flight
-// over the memory latency.  Every step waits for its own slot, meets the
-// other waves at one barrier, refills the slot the previous step freed,
-// then reads its fragments and issues its MFMAs.
+// (buffer_load ... lds) through two rings of 64-k steps: one for the tile's
+// token rows that exist (16 per token block, 128 bytes each), loaded by half
+// of the waves, and a deeper one for the step's 64 x BN weight block, loaded
+// by the other half (a wave's loads complete in issue order, so token rows,
+// mostly L2 hits, must not queue behind weight loads from HBM).  A tile with
+// fewer tokens has smaller token slots, leaving more room to the weights.
+// Every step waits for the wave's own loads of the step, meets the other
+// waves at one barrier, refills the slots the previous step freed, then
+// reads its fragments and issues its MFMAs.
 //
 // Swizzles.  Token rows (and k-contiguous weight rows, [n][k]) use the
 // direct-to-LDS tile's chunk swizzle dswz (conflict-free for the 16 x 16
@@ -118,42 +119,51 @@ struct NarrowTile {
     static constexpr int NT = 64 * NW;
     static constexpr int NB = BN / 16 / NW;       // column blocks per wave
     static constexpr int B_BYTES = 64 * BN * 2;        // one step of weights
-    static constexpr int LB = B_BYTES / 1024 / NW;     // weight loads per wave and step
-    // The ring for NV token blocks (1..8): a slot holds one 64-k step, the
-    // 16 NV token rows that exist (128 B each) then the weights, so a tile
-    // with few tokens keeps more weight steps in flight -- its rate is the
-    // bytes in flight over the memory latency.  Token loads (1 KiB = 8 rows
-    // each, 2 NV per step) go round the waves; every wave issues LA(NV) of
-    // them, those past the tile's rows into a 1 KiB scratch area (offset
-    // out of range: zeros, no memory traffic), so that every wave counts the
-    // same loads per step.  Slots: as many as fit beside the scratch, with
-    // at most 63 loads per wave in flight (NST - 1 steps ahead), the most
-    // s_waitcnt vmcnt counts.
+    // Two rings, one per operand.  The weights stream from HBM while the
+    // token rows, read by every tile of the launch, mostly hit L2, so the
+    // weights need many more bytes in flight; but one wave's loads complete
+    // in the order it issued them, so in a wave that issued both kinds a
+    // token row would wait behind every weight load issued before it.  The
+    // first WA waves therefore load only token rows and the other waves only
+    // weights, each kind into a ring of its own depth: DA token slots (one
+    // 64-k step of the tile's 16 NV token rows, 128 B each) and DB weight
+    // slots (one 64 x BN step).  Every wave waits for its own loads only,
+    // and all waves meet at one barrier per step.  A token wave issues LA
+    // loads per step (1 KiB = 8 rows each; those past the tile's rows go to
+    // a 1 KiB scratch area with an out-of-range offset: zeros, no memory
+    // traffic, so that every token wave counts the same loads), a weight
+    // wave LBW; at most 63 loads per wave are in flight (the vmcnt range).
+    // A tile with fewer tokens has smaller token slots, so its weights get
+    // more of the space (up to the vmcnt bound).
     static constexpr int LDS_BYTES = 160 * 1024;
-    static constexpr int SCRATCH = LDS_BYTES - 1024;
+    static constexpr int WORDS = LDS_BYTES - 256;   // 256 bytes no load touches (hand-over words)
+    static constexpr int SCRATCH = WORDS - 1024;    // target of the token loads past the tile's rows
+    static constexpr int WA = NW / 2;               // token-loading waves; waves WA.. load weights
+    static constexpr int LBW = B_BYTES / 1024 / (NW - WA);   // weight loads per weight wave and step
+    static_assert(LBW * (NW - WA) * 1024 == B_BYTES, "");
     template <int NV>
     struct Ring {
         static constexpr int A_BYTES = NV * 16 * kRowBytes;
-        static constexpr int SLOT = A_BYTES + B_BYTES;
-        static constexpr int LA = (2 * NV + NW - 1) / NW;
-        static constexpr int LOADS = LA + LB;
-        static constexpr bool DUMMY = LA * NW != 2 * NV;   // some token loads go to the scratch area
-        static constexpr int FIT = (DUMMY ? SCRATCH : LDS_BYTES) / SLOT;
-        static constexpr int NST = FIT < 63 / LOADS + 1 ? FIT : 63 / LOADS + 1;
-        static_assert(NST >= 3 && (NST - 1) * LOADS <= 63, "");
+        static constexpr int LA = (2 * NV + WA - 1) / WA;
+        static constexpr int DA_VM = 63 / LA + 1, DB_VM = 63 / LBW + 1;
+        // token depth: up to six steps within 3/8 of the space, at least three
+        static constexpr int DA_FIT = SCRATCH * 3 / 8 / A_BYTES;
+        static constexpr int DA_WANT = DA_FIT < 3 ? 3 : (DA_FIT > 6 ? 6 : DA_FIT);
+        static constexpr int DA = DA_WANT < DA_VM ? DA_WANT : DA_VM;
+        static constexpr int DB_FIT = (SCRATCH - DA * A_BYTES) / B_BYTES;
+        static constexpr int DB = DB_FIT < DB_VM ? DB_FIT : DB_VM;
+        static constexpr int B_BASE = DA * A_BYTES;   // the weight ring
+        static_assert(DA >= 3 && DB >= 3 && B_BASE + DB * B_BYTES <= SCRATCH, "");
     };
     static constexpr int LA_MAX = Ring<NTB>::LA;
-    // the ring of a full tile (8 token blocks): its last slot is free once
-    // the K loop is done
-    static constexpr int NST = Ring<NTB>::NST, SLOT = Ring<NTB>::SLOT;
     static constexpr int BROW = BN * 2;           // bytes of a k row of a row-major weight step
     static constexpr int RPL = 1024 / BROW;       // k rows per (1 KiB) load of a row-major weight step
     static constexpr int LG_R = BN == 128 ? 0 : (BN == 64 ? 1 : 2);   // log2 of k rows per 256 bytes
-    static_assert(NB >= 1 && LB >= 1, "");
+    static_assert(NB >= 1 && LBW >= 1, "");
 
     f32x4_t acc[NTB][NB];
-    uint32_t va[LA_MAX], vb[LB];   // per-lane global byte offsets within a step
-    int kca[LA_MAX], kcb[LB];      // k of this lane's 16-byte chunk (k-contiguous operands)
+    uint32_t va[LA_MAX], vb[LBW];  // per-lane global byte offsets within a step
+    int kca[LA_MAX], kcb[LBW];     // k of this lane's 16-byte chunk (k-contiguous operands)
     int afr[2];                // A fragment of token block 0, sub-step s (LDS offset in a slot)
     int bfr[NB][2];            // k-contiguous B: fragment of column block nb, sub-step s (from the weights)
     int btr[NB];               // row-major B: transpose-read piece of column block nb (k row 0, from the weights)
@@ -175,8 +185,8 @@ struct NarrowTile {
     __device__ __forceinline__ void setup(int lane, int wave, int lda, int ldb, const RowGather &ga)
     {
         using R = Ring<NV>;
-        // A: load j of wave w fills token rows 8 (LA w + j) .. +7 when they
-        // exist, else the scratch area
+        // A: load j of token wave w fills token rows 8 (LA w + j) .. +7 when
+        // they exist, else the scratch area
 #pragma unroll
         for (int j = 0; j < R::LA; ++j) {
             const int blk = wave * R::LA + j;
@@ -193,20 +203,23 @@ struct NarrowTile {
                 va[j] = (uint32_t)row * (uint32_t)lda * 2u + (uint32_t)c * 16u;
             }
         }
+        // B: load j of weight wave w (counted from WA) is the step's 1 KiB
+        // piece LBW w + j (the token waves' offsets are not used)
+        const int ww = wave < WA ? 0 : wave - WA;
 #pragma unroll
-        for (int j = 0; j < LB; ++j) {
+        for (int j = 0; j < LBW; ++j) {
             if constexpr (BKM) {
-                // [n][k]: load j of wave w fills columns 8 (LB w + j) .. +7 (the wave's own)
-                const int row = (wave * LB + j) * 8 + (lane >> 3);
+                // [n][k]: piece i holds columns 8 i .. 8 i + 7
+                const int row = (ww * LBW + j) * 8 + (lane >> 3);
                 const int c = (lane & 7) ^ DtlTile<IN, true>::dswz(row);
                 kcb[j] = c * 8;
                 vb[j] = (uint32_t)row * (uint32_t)ldb * 2u + (uint32_t)c * 16u;
             } else {
-                // [k][n]: load j of wave w fills k rows RPL (LB w + j) .. +RPL-1;
-                // lane l the 16 bytes at 16 (l % (BROW/16)) of row l / (BROW/16),
-                // i.e. physical segment (l % (BROW/16)) / 2, half l & 1
+                // [k][n]: piece i holds k rows RPL i .. RPL i + RPL - 1; lane l
+                // the 16 bytes at 16 (l % (BROW/16)) of row l / (BROW/16), i.e.
+                // physical segment (l % (BROW/16)) / 2, half l & 1
                 constexpr int CPR = BROW / 16;   // 16-byte chunks per k row
-                const int kr = (wave * LB + j) * RPL + lane / CPR;
+                const int kr = (ww * LBW + j) * RPL + lane / CPR;
                 const int pc = lane % CPR;
                 const int seg = (pc >> 1) ^ bseg(kr);
                 kcb[j] = 0;
@@ -236,11 +249,12 @@ struct NarrowTile {
         }
     }
 
-    // the loads of one K step into slot `slot`; ra / rb point at the step,
-    // k_left = K minus the step's first k (<= 0: a step past K, all zeros)
+    // A token wave's loads of one K step into token slot `slot`; ra points
+    // at the step, k_left = K minus the step's first k (<= 0: a step past K,
+    // all zeros)
     template <int NV>
-    __device__ __forceinline__ void load_step(char *lds, char *slot, int wave, __amdgpu_buffer_rsrc_t ra,
-                                              __amdgpu_buffer_rsrc_t rb, int k_left) const
+    __device__ __forceinline__ void load_tokens(char *lds, char *slot, int wave, __amdgpu_buffer_rsrc_t ra,
+                                                int k_left) const
     {
         using R = Ring<NV>;
 #pragma unroll
@@ -250,12 +264,17 @@ struct NarrowTile {
             load_to_lds16(ra, lds_addr(blk < 2 * NV ? slot + blk * 1024 : lds + SCRATCH),
                           kca[j] < k_left ? va[j] : kOOB);
         }
+    }
+
+    // A weight wave's loads of one K step into weight slot `slot`
+    __device__ __forceinline__ void load_weights(char *slot, int wave, __amdgpu_buffer_rsrc_t rb, int k_left) const
+    {
 #pragma unroll
-        for (int j = 0; j < LB; ++j) {
+        for (int j = 0; j < LBW; ++j) {
             uint32_t off = vb[j];
             if constexpr (BKM)
                 off = kcb[j] < k_left ? off : kOOB;
-            load_to_lds16(rb, lds_addr(slot + R::A_BYTES + (wave * LB + j) * 1024), off);
+            load_to_lds16(rb, lds_addr(slot + ((wave - WA) * LBW + j) * 1024), off);
         }
     }
 
@@ -286,18 +305,18 @@ struct NarrowTile {
             c = mfma16<IN>(a, b, c);
     }
 
-    // One K step on slot `slot`: both sub-steps' fragments first, then the
-    // MFMAs of the NV token blocks.
+    // One K step on token slot `tok` and weight slot `wts`: both sub-steps'
+    // fragments first, then the MFMAs of the NV token blocks.
     template <int NV>
-    __device__ __forceinline__ void compute(const char *slot)
+    __device__ __forceinline__ void compute(const char *tok, const char *wts)
     {
         u32x4_t b0[NB], b1[NB], a0[NV], a1[NV];
-        read_b<0>(slot + Ring<NV>::A_BYTES, b0);
-        read_b<1>(slot + Ring<NV>::A_BYTES, b1);
+        read_b<0>(wts, b0);
+        read_b<1>(wts, b1);
 #pragma unroll
         for (int tb = 0; tb < NV; ++tb) {
-            a0[tb] = *(const u32x4_t *)(slot + afr[0] + tb * 16 * kRowBytes);
-            a1[tb] = *(const u32x4_t *)(slot + afr[1] + tb * 16 * kRowBytes);
+            a0[tb] = *(const u32x4_t *)(tok + afr[0] + tb * 16 * kRowBytes);
+            a1[tb] = *(const u32x4_t *)(tok + afr[1] + tb * 16 * kRowBytes);
         }
 #pragma unroll
         for (int tb = 0; tb < NV; ++tb)
@@ -311,10 +330,11 @@ struct NarrowTile {
                 mma(acc[tb][nb], b1[nb], a1[tb]);
     }
 
-    // The K loop for NV token blocks on its ring.  Step kt: this wave's
-    // loads of step kt have landed (only the NST - 2 later steps' may be in
-    // flight); after the barrier every wave's have, and every wave is done
-    // with step kt - 1, whose slot takes step kt + NST - 1.
+    // The K loop for NV token blocks on its two rings.  Step kt: this
+    // wave's loads of step kt have landed (only those of the later steps of
+    // its ring may be in flight); after the barrier every wave's have, and
+    // every wave is done with step kt - 1, whose slots take the token step
+    // kt + DA - 1 and the weight step kt + DB - 1.
     template <int NV>
     __device__ __forceinline__ void kloop(char *lds, const OperandSrc &sa, const OperandSrc &sb, int lda, int ldb,
                                           int K, int ksteps, int lane, int wave, const RowGather &ga)
@@ -322,28 +342,38 @@ struct NarrowTile {
         using R = Ring<NV>;
         setup<NV>(lane, wave, lda, ldb, ga);
         const OperandSrc ua = uniform_src(sa), ub = uniform_src(sb);
-        // prologue: steps 0 .. NST-2 (unrolled for the shallow rings; a loop
-        // for the deep ones, whose unrolled buffer descriptors would all be
+        char *const wring = lds + R::B_BASE;
+        const bool tw = wave < WA;   // uniform
+        // prologue: token steps 0 .. DA-2 or weight steps 0 .. DB-2 (a loop
+        // for the deep ring, whose unrolled buffer descriptors would all be
         // live at once)
-        if constexpr (R::NST <= 7) {
+        if (tw) {
 #pragma unroll
-            for (int s = 0; s < R::NST - 1; ++s)
-                load_step<NV>(lds, lds + s * R::SLOT, wave, ua.at_step(s), ub.at_step(s), K - s * kBK);
+            for (int s = 0; s < R::DA - 1; ++s)
+                load_tokens<NV>(lds, lds + s * R::A_BYTES, wave, ua.at_step(s), K - s * kBK);
         } else {
 #pragma unroll 1
-            for (int s = 0; s < R::NST - 1; ++s)
-                load_step<NV>(lds, lds + s * R::SLOT, wave, ua.at_step(s), ub.at_step(s), K - s * kBK);
+            for (int s = 0; s < R::DB - 1; ++s)
+                load_weights(wring + s * B_BYTES, wave, ub.at_step(s), K - s * kBK);
         }
         mfma_drain();
-        int slot = 0, fill = R::NST - 1;
+        int ta = 0, fa = R::DA - 1, tb = 0, fb = R::DB - 1;
         for (int kt = 0; kt < ksteps; ++kt) {
-            wait_vm<(R::NST - 2) * R::LOADS>();
+            if (tw)
+                wait_vm<(R::DA - 2) * R::LA>();
+            else
+                wait_vm<(R::DB - 2) * LBW>();
             lds_barrier();
-            load_step<NV>(lds, lds + fill * R::SLOT, wave, ua.at_step(kt + R::NST - 1), ub.at_step(kt + R::NST - 1),
-                          K - (kt + R::NST - 1) * kBK);
-            compute<NV>(lds + slot * R::SLOT);
-            slot = slot == R::NST - 1 ? 0 : slot + 1;
-            fill = fill == R::NST - 1 ? 0 : fill + 1;
+            if (tw)
+                load_tokens<NV>(lds, lds + fa * R::A_BYTES, wave, ua.at_step(kt + R::DA - 1),
+                                K - (kt + R::DA - 1) * kBK);
+            else
+                load_weights(wring + fb * B_BYTES, wave, ub.at_step(kt + R::DB - 1), K - (kt + R::DB - 1) * kBK);
+            compute<NV>(lds + ta * R::A_BYTES, wring + tb * B_BYTES);
+            ta = ta == R::DA - 1 ? 0 : ta + 1;
+            fa = fa == R::DA - 1 ? 0 : fa + 1;
+            tb = tb == R::DB - 1 ? 0 : tb + 1;
+            fb = fb == R::DB - 1 ? 0 : fb + 1;
         }
     }
 
