@@ -9,10 +9,10 @@ the MoE workload FC1 (SiLU-gated) plus FC2 over all experts.
 Timing protocol ("B200 的 2CTA 怎样调优" section 十: warm up separately,
 repeat, report the spread; hot and rotating input buffers):
   * warm-up: at least W untimed steps, and at least WARMUP_SECONDS of them.
-    The engine clock idles near 150 MHz and takes tens of milliseconds of
-    load to reach its settled ~2.1 GHz, so five steps of 8192^3 (4 ms)
-    would time the clock's ramp, not the kernel; the line reports the W
-    asked for and the steps actually run;
+    The engine clock idles low and takes tens of milliseconds of load to
+    settle (1.7-2.0 GHz under sustained MFMA load), so five steps of 8192^3
+    (4 ms) would time the clock's ramp, not the kernel; the line reports
+    the W asked for and the steps actually run;
   * then exactly K steps, bracketed by device synchronisation, split into
     (up to) ten windows by events recorded on the stream the kernels are
     launched on: the value is K steps over the whole bracket, the windows
