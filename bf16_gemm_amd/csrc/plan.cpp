@@ -181,15 +181,18 @@ static double task_model_us(const TileShape &t, int64_t M, int64_t N, int64_t K,
 
 // Time model (microseconds) of a few-token plan: width `bn`, `splits` K
 // ranges.  Fitted to MI355X runs of the tile on decode-sized products
-// (16-128 tokens, N 2048-7168, K 2048-7168): ~2.5 us until the first K
-// step's operands have landed, then each task streams its token rows and
-// weight columns at ~45 GB/s per CU; a split then costs ~3 us of device-
-// scope round trips (partial stored, arrival, partials read) plus its
-// partial tiles moved at the same rate (every range writes one, the last
-// reads the others).  Tasks beyond one per CU run in further rounds.
+// (16-128 tokens, N 2048-7168, K 2048-7168, every width and split that fits
+// one round): ~2.5 us until the first K step's operands have landed, then
+// each task streams its token rows and weight columns at ~55 GB/s per CU;
+// a split adds its partial tiles moved at the same rate (every range writes
+// one, the last reads the others).  With more than three quarters of the
+// CUs streaming the per-task rate falls (the fit charges 2 us per further
+// quarter).  Tasks beyond one per CU run in further rounds.  Over the
+// fitted shapes the pick is within 7 % of the fastest width and split
+// (2 % on average).
 static double narrow_model_us(int64_t M, int64_t N, int64_t K, int bn, int splits, int cus)
 {
-    const double rate = 45e3;   // bytes per microsecond per CU
+    const double rate = 55e3;   // bytes per microsecond per CU
     const int64_t tokens = std::min<int64_t>(mgemm_round_tokens(std::min<int64_t>(M, 128), 16), 128);
     const int64_t tiles = cdiv(M, 128) * cdiv(N, bn);
     const int64_t tasks = tiles * splits;
@@ -197,7 +200,10 @@ static double narrow_model_us(int64_t M, int64_t N, int64_t K, int bn, int split
     const double task_bytes = kr * 2.0 * (double)(tokens + bn);
     double us = 2.5 + (double)cdiv(tasks, cus) * task_bytes / rate;
     if (splits > 1)
-        us += 3.0 + (double)splits * (double)(tokens * bn * 4) / rate;
+        us += (double)splits * (double)(tokens * bn * 4) / rate;
+    const int64_t busy = std::min<int64_t>(tasks, cus) - 3 * (int64_t)cus / 4;
+    if (busy > 0)
+        us += 2.0 * (double)busy / ((double)cus / 4.0);
     return us;
 }
 

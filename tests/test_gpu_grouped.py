@@ -3,7 +3,7 @@
 FC1 runs with the fused SiLU gate (gate/up interleaved by 8 columns), FC2
 plainly; expert row counts are ragged and include empty and one-row
 experts.  Small cases are compared element by element with the full
-oracle; the 64-expert workload on sampled rows of many experts.
+oracle; the 64-expert workload on sampled rows of every expert.
 """
 import math
 import sys
@@ -233,14 +233,13 @@ def test_moe64_full_size_sampled():
     log("  " + p1.describe())
     log("  " + p2.describe())
     assert torch.isfinite(h.float()).all() and torch.isfinite(y.float()).all()
-    # experts of every size class, two rows each (first and last)
+    # every expert that has rows: its first and last row, and the rows on
+    # both sides of its first 256-row tile boundary (all columns of each)
     cnt = r.counts
-    order = np.argsort(cnt)
-    picks = [e for e in order if cnt[e] > 0]
-    picks = sorted(set(picks[:6] + picks[len(picks) // 2 - 2: len(picks) // 2 + 2] + picks[-4:]))
+    picks = [e for e in range(E) if cnt[e] > 0]
     for e in picks:
         lo, hi = int(r.offsets[e]), int(r.offsets[e + 1])
-        sel = sorted({lo, hi - 1})
+        sel = sorted({lo, hi - 1} | ({lo + 255, lo + 256} if hi - lo > 256 else set()))
         a_rows = from_dev_bits(A[sel])
         w1 = from_dev_bits(W1[e])
         w2 = from_dev_bits(W2[e])
