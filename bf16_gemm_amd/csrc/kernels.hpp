@@ -134,8 +134,9 @@ __device__ __forceinline__ void tile_coords(int t, int tiles_m, int tiles_n, int
 // origin is the tile's first row; the bytes that exist end after the last
 // existing row; one K step moves 64 elements along the row.  Row-contiguous
 // operand ([K][rows]): the origin is the tile's first column; the bytes end
-// after element (K-1, last existing column), so every k >= K reads as zero;
-// one K step moves 64 rows of ld elements.
+// after element (K-1, last existing column), rounded up to its 16-byte
+// chunk, so every k >= K reads as zero; one K step moves 64 rows of ld
+// elements.
 template <bool KMAJOR>
 __device__ __forceinline__ OperandSrc operand_src(const uint16_t *tile_origin, int ld, int rows_left, int K)
 {
@@ -145,7 +146,13 @@ __device__ __forceinline__ OperandSrc operand_src(const uint16_t *tile_origin, i
         s.bytes = (uint64_t)rows_left * (uint64_t)ld * 2u;
         s.step_bytes = kBK * 2;
     } else {
-        s.bytes = K > 0 ? ((uint64_t)(K - 1) * (uint64_t)ld + (uint64_t)rows_left) * 2u : 0;
+        // up to the end of the 16-byte chunk that holds the last row's last
+        // element: the range check zeroes a whole dword that reaches past
+        // the records, so ending at an odd element would zero the last
+        // element of the last k row with its neighbour.  The chunk lies in
+        // the same page as that element (16-byte aligned base and rows),
+        // and its extra elements feed only rows past the operand's end.
+        s.bytes = K > 0 ? ((uint64_t)(K - 1) * (uint64_t)ld + (((uint64_t)rows_left + 7u) & ~(uint64_t)7u)) * 2u : 0;
         s.step_bytes = (uint32_t)kBK * (uint32_t)ld * 2u;
     }
     return s;

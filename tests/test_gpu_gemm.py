@@ -380,3 +380,17 @@ def test_full_size_workloads(name, flags, variant):
     # no NaN/Inf anywhere in the output
     vals = D.float()
     assert torch.isfinite(vals).all()
+
+
+@pytest.mark.parametrize("tile", ["auto", "128", "256"])
+@pytest.mark.parametrize("out_t", ["f32", "bf16"])
+def test_col_major_a_odd_row_count(tile, out_t):
+    """Column-major A with an odd M: the last row's last element shares a
+    dword with the storage padding at the last k row, which must not be
+    read as zero (every element, integer inputs, bit for bit)."""
+    M, N, K = 431, 138, 320
+    log(f"case col-major A odd M tile={tile} bf16->{out_t} M={M} N={N} K={K}")
+    cfg = datagen.GemmConfig("t", M, N, K, "bf16", out_t, "col", "row", seed=11, int_seed=12)
+    a, b = datagen.gemm_inputs(cfg, "int")
+    got, plan = run_dense(a, b, M, N, K, "bf16", out_t, "col", "row", TILES[tile], sentinel=True)
+    assert_bits_equal(got, oracle.gemm_ref(a, b, "bf16", "bf16", "col", "row"), out_t, plan.describe())
