@@ -62,6 +62,37 @@ def assert_close(got_bits: np.ndarray, ref: np.ndarray, K: int, out: str, what: 
     return float(err.max()) if err.size else 0.0
 
 
+# Chains of products (FC1 -> h -> FC2 -> combine).  The oracle runs its own
+# chain on the inputs alone: its next stage takes its own rounding of the
+# previous stage's exact result.  The GPU's next stage took the GPU's
+# rounding, which may differ from the oracle's by the stage's acceptance
+# rule plus the oracle's own rounding (at most half an ulp: 2^-8 relative in
+# bf16, 2^-11 in fp16).  That difference is carried through the next
+# product: |sum_k (x_gpu_k - x_oracle_k) w_kj| <= sum_k bound_k |w_kj|.
+HALF_ULP = {"bf16": 2.0 ** -8, "f16": 2.0 ** -11}
+RULE_REL = {"f32": 0.0, "bf16": 2.0 ** -7, "f16": 2.0 ** -10}
+
+
+def stage_gap(x_ref: np.ndarray, K: int, dtype: str) -> np.ndarray:
+    """Largest |GPU rounding - oracle rounding| of a stage output whose exact
+    value is x_ref (a sum over K terms)."""
+    return (RULE_REL[dtype] + HALF_ULP[dtype]) * np.abs(x_ref) + 1e-4 * math.sqrt(max(K, 1))
+
+
+def assert_close_carried(got_bits: np.ndarray, ref: np.ndarray, K: int, out: str, carry: np.ndarray,
+                         what: str = ""):
+    """The acceptance rule for a stage fed the previous stage's GPU output,
+    widened by the carried difference ``carry`` (same shape as ref)."""
+    got = values(got_bits, out)
+    tol = tolerance(ref, K, out) + carry
+    err = np.abs(got - ref)
+    bad = ~(err <= tol)
+    if bad.any():
+        i = tuple(np.argwhere(bad)[0])
+        raise AssertionError(f"{what}: {int(bad.sum())} of {bad.size} outside the carried tolerance; first at "
+                             f"{list(i)}: got {got[i]!r} ref {ref[i]!r} tol {tol[i]!r}")
+
+
 def assert_bits_equal(got_bits: np.ndarray, ref: np.ndarray, out: str, what: str = ""):
     want = oracle.encode(ref, out)
     if not np.array_equal(got_bits, want):

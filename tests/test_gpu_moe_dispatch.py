@@ -10,7 +10,7 @@ import pytest
 
 import datagen
 import oracle
-from helpers import assert_bits_equal, assert_close, from_dev_bits, to_dev, values
+from helpers import assert_bits_equal, assert_close, assert_close_carried, from_dev_bits, stage_gap, to_dev, values
 
 torch = pytest.importorskip("torch")
 mg = pytest.importorskip("bf16_gemm_amd")
@@ -124,8 +124,7 @@ def test_gather_equals_pregathered_moe64():
 
 def test_moe_layer_dispatch_to_combine():
     """X -> gathered FC1 with the SiLU gate -> FC2 -> weighted top-k combine,
-    on the small MoE config, against the oracle's chain (FC2 checked on the
-    GPU's h, so each stage's tolerance stays its own)."""
+    on the small MoE config, against the oracle's own chain on the inputs."""
     cfg = datagen.MOE["moe_small"]
     r = datagen.moe_route(cfg)
     rows, H, I, E = int(r.offsets[-1]), cfg.hidden, cfg.inter, cfg.num_experts
@@ -143,18 +142,31 @@ def test_moe_layer_dispatch_to_combine():
     mg.grouped_gemm_run(p2, h, to_dev(W2, "bf16"), z, offs)
     mg.moe_combine(z, dev_i32(r.pos), torch.from_numpy(r.weight).cuda(), y, cfg.top_k)
     torch.cuda.synchronize()
+    # the oracle's own chain on the inputs: FC1 + gate, FC2 on its rounding
+    # of h, the combine on its rounding of z; each GPU stage is held to its
+    # rule widened by the gap the earlier rules allow, carried forward
     A = X[r.token_of_row]
     h_ref = oracle.silu_gate(oracle.grouped_ref(A, W1, r.offsets))
-    h_got = from_dev_bits(h)
-    tol = 2.0 ** -7 * np.abs(h_ref) + 1e-4 * math.sqrt(H)
-    assert np.all(np.abs(values(h_got, "bf16") - h_ref) <= tol), "FC1 (gathered) outside tolerance"
-    z_ref = oracle.grouped_ref(h_got, W2, r.offsets)
-    z_got = from_dev_bits(z)
-    assert_close(z_got, z_ref, I, "bf16", "FC2")
-    y_ref = oracle.moe_combine_ref(z_got, r.pos, r.weight.astype(np.float64))
+    assert_close(from_dev_bits(h), h_ref, H, "bf16", "FC1 (gathered)")
+    z_ref = oracle.grouped_ref(oracle.encode(h_ref, "bf16"), W2, r.offsets)
+    h_gap = stage_gap(h_ref, H, "bf16")
+    z_carry = np.zeros_like(z_ref)
+    for e in range(E):
+        lo, hi = int(r.offsets[e]), int(r.offsets[e + 1])
+        if hi > lo:
+            z_carry[lo:hi] = h_gap[lo:hi] @ np.abs(oracle.decode(W2[e], "bf16"))
+    assert_close_carried(from_dev_bits(z), z_ref, I, "bf16", z_carry, "FC2")
+    w = r.weight.astype(np.float64)
+    y_ref = oracle.moe_combine_ref(oracle.encode(z_ref, "bf16"), r.pos, w)
+    z_gap = stage_gap(z_ref, I, "bf16") + z_carry
+    y_carry = np.zeros_like(y_ref)
+    for k in range(r.pos.shape[1]):
+        p = np.asarray(r.pos)[:, k]
+        ok = (p >= 0) & (p < rows)
+        y_carry[ok] += np.abs(w[ok, k])[:, None] * z_gap[p[ok]]
     err = np.abs(values(from_dev_bits(y), "bf16") - y_ref)
-    assert np.all(err <= 2.0 ** -8 * np.abs(y_ref) + cfg.top_k * 2.0 ** -20 * np.abs(y_ref).max()), \
-        f"combine max err {err.max():.3e}"
+    tol = 2.0 ** -8 * np.abs(y_ref) + cfg.top_k * 2.0 ** -20 * np.abs(y_ref).max() + y_carry
+    assert np.all(err <= tol), f"combine max err {err.max():.3e}, worst ratio {(err / tol).max():.3f}"
 
 
 def test_gather_rejects_tiles_without_it():
