@@ -394,3 +394,31 @@ def test_col_major_a_odd_row_count(tile, out_t):
     a, b = datagen.gemm_inputs(cfg, "int")
     got, plan = run_dense(a, b, M, N, K, "bf16", out_t, "col", "row", TILES[tile], sentinel=True)
     assert_bits_equal(got, oracle.gemm_ref(a, b, "bf16", "bf16", "col", "row"), out_t, plan.describe())
+
+
+@pytest.mark.parametrize("M,N,K", [(64, 64, 65536), (1, 1, 8), (3, 2056, 32768), (700, 9, 4104)])
+def test_extreme_aspect_ratios(M, N, K):
+    """Very long K against tiny M and N (the planner's split and few-token
+    choices), and one-element outputs; integer inputs (sums below 2^24, so
+    exact in fp32), every element bit for bit."""
+    log(f"case extreme M={M} N={N} K={K}")
+    for bl in ("row", "col"):
+        cfg = datagen.GemmConfig("t", M, N, K, "bf16", "f32", "row", bl, seed=21, int_seed=22)
+        a, b = datagen.gemm_inputs(cfg, "int")
+        got, plan = run_dense(a, b, M, N, K, "bf16", "f32", "row", bl, sentinel=True)
+        log("  " + plan.describe())
+        assert_bits_equal(got, oracle.gemm_ref(a, b, "bf16", "bf16", "row", bl), "f32", plan.describe())
+
+
+def test_largest_leading_dimension():
+    """lda and ldb at the 2^20-element limit (rows 2 MiB apart), a few rows."""
+    M, N, K, ld = 5, 24, 64, 1 << 20
+    log(f"case largest leading dimension ld={ld}")
+    cfg = datagen.GemmConfig("t", M, N, K, "bf16", "f32", "row", "col", seed=23, int_seed=24)
+    a, b = datagen.gemm_inputs(cfg, "int")
+    A = np.zeros((M, ld), dtype=np.uint16)
+    A[:, :K] = a
+    B = np.zeros((N, ld), dtype=np.uint16)
+    B[:, :K] = b
+    got, plan = run_dense(A, B, M, N, K, "bf16", "f32", "row", "col", sentinel=True)
+    assert_bits_equal(got, oracle.gemm_ref(a, b, "bf16", "bf16", "row", "col"), "f32", plan.describe())
