@@ -84,3 +84,29 @@ def test_noalloc_rejects_plans_beyond_the_array():
         mg.gemm_run_noalloc(plan, D, D, D)
     assert e.value.status == mg.ERR_WORKSPACE
     assert (D == 0).all()
+
+
+def draw_noalloc_cases():
+    """Seeded split plans (RandomState(2039)) run one after another, so each
+    finds the previous one's partial sums in the library's array."""
+    rs = np.random.RandomState(2039)
+    tiles = {"nrw": mg.PLAN_FORCE_TILE_NARROW, "nrw64": mg.PLAN_FORCE_TILE_NARROW64,
+             "nrw32": mg.PLAN_FORCE_TILE_NARROW32, "128": mg.PLAN_FORCE_TILE_128x128,
+             "256": mg.PLAN_FORCE_TILE_256x256}
+    cases = []
+    for i in range(12):
+        tile = list(tiles)[rs.randint(len(tiles))]
+        M = int(rs.randint(1, 129)) if tile.startswith("nrw") else int(rs.randint(1, 600))
+        N = 8 * int(rs.randint(1, 88))
+        K = 8 * int(rs.randint(8, 200))
+        cases.append((i, M, N, K, ["row", "col"][rs.randint(2)], int(rs.randint(2, 6)), tiles[tile], tile))
+    return cases
+
+
+NOALLOC_CASES = draw_noalloc_cases()
+
+
+def test_noalloc_random_split_plans_in_sequence():
+    for i, M, N, K, bl, splits, flags, tile in NOALLOC_CASES:
+        log(f"case noalloc random {i}: tile={tile} splits={splits}")
+        run_both(M, N, K, bl, splits, "int", 4000 + i, tile_flags=flags)
