@@ -51,11 +51,33 @@ static int64_t ring_lds_bytes(const TileShape &t, int a_slots, int b_slots)
     return operand_ring_bytes(t.bm, kBK, a_slots, 2) + operand_ring_bytes(t.bn, kBK, b_slots, 2);
 }
 
+// The few-token tile's two rings for nv token blocks (1..8): token slots
+// (a) and weight slots (b), as the kernel lays them out.
+template <int BN>
+static void narrow_rings(int nv, int &a_slots, int &b_slots)
+{
+    using T = NarrowTile<IN_BF16, false, BN>;
+    switch (nv) {
+#define MG_R(V)                                  \
+    case V:                                      \
+        a_slots = T::template Ring<V>::DA;       \
+        b_slots = T::template Ring<V>::DB;       \
+        break;
+        MG_R(1) MG_R(2) MG_R(3) MG_R(4) MG_R(5) MG_R(6) MG_R(7)
+    default:
+        a_slots = T::template Ring<8>::DA;
+        b_slots = T::template Ring<8>::DB;
+        break;
+#undef MG_R
+    }
+}
+
 // Wave layout and ring depths of a dense plan's tile: the direct-to-LDS
 // tile runs dense plans on four waves of 128 x 128 (the tile table's 2x4 is
 // its grouped launches' layout), with the 3-slot ring on B when B is
-// column-major, else on A.
-static void dense_waves(int tile, bool bk, int &wm, int &wn, int &a_slots, int &b_slots)
+// column-major, else on A; the few-token tiles' rings (tokens as a, weights
+// as b) depend on the token count.
+static void dense_waves(int tile, bool bk, int &wm, int &wn, int &a_slots, int &b_slots, int64_t tokens = 128)
 {
     const TileShape &ts = tile_shape(tile);
     wm = ts.wm;
@@ -66,12 +88,13 @@ static void dense_waves(int tile, bool bk, int &wm, int &wn, int &a_slots, int &
         a_slots = bk ? 2 : 3;
         b_slots = bk ? 3 : 2;
     }
+    const int nv = (int)std::min<int64_t>(std::max<int64_t>((tokens + 15) / 16, 1), 8);
     if (tile == TILE_NARROW)
-        a_slots = b_slots = 5;
+        narrow_rings<128>(nv, a_slots, b_slots);
     if (tile == TILE_NARROW64)
-        a_slots = b_slots = 6;
+        narrow_rings<64>(nv, a_slots, b_slots);
     if (tile == TILE_NARROW32)
-        a_slots = b_slots = 7;
+        narrow_rings<32>(nv, a_slots, b_slots);
 }
 
 static const char *tile_name(int tile)
@@ -483,10 +506,14 @@ static mgemm_status_t plan_dense(const mgemm_desc_t *d, uint32_t flags, mgemm_pl
     const int64_t tasks = p->sk_tiles > 0 ? p->tiles - p->sk_tiles + (int64_t)p->sk_tiles * p->splits
                                           : p->tiles * p->splits;
     int wm, wn, a_slots, b_slots;
-    dense_waves(tile, bk, wm, wn, a_slots, b_slots);
+    dense_waves(tile, bk, wm, wn, a_slots, b_slots, d->M);
     // the ring must fit the LDS, and as many workgroups per CU as the tile
     // assumes must fit beside each other, else fewer
     p->lds_bytes = ring_lds_bytes(ts, a_slots, b_slots);
+    if (is_narrow(tile))   // the token slots hold the tile's token rows only
+        p->lds_bytes = operand_ring_bytes(16 * std::min<int64_t>(cdiv(std::max<int64_t>(d->M, 1), 16), 8), kBK,
+                                          a_slots, 2) +
+                       operand_ring_bytes(ts.bn, kBK, b_slots, 2);
     if (p->lds_bytes > kLdsPerCu) {
         set_error("the %s tile's ring (%d + %d stages) needs %lld bytes of LDS, more than a CU's %lld",
                   tile_name(tile), a_slots, b_slots, (long long)p->lds_bytes, (long long)kLdsPerCu);
@@ -848,7 +875,7 @@ extern "C" mgemm_status_t gemm_plan_info(mgemm_plan_t plan, mgemm_plan_info_t *i
     if (plan->kind == PLAN_DENSE) {
         int a_slots, b_slots;
         dense_waves(plan->tile, plan->dense.b_layout == MGEMM_COL_MAJOR, info->waves_m, info->waves_n, a_slots,
-                    b_slots);
+                    b_slots, plan->dense.M);
         info->stages = std::max(a_slots, b_slots);
     }
     info->lds_bytes = plan->kind == PLAN_DENSE ? (int32_t)plan->lds_bytes : ts.lds_bytes;
