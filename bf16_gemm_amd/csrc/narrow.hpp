@@ -146,9 +146,17 @@ struct NarrowTile {
         static constexpr int A_BYTES = NV * 16 * kRowBytes;
         static constexpr int LA = (2 * NV + WA - 1) / WA;
         static constexpr int DA_VM = 63 / LA + 1, DB_VM = 63 / LBW + 1;
-        // token depth: up to six steps within 3/8 of the space, at least three
-        static constexpr int DA_FIT = SCRATCH * 3 / 8 / A_BYTES;
-        static constexpr int DA_WANT = DA_FIT < 3 ? 3 : (DA_FIT > 6 ? 6 : DA_FIT);
+        // token depth: up to eight steps within 7/8 of the space, at least
+        // three, and never so many that fewer than three weight slots remain.
+        // Token rows are re-read by every tile of the launch (from L2), so at
+        // 64-128 tokens they are most of a step's bytes and their latency,
+        // not the weights', sets the step rate: 128 x 7168 x 2048 ran 18.0
+        // us with three token slots, 16.9 us with eight (and three weight
+        // slots), 128 x 2048 x 7168 20.7 -> 19.9 us; 16 tokens unchanged.
+        static constexpr int DA_FIT = SCRATCH * 7 / 8 / A_BYTES;
+        static constexpr int DA_CAP = DA_FIT < 3 ? 3 : (DA_FIT > 8 ? 8 : DA_FIT);
+        static constexpr int DA_ROOM = (SCRATCH - 3 * B_BYTES) / A_BYTES;
+        static constexpr int DA_WANT = DA_CAP < DA_ROOM ? DA_CAP : DA_ROOM;
         static constexpr int DA = DA_WANT < DA_VM ? DA_WANT : DA_VM;
         static constexpr int DB_FIT = (SCRATCH - DA * A_BYTES) / B_BYTES;
         static constexpr int DB = DB_FIT < DB_VM ? DB_FIT : DB_VM;

@@ -101,19 +101,22 @@ def test_plan_choices_for_workloads():
     p = mg.gemm_plan(128, 7168, 2048, "bf16", d_type="bf16")
     i = p.info()
     assert "tile=narrow64 tokens=128" in p.describe() and (i.block_m, i.block_n) == (128, 64), p.describe()
-    # two rings at 128 tokens: 3 token slots, 13 weight slots (the deeper one is info().stages)
-    assert i.splits == 2 and i.tiles == 112 and i.grid == 224 and i.stages == 13, p.describe()
-    assert "stages=3a/13b" in p.describe() and i.lds_bytes == 3 * 128 * 128 + 13 * 64 * 128, p.describe()
+    # two rings at 128 tokens: 8 token slots, 3 weight slots (the deeper one is info().stages)
+    assert i.splits == 2 and i.tiles == 112 and i.grid == 224 and i.stages == 8, p.describe()
+    assert "stages=8a/3b" in p.describe() and i.lds_bytes == 8 * 128 * 128 + 3 * 64 * 128, p.describe()
     p = mg.gemm_plan(128, 7168, 2048, "bf16", d_type="bf16", flags=mg.PLAN_SPLIT_K(1))
     assert "narrow" in p.describe() and p.info().splits == 1 and p.workspace_size() == 0, p.describe()
-    # forced widths: 128 columns (six weight slots), 32 columns (two waves, sixteen)
+    # forced widths: 128 columns (six token slots, three weight slots), 32
+    # columns (two waves; four token slots, the vmcnt bound of one token
+    # wave's 16 loads a step, and sixteen weight slots)
     p = mg.gemm_plan(128, 7168, 2048, "bf16", d_type="bf16", flags=mg.PLAN_FORCE_TILE_NARROW)
-    assert "tile=narrow128" in p.describe() and p.info().stages == 6 and p.info().splits == 4, p.describe()
+    assert "tile=narrow128" in p.describe() and "stages=6a/3b" in p.describe() and p.info().splits == 4, \
+        p.describe()
     p = mg.gemm_plan(128, 7168, 2048, "bf16", d_type="bf16", flags=mg.PLAN_FORCE_TILE_NARROW32)
     assert "tile=narrow32" in p.describe() and "waves=1x2" in p.describe() and p.info().stages == 16
-    # fewer tokens: smaller token slots, more of them (up to six), more weight slots
+    # fewer tokens: smaller token slots, more of them (up to eight), more weight slots
     p = mg.gemm_plan(16, 7168, 2048, "bf16", d_type="bf16", flags=mg.PLAN_FORCE_TILE_NARROW64)
-    assert "stages=6a/16b" in p.describe() and p.info().lds_bytes == 6 * 16 * 128 + 16 * 64 * 128, p.describe()
+    assert "stages=8a/16b" in p.describe() and p.info().lds_bytes == 8 * 16 * 128 + 16 * 64 * 128, p.describe()
     # the token width is the row count rounded up to 16 (mgemm_round_tokens)
     for M, w in [(1, 16), (16, 16), (17, 32), (100, 112), (128, 128)]:
         assert f"tokens={w} " in mg.gemm_plan(M, 4096, 1024, "bf16", d_type="bf16").describe()
