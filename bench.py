@@ -17,9 +17,9 @@ repeat, report the spread; hot and rotating input buffers):
     (up to) ten windows by events recorded on the stream the kernels are
     launched on: the value is K steps over the whole bracket, the windows
     give median / min / max per step;
-  * the engine and memory clocks are sampled from sysfs while the timed
-    steps run, and the clock-adjusted MFMA peak is reported beside the
-    nominal 2.4 GHz one;
+  * the engine and memory clocks and the board power are sampled from
+    sysfs while the timed steps run (and once before the warm-up), and the
+    clock-adjusted MFMA peak is reported beside the nominal 2.4 GHz one;
   * workloads whose operands fit the 256 MB MALL (the decode shape) are also
     timed over rotating copies of their buffers (more bytes than the MALL
     holds), so every step reads its weights from HBM.
@@ -477,13 +477,36 @@ WINDOWS = 10
 class ClockSampler:
     """Engine (sclk) and memory (mclk) clocks read from the GPU's sysfs
     performance-level files every ~2 ms in a background thread (the level
-    marked current); None where the files are not visible."""
+    marked current), and the board power the driver's hwmon reports
+    (power1_input, else power1_average, in microwatts); None where the files
+    are not visible."""
 
     def __init__(self):
         self.card = self._find_card()
+        self.power_file = self._find_power(self.card)
         self.samples = []
         self._stop = None
         self._thread = None
+
+    @staticmethod
+    def _find_power(card):
+        import glob
+        if not card:
+            return None
+        for name in ("power1_input", "power1_average"):
+            hits = sorted(glob.glob(os.path.join(card, "hwmon", "hwmon*", name)))
+            if hits:
+                return hits[0]
+        return None
+
+    def read_power_w(self):
+        if not self.power_file:
+            return None
+        try:
+            with open(self.power_file) as f:
+                return int(f.read().strip()) / 1e6
+        except (OSError, ValueError):
+            return None
 
     @staticmethod
     def _find_card():
@@ -530,7 +553,7 @@ class ClockSampler:
             while not self._stop.is_set():
                 sc, mc = self.read()
                 if sc is not None:
-                    self.samples.append((sc, mc))
+                    self.samples.append((sc, mc, self.read_power_w()))
                 self._stop.wait(0.002)
         self._thread = threading.Thread(target=run, daemon=True)
         self._thread.start()
@@ -547,8 +570,10 @@ class ClockSampler:
             return None
         sc = sorted(x[0] for x in self.samples)
         mc = sorted(x[1] for x in self.samples if x[1] is not None)
+        pw = sorted(x[2] for x in self.samples if x[2] is not None)
         return {"sclk_mhz": {"median": sc[len(sc) // 2], "min": sc[0], "max": sc[-1]},
-                "mclk_mhz": mc[len(mc) // 2] if mc else None, "samples": len(sc)}
+                "mclk_mhz": mc[len(mc) // 2] if mc else None, "samples": len(sc),
+                "power_w": {"median": pw[len(pw) // 2], "min": pw[0], "max": pw[-1]} if pw else None}
 
 
 def time_steps(torch, step, steps, warmup):
@@ -560,6 +585,7 @@ def time_steps(torch, step, steps, warmup):
     fns = step if isinstance(step, (list, tuple)) else [step]
     clk = ClockSampler()
     idle = clk.read()
+    idle_w = clk.read_power_w()
     asked = 10 if warmup is None else warmup
     n, t0 = 0, time.perf_counter()
     t_end = t0 + WARMUP_SECONDS
@@ -589,6 +615,7 @@ def time_steps(torch, step, steps, warmup):
     clocks = clk.summary()
     if clocks is not None:
         clocks["idle_before_mhz"] = {"sclk": idle[0], "mclk": idle[1]}
+        clocks["idle_before_w"] = idle_w
     ws = sorted(win)
     print(f"# {steps} steps in {nwin} windows after {n} warmup steps ({warm_s:.2f} s): {ms * 1e3:.1f} us/step "
           f"(events; windows median {ws[len(ws) // 2] * 1e3:.1f}, min {ws[0] * 1e3:.1f}, max {ws[-1] * 1e3:.1f}), "
