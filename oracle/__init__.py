@@ -84,6 +84,7 @@ def _load():
     lib.oracle_silu.argtypes = [ctypes.c_double]
     lib.oracle_silu.restype = ctypes.c_double
     lib.oracle_silu_gate.argtypes = [i64, i64, i64, dp, dp]
+    lib.oracle_silu_gate_weighted.argtypes = [i64, i64, i64, dp, dp, dp]
     lib.oracle_num_threads.restype = i32
     lib.oracle_e4m3_to_double.argtypes = [ctypes.c_uint8]
     lib.oracle_e4m3_to_double.restype = ctypes.c_double
@@ -191,15 +192,26 @@ def silu(x: float) -> float:
     return float(_load().oracle_silu(float(x)))
 
 
-def silu_gate(G: np.ndarray, interleave: int = GATE_UP_INTERLEAVE) -> np.ndarray:
+def silu_gate(G: np.ndarray, interleave: int = GATE_UP_INTERLEAVE, row_weight=None) -> np.ndarray:
     """h = SiLU(gate) * up (fp64, unrounded) from an rows x N fp64 GEMM output
-    whose columns interleave gate and up in blocks of ``interleave``."""
+    whose columns interleave gate and up in blocks of ``interleave``.
+
+    ``row_weight``: None, or one weight per row, multiplied into that row's h
+    after SwiGLU and before any rounding (the FC1 epilogue's optional routing
+    weight, "MegaMoE：Blackwell 与 Hopper 的融合算子解读", Hopper section 09:
+    taken into FC2's input, p(hW2) = (ph)W2)."""
     G = np.ascontiguousarray(G, dtype=np.float64)
     rows, N = G.shape
     if N % (2 * interleave):
         raise ValueError("N must be a multiple of twice the interleave")
     h = np.empty((rows, N // 2), dtype=np.float64)
-    _load().oracle_silu_gate(rows, N, interleave, _p(G), _p(h))
+    if row_weight is None:
+        _load().oracle_silu_gate(rows, N, interleave, _p(G), _p(h))
+    else:
+        w = np.ascontiguousarray(row_weight, dtype=np.float64).reshape(-1)
+        if w.size != rows:
+            raise ValueError("one weight per row")
+        _load().oracle_silu_gate_weighted(rows, N, interleave, _p(G), _p(w), _p(h))
     return h
 
 
@@ -242,13 +254,14 @@ def moe_combine_ref(Z: np.ndarray, pos, weights, dtype: str = "bf16") -> np.ndar
     weight p scales an expert's contribution, p(hW2) = (ph)W2).
 
     ``Z``: [rows][H] 16-bit bits (expert outputs in expert order); ``pos``:
-    [T][top_k] row of Z for each (token, choice); ``weights``: [T][top_k].
+    [T][top_k] row of Z for each (token, choice); ``weights``: [T][top_k], or
+    None for a plain sum (expert outputs that already carry their weights).
     Returns y[t] = sum_k weights[t, k] * Z[pos[t, k]] (fp64, unrounded); a
     position outside [0, rows) adds nothing.
     """
     z = decode(Z, dtype)
     pos = np.asarray(pos)
-    w = np.asarray(weights, dtype=np.float64)
+    w = np.ones(pos.shape, dtype=np.float64) if weights is None else np.asarray(weights, dtype=np.float64)
     y = np.zeros((pos.shape[0], z.shape[1]), dtype=np.float64)
     for k in range(pos.shape[1]):
         p = pos[:, k]

@@ -288,6 +288,25 @@ void oracle_silu_gate(int64_t rows, int64_t N, int64_t il, const double *G, doub
         }
 }
 
+/*
+ * The same with one weight per row multiplied into that row's outputs, after
+ * SwiGLU and before any rounding (the FC1 epilogue's optional routing weight:
+ * "MegaMoE：Blackwell 与 Hopper 的融合算子解读", Hopper section 09):
+ * h[r, c] = SiLU(gate) * up * w[r].
+ */
+void oracle_silu_gate_weighted(int64_t rows, int64_t N, int64_t il, const double *G, const double *w, double *h)
+{
+    int64_t half = N / 2;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t c = 0; c < half; ++c) {
+            int64_t blk = c / il, j = c % il;
+            double g = G[r * N + 2 * il * blk + j];
+            double u = G[r * N + 2 * il * blk + il + j];
+            h[r * half + c] = oracle_silu(g) * u * w[r];
+        }
+}
+
 /* Number of OpenMP threads a parallel region of this library would use. */
 int oracle_num_threads(void)
 {
