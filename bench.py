@@ -212,10 +212,12 @@ def moe_fused_case(torch, mg, datagen):
     return step, info, None
 
 
-def moe_layer_case(torch, mg, datagen):
+def moe_layer_case(torch, mg, datagen, fold=False):
     """The whole 64-expert layer: FC1 reading the routed rows of X through
     the routing's row index (the dispatch fused into its A loads), FC2, and
-    the weighted top-k combine into each token's output row."""
+    the weighted top-k combine into each token's output row.  fold: the
+    routing weights multiplied into FC1's SiLU-gate epilogue instead
+    (p(hW2) = (ph)W2), the combine a plain sum."""
     import numpy as np
     cfg = datagen.MOE["moe64"]
     r, A, W1, W2 = datagen.moe_inputs_device(cfg, "cuda")
@@ -234,11 +236,19 @@ def moe_layer_case(torch, mg, datagen):
     y = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
     p1 = mg.grouped_gemm_plan(E, rows, 2 * I, H, stride_b=H * 2 * I, epilogue=mg.EPI_SILU_GATE_I8)
     p2 = mg.grouped_gemm_plan(E, rows, H, I, stride_b=I * H)
+    w_row = np.empty(rows, dtype=np.float32)
+    w_row[r.pos] = r.weight                               # each routed row's routing weight
+    w_row = torch.from_numpy(w_row).cuda()
 
     def step():
         mg.grouped_gemm_run_gather(p1, X, W1, h, offs, idx)
         mg.grouped_gemm_run(p2, h, W2, z, offs)
         mg.moe_combine(z, pos, wts, y, cfg.top_k)
+
+    def step_fold():
+        mg.grouped_gemm_run_weighted(p1, X, W1, h, offs, w_row, row_index=idx)
+        mg.grouped_gemm_run(p2, h, W2, z, offs)
+        mg.moe_combine(z, pos, None, y, cfg.top_k)
 
     flops = 2.0 * rows * (2 * I) * H + 2.0 * rows * H * I
     active = int((r.counts > 0).sum())
@@ -246,11 +256,12 @@ def moe_layer_case(torch, mg, datagen):
     abytes = T * H * 2 + rows * I * 2 * 2 + rows * H * 2 * 2 + T * H * 2
     info = dict(flops=flops, bytes=wbytes + abytes, plan=p1.describe() + " | " + p2.describe() + " | combine",
                 dtype="bf16",
-                config={"workload": "moe64_layer", "experts": E, "hidden": H, "inter": I, "tokens": T,
-                        "top_k": cfg.top_k, "routed_rows": rows, "active_experts": active,
-                        "stages": "gathered FC1 (SiLU gate) + FC2 + weighted top-k combine"},
+                config={"workload": "moe64_layer_fold" if fold else "moe64_layer", "experts": E, "hidden": H,
+                        "inter": I, "tokens": T, "top_k": cfg.top_k, "routed_rows": rows, "active_experts": active,
+                        "stages": ("gathered FC1 (SiLU gate x routing weight) + FC2 + plain top-k sum" if fold else
+                                   "gathered FC1 (SiLU gate) + FC2 + weighted top-k combine")},
                 launches_per_step=len(p1.describe().split("grid=")) - 1 + len(p2.describe().split("grid=")) - 1 + 1)
-    return step, info, None
+    return (step_fold if fold else step), info, None
 
 
 # E4M3 workloads: per-tensor scales, B column-major, bf16 out
@@ -374,8 +385,8 @@ def main():
         step, info, case = moe_case(torch, mg, datagen)
     elif args.workload == "moe64_fused":
         step, info, case = moe_fused_case(torch, mg, datagen)
-    elif args.workload == "moe64_layer":
-        step, info, case = moe_layer_case(torch, mg, datagen)
+    elif args.workload in ("moe64_layer", "moe64_layer_fold"):
+        step, info, case = moe_layer_case(torch, mg, datagen, fold=args.workload == "moe64_layer_fold")
     elif args.workload in E4M3:
         step, info, case = e4m3_case(torch, mg, datagen, args.workload)
     else:

@@ -86,7 +86,7 @@ EXPORTS = ["gemm_plan", "grouped_gemm_plan", "gemm_plan_workspace_size", "gemm_r
            "gemm_plan_describe", "gemm_plan_info", "gemm_plan_destroy", "gemm_status_string",
            "gemm_last_error_message", "mgemm_tile_budget", "mgemm_group_working_set", "mgemm_round_tokens",
            "mgemm_version", "mgemm_moe_combine", "grouped_gemm_run_gather", "gemm_run_noalloc",
-           "moe_fused_plan", "moe_fused_run", "gemm_run_blockscaled"]
+           "moe_fused_plan", "moe_fused_run", "gemm_run_blockscaled", "grouped_gemm_run_weighted"]
 
 
 def _load():
@@ -132,6 +132,8 @@ def _load():
     lib.mgemm_version.restype = ctypes.c_char_p
     lib.grouped_gemm_run_gather.argtypes = [vp, vp, i64, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.grouped_gemm_run_gather.restype = st
+    lib.grouped_gemm_run_weighted.argtypes = [vp, vp, i64, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.grouped_gemm_run_weighted.restype = st
     lib.gemm_run_blockscaled.argtypes = [vp, vp, vp, vp, vp, i64, vp, i64, vp, ctypes.c_size_t, vp]
     lib.gemm_run_blockscaled.restype = st
     lib.moe_fused_plan.argtypes = [ctypes.POINTER(MoeDesc), u32, ctypes.POINTER(vp)]
@@ -306,6 +308,19 @@ def grouped_gemm_run_gather(plan: Plan, X, B, D, row_offsets, row_index, x_rows=
                                        _ptr(row_index), None, 0, _stream(stream)), "grouped_gemm_run_gather")
 
 
+def grouped_gemm_run_weighted(plan: Plan, A, B, D, row_offsets, row_weight, row_index=None, x_rows=None,
+                              stream=None):
+    """Enqueue the SiLU-gated grouped product with routed row r's h
+    multiplied by ``row_weight[r]`` (float32 cuda tensor, one per routed row)
+    before the rounding.  ``row_index``: None (A holds the routed rows) or the
+    gathered form's int32 index into A = X."""
+    if row_index is not None:
+        x_rows = A.shape[0] if x_rows is None else x_rows
+    _check(lib.grouped_gemm_run_weighted(plan.handle, _ptr(A), x_rows or 0, _ptr(B), _ptr(D), _ptr(row_offsets),
+                                         _ptr(row_index), _ptr(row_weight), None, 0, _stream(stream)),
+           "grouped_gemm_run_weighted")
+
+
 def moe_fused_plan(num_experts, max_total_rows, hidden, inter, dtype="bf16", lda=None, ldw1=None,
                    stride_w1=None, ldw2=None, stride_w2=None, ldh=None, ldy=None, flags: int = 0) -> Plan:
     """Plan the fused MoE layer (FC1 with the SiLU gate, then FC2, one
@@ -340,7 +355,7 @@ def moe_combine(Z, pos, weights, Y, top_k: int, z_rows=None, stream=None):
     """Enqueue Y[t] = sum_k weights[t, k] * Z[pos[t, k]] (fp32 accumulate,
     one rounding).  Z: [z_rows, H] and Y: [T, H] 16-bit cuda tensors with
     unit column stride; pos: int32 and weights: float32 cuda tensors of
-    T * top_k entries."""
+    T * top_k entries; weights None: a plain sum (weights of 1)."""
     T, H = Y.shape
     z_rows = Z.shape[0] if z_rows is None else z_rows
     _check(lib.mgemm_moe_combine(_ptr(Z), z_rows, Z.stride(0), _ptr(pos), _ptr(weights), _ptr(Y), Y.stride(0), T,

@@ -256,10 +256,12 @@ extern "C" mgemm_status_t gemm_run_blockscaled(mgemm_plan_t plan, const void *A,
 }
 
 // row_index: nullptr, or the gathered form's index (x_rows rows of A exist).
+// row_weight: nullptr, or one fp32 weight per routed row for the SiLU-gate
+// epilogue.
 static mgemm_status_t grouped_run(mgemm_plan_t plan, const void *A, const void *B, void *D,
                                   const int32_t *d_row_offsets, const int32_t *row_index, int64_t x_rows,
                                   mgemm_stream_t stream, const float *scale_a = nullptr,
-                                  const float *scale_b = nullptr)
+                                  const float *scale_b = nullptr, const float *row_weight = nullptr)
 {
     if (!plan || plan->kind != PLAN_GROUPED) {
         set_error("grouped_gemm_run: null or non-grouped plan");
@@ -330,6 +332,7 @@ static mgemm_status_t grouped_run(mgemm_plan_t plan, const void *A, const void *
         a.xcd_remap = plan->xcd_remap;
         a.row_index = row_index;
         a.x_rows = (int)x_rows;
+        a.row_weight = row_weight;
         GroupedFn f = grouped_fn(L.tile, bk, in, out, epi);
         if (!f) {
             set_error("grouped_gemm_run: kernel missing for the planned variant");
@@ -422,6 +425,29 @@ extern "C" mgemm_status_t grouped_gemm_run_gather(mgemm_plan_t plan, const void 
     return grouped_run(plan, X, B, D, d_row_offsets, d_row_index, x_rows, stream);
 }
 
+extern "C" mgemm_status_t grouped_gemm_run_weighted(mgemm_plan_t plan, const void *A, int64_t x_rows, const void *B,
+                                                    void *D, const int32_t *d_row_offsets,
+                                                    const int32_t *d_row_index, const float *d_row_weight,
+                                                    void *workspace, size_t workspace_bytes, mgemm_stream_t stream)
+{
+    (void)workspace;
+    (void)workspace_bytes;
+    if (!plan || plan->kind != PLAN_GROUPED) {
+        set_error("grouped_gemm_run_weighted: null or non-grouped plan");
+        return MGEMM_ERR_INVALID_ARG;
+    }
+    if (plan->grouped.epilogue != MGEMM_EPI_SILU_GATE_I8) {
+        set_error("grouped_gemm_run_weighted: the row weights scale the SiLU-gate epilogue; the plan has none");
+        return MGEMM_ERR_UNSUPPORTED;
+    }
+    if (!d_row_weight || ((uintptr_t)d_row_weight & 3)) {
+        set_error("grouped_gemm_run_weighted: the row weights must be a non-null, 4-byte aligned device array");
+        return MGEMM_ERR_INVALID_ARG;
+    }
+    return grouped_run(plan, A, B, D, d_row_offsets, d_row_index, d_row_index ? x_rows : 0, stream, nullptr,
+                       nullptr, d_row_weight);
+}
+
 extern "C" mgemm_status_t grouped_gemm_run_scaled(mgemm_plan_t plan, const void *A, const void *B, void *D,
                                                   const int32_t *d_row_offsets, const float *d_scale_a,
                                                   const float *d_scale_b, void *workspace, size_t workspace_bytes,
@@ -464,7 +490,7 @@ extern "C" mgemm_status_t mgemm_moe_combine(const void *Z, int64_t z_rows, int64
                   (long long)H);
         return MGEMM_ERR_INVALID_ARG;
     }
-    if (!Z || !Y || !d_pos || !d_weights) {
+    if (!Z || !Y || !d_pos) {
         set_error("mgemm_moe_combine: null pointer");
         return MGEMM_ERR_INVALID_ARG;
     }

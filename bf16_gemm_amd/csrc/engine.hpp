@@ -1695,8 +1695,16 @@ __device__ __forceinline__ uint32_t pack2_bf16(float a, float b)
 {
     return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)a) | ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)b) << 16);
 }
+// Each fp32 value is converted as it stands (one IEEE round-to-nearest-even
+// each).  The values are made opaque first: otherwise the compiler may fold
+// the product that made a value and its conversion into one mixed-precision
+// FMA that rounds the exact product straight to fp16, so the same epilogue
+// would round differently in kernels where the fold happens and where it
+// does not.
 __device__ __forceinline__ uint32_t pack2_f16(float a, float b)
 {
+    a = opaque(a);
+    b = opaque(b);
     return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)a) | ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)b) << 16);
 }
 
@@ -1739,8 +1747,13 @@ constexpr int out_size(int out) { return out == OUT_F32 ? 4 : 2; }
 // AUX: the stores' cache-policy bits (kDeviceScope: written through to the
 // level every XCD shares, for outputs another workgroup reads in the same
 // launch).
+// rw (SILU_GATE only, may be null): the tile's row weights, rw[r] for tile
+// row r < m_valid; each gated value is multiplied by its row's weight before
+// the rounding ("MegaMoE：Blackwell 与 Hopper 的融合算子解读", Hopper section 09:
+// the routing weight taken into FC2's input, p(hW2) = (ph)W2).
 template <class T, int EPI, int OUT, int AUX = 0>
-__device__ __forceinline__ void epilogue(const T &t, void *D, int64_t ldd, int m_valid, int n_valid, int tid)
+__device__ __forceinline__ void epilogue(const T &t, void *D, int64_t ldd, int m_valid, int n_valid, int tid,
+                                         const float *rw = nullptr)
 {
     constexpr int esize = out_size(OUT);
     const int lane = tid & 63;
@@ -1753,12 +1766,19 @@ __device__ __forceinline__ void epilogue(const T &t, void *D, int64_t ldd, int m
         return;
     const __amdgpu_buffer_rsrc_t r =
         make_rsrc(D, ((uint64_t)(m_valid - 1) * (uint64_t)ldd + (uint64_t)out_cols) * (uint64_t)esize);
+    // row weights: rows past m_valid read 0 (their outputs are not stored)
+    const __amdgpu_buffer_rsrc_t rwr = make_rsrc(rw, rw ? (uint64_t)m_valid * 4u : 0u);
     if constexpr (T::MI == 16) {
         // 16 x 16 blocks: lane l holds row (l mod 16), columns 4(l/16) .. +3
 #pragma unroll
         for (int i = 0; i < T::FM; ++i) {
             const int m = wm0 + 16 * i + (lane & 15);
             const uint32_t rowoff = (uint32_t)m * row_bytes;
+            float w = 1.0f;
+            if constexpr (EPI == EPI_SILU_GATE) {
+                if (rw)
+                    w = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rwr, (uint32_t)m * 4u, 0, 0));
+            }
 #pragma unroll
             for (int j = 0; j < T::FN; ++j) {
                 const f32x4_t &a = t.acc[i][j];
@@ -1773,8 +1793,15 @@ __device__ __forceinline__ void epilogue(const T &t, void *D, int64_t ldd, int m
                     const float u2 = __shfl_xor(a[2], 32, 64), u3 = __shfl_xor(a[3], 32, 64);
                     const int hc = (n >> 4) * 8 + (n & 15);
                     const uint32_t off = (lane < 32 && n < n_valid) ? rowoff + (uint32_t)hc * esize : kOOB;
-                    bstore4<OUT, AUX>(r, off, silu_mul(a[0], u0), silu_mul(a[1], u1), silu_mul(a[2], u2),
-                                 silu_mul(a[3], u3));
+                    float h0 = silu_mul(a[0], u0), h1 = silu_mul(a[1], u1), h2 = silu_mul(a[2], u2),
+                          h3 = silu_mul(a[3], u3);
+                    if (rw) {
+                        h0 *= w;
+                        h1 *= w;
+                        h2 *= w;
+                        h3 *= w;
+                    }
+                    bstore4<OUT, AUX>(r, off, h0, h1, h2, h3);
                 }
             }
         }
@@ -1783,6 +1810,11 @@ __device__ __forceinline__ void epilogue(const T &t, void *D, int64_t ldd, int m
         for (int i = 0; i < T::FM; ++i) {
             const int m = wm0 + 32 * i + (lane & 31);
             const uint32_t rowoff = (uint32_t)m * row_bytes;
+            float w = 1.0f;
+            if constexpr (EPI == EPI_SILU_GATE) {
+                if (rw)
+                    w = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rwr, (uint32_t)m * 4u, 0, 0));
+            }
 #pragma unroll
             for (int j = 0; j < T::FN; ++j) {
                 const f32x16_t &a = t.acc[i][j];
@@ -1801,8 +1833,15 @@ __device__ __forceinline__ void epilogue(const T &t, void *D, int64_t ldd, int m
                         const int n = wn0 + 32 * j + 8 * rg + 4 * (lane >> 5);
                         const int hc = (n >> 4) * 8 + (n & 15);
                         const uint32_t off = n < n_valid ? rowoff + (uint32_t)hc * esize : kOOB;
-                        bstore4<OUT, AUX>(r, off, silu_mul(a[4 * rg + 0], a[4 * rg + 4]), silu_mul(a[4 * rg + 1], a[4 * rg + 5]),
-                                     silu_mul(a[4 * rg + 2], a[4 * rg + 6]), silu_mul(a[4 * rg + 3], a[4 * rg + 7]));
+                        float h0 = silu_mul(a[4 * rg + 0], a[4 * rg + 4]), h1 = silu_mul(a[4 * rg + 1], a[4 * rg + 5]);
+                        float h2 = silu_mul(a[4 * rg + 2], a[4 * rg + 6]), h3 = silu_mul(a[4 * rg + 3], a[4 * rg + 7]);
+                        if (rw) {
+                            h0 *= w;
+                            h1 *= w;
+                            h2 *= w;
+                            h3 *= w;
+                        }
+                        bstore4<OUT, AUX>(r, off, h0, h1, h2, h3);
                     }
                 }
             }
@@ -1870,12 +1909,12 @@ __device__ __forceinline__ void epilogue_staged(const T &t, char *lds, void *D, 
 // without a gate, else straight from the registers.
 template <class T, int EPI, int OUT>
 __device__ __forceinline__ void tile_epilogue(const T &t, char *lds, void *D, int64_t ldd, int m_valid, int n_valid,
-                                              int tid)
+                                              int tid, const float *rw = nullptr)
 {
     if constexpr (T::MI == 16 && EPI == EPI_NONE)
         epilogue_staged<T, OUT>(t, lds, D, ldd, m_valid, n_valid, tid);
     else
-        epilogue<T, EPI, OUT>(t, D, ldd, m_valid, n_valid, tid);
+        epilogue<T, EPI, OUT>(t, D, ldd, m_valid, n_valid, tid, rw);
     // The direct-to-LDS loops count their own loads with vmcnt waits, and
     // the counter also counts these stores.  Rather than rely on loads and
     // earlier stores retiring in order (the compiler's own wait placement

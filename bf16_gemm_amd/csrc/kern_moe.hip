@@ -17,9 +17,10 @@ __device__ __forceinline__ float half_to_float(uint32_t h)
 
 // Y[t, 8c .. 8c+7] = sum_k w[t,k] * Z[pos[t,k], 8c .. 8c+7]: one lane per
 // 16-byte column chunk, the k terms added in order with fused multiply-adds
-// in fp32, one rounding to the 16-bit type.  Z is read through a buffer
-// resource that ends after its last row, so a position outside [0, z_rows)
-// reads zeros and contributes nothing.
+// in fp32, one rounding to the 16-bit type (w null: every weight 1, a plain
+// sum, for expert outputs that already carry their routing weight).  Z is
+// read through a buffer resource that ends after its last row, so a
+// position outside [0, z_rows) reads zeros and contributes nothing.
 template <int OUT>
 __global__ void __launch_bounds__(256) moe_combine_kernel(const uint16_t *Z, int64_t z_rows, int64_t ldz,
                                                           const int32_t *pos, const float *w, char *Y, int64_t ldy,
@@ -29,12 +30,11 @@ __global__ void __launch_bounds__(256) moe_combine_kernel(const uint16_t *Z, int
     const uint64_t zbytes = (uint64_t)z_rows * (uint64_t)ldz * 2u;
     const __amdgpu_buffer_rsrc_t rz = make_rsrc(Z, zbytes);
     const int32_t *pt = pos + t * top_k;
-    const float *wt = w + t * top_k;
     for (int c = blockIdx.y * 256 + (int)threadIdx.x; c < H8; c += gridDim.y * 256) {
         f32x8_t acc = {};
         for (int k = 0; k < top_k; ++k) {
             const int p = pt[k];
-            const float wk = wt[k];
+            const float wk = w ? w[t * top_k + k] : 1.0f;
             const uint64_t row_off = (uint64_t)(int64_t)p * (uint64_t)ldz * 2u + (uint64_t)c * 16u;
             const uint32_t off = (p >= 0 && (int64_t)p < z_rows && row_off < zbytes) ? (uint32_t)row_off : kOOB;
             const u32x4_t v = bload16(rz, off);

@@ -50,6 +50,7 @@ struct GroupedArgs {
     int x_rows = 0;                      // rows of A that exist when gathering
     const float *scale_a = nullptr;      // E4M3: the activations' scale (device, one float; null = 1)
     const float *scale_b = nullptr;      // E4M3: one weight scale per expert (device, G floats; null = 1)
+    const float *row_weight = nullptr;   // SILU_GATE: routed row r's h multiplied by row_weight[r] (null = 1)
 };
 
 
@@ -472,7 +473,8 @@ __global__ void __launch_bounds__(T::NT) grouped_kernel(GroupedArgs p)
         tile.mainloop(lds, sa, p.lda, sb, p.ldb, p.K, opaque((int)threadIdx.x), ga);
         const int dcol0 = EPI == EPI_SILU_GATE ? n0 / 2 : n0;
         char *Dt = (char *)p.D + ((int64_t)m0 * p.ldd + dcol0) * esize;
-        tile_epilogue<T, EPI, OUT>(tile, lds, Dt, p.ldd, m_valid, min(T::BN, p.N - n0), opaque((int)threadIdx.x));
+        tile_epilogue<T, EPI, OUT>(tile, lds, Dt, p.ldd, m_valid, min(T::BN, p.N - n0), opaque((int)threadIdx.x),
+                                   p.row_weight ? p.row_weight + m0 : nullptr);
     }
 }
 
@@ -586,7 +588,8 @@ __global__ void __launch_bounds__(T::NT) grouped_kernel_wt(GroupedArgs p)
         tile.mainloop(lds, sa, p.lda, sb, p.ldb, p.K, opaque((int)threadIdx.x), ga);
         const int dcol0 = EPI == EPI_SILU_GATE ? n0 / 2 : n0;
         char *Dt = (char *)p.D + ((int64_t)m0 * p.ldd + dcol0) * esize;
-        tile_epilogue<T, EPI, OUT>(tile, lds, Dt, p.ldd, m_valid, min(T::BN, p.N - n0), opaque((int)threadIdx.x));
+        tile_epilogue<T, EPI, OUT>(tile, lds, Dt, p.ldd, m_valid, min(T::BN, p.N - n0), opaque((int)threadIdx.x),
+                                   p.row_weight ? p.row_weight + m0 : nullptr);
     }
 }
 
@@ -777,7 +780,8 @@ __global__ void __launch_bounds__((NarrowTile<IN, BKM, BN>::NT)) narrow_grouped_
         tile.values(v, ntb);
         const int dcol0 = EPI == EPI_SILU_GATE ? n0 / 2 : n0;
         char *Dt = (char *)p.D + ((int64_t)m0 * p.ldd + dcol0) * esize;
-        narrow_store<EPI, OUT>(v, Dt, p.ldd, m_valid, min(T::BN, p.N - n0), ntb, tid);
+        narrow_store<EPI, OUT>(v, Dt, p.ldd, m_valid, min(T::BN, p.N - n0), ntb, tid,
+                               p.row_weight ? p.row_weight + m0 : nullptr);
         wait_vm<0>();
     }
 }
@@ -820,7 +824,7 @@ __global__ void __launch_bounds__(256) edge_cols_kernel(DenseArgs p, int a_kmajo
         else if constexpr (OUT == OUT_BF16)
             *(__bf16 *)d = (__bf16)s;
         else
-            *(_Float16 *)d = (_Float16)s;
+            *(_Float16 *)d = (_Float16)opaque(s);   // the fp32 sum, then one conversion (see pack2_f16)
     }
 }
 

@@ -443,10 +443,12 @@ struct NarrowTile {
 // n_valid: tokens and GEMM columns of the tile that exist (n_valid a
 // multiple of 4).  Rows past m_valid fall past the resource; column groups
 // past n_valid take an out-of-range offset.
-// AUX: the stores' cache-policy bits.
+// AUX: the stores' cache-policy bits.  rw (SILU_GATE only, may be null): the
+// tile's token weights, rw[t] for token t < m_valid, multiplied into each
+// gated value before the rounding (as in epilogue()).
 template <int EPI, int OUT, int NTB, int NB, int AUX = 0>
 __device__ __forceinline__ void narrow_store(const f32x4_t (&v)[NTB][NB], void *D, int64_t ldd, int m_valid,
-                                             int n_valid, int ntb, int tid)
+                                             int n_valid, int ntb, int tid, const float *rw = nullptr)
 {
     constexpr int esize = out_size(OUT);
     const int lane = tid & 63;
@@ -457,11 +459,19 @@ __device__ __forceinline__ void narrow_store(const f32x4_t (&v)[NTB][NB], void *
     const uint32_t row_bytes = (uint32_t)ldd * (uint32_t)esize;
     const __amdgpu_buffer_rsrc_t r =
         make_rsrc(D, ((uint64_t)(m_valid - 1) * (uint64_t)ldd + (uint64_t)out_cols) * (uint64_t)esize);
+    // token weights: tokens past m_valid read 0 (their outputs are not stored)
+    const __amdgpu_buffer_rsrc_t rwr = make_rsrc(rw, rw ? (uint64_t)m_valid * 4u : 0u);
 #pragma unroll
     for (int tb = 0; tb < NTB; ++tb) {
         if (tb >= ntb)
             break;
         const uint32_t rowoff = (uint32_t)(16 * tb + (lane & 15)) * row_bytes;
+        float w = 1.0f;
+        if constexpr (EPI == EPI_SILU_GATE) {
+            if (rw)
+                w = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                  rwr, (uint32_t)(16 * tb + (lane & 15)) * 4u, 0, 0));
+        }
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
             const f32x4_t &a = v[tb][nb];
@@ -475,7 +485,14 @@ __device__ __forceinline__ void narrow_store(const f32x4_t (&v)[NTB][NB], void *
                 const float u2 = __shfl_xor(a[2], 32, 64), u3 = __shfl_xor(a[3], 32, 64);
                 const int hc = (n >> 4) * 8 + (n & 15);
                 const uint32_t off = (lane < 32 && n < n_valid) ? rowoff + (uint32_t)hc * esize : kOOB;
-                bstore4<OUT, AUX>(r, off, silu_mul(a[0], u0), silu_mul(a[1], u1), silu_mul(a[2], u2), silu_mul(a[3], u3));
+                float h0 = silu_mul(a[0], u0), h1 = silu_mul(a[1], u1), h2 = silu_mul(a[2], u2), h3 = silu_mul(a[3], u3);
+                if (rw) {
+                    h0 *= w;
+                    h1 *= w;
+                    h2 *= w;
+                    h3 *= w;
+                }
+                bstore4<OUT, AUX>(r, off, h0, h1, h2, h3);
             }
         }
     }

@@ -323,6 +323,28 @@ mgemm_status_t grouped_gemm_run_gather(mgemm_plan_t plan, const void *X, int64_t
                                        const int32_t *d_row_offsets, const int32_t *d_row_index, void *workspace,
                                        size_t workspace_bytes, mgemm_stream_t stream);
 
+/* The SiLU-gated grouped product (FC1 of an MoE layer) with each routed
+ * row's output multiplied by that row's routing weight before the rounding:
+ *   h[r, c] = round(SiLU(gate[r, c]) * up[r, c] * d_row_weight[r])
+ * ("MegaMoE：Blackwell 与 Hopper 的融合算子解读", Hopper section 09: the FC1
+ * epilogue chain optionally multiplies by the routing weight, and taking
+ * that weight into FC2's input lets the final combine add the experts'
+ * contributions as they are, since p(hW2) = (ph)W2 for the linear FC2; run
+ * FC2 with grouped_gemm_run, then mgemm_moe_combine with d_weights NULL).
+ * SwiGLU and the weight product are fp32; one rounding to the output type.
+ * d_row_weight: device fp32, 4-byte aligned, one weight per routed row
+ * (off[num_groups] entries, in routed-row order: the weight of the (token,
+ * choice) pair routed to that row).  d_row_index: NULL (A holds the routed
+ * rows, as in grouped_gemm_run; x_rows is ignored) or the gathered form's
+ * index into X = A of x_rows rows (as in grouped_gemm_run_gather, with its
+ * rules on tiles).  Only plans with MGEMM_EPI_SILU_GATE_I8 (else
+ * MGEMM_ERR_UNSUPPORTED); a null or misaligned d_row_weight gives
+ * MGEMM_ERR_INVALID_ARG.  Everything else is grouped_gemm_run's. */
+mgemm_status_t grouped_gemm_run_weighted(mgemm_plan_t plan, const void *A, int64_t x_rows, const void *B, void *D,
+                                         const int32_t *d_row_offsets, const int32_t *d_row_index,
+                                         const float *d_row_weight, void *workspace, size_t workspace_bytes,
+                                         mgemm_stream_t stream);
+
 /* MoE combine: every token's output row is the routing-weighted sum of the
  * rows its top-k experts produced ("MegaMoE：Blackwell 与 Hopper 的融合算子解读",
  * Blackwell section 13: a separate top-k reduce reads each branch and adds
@@ -331,7 +353,10 @@ mgemm_status_t grouped_gemm_run_gather(mgemm_plan_t plan, const void *X, int64_t
  *   Y[t, j] = sum_{k < top_k} weights[t*top_k + k] * Z[pos[t*top_k + k], j]
  * for t < T, j < H.  Z: 16-bit rows (the FC2 output in expert order),
  * z_rows x H, row pitch ldz; Y: T x H of the same type, row pitch ldy; pos
- * (int32) and weights (fp32): device arrays of T*top_k entries.  The terms
+ * (int32) and weights (fp32): device arrays of T*top_k entries; weights may
+ * be NULL, every weight then 1 (a plain sum, for expert outputs whose
+ * routing weights were taken into FC1's epilogue by
+ * grouped_gemm_run_weighted).  The terms
  * are added in k order with fp32 fused multiply-adds, then rounded once
  * (RNE) to the 16-bit type.  A position outside [0, z_rows) contributes
  * nothing.  dtype: BF16 or F16.  H % 8 == 0, ldz and ldy multiples of 8 and

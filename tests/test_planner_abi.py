@@ -391,3 +391,19 @@ def test_moe_fused_plan_rules():
     # no rows: nothing to do, nothing touched
     mg.moe_fused_run(mg.moe_fused_plan(8, 0, 256, 128), fake, fake, fake, fake, fake, fake, workspace=None,
                      stream=0)
+
+
+def test_weighted_run_rules():
+    """grouped_gemm_run_weighted: only SiLU-gate plans, a non-null 4-byte
+    aligned weight array; refused before anything is launched (the fake
+    device addresses are never touched)."""
+    fake = 1 << 20
+    plain = mg.grouped_gemm_plan(4, 256, 256, 256)
+    with pytest.raises(mg.MgemmError) as e:
+        mg.grouped_gemm_run_weighted(plain, fake, fake, fake, fake, fake, stream=0)
+    assert e.value.status == mg.ERR_UNSUPPORTED and "SiLU" in str(e.value)
+    gated = mg.grouped_gemm_plan(4, 256, 256, 256, epilogue=mg.EPI_SILU_GATE_I8)
+    for w in (None, fake + 2):
+        with pytest.raises(mg.MgemmError) as e:
+            mg.grouped_gemm_run_weighted(gated, fake, fake, fake, fake, w, stream=0)
+        assert e.value.status == mg.ERR_INVALID_ARG, w
