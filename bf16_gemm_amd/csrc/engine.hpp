@@ -1426,8 +1426,10 @@ struct DtlTile4E4M3X {
     // steps (set p % 2 for steps 2p, 2p + 1): sca[set][b] holds A's scale of
     // the lane's row in row block b, step 2p in byte 0 and step 2p + 1 in
     // byte 1; scb[set] B's scale of the wave's 128 columns, same bytes.
+    // The loads fill only sca[set][0..1] (lane l: row l and row 64 + l of
+    // the wave's rows); bcast_scales spreads them over the 8 row blocks.
     uint32_t sca[2][8], scb[2];
-    uint32_t sc_lane;     // byte offset of the lane's row of A scales in row block 0
+    uint32_t sc_lane;     // byte offset of row (lane) of the wave's A scales
     int sc_brow;          // byte offset of the wave's row of B scales
 
     __device__ __forceinline__ void setup(int lane, int wave, int wm0, int wn0, int lda, int ldb)
@@ -1487,19 +1489,35 @@ struct DtlTile4E4M3X {
     // 16 MFMAs on m blocks 4 HM .. +3 x n blocks 4 HN .. +3 (n outer); read
     // i (of 8) after MFMAs 0, 2, .., 14, load j (of NL) after MFMA
     // j * 16 / NL + 1
-    // The scales of step pair p into set SET: A's for the lane's row of each
-    // row block, then B's, two bytes (steps 2p and 2p + 1) per load (the
-    // scale rows' pitches are even, so both bytes lie in the row); a pair
-    // at or past the last k block, and rows past M, read as zeros through an
-    // out-of-range offset.  9 loads.
+    // The scales of step pair p into set SET: A's of the wave's 128 rows in
+    // two loads (lane l: rows l and 64 + l; the 16 lanes of a row block read
+    // 16 lines, where a load per row block had all 64 lanes read one line
+    // each), then B's; two bytes (steps 2p and 2p + 1) per load (the scale
+    // rows' pitches are even, so both bytes lie in the row); a pair at or
+    // past the last k block, and rows past M, read as zeros through an
+    // out-of-range offset.  3 loads.
     template <int SET>
     __device__ __forceinline__ void load_scales(const BlockScaleSrc &bs, int p)
     {
         const bool in_k = 2 * p < bs.kb;
+        load_scale_pair(sca[SET][0], bs.ra, in_k ? sc_lane + (uint32_t)(2 * p) : kOOB);
+        load_scale_pair(sca[SET][1], bs.ra, in_k ? sc_lane + (uint32_t)(64 * bs.lds_a + 2 * p) : kOOB);
+        load_scale_pair(scb[SET], bs.rb, in_k ? (uint32_t)(sc_brow + 2 * p) : kOOB);
+    }
+    // Lane l's row of row block b is row 16b + (l mod 16), held by lane
+    // 16 (b mod 4) + (l mod 16) of load b / 4: one cross-lane read per row
+    // block.  Only once the set's loads have been counted complete: the
+    // empty asm keeps the reads below the wait and barrier before it (the
+    // compiler takes an asm load's result as written at once).
+    template <int SET>
+    __device__ __forceinline__ void bcast_scales(int lane)
+    {
+        uint32_t r0 = sca[SET][0], r1 = sca[SET][1];
+        asm volatile("" : "+v"(r0), "+v"(r1));
 #pragma unroll
         for (int b = 0; b < 8; ++b)
-            load_scale_pair(sca[SET][b], bs.ra, in_k ? sc_lane + (uint32_t)(16 * b * bs.lds_a + 2 * p) : kOOB);
-        load_scale_pair(scb[SET], bs.rb, in_k ? (uint32_t)(sc_brow + 2 * p) : kOOB);
+            sca[SET][b] = (uint32_t)__builtin_amdgcn_ds_bpermute((16 * (b % 4) + (lane & 15)) << 2,
+                                                                 (int)(b < 4 ? r0 : r1));
     }
     // A pair whose second step lies past the last k block read a byte past
     // the scales (padding): keep only the first step's.
@@ -1545,7 +1563,7 @@ struct DtlTile4E4M3X {
         if constexpr (BS) {
             // the wave's 128 columns are one scale block (TN == 128)
             static_assert(TN == 128, "");
-            sc_lane = (uint32_t)((wm0 + (lane & 15)) * bs.lds_a);
+            sc_lane = (uint32_t)((wm0 + lane) * bs.lds_a);
             sc_brow = (bs.nblk0 + wn0 / 128) * bs.lds_b;
         }
         const int ksteps = (K + KSTEP - 1) / KSTEP;
@@ -1588,6 +1606,8 @@ struct DtlTile4E4M3X {
             wait_vm<LOADS>();
         }
         lds_barrier();
+        if constexpr (BS)
+            bcast_scales<0>(lane);
         F8 Al, Ah, Bh, BlX, BlY;
 #pragma unroll
         for (int i = 0; i < 8; ++i)
@@ -1605,7 +1625,7 @@ struct DtlTile4E4M3X {
         // form: the first step of pair p loads pair p + 1's scales into the
         // other set, right after its barrier; they are counted complete by
         // the next step's wait, which leaves only the last quarter's B loads
-        // outstanding)
+        // outstanding, and spread over the row blocks after its barrier)
         auto step = [&](int kt, auto mask, auto par, auto set) {
             constexpr int P = decltype(par)::value;
             constexpr int SET = decltype(set)::value;
@@ -1625,6 +1645,8 @@ struct DtlTile4E4M3X {
             lds_barrier();
             if constexpr (BS && P == 0)
                 load_scales<SET ^ 1>(bs, (kt >> 1) + 1);
+            if constexpr (BS && P == 1)
+                bcast_scales<SET ^ 1>(lane);  // loaded by the step before, counted complete by the wait above
             const auto rA = MASK ? ua.at_step(kt + 2) : step_rsrc(ua, true, kt + 2);
             const int ka = K - (kt + 2) * KSTEP;
             char *const aw = A0 + P * OPS;
