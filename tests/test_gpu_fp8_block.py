@@ -142,11 +142,14 @@ def test_scale_moves_only_its_block():
     M, N, K = 256, 512, 512
     A, B, sa, sb = inputs(M, N, K, "int", seed=21)
     _, base = run(A, B, sa, sb, M, N, K, "f32")
-    sa2 = sa.copy()
-    sa2[37, 2] += 1
-    _, got = run(A, B, sa2, sb, M, N, K, "f32")
-    assert_bits_equal(got, oracle.gemm_e4m3_block_ref(A, B, sa2, sb), "f32", "A scale raised")
-    assert np.array_equal(np.delete(got, 37, 0), np.delete(base, 37, 0))
+    # rows in each half of both wave rows of the tile (the kernel loads a
+    # wave's 128 rows of scales as two halves of 64)
+    for row, kb in ((37, 2), (100, 0), (131, 3), (250, 1)):
+        sa2 = sa.copy()
+        sa2[row, kb] += 1
+        _, got = run(A, B, sa2, sb, M, N, K, "f32")
+        assert_bits_equal(got, oracle.gemm_e4m3_block_ref(A, B, sa2, sb), "f32", f"A scale of row {row} raised")
+        assert np.array_equal(np.delete(got, row, 0), np.delete(base, row, 0))
     sb2 = sb.copy()
     sb2[3, 1] -= 2
     _, got = run(A, B, sa, sb2, M, N, K, "f32")
