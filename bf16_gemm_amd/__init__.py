@@ -86,7 +86,8 @@ EXPORTS = ["gemm_plan", "grouped_gemm_plan", "gemm_plan_workspace_size", "gemm_r
            "gemm_plan_describe", "gemm_plan_info", "gemm_plan_destroy", "gemm_status_string",
            "gemm_last_error_message", "mgemm_tile_budget", "mgemm_group_working_set", "mgemm_round_tokens",
            "mgemm_version", "mgemm_moe_combine", "grouped_gemm_run_gather", "gemm_run_noalloc",
-           "moe_fused_plan", "moe_fused_run", "gemm_run_blockscaled", "grouped_gemm_run_weighted"]
+           "moe_fused_plan", "moe_fused_run", "gemm_run_blockscaled", "grouped_gemm_run_weighted",
+           "moe_fused_run_weighted"]
 
 
 def _load():
@@ -140,6 +141,8 @@ def _load():
     lib.moe_fused_plan.restype = st
     lib.moe_fused_run.argtypes = [vp, vp, i64, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.moe_fused_run.restype = st
+    lib.moe_fused_run_weighted.argtypes = [vp, vp, i64, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.moe_fused_run_weighted.restype = st
     lib.mgemm_moe_combine.argtypes = [vp, i64, i64, vp, vp, vp, i64, i64, ctypes.c_int32, i64, ctypes.c_int, vp]
     lib.mgemm_moe_combine.restype = st
     return lib
@@ -349,6 +352,19 @@ def moe_fused_run(plan: Plan, X, W1, W2, H, Y, row_offsets, workspace=None, row_
     _check(lib.moe_fused_run(plan.handle, _ptr(X), x_rows or 0, _ptr(row_index), _ptr(W1), _ptr(W2), _ptr(H),
                              _ptr(Y), _ptr(row_offsets), _ptr(workspace), _nbytes(workspace, workspace_bytes),
                              _stream(stream)), "moe_fused_run")
+
+
+def moe_fused_run_weighted(plan: Plan, X, W1, W2, H, Y, row_offsets, row_weight, workspace=None, row_index=None,
+                           x_rows=None, workspace_bytes: int = 0, stream=None):
+    """``moe_fused_run`` with routed row r's h multiplied by row_weight[r]
+    (float32 cuda tensor, one entry per routed row) before its rounding."""
+    if workspace is None and isinstance(Y, torch.Tensor):
+        workspace = workspace_for(plan, Y.device)
+    if row_index is not None and x_rows is None:
+        x_rows = X.shape[0]
+    _check(lib.moe_fused_run_weighted(plan.handle, _ptr(X), x_rows or 0, _ptr(row_index), _ptr(W1), _ptr(W2),
+                                      _ptr(H), _ptr(Y), _ptr(row_offsets), _ptr(row_weight), _ptr(workspace),
+                                      _nbytes(workspace, workspace_bytes), _stream(stream)), "moe_fused_run_weighted")
 
 
 def moe_combine(Z, pos, weights, Y, top_k: int, z_rows=None, stream=None):

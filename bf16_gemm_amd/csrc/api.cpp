@@ -344,33 +344,33 @@ static mgemm_status_t grouped_run(mgemm_plan_t plan, const void *A, const void *
     return MGEMM_OK;
 }
 
-extern "C" mgemm_status_t moe_fused_run(mgemm_plan_t plan, const void *X, int64_t x_rows, const int32_t *d_row_index,
-                                        const void *W1, const void *W2, void *H, void *Y,
-                                        const int32_t *d_row_offsets, void *workspace, size_t workspace_bytes,
-                                        mgemm_stream_t stream)
+static mgemm_status_t moe_fused(const char *name, mgemm_plan_t plan, const void *X, int64_t x_rows,
+                                const int32_t *d_row_index, const void *W1, const void *W2, void *H, void *Y,
+                                const int32_t *d_row_offsets, const float *d_row_weight, void *workspace,
+                                size_t workspace_bytes, mgemm_stream_t stream)
 {
     if (!plan || plan->kind != PLAN_MOE) {
-        set_error("moe_fused_run: null or non-MoE plan");
+        set_error("%s: null or non-MoE plan", name);
         return MGEMM_ERR_INVALID_ARG;
     }
     const mgemm_moe_desc_t &d = plan->moe;
     if (plan->noop)
         return MGEMM_OK;
     if (!X || !W1 || !W2 || !H || !Y || !d_row_offsets) {
-        set_error("moe_fused_run: null pointer");
+        set_error("%s: null pointer", name);
         return MGEMM_ERR_INVALID_ARG;
     }
     if (d_row_index && (x_rows < 0 || x_rows > INT32_MAX ||
                         (uint64_t)x_rows * (uint64_t)d.lda * 2u > (uint64_t)kMaxRecords)) {
-        set_error("moe_fused_run: x_rows=%lld out of range (x_rows * lda * 2 must be < 2^31)", (long long)x_rows);
+        set_error("%s: x_rows=%lld out of range (x_rows * lda * 2 must be < 2^31)", name, (long long)x_rows);
         return MGEMM_ERR_INVALID_ARG;
     }
     if (!aligned16(X) || !aligned16(W1) || !aligned16(W2) || !aligned16(Y) || ((uintptr_t)H & 127u)) {
-        set_error("moe_fused_run: X, W1, W2 and Y must be 16-byte aligned, H 128-byte aligned");
+        set_error("%s: X, W1, W2 and Y must be 16-byte aligned, H 128-byte aligned", name);
         return MGEMM_ERR_UNSUPPORTED;
     }
     if (!workspace || workspace_bytes < plan->workspace_bytes || !aligned16(workspace)) {
-        set_error("moe_fused_run: needs a 16-byte aligned workspace of %zu bytes (got %zu at %p)",
+        set_error("%s: needs a 16-byte aligned workspace of %zu bytes (got %zu at %p)", name,
                   plan->workspace_bytes, workspace_bytes, workspace);
         return MGEMM_ERR_WORKSPACE;
     }
@@ -382,6 +382,7 @@ extern "C" mgemm_status_t moe_fused_run(mgemm_plan_t plan, const void *X, int64_
     a.W2 = W2;
     a.H = H;
     a.Y = Y;
+    a.row_weight = d_row_weight;
     a.offs = d_row_offsets;
     a.G = d.num_experts;
     a.hidden = (int)d.hidden;
@@ -399,7 +400,29 @@ extern "C" mgemm_status_t moe_fused_run(mgemm_plan_t plan, const void *X, int64_
     // about four seconds of polling before an FC2 task gives up; with valid
     // offsets every count completes long before
     a.spin_limit = 1u << 22;
-    return hip_status(launch_moe_fused(a, in_code(d.dtype), plan->grid, (hipStream_t)stream), "moe_fused_run launch");
+    return hip_status(launch_moe_fused(a, in_code(d.dtype), plan->grid, (hipStream_t)stream), name);
+}
+
+extern "C" mgemm_status_t moe_fused_run(mgemm_plan_t plan, const void *X, int64_t x_rows, const int32_t *d_row_index,
+                                        const void *W1, const void *W2, void *H, void *Y,
+                                        const int32_t *d_row_offsets, void *workspace, size_t workspace_bytes,
+                                        mgemm_stream_t stream)
+{
+    return moe_fused("moe_fused_run", plan, X, x_rows, d_row_index, W1, W2, H, Y, d_row_offsets, nullptr, workspace,
+                     workspace_bytes, stream);
+}
+
+extern "C" mgemm_status_t moe_fused_run_weighted(mgemm_plan_t plan, const void *X, int64_t x_rows,
+                                                 const int32_t *d_row_index, const void *W1, const void *W2, void *H,
+                                                 void *Y, const int32_t *d_row_offsets, const float *d_row_weight,
+                                                 void *workspace, size_t workspace_bytes, mgemm_stream_t stream)
+{
+    if (!d_row_weight || ((uintptr_t)d_row_weight & 3)) {
+        set_error("moe_fused_run_weighted: the row weights must be a non-null, 4-byte aligned device array");
+        return MGEMM_ERR_INVALID_ARG;
+    }
+    return moe_fused("moe_fused_run_weighted", plan, X, x_rows, d_row_index, W1, W2, H, Y, d_row_offsets,
+                     d_row_weight, workspace, workspace_bytes, stream);
 }
 
 extern "C" mgemm_status_t grouped_gemm_run(mgemm_plan_t plan, const void *A, const void *B, void *D,

@@ -63,6 +63,7 @@ struct MoeArgs {
     const void *W2;                      // [G][inter][hidden] row-major
     void *H;                             // [rows][inter]
     void *Y;                             // [rows][hidden]
+    const float *row_weight = nullptr;   // routed row r's h scaled by row_weight[r], or none
     const int32_t *offs;                 // [G + 1] device prefix sums
     int G, hidden, inter, max_rows;
     int lda, ldw1, ldw2, ldh, ldy;

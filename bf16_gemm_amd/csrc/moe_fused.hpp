@@ -144,7 +144,9 @@ __device__ __forceinline__ int moe_find(const int (&s)[4], int t, int &first)
     return 4 * L + i;
 }
 
-template <int IN>
+// WEIGHTED: FC1's h rows scaled by p.row_weight (a separate instance, so
+// the unweighted layer carries no weight code)
+template <int IN, bool WEIGHTED>
 __global__ void __launch_bounds__(512) moe_fused_kernel(MoeArgs p)
 {
     using Big = DtlTile<IN, false>;
@@ -246,6 +248,7 @@ __global__ void __launch_bounds__(512) moe_fused_kernel(MoeArgs p)
             const uint16_t *Bt = W1 + (int64_t)e * p.stride_w1 + n0;
             const OperandSrc sb = operand_src<false>(Bt, p.ldw1, N1 - n0, p.hidden);
             char *Ht = (char *)p.H + ((int64_t)m0 * p.ldh + n0 / 2) * esize;
+            const float *rw = WEIGHTED ? p.row_weight + m0 : nullptr;
             if (narrow) {
                 const int ntb = (m_valid + 15) >> 4;
                 nar.mainloop(lds, sa, p.lda, sb, p.ldw1, p.hidden, ntb, opaque(tid), ga);
@@ -255,14 +258,14 @@ __global__ void __launch_bounds__(512) moe_fused_kernel(MoeArgs p)
                 f32x4_t v[Nar::NTB][Nar::NB];
                 nar.values(v, ntb);
                 narrow_store<EPI_SILU_GATE, OUT, Nar::NTB, Nar::NB, kDeviceScope>(v, Ht, p.ldh, m_valid,
-                                                                                   min(128, N1 - n0), ntb, tid);
+                                                                                   min(128, N1 - n0), ntb, tid, rw);
             } else {
                 big.mainloop(lds, sa, p.lda, sb, p.ldw1, p.hidden, opaque(tid), ga);
                 wait_vm<0>();
                 __syncthreads();
                 publish();
                 epilogue<Big, EPI_SILU_GATE, OUT, kDeviceScope>(big, Ht, p.ldh, m_valid, min(256, N1 - n0),
-                                                               opaque(tid));
+                                                               opaque(tid), rw);
             }
             pending = slot;
         } else {

@@ -428,6 +428,22 @@ mgemm_status_t moe_fused_run(mgemm_plan_t plan, const void *X, int64_t x_rows, c
                              const void *W1, const void *W2, void *H, void *Y, const int32_t *d_row_offsets,
                              void *workspace, size_t workspace_bytes, mgemm_stream_t stream);
 
+/* The fused layer with each routed row's h multiplied by that row's routing
+ * weight before its rounding, as grouped_gemm_run_weighted does for FC1
+ * ("MegaMoE：Blackwell 与 Hopper 的融合算子解读", Hopper section 09: the FC1
+ * epilogue chain optionally applies the routing weight; FC2 being linear,
+ * Y's rows are then the weighted expert outputs, p(hW2) = (ph)W2, and
+ * mgemm_moe_combine with d_weights NULL adds them into the tokens' rows).
+ * d_row_weight: device fp32, 4-byte aligned, one weight per routed row
+ * (off[num_experts] entries in routed-row order); null or misaligned gives
+ * MGEMM_ERR_INVALID_ARG.  Same tiles and k order as moe_fused_run, so h
+ * and Y equal grouped_gemm_run_weighted's h and grouped_gemm_run's FC2 on
+ * it bit for bit.  Everything else is moe_fused_run's. */
+mgemm_status_t moe_fused_run_weighted(mgemm_plan_t plan, const void *X, int64_t x_rows, const int32_t *d_row_index,
+                                      const void *W1, const void *W2, void *H, void *Y,
+                                      const int32_t *d_row_offsets, const float *d_row_weight, void *workspace,
+                                      size_t workspace_bytes, mgemm_stream_t stream);
+
 /* Library version, e.g. "mgemm 0.1 gfx950". */
 const char *mgemm_version(void);
 

@@ -280,3 +280,75 @@ def test_fused_moe64_full_size():
         carry = stage_gap(h_ref, H, "bf16") @ np.abs(oracle.decode(w2, "bf16"))
         assert_close_carried(from_dev_bits(y[sel]), y_ref, I, "bf16", carry, f"FC2 expert {e} rows {sel}")
     log(f"  checked experts {picks}")
+
+
+def fused_weighted(A, W1, W2, offs, w, E, rows, H, I, dtype="bf16", row_index=None, x_rows=None):
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float16
+    plan = mg.moe_fused_plan(E, rows, H, I, dtype=dtype)
+    h = torch.full((rows, I), -1, dtype=torch.int16, device="cuda").view(tdt)
+    y = torch.full((rows, H), -1, dtype=torch.int16, device="cuda").view(tdt)
+    ws = torch.full((plan.workspace_size(),), 0xA5, dtype=torch.uint8, device="cuda")
+    mg.moe_fused_run_weighted(plan, A, W1, W2, h, y, offs, w, workspace=ws, row_index=row_index, x_rows=x_rows)
+    return h, y, plan, ws
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_fused_weighted_equals_grouped_weighted(dtype):
+    """The fused layer with routing weights taken into FC1's gate epilogue:
+    h bit for bit the weighted grouped FC1's and y the grouped FC2's on it
+    (experts of every size class, both tiles); h against the oracle's gate
+    with the row weights, y within the FC2 rule widened by the carried gap."""
+    H, I = 400, 192
+    E = len(COUNTS)
+    off = offsets(COUNTS)
+    rows = int(off[-1])
+    log(f"case fused weighted {dtype} rows={rows}")
+    rs = np.random.RandomState(41 if dtype == "bf16" else 42)
+    A = datagen.matrix((rows, H), ("normal", 1.0), dtype, rs)
+    W1 = datagen.matrix((E, H, 2 * I), ("normal", 0.05), dtype, rs)
+    W2 = datagen.matrix((E, I, H), ("normal", 0.05), dtype, rs)
+    w = rs.uniform(0.02, 1.0, rows).astype(np.float32)
+    Ad, W1d, W2d = to_dev(A, dtype), to_dev(W1, dtype), to_dev(W2, dtype)
+    offs, wd = dev_i32(off), torch.from_numpy(w).cuda()
+    h, y, plan, ws = fused_weighted(Ad, W1d, W2d, offs, wd, E, rows, H, I, dtype=dtype)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float16
+    p1 = mg.grouped_gemm_plan(E, rows, 2 * I, H, a_type=dtype, d_type=dtype, stride_b=H * 2 * I,
+                              epilogue=mg.EPI_SILU_GATE_I8)
+    p2 = mg.grouped_gemm_plan(E, rows, H, I, a_type=dtype, d_type=dtype, stride_b=I * H)
+    h2 = torch.empty(rows, I, dtype=tdt, device="cuda")
+    y2 = torch.empty(rows, H, dtype=tdt, device="cuda")
+    mg.grouped_gemm_run_weighted(p1, Ad, W1d, h2, offs, wd)
+    mg.grouped_gemm_run(p2, h2, W2d, y2, offs)
+    torch.cuda.synchronize()
+    assert status(ws) == 0
+    assert torch.equal(h.view(torch.int16), h2.view(torch.int16)), "h differs from the weighted grouped FC1"
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16)), "y differs from the grouped FC2"
+    h_ref = oracle.silu_gate(oracle.grouped_ref(A, W1, off, dtype, dtype), row_weight=w.astype(np.float64))
+    assert_close(from_dev_bits(h), h_ref, H, dtype, f"{plan.describe()} weighted FC1")
+    y_ref = oracle.grouped_ref(oracle.encode(h_ref, dtype), W2, off, dtype, dtype)
+    assert_close_carried(from_dev_bits(y), y_ref, I, dtype, fc2_carry(h_ref, W2, off, H, dtype),
+                         f"{plan.describe()} FC2 on weighted h")
+
+
+def test_fused_weighted_power_of_two_gathered():
+    """Power-of-two routing weights scale exactly: with FC1 reading X through
+    the row index, the weighted fused layer's h and y are the unweighted
+    layer's rows times their weights, bit for bit."""
+    cfg = datagen.MOE["moe_small"]
+    r = datagen.moe_route(cfg)
+    rows, H, I, E, T = int(r.offsets[-1]), cfg.hidden, cfg.inter, cfg.num_experts, cfg.num_tokens
+    log(f"case fused weighted power of two gathered rows={rows}")
+    rs = np.random.RandomState(cfg.x_seed + 1)
+    X = datagen.matrix((T, H), ("normal", 1.0), "bf16", rs)
+    _, _, W1, W2 = datagen.moe_inputs_host(cfg)
+    idx = dev_i32(r.token_of_row)
+    w = np.ldexp(1.0, rs.randint(-3, 3, rows)).astype(np.float32)
+    Xd, W1d, W2d, offs = to_dev(X, "bf16"), to_dev(W1, "bf16"), to_dev(W2, "bf16"), dev_i32(r.offsets)
+    wd = torch.from_numpy(w).cuda()
+    h0, y0, _, _ = fused(Xd, W1d, W2d, offs, E, rows, H, I, row_index=idx, x_rows=T)
+    h1, y1, _, ws = fused_weighted(Xd, W1d, W2d, offs, wd, E, rows, H, I, row_index=idx, x_rows=T)
+    torch.cuda.synchronize()
+    assert status(ws) == 0
+    scale = wd[:, None]
+    assert torch.equal(h1.view(torch.int16), (h0.float() * scale).to(torch.bfloat16).view(torch.int16))
+    assert torch.equal(y1.view(torch.int16), (y0.float() * scale).to(torch.bfloat16).view(torch.int16))

@@ -407,3 +407,15 @@ def test_weighted_run_rules():
         with pytest.raises(mg.MgemmError) as e:
             mg.grouped_gemm_run_weighted(gated, fake, fake, fake, fake, w, stream=0)
         assert e.value.status == mg.ERR_INVALID_ARG, w
+
+
+def test_fused_weighted_run_rules():
+    """moe_fused_run_weighted: a non-null 4-byte aligned weight array, checked
+    before anything else runs (the fake device addresses are never touched)."""
+    fake = 1 << 20
+    plan = mg.moe_fused_plan(8, 384, 256, 128)
+    for w in (None, fake + 2):
+        with pytest.raises(mg.MgemmError) as e:
+            mg.moe_fused_run_weighted(plan, fake, fake, fake, fake, fake, fake, w, workspace=fake,
+                                      workspace_bytes=1 << 20, stream=0)
+        assert e.value.status == mg.ERR_INVALID_ARG and "weight" in str(e.value), w
