@@ -212,12 +212,13 @@ def moe_fused_case(torch, mg, datagen):
     return step, info, None
 
 
-def moe_layer_case(torch, mg, datagen, fold=False):
+def moe_layer_case(torch, mg, datagen, fold=False, fused=False):
     """The whole 64-expert layer: FC1 reading the routed rows of X through
     the routing's row index (the dispatch fused into its A loads), FC2, and
     the weighted top-k combine into each token's output row.  fold: the
     routing weights multiplied into FC1's SiLU-gate epilogue instead
-    (p(hW2) = (ph)W2), the combine a plain sum."""
+    (p(hW2) = (ph)W2), the combine a plain sum.  fused: FC1 and FC2 in the
+    one persistent launch (moe_fused_run / moe_fused_run_weighted)."""
     import numpy as np
     cfg = datagen.MOE["moe64"]
     r, A, W1, W2 = datagen.moe_inputs_device(cfg, "cuda")
@@ -239,6 +240,16 @@ def moe_layer_case(torch, mg, datagen, fold=False):
     w_row = np.empty(rows, dtype=np.float32)
     w_row[r.pos] = r.weight                               # each routed row's routing weight
     w_row = torch.from_numpy(w_row).cuda()
+    pf = mg.moe_fused_plan(E, rows, H, I) if fused else None
+    ws = mg.workspace_for(pf) if fused else None
+
+    def step_fused():
+        mg.moe_fused_run(pf, X, W1, W2, h, z, offs, workspace=ws, row_index=idx, x_rows=T)
+        mg.moe_combine(z, pos, wts, y, cfg.top_k)
+
+    def step_fused_fold():
+        mg.moe_fused_run_weighted(pf, X, W1, W2, h, z, offs, w_row, workspace=ws, row_index=idx, x_rows=T)
+        mg.moe_combine(z, pos, None, y, cfg.top_k)
 
     def step():
         mg.grouped_gemm_run_gather(p1, X, W1, h, offs, idx)
@@ -254,14 +265,23 @@ def moe_layer_case(torch, mg, datagen, fold=False):
     active = int((r.counts > 0).sum())
     wbytes = active * (H * 2 * I + I * H) * 2
     abytes = T * H * 2 + rows * I * 2 * 2 + rows * H * 2 * 2 + T * H * 2
-    info = dict(flops=flops, bytes=wbytes + abytes, plan=p1.describe() + " | " + p2.describe() + " | combine",
-                dtype="bf16",
-                config={"workload": "moe64_layer_fold" if fold else "moe64_layer", "experts": E, "hidden": H,
+    name = "moe64_layer" + ("_fused" if fused else "") + ("_fold" if fold else "")
+    stages = ("gathered FC1 (SiLU gate x routing weight) + FC2 + plain top-k sum" if fold else
+              "gathered FC1 (SiLU gate) + FC2 + weighted top-k combine")
+    if fused:
+        plan, launches = pf.describe() + " | combine", 3
+        stages += ", FC1 and FC2 in one persistent launch"
+    else:
+        plan = p1.describe() + " | " + p2.describe() + " | combine"
+        launches = len(p1.describe().split("grid=")) - 1 + len(p2.describe().split("grid=")) - 1 + 1
+    info = dict(flops=flops, bytes=wbytes + abytes, plan=plan, dtype="bf16",
+                config={"workload": name, "experts": E, "hidden": H,
                         "inter": I, "tokens": T, "top_k": cfg.top_k, "routed_rows": rows, "active_experts": active,
-                        "stages": ("gathered FC1 (SiLU gate x routing weight) + FC2 + plain top-k sum" if fold else
-                                   "gathered FC1 (SiLU gate) + FC2 + weighted top-k combine")},
-                launches_per_step=len(p1.describe().split("grid=")) - 1 + len(p2.describe().split("grid=")) - 1 + 1)
-    return (step_fold if fold else step), info, None
+                        "stages": stages},
+                launches_per_step=launches)
+    steps = {(False, False): step, (True, False): step_fold, (False, True): step_fused,
+             (True, True): step_fused_fold}
+    return steps[(fold, fused)], info, None
 
 
 # E4M3 workloads: per-tensor scales, B column-major, bf16 out
@@ -385,8 +405,9 @@ def main():
         step, info, case = moe_case(torch, mg, datagen)
     elif args.workload == "moe64_fused":
         step, info, case = moe_fused_case(torch, mg, datagen)
-    elif args.workload in ("moe64_layer", "moe64_layer_fold"):
-        step, info, case = moe_layer_case(torch, mg, datagen, fold=args.workload == "moe64_layer_fold")
+    elif args.workload in ("moe64_layer", "moe64_layer_fold", "moe64_layer_fused", "moe64_layer_fused_fold"):
+        step, info, case = moe_layer_case(torch, mg, datagen, fold=args.workload.endswith("_fold"),
+                                          fused="_fused" in args.workload)
     elif args.workload in E4M3:
         step, info, case = e4m3_case(torch, mg, datagen, args.workload)
     else:
