@@ -27,14 +27,18 @@ and from which passage of the pages:
   weight scales per 128 x 128 block, each K block's partial product scaled
   before it is added): scales are E8M0 bytes (2^(v - 127), 255 NaN), the
   power-of-two scale format the pages name for MXFP8 blocks.
+* ``grouped_e4m3_ref`` / ``grouped_e4m3_block_ref`` -- the per-expert FP8
+  products (per-tensor scales with one weight scale per expert; block
+  scales per routed row and per 128 x 128 block of each expert's weight).
 * ``grouped_ref`` / ``moe_ref`` -- the per-expert form: expert e owns rows
   [off[e], off[e+1]) of the routed activations and multiplies them by its
   own weight matrix ("MegaMoE", Recap 1 on the MoE stages: FC1 -> activation
   -> FC2 per expert).  The intermediate h is rounded to bf16 before FC2.
 
 Parity status: every function here is pinned by the CPU tests in
-``tests/test_oracle.py`` (exhaustive codec checks, exact rational brute force,
-closed forms); none is "parity unpinned".
+``tests/test_oracle*.py`` (exhaustive codec checks, exact rational brute
+force, closed forms, reductions to other pinned forms); none is "parity
+unpinned".
 """
 from __future__ import annotations
 
@@ -348,6 +352,28 @@ def gemm_e4m3_ref_sampled(A: np.ndarray, B: np.ndarray, rows, cols, scale_a: flo
     out = np.empty(r.shape, dtype=np.float64)
     _load().oracle_gemm_e4m3_ref_sampled(A.shape[1], _p(A), A.shape[1], _p(B), B.shape[1], float(scale_a),
                                          float(scale_b), _p(r), _p(c), r.size, _p(out))
+    return out
+
+
+def grouped_e4m3_block_ref(A: np.ndarray, W: np.ndarray, offsets, sa: np.ndarray, sb: np.ndarray) -> np.ndarray:
+    """The per-expert blockwise-scaled E4M3 product ("MegaMoE：Blackwell 与
+    Hopper 的融合算子解读", Recap 1: expert e multiplies its rows [off[e],
+    off[e+1]) by its own weights; Hopper section 04, the blockwise path:
+    activation scales per token and 128-k block, weight scales per 128 x 128
+    block of the expert's weight).  ``A``: [rows][K] uint8; ``W``: [G][N][K]
+    uint8; ``sa``: [rows][>= ceil(K/128)] E8M0 bytes (routed row r's scales);
+    ``sb``: [G][ceil(N/128)][>= ceil(K/128)] E8M0 bytes.  Returns [rows][N]
+    float64; rows past off[G] stay NaN (not produced)."""
+    off = np.asarray(offsets, dtype=np.int64)
+    G, N, K = W.shape
+    if sb.ndim != 3 or sb.shape[0] != G:
+        raise ValueError(f"sb must be [G][ceil(N/128)][kb], got {sb.shape}")
+    out = np.full((A.shape[0], N), np.nan)
+    for e in range(G):
+        lo, hi = int(off[e]), int(off[e + 1])
+        if hi > lo:
+            out[lo:hi] = gemm_e4m3_block_ref(np.ascontiguousarray(A[lo:hi]), np.ascontiguousarray(W[e]),
+                                             np.ascontiguousarray(sa[lo:hi]), np.ascontiguousarray(sb[e]))
     return out
 
 

@@ -231,3 +231,63 @@ def test_block_nan_scale():
     assert np.isnan(got[2]).all()
     assert np.isnan(got[:, 128:]).all()
     assert np.isfinite(np.delete(got, 2, 0)[:, :128]).all()
+
+
+# --- grouped form with block scales ---
+
+def test_grouped_block_unit_and_uniform_scales_are_the_per_tensor_grouped():
+    """Unit block scales give the per-tensor grouped product with scales 1;
+    scales uniform per expert (one byte u for all of A's, v_e for all of
+    expert e's weight blocks) give it with scale_a = 2^(u-127), scale_b[e] =
+    2^(v_e-127).  Empty experts produce nothing; rows past off[G] stay NaN."""
+    rs = np.random.RandomState(12)
+    counts = [0, 3, 9, 0, 14, 1]
+    off = np.concatenate([[0], np.cumsum(counts)])
+    rows, G, N, K = int(off[-1]), len(counts), 260, 300
+    A = finite_codes((rows + 2, K), rs)
+    W = finite_codes((G, N, K), rs)
+    kb, nb = -(-K // 128), -(-N // 128)
+    sa = np.full((rows + 2, kb + 1), 127, np.uint8)
+    sb = np.full((G, nb, kb + 1), 127, np.uint8)
+    g = oracle.grouped_e4m3_block_ref(A, W, off, sa, sb)
+    assert np.isnan(g[rows:]).all()
+    assert np.array_equal(g[:rows], oracle.grouped_e4m3_ref(A, W, off, 1.0, np.ones(G))[:rows])
+    v = np.array([127, 125, 130, 127, 126, 129])
+    sa[:] = 126
+    for e in range(G):
+        sb[e] = v[e]
+    g = oracle.grouped_e4m3_block_ref(A, W, off, sa, sb)
+    assert np.array_equal(g[:rows], oracle.grouped_e4m3_ref(A, W, off, 0.5, 2.0 ** (v - 127.0))[:rows])
+
+
+def test_grouped_block_scale_moves_only_its_part():
+    """Raising routed row r's scale of k block b by one adds exactly that
+    row's block-b partial product (the per-tensor product over that k range,
+    times the weight block's scale) once more; raising expert e's scale of
+    column block c and k block b changes only e's rows in c's columns."""
+    rs = np.random.RandomState(13)
+    counts = [5, 0, 11, 6]
+    off = np.concatenate([[0], np.cumsum(counts)])
+    rows, G, N, K = int(off[-1]), len(counts), 200, 384
+    A = finite_codes((rows, K), rs)
+    W = finite_codes((G, N, K), rs)
+    kb, nb = K // 128, -(-N // 128)
+    sa = rs.randint(125, 130, size=(rows, kb)).astype(np.uint8)
+    sb = rs.randint(125, 130, size=(G, nb, kb)).astype(np.uint8)
+    base = oracle.grouped_e4m3_block_ref(A, W, off, sa, sb)
+    r, b, e = 7, 1, 2                          # row 7 is expert 2's third row
+    sa2 = sa.copy()
+    sa2[r, b] += 1
+    got = oracle.grouped_e4m3_block_ref(A, W, off, sa2, sb)
+    part = oracle.gemm_e4m3_ref(A[r:r + 1, 128 * b:128 * (b + 1)], W[e][:, 128 * b:128 * (b + 1)])[0]
+    wscale = np.array([oracle.e8m0(sb[e, j // 128, b]) for j in range(N)])
+    assert np.array_equal(got[r], base[r] + part * oracle.e8m0(sa[r, b]) * wscale)
+    assert np.array_equal(np.delete(got, r, 0), np.delete(base, r, 0))
+    sb2 = sb.copy()
+    sb2[3, 1, 2] -= 1
+    got = oracle.grouped_e4m3_block_ref(A, W, off, sa, sb2)
+    lo, hi = off[3], off[4]
+    changed = np.zeros_like(got, dtype=bool)
+    changed[lo:hi, 128:] = True
+    assert np.array_equal(got[~changed], base[~changed])
+    assert not np.array_equal(got[changed], base[changed])
