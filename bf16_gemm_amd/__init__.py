@@ -87,7 +87,7 @@ EXPORTS = ["gemm_plan", "grouped_gemm_plan", "gemm_plan_workspace_size", "gemm_r
            "gemm_last_error_message", "mgemm_tile_budget", "mgemm_group_working_set", "mgemm_round_tokens",
            "mgemm_version", "mgemm_moe_combine", "grouped_gemm_run_gather", "gemm_run_noalloc",
            "moe_fused_plan", "moe_fused_run", "gemm_run_blockscaled", "grouped_gemm_run_weighted",
-           "moe_fused_run_weighted"]
+           "moe_fused_run_weighted", "grouped_gemm_run_blockscaled"]
 
 
 def _load():
@@ -136,6 +136,8 @@ def _load():
     lib.grouped_gemm_run_weighted.argtypes = [vp, vp, i64, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.grouped_gemm_run_weighted.restype = st
     lib.gemm_run_blockscaled.argtypes = [vp, vp, vp, vp, vp, i64, vp, i64, vp, ctypes.c_size_t, vp]
+    lib.grouped_gemm_run_blockscaled.argtypes = [vp, vp, vp, vp, vp, vp, i64, vp, i64, i64, vp, ctypes.c_size_t, vp]
+    lib.grouped_gemm_run_blockscaled.restype = st
     lib.gemm_run_blockscaled.restype = st
     lib.moe_fused_plan.argtypes = [ctypes.POINTER(MoeDesc), u32, ctypes.POINTER(vp)]
     lib.moe_fused_plan.restype = st
@@ -293,6 +295,16 @@ def grouped_gemm_run_scaled(plan: Plan, A, B, D, row_offsets, scale_a, scale_b, 
     one element, ``scale_b``: one float32 per expert (device)."""
     _check(lib.grouped_gemm_run_scaled(plan.handle, _ptr(A), _ptr(B), _ptr(D), _ptr(row_offsets), _ptr(scale_a),
                                        _ptr(scale_b), None, 0, _stream(stream)), "grouped_gemm_run_scaled")
+
+
+def grouped_gemm_run_blockscaled(plan: Plan, A, B, D, row_offsets, scale_a, scale_b, stream=None):
+    """Enqueue the grouped E4M3 product with E8M0 block scales: ``scale_a`` a
+    uint8 device tensor [rows, >= ceil(K/128)] (one byte per routed row and
+    128-k block), ``scale_b`` [G, ceil(N/128), >= ceil(K/128)] (one per
+    expert, 128 columns and 128-k block); pitches from the tensors' strides."""
+    _check(lib.grouped_gemm_run_blockscaled(plan.handle, _ptr(A), _ptr(B), _ptr(D), _ptr(row_offsets), _ptr(scale_a),
+                                            scale_a.stride(0), _ptr(scale_b), scale_b.stride(1), scale_b.stride(0),
+                                            None, 0, _stream(stream)), "grouped_gemm_run_blockscaled")
 
 
 def grouped_gemm_run(plan: Plan, A, B, D, row_offsets, workspace=None, workspace_bytes: int = 0, stream=None):

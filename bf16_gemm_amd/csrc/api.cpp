@@ -255,13 +255,20 @@ extern "C" mgemm_status_t gemm_run_blockscaled(mgemm_plan_t plan, const void *A,
                      d_scale_b, lds_b);
 }
 
+// E4M3 block scales of the grouped product (checked by the caller).
+struct GroupedBlockScales {
+    const uint8_t *sa = nullptr, *sb = nullptr;
+    int64_t lds_a = 0, lds_b = 0, stride_sb = 0;
+};
+
 // row_index: nullptr, or the gathered form's index (x_rows rows of A exist).
 // row_weight: nullptr, or one fp32 weight per routed row for the SiLU-gate
-// epilogue.
+// epilogue.  blk: nullptr, or the E4M3 block scales.
 static mgemm_status_t grouped_run(mgemm_plan_t plan, const void *A, const void *B, void *D,
                                   const int32_t *d_row_offsets, const int32_t *row_index, int64_t x_rows,
                                   mgemm_stream_t stream, const float *scale_a = nullptr,
-                                  const float *scale_b = nullptr, const float *row_weight = nullptr)
+                                  const float *scale_b = nullptr, const float *row_weight = nullptr,
+                                  const GroupedBlockScales *blk = nullptr)
 {
     if (!plan || plan->kind != PLAN_GROUPED) {
         set_error("grouped_gemm_run: null or non-grouped plan");
@@ -333,7 +340,17 @@ static mgemm_status_t grouped_run(mgemm_plan_t plan, const void *A, const void *
         a.row_index = row_index;
         a.x_rows = (int)x_rows;
         a.row_weight = row_weight;
-        GroupedFn f = grouped_fn(L.tile, bk, in, out, epi);
+        GroupedFn f;
+        if (blk) {
+            a.block_sa = blk->sa;
+            a.block_sb = blk->sb;
+            a.block_lda = (int)blk->lds_a;
+            a.block_ldb = (int)blk->lds_b;
+            a.block_stride_sb = blk->stride_sb;
+            f = L.tile == TILE_256x256_DTL ? grouped_block_fn_256x256dtl_e4m3(bk, out, epi) : nullptr;
+        } else {
+            f = grouped_fn(L.tile, bk, in, out, epi);
+        }
         if (!f) {
             set_error("grouped_gemm_run: kernel missing for the planned variant");
             return MGEMM_ERR_UNSUPPORTED;
@@ -491,6 +508,47 @@ extern "C" mgemm_status_t grouped_gemm_run_scaled(mgemm_plan_t plan, const void 
         return MGEMM_ERR_INVALID_ARG;
     }
     return grouped_run(plan, A, B, D, d_row_offsets, nullptr, 0, stream, d_scale_a, d_scale_b);
+}
+
+extern "C" mgemm_status_t grouped_gemm_run_blockscaled(mgemm_plan_t plan, const void *A, const void *B, void *D,
+                                                       const int32_t *d_row_offsets, const uint8_t *d_scale_a,
+                                                       int64_t lds_a, const uint8_t *d_scale_b, int64_t lds_b,
+                                                       int64_t stride_sb, void *workspace, size_t workspace_bytes,
+                                                       mgemm_stream_t stream)
+{
+    (void)workspace;
+    (void)workspace_bytes;
+    if (!plan || plan->kind != PLAN_GROUPED) {
+        set_error("grouped_gemm_run_blockscaled: null or non-grouped plan");
+        return MGEMM_ERR_INVALID_ARG;
+    }
+    const mgemm_grouped_desc_t &d = plan->grouped;
+    if (d.a_type != MGEMM_E4M3) {
+        set_error("grouped_gemm_run_blockscaled: the plan's inputs are not E4M3");
+        return MGEMM_ERR_UNSUPPORTED;
+    }
+    const int64_t kb = (d.K + 127) / 128, nb = (d.N + 127) / 128;
+    if (!d_scale_a || !d_scale_b || lds_a < kb || lds_b < kb || lds_a < 1 || lds_b < 1 || stride_sb < nb * lds_b) {
+        set_error("grouped_gemm_run_blockscaled: scale pointers must be non-null, lds_a, lds_b >= ceil(K / 128) "
+                  "(= %lld) and stride_sb >= ceil(N / 128) * lds_b (= %lld)", (long long)kb, (long long)(nb * lds_b));
+        return MGEMM_ERR_INVALID_ARG;
+    }
+    if ((lds_a | lds_b) & 1) {
+        set_error("grouped_gemm_run_blockscaled: lds_a and lds_b must be even (two k blocks' scales are read at once)");
+        return MGEMM_ERR_UNSUPPORTED;
+    }
+    if ((uint64_t)d.max_total_rows * (uint64_t)lds_a > (uint64_t)kMaxRecords ||
+        (uint64_t)d.num_groups * (uint64_t)stride_sb > (uint64_t)kMaxRecords) {
+        set_error("grouped_gemm_run_blockscaled: each scale array must span less than 2^31 bytes");
+        return MGEMM_ERR_INVALID_ARG;
+    }
+    GroupedBlockScales blk;
+    blk.sa = d_scale_a;
+    blk.sb = d_scale_b;
+    blk.lds_a = lds_a;
+    blk.lds_b = lds_b;
+    blk.stride_sb = stride_sb;
+    return grouped_run(plan, A, B, D, d_row_offsets, nullptr, 0, stream, nullptr, nullptr, nullptr, &blk);
 }
 
 extern "C" mgemm_status_t mgemm_moe_combine(const void *Z, int64_t z_rows, int64_t ldz, const int32_t *d_pos,

@@ -74,6 +74,8 @@ DenseFn dense_block_fn_256x256dtl_e4m3(bool ak, bool bk, int out);
 DenseFn dense_sk_fn_256x256dtl_bf16(bool bk, int out);
 DenseFn dense_sk_fn_256x256dtl_f16(bool bk, int out);
 GroupedFn grouped_fn_256x256dtl_e4m3(bool bk, int out, int epi);
+// the grouped E4M3 product with E8M0 block scales
+GroupedFn grouped_block_fn_256x256dtl_e4m3(bool bk, int out, int epi);
 
 using EdgeFn = hipError_t (*)(const DenseArgs &, int a_kmajor, int b_kmajor, int n_first, hipStream_t);
 EdgeFn edge_fn(int in, int out);

@@ -51,6 +51,12 @@ struct GroupedArgs {
     const float *scale_a = nullptr;      // E4M3: the activations' scale (device, one float; null = 1)
     const float *scale_b = nullptr;      // E4M3: one weight scale per expert (device, G floats; null = 1)
     const float *row_weight = nullptr;   // SILU_GATE: routed row r's h multiplied by row_weight[r] (null = 1)
+    // E4M3 block scales (E8M0 bytes): routed row r's at block_sa + r * block_lda,
+    // expert e's [ceil(N/128)][block_ldb] at block_sb + e * block_stride_sb
+    const uint8_t *block_sa = nullptr;
+    const uint8_t *block_sb = nullptr;
+    int block_lda = 0, block_ldb = 0;
+    int64_t block_stride_sb = 0;
 };
 
 
@@ -633,6 +639,54 @@ __global__ void __launch_bounds__(DtlTile4E4M3::NT) grouped_e4m3_kernel(GroupedA
         char *Dt = (char *)p.D + ((int64_t)m0 * p.ldd + n0) * esize;
         epilogue_staged<T, OUT, true>(tile, lds, Dt, p.ldd, m_valid, min(T::BN, p.N - n0),
                                       opaque((int)threadIdx.x), scale);
+        wait_vm<0>();
+    }
+}
+
+// The grouped product with block scales: the per-expert task walk of
+// grouped_e4m3_kernel on the block-scaled tile of dense_e4m3_block_kernel,
+// each task's A scales from its first routed row (rows past the task's
+// expert read as zeros: their outputs are not stored) and its B scales
+// from its expert's block ("MegaMoE", Hopper section 04, the blockwise path
+// for the expert GEMMs).
+template <int OUT>
+__global__ void __launch_bounds__(DtlTile4E4M3::NT) grouped_e4m3_block_kernel(GroupedArgs p)
+{
+    using T = DtlTile4E4M3X<true>;
+    __shared__ __attribute__((aligned(16))) char lds[T::LDS_BYTES];
+    WaveTasks wt;
+    wt.build(p, T::BM, (int)threadIdx.x & 63);
+    T tile;
+    const int grid = gridDim.x;
+    const int L = logical_block(blockIdx.x, grid, p.xcd_remap);
+    const char *A = (const char *)p.A;
+    const char *B = (const char *)p.B;
+    constexpr int esize = out_size(OUT);
+    BlockScaleSrc bs;
+    bs.kb = (p.K + T::KSTEP - 1) / T::KSTEP;
+    bs.lds_a = p.block_lda;
+    bs.lds_b = p.block_ldb;
+    const uint64_t sb_bytes = (uint64_t)((p.N + 127) / 128) * (uint64_t)p.block_ldb;
+    for (int t = L; t < wt.total; t += grid) {
+        int e, local, rows0, rows_e;
+        wt.find(t, e, local, rows0, rows_e);
+        const int tm = (rows_e + T::BM - 1) / T::BM;
+        const int mb = local % tm, nb = local / tm;
+        const int m0 = rows0 + mb * T::BM, n0 = nb * T::BN;
+        const int m_valid = min(T::BM, rows_e - mb * T::BM);
+        OperandSrc sa_src, sb_src;
+        sa_src.base = A + (int64_t)m0 * p.lda;
+        sa_src.bytes = (uint64_t)m_valid * (uint64_t)p.lda;
+        sa_src.step_bytes = T::KSTEP;
+        sb_src.base = B + (int64_t)e * p.stride_b + (int64_t)n0 * p.ldb;
+        sb_src.bytes = (uint64_t)(p.N - n0) * (uint64_t)p.ldb;
+        sb_src.step_bytes = T::KSTEP;
+        bs.ra = make_rsrc(p.block_sa + (int64_t)m0 * p.block_lda, (uint64_t)m_valid * (uint64_t)p.block_lda);
+        bs.rb = make_rsrc(p.block_sb + (int64_t)e * p.block_stride_sb, sb_bytes);
+        bs.nblk0 = n0 / 128;
+        tile.mainloop(lds, sa_src, p.lda, sb_src, p.ldb, p.K, opaque((int)threadIdx.x), bs);
+        char *Dt = (char *)p.D + ((int64_t)m0 * p.ldd + n0) * esize;
+        epilogue_staged<T, OUT>(tile, lds, Dt, p.ldd, m_valid, min(T::BN, p.N - n0), opaque((int)threadIdx.x));
         wait_vm<0>();
     }
 }

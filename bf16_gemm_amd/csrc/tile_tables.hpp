@@ -135,6 +135,23 @@ hipError_t launch_grouped_e4m3(const GroupedArgs &a, int grid, hipStream_t s)
     hipLaunchKernelGGL((grouped_e4m3_kernel<OUT>), dim3(grid), dim3(DtlTile4E4M3::NT), 0, s, a);
     return hipGetLastError();
 }
+template <int OUT>
+hipError_t launch_grouped_e4m3_block(const GroupedArgs &a, int grid, hipStream_t s)
+{
+    hipLaunchKernelGGL((grouped_e4m3_block_kernel<OUT>), dim3(grid), dim3(DtlTile4E4M3::NT), 0, s, a);
+    return hipGetLastError();
+}
+inline GroupedFn grouped_e4m3_block_table(bool bk, int out, int epi)
+{
+    if (!bk || epi != EPI_NONE)
+        return nullptr;
+    switch (out) {
+    case OUT_F32: return launch_grouped_e4m3_block<OUT_F32>;
+    case OUT_BF16: return launch_grouped_e4m3_block<OUT_BF16>;
+    case OUT_F16: return launch_grouped_e4m3_block<OUT_F16>;
+    }
+    return nullptr;
+}
 inline GroupedFn grouped_e4m3_table(bool bk, int out, int epi)
 {
     if (!bk || epi != EPI_NONE)

@@ -51,7 +51,8 @@ typedef struct ihipStream_t *mgemm_stream_t;
 /* E4M3: the OCP 8-bit float with 1 sign, 4 exponent (bias 7) and 3 fraction
  * bits, subnormals, no infinities, NaN = S.1111.111 (largest finite 448).
  * An input type only, of dense and grouped plans (gemm_run_scaled,
- * grouped_gemm_run_scaled). */
+ * gemm_run_blockscaled, grouped_gemm_run_scaled,
+ * grouped_gemm_run_blockscaled). */
 typedef enum { MGEMM_F16 = 1, MGEMM_BF16 = 2, MGEMM_F32 = 3, MGEMM_E4M3 = 4 } mgemm_dtype_t;
 
 /* Storage of a logical rows x cols operand.  ROW_MAJOR: element (r,c) at
@@ -242,6 +243,28 @@ mgemm_status_t grouped_gemm_run_scaled(mgemm_plan_t plan, const void *A, const v
                                        const int32_t *d_row_offsets, const float *d_scale_a,
                                        const float *d_scale_b, void *workspace, size_t workspace_bytes,
                                        mgemm_stream_t stream);
+
+/* Enqueue the grouped product of a plan with E4M3 inputs with block scales
+ * ("MegaMoE：Blackwell 与 Hopper 的融合算子解读", Hopper section 04, the
+ * blockwise path of the expert GEMMs): expert e's rows [off[e], off[e+1])
+ * times its weight, each 128-k block's partial product scaled before it
+ * joins the sum, as gemm_run_blockscaled per expert:
+ *   D[r,j] = sum over k blocks b of sa[r][b] x sb[e][j / 128][b] x
+ *            sum_{k in block b, k < K} A[r,k] B_e[k,j]
+ * accumulated in fp32 and rounded once to d_type.  Scales are E8M0 bytes.
+ * d_scale_a: device bytes [max_total_rows][lds_a], routed row r's scales at
+ * r * lds_a; d_scale_b: device bytes, expert e's [ceil(N / 128)][lds_b]
+ * block at e * stride_sb.  lds_a, lds_b >= ceil(K / 128) and stride_sb >=
+ * ceil(N / 128) * lds_b, each array below 2^31 bytes (else
+ * MGEMM_ERR_INVALID_ARG); lds_a and lds_b even (else MGEMM_ERR_UNSUPPORTED).
+ * Bytes past ceil(K / 128) in a row are padding: they may be read, never
+ * used.  Operands, offsets, outputs and errors as grouped_gemm_run_scaled
+ * (rows past off[G] are not written); a non-E4M3 plan gives
+ * MGEMM_ERR_UNSUPPORTED. */
+mgemm_status_t grouped_gemm_run_blockscaled(mgemm_plan_t plan, const void *A, const void *B, void *D,
+                                            const int32_t *d_row_offsets, const uint8_t *d_scale_a, int64_t lds_a,
+                                            const uint8_t *d_scale_b, int64_t lds_b, int64_t stride_sb,
+                                            void *workspace, size_t workspace_bytes, mgemm_stream_t stream);
 
 /* Enqueue the grouped product on `stream`.  d_row_offsets is a device array
  * of num_groups + 1 int32 prefix sums; it is read by the kernels only (no

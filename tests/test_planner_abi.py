@@ -419,3 +419,24 @@ def test_fused_weighted_run_rules():
             mg.moe_fused_run_weighted(plan, fake, fake, fake, fake, fake, fake, w, workspace=fake,
                                       workspace_bytes=1 << 20, stream=0)
         assert e.value.status == mg.ERR_INVALID_ARG and "weight" in str(e.value), w
+
+
+def test_grouped_blockscaled_run_rules():
+    """grouped_gemm_run_blockscaled refuses, before any launch: a non-E4M3
+    plan; scale pitches below ceil(K/128), an expert stride below
+    ceil(N/128) x lds_b (INVALID_ARG); an odd pitch (UNSUPPORTED)."""
+    fake = 1 << 20
+
+    def run(plan, lds_a, lds_b, stride_sb):
+        st = mg.lib.grouped_gemm_run_blockscaled(plan.handle, fake, fake, fake, fake, fake, lds_a, fake, lds_b,
+                                                 stride_sb, None, 0, None)
+        return st, mg.lib.gemm_last_error_message().decode()
+
+    st, msg = run(mg.grouped_gemm_plan(4, 256, 256, 512), 4, 4, 8)
+    assert st == mg.ERR_UNSUPPORTED and "E4M3" in msg
+    p = mg.grouped_gemm_plan(4, 256, 256, 512, a_type="e4m3", d_type="f32", b_layout="col")   # 4 k blocks, 2 column blocks
+    for lds_a, lds_b, stride in ((2, 4, 8), (4, 2, 8), (4, 4, 7), (0, 4, 8)):
+        st, msg = run(p, lds_a, lds_b, stride)
+        assert st == mg.ERR_INVALID_ARG, (lds_a, lds_b, stride, msg)
+    st, msg = run(p, 5, 4, 8)
+    assert st == mg.ERR_UNSUPPORTED and "even" in msg
