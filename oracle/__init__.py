@@ -43,6 +43,7 @@ unpinned".
 from __future__ import annotations
 
 import ctypes
+import math
 import os
 
 import numpy as np
@@ -393,3 +394,51 @@ def grouped_e4m3_ref(A: np.ndarray, W: np.ndarray, offsets, scale_a: float, scal
             out[lo:hi] = gemm_e4m3_ref(np.ascontiguousarray(A[lo:hi]), np.ascontiguousarray(W[e]),
                                        scale_a, float(scale_b[e]))
     return out
+
+
+def quantize_e4m3_block(x: np.ndarray, block: int = 128):
+    """Blockwise FP8 quantisation of a [rows][cols] matrix ("MegaMoE：Blackwell
+    与 Hopper 的融合算子解读", Hopper sections 04 and 09: after SwiGLU each
+    block's absolute maximum gives a power-of-two (MXFP8, E8M0) scale, and
+    the block is multiplied by the scale's reciprocal and converted to FP8).
+
+    Blocks are ``block`` consecutive columns of one row (the last one may be
+    shorter).  Scale of a block: the smallest power of two 2^E with
+    amax <= 448 * 2^E (448: the largest finite E4M3 value), E clamped to the
+    E8M0 range [-127, 127]; an all-zero block takes E = 0; a block holding a
+    NaN or an infinity takes the NaN scale byte 255 and NaN codes.  Codes:
+    x / 2^E rounded to the nearest E4M3 value, ties to the even code.
+    Returns (codes uint8 [rows][cols], scale bytes uint8 [rows][ceil(cols /
+    block)]), scale byte = E + 127."""
+    x = np.asarray(x, dtype=np.float64)
+    rows, cols = x.shape
+    nblk = -(-cols // block)
+    # every non-negative finite E4M3 value, in code order (codes 0 .. 126)
+    grid = decode_e4m3(np.arange(127, dtype=np.uint8))
+    codes = np.zeros((rows, cols), dtype=np.uint8)
+    scales = np.zeros((rows, nblk), dtype=np.uint8)
+    for r in range(rows):
+        for b in range(nblk):
+            v = x[r, block * b:min(block * b + block, cols)]
+            if not np.all(np.isfinite(v)):
+                scales[r, b] = 255
+                codes[r, block * b:block * b + v.size] = 0x7F
+                continue
+            amax = float(np.max(np.abs(v))) if v.size else 0.0
+            if amax == 0.0:
+                E = 0
+            else:
+                E = math.frexp(amax)[1] - 1 - 8          # floor(log2 amax) - 8
+                if amax > 448.0 * 2.0 ** E:
+                    E += 1
+                E = min(max(E, -127), 127)
+            scales[r, b] = E + 127
+            y = np.abs(v) * 2.0 ** -E                      # exact: a power-of-two scaling
+            hi = np.searchsorted(grid, y, side="left")     # first grid value >= y
+            hi = np.minimum(hi, 126)
+            lo = np.maximum(hi - 1, 0)
+            dlo, dhi = y - grid[lo], grid[hi] - y
+            pick = np.where(dlo < dhi, lo, np.where(dhi < dlo, hi, np.where(lo % 2 == 0, lo, hi)))
+            pick = np.where(grid[hi] == y, hi, pick)
+            codes[r, block * b:block * b + v.size] = pick.astype(np.uint8) | np.where(np.signbit(v), 0x80, 0)
+    return codes, scales

@@ -291,3 +291,64 @@ def test_grouped_block_scale_moves_only_its_part():
     changed[lo:hi, 128:] = True
     assert np.array_equal(got[~changed], base[~changed])
     assert not np.array_equal(got[changed], base[changed])
+
+
+# --- blockwise quantisation to E4M3 with E8M0 scales ---
+
+def test_quantize_codes_are_torchs_conversion_of_the_scaled_block():
+    """Each block's codes are torch's float8_e4m3fn conversion (round to
+    nearest even) of x / 2^E, and 2^E is the smallest power of two that
+    brings the block's largest magnitude to 448 or below: 224 < amax / 2^E
+    <= 448.  Ragged last block (cols = 300), magnitudes from 2^-30 to 2^30,
+    negative zeros."""
+    rs = np.random.RandomState(21)
+    rows, cols = 6, 300
+    x = rs.standard_normal((rows, cols)) * 2.0 ** rs.randint(-30, 31, size=(rows, 1))
+    x = torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
+    x[2, 5] = -0.0
+    q, s = oracle.quantize_e4m3_block(x)
+    assert s.shape == (rows, 3)
+    for r in range(rows):
+        for b in range(3):
+            v = x[r, 128 * b:min(128 * b + 128, cols)]
+            scale = 2.0 ** (int(s[r, b]) - 127)
+            amax = np.abs(v).max()
+            assert 224.0 < amax / scale <= 448.0, (r, b)
+            want = torch.from_numpy(v / scale).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+            assert np.array_equal(q[r, 128 * b:128 * b + v.size], want), (r, b)
+    assert q[2, 5] == 0x80
+
+
+def test_quantize_exact_values_round_trip_and_special_blocks():
+    """Values that are E4M3 values times the block's power of two come back
+    exactly; an all-zero block takes scale 2^0 and zero codes; a block with
+    a NaN or an infinity takes the NaN scale byte and NaN codes; the largest
+    magnitude 448 * 2^k maps to code 0x7E with scale 2^k."""
+    rs = np.random.RandomState(22)
+    codes = rs.randint(0, 127, size=(4, 256)).astype(np.uint8) | (rs.randint(0, 2, size=(4, 256)) << 7).astype(np.uint8)
+    codes[:, 0] = 0x7E                                     # 448 in every block
+    codes[:, 128] = 0xFE
+    k = np.array([-20, 0, 7, 33])
+    x = oracle.decode_e4m3(codes) * 2.0 ** k[:, None]
+    q, s = oracle.quantize_e4m3_block(x)
+    assert np.array_equal(s, np.repeat((k + 127)[:, None], 2, axis=1).astype(np.uint8))
+    dec = oracle.decode_e4m3(q) * 2.0 ** (s.astype(np.int64).repeat(128, axis=1) - 127)
+    assert np.array_equal(dec, x)
+    z = np.zeros((2, 130))
+    z[1, 129] = np.nan
+    z[1, 3] = np.inf
+    q, s = oracle.quantize_e4m3_block(z)
+    assert list(s[0]) == [127, 127] and not q[0].any()
+    assert list(s[1]) == [255, 255] and (q[1] == 0x7F).all()
+
+
+def test_quantize_error_within_half_an_e4m3_step():
+    """|decode(code) * 2^E - x| is at most half of the E4M3 spacing at x / 2^E
+    (2^-10 below 2^-6, 2^(floor(log2|y|) - 4) above), times 2^E."""
+    rs = np.random.RandomState(23)
+    x = torch.from_numpy(rs.standard_normal((8, 512)) * 3.0).to(torch.bfloat16).to(torch.float64).numpy()
+    q, s = oracle.quantize_e4m3_block(x)
+    scale = 2.0 ** (s.astype(np.int64).repeat(128, axis=1) - 127)
+    y = np.abs(x) / scale
+    half = np.where(y < 2.0 ** -6, 2.0 ** -10, 2.0 ** (np.floor(np.log2(np.maximum(y, 2.0 ** -6))) - 4))
+    assert np.all(np.abs(oracle.decode_e4m3(q) * scale - x) <= half * scale)
