@@ -87,7 +87,7 @@ EXPORTS = ["gemm_plan", "grouped_gemm_plan", "gemm_plan_workspace_size", "gemm_r
            "gemm_last_error_message", "mgemm_tile_budget", "mgemm_group_working_set", "mgemm_round_tokens",
            "mgemm_version", "mgemm_moe_combine", "grouped_gemm_run_gather", "gemm_run_noalloc",
            "moe_fused_plan", "moe_fused_run", "gemm_run_blockscaled", "grouped_gemm_run_weighted",
-           "moe_fused_run_weighted", "grouped_gemm_run_blockscaled"]
+           "moe_fused_run_weighted", "grouped_gemm_run_blockscaled", "mgemm_quantize_e4m3_block"]
 
 
 def _load():
@@ -147,6 +147,8 @@ def _load():
     lib.moe_fused_run_weighted.restype = st
     lib.mgemm_moe_combine.argtypes = [vp, i64, i64, vp, vp, vp, i64, i64, ctypes.c_int32, i64, ctypes.c_int, vp]
     lib.mgemm_moe_combine.restype = st
+    lib.mgemm_quantize_e4m3_block.argtypes = [vp, i64, i64, i64, ctypes.c_int, vp, i64, vp, i64, vp]
+    lib.mgemm_quantize_e4m3_block.restype = st
     return lib
 
 
@@ -388,6 +390,15 @@ def moe_combine(Z, pos, weights, Y, top_k: int, z_rows=None, stream=None):
     z_rows = Z.shape[0] if z_rows is None else z_rows
     _check(lib.mgemm_moe_combine(_ptr(Z), z_rows, Z.stride(0), _ptr(pos), _ptr(weights), _ptr(Y), Y.stride(0), T,
                                  top_k, H, TORCH_DTYPE[Y.dtype], _stream(stream)), "mgemm_moe_combine")
+
+
+def quantize_e4m3_block(X, Q, S, stream=None):
+    """Enqueue the blockwise E4M3 quantisation of X (a 16-bit cuda tensor
+    [rows, cols], unit column stride) into Q (uint8 [rows, >= cols]) and S
+    (uint8 [rows, >= ceil(cols / 128)] E8M0 scales); pitches from strides."""
+    rows, cols = X.shape
+    _check(lib.mgemm_quantize_e4m3_block(_ptr(X), rows, cols, X.stride(0), TORCH_DTYPE[X.dtype], _ptr(Q), Q.stride(0),
+                                         _ptr(S), S.stride(0), _stream(stream)), "mgemm_quantize_e4m3_block")
 
 
 def tile_budget(M, N, K, BM, BN, BK, stages, elt_bytes) -> Budget:

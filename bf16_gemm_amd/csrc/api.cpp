@@ -589,6 +589,40 @@ extern "C" mgemm_status_t mgemm_moe_combine(const void *Z, int64_t z_rows, int64
                       "mgemm_moe_combine launch");
 }
 
+extern "C" mgemm_status_t mgemm_quantize_e4m3_block(const void *X, int64_t rows, int64_t cols, int64_t ldx,
+                                                    mgemm_dtype_t x_type, uint8_t *Q, int64_t ldq, uint8_t *S,
+                                                    int64_t lds, mgemm_stream_t stream)
+{
+    if (rows < 0 || cols < 0 || rows > INT32_MAX || cols > INT32_MAX) {
+        set_error("mgemm_quantize_e4m3_block: bad sizes (rows=%lld cols=%lld)", (long long)rows, (long long)cols);
+        return MGEMM_ERR_INVALID_ARG;
+    }
+    if (x_type != MGEMM_BF16 && x_type != MGEMM_F16) {
+        set_error("mgemm_quantize_e4m3_block: x_type must be BF16 or F16");
+        return MGEMM_ERR_UNSUPPORTED;
+    }
+    if (rows == 0 || cols == 0)
+        return MGEMM_OK;
+    const int64_t nblk = (cols + 127) / 128;
+    if (!X || !Q || !S || ldx < cols || ldq < cols || lds < nblk) {
+        set_error("mgemm_quantize_e4m3_block: null pointer, or ldx=%lld / ldq=%lld below cols=%lld, or lds=%lld "
+                  "below ceil(cols / 128)=%lld", (long long)ldx, (long long)ldq, (long long)cols, (long long)lds,
+                  (long long)nblk);
+        return MGEMM_ERR_INVALID_ARG;
+    }
+    if ((cols | ldx | ldq) & 1 || ((uintptr_t)X & 3) || ((uintptr_t)Q & 1)) {
+        set_error("mgemm_quantize_e4m3_block: cols, ldx and ldq must be even, X 4-byte and Q 2-byte aligned");
+        return MGEMM_ERR_UNSUPPORTED;
+    }
+    if ((rows * nblk + 3) / 4 > (int64_t)UINT32_MAX / 2) {
+        set_error("mgemm_quantize_e4m3_block: too many blocks");
+        return MGEMM_ERR_UNSUPPORTED;
+    }
+    return hip_status(launch_quantize_e4m3_block(X, rows, cols, ldx, in_code(x_type), Q, ldq, S, lds,
+                                                 (hipStream_t)stream),
+                      "mgemm_quantize_e4m3_block launch");
+}
+
 extern "C" const char *gemm_status_string(mgemm_status_t s)
 {
     switch (s) {

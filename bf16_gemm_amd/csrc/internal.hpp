@@ -82,6 +82,8 @@ EdgeFn edge_fn(int in, int out);
 hipError_t launch_zero_fill(void *D, int rows, int cols, int64_t ld_bytes, int esize, hipStream_t s);
 // the fused MoE layer: the prepare kernel, then the persistent kernel on `grid` workgroups
 hipError_t launch_moe_fused(const MoeArgs &a, int in, int grid, hipStream_t s);
+hipError_t launch_quantize_e4m3_block(const void *X, int64_t rows, int64_t cols, int64_t ldx, int in, uint8_t *Q,
+                                      int64_t ldq, uint8_t *S, int64_t lds, hipStream_t s);
 hipError_t launch_moe_combine(const void *Z, int64_t z_rows, int64_t ldz, const int32_t *pos, const float *w,
                               void *Y, int64_t ldy, int64_t T, int top_k, int64_t H, int out, hipStream_t s);
 // D[M x N] = sum over r < splits of W[r][M x N] (fp32, row pitch ldw, slabs

@@ -390,6 +390,28 @@ mgemm_status_t mgemm_moe_combine(const void *Z, int64_t z_rows, int64_t ldz, con
                                  const float *d_weights, void *Y, int64_t ldy, int64_t T, int32_t top_k, int64_t H,
                                  mgemm_dtype_t dtype, mgemm_stream_t stream);
 
+/* Blockwise FP8 quantisation of a 16-bit matrix into the activation layout
+ * of the block-scaled products ("MegaMoE：Blackwell 与 Hopper 的融合算子解读",
+ * Hopper sections 04 and 09: after SwiGLU, each block's absolute maximum
+ * gives a power-of-two E8M0 scale, and the block is multiplied by the
+ * scale's reciprocal and converted to FP8).  Blocks are 128 consecutive
+ * columns of a row (the last may be shorter).  Scale 2^E: the smallest
+ * power of two with amax <= 448 * 2^E, E in [-127, 127]; 2^0 for an
+ * all-zero block; a block with a NaN or infinity gets scale byte 255 and
+ * NaN codes.  Codes: x / 2^E rounded to the nearest E4M3 value, ties to
+ * the even code.  X: rows x cols, row pitch ldx elements, BF16 or F16
+ * (x_type); Q: rows x cols E4M3 bytes, pitch ldq; S: rows x lds E8M0 bytes
+ * (byte b of row r: the scale of columns [128 b, 128 b + 128)), lds >=
+ * ceil(cols / 128); all device memory, read and written when the kernel
+ * runs on `stream`.  Q and S feed gemm_run_blockscaled /
+ * grouped_gemm_run_blockscaled as A and its scales (lda = ldq, lds_a = lds,
+ * which those require to be even).  cols, ldx and ldq even, X 4-byte and Q
+ * 2-byte aligned, else MGEMM_ERR_UNSUPPORTED; null pointers or short
+ * pitches give MGEMM_ERR_INVALID_ARG.  rows or cols 0: nothing is done. */
+mgemm_status_t mgemm_quantize_e4m3_block(const void *X, int64_t rows, int64_t cols, int64_t ldx,
+                                         mgemm_dtype_t x_type, uint8_t *Q, int64_t ldq, uint8_t *S, int64_t lds,
+                                         mgemm_stream_t stream);
+
 /* The MoE expert layer's two GEMMs in one persistent launch ("MegaMoE：
  * Blackwell 与 Hopper 的融合算子解读", Hopper section 01 on the resident
  * FC1 -> SwiGLU -> FC2 pipeline and its fc1_done counters, Blackwell section

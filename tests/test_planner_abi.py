@@ -440,3 +440,22 @@ def test_grouped_blockscaled_run_rules():
         assert st == mg.ERR_INVALID_ARG, (lds_a, lds_b, stride, msg)
     st, msg = run(p, 5, 4, 8)
     assert st == mg.ERR_UNSUPPORTED and "even" in msg
+
+
+def test_quantize_rules():
+    """mgemm_quantize_e4m3_block refuses, before any launch: odd cols or
+    pitches, a misaligned X (UNSUPPORTED); short pitches, null pointers, a
+    16-bit type other than BF16 / F16 (INVALID_ARG / UNSUPPORTED)."""
+    fake = 1 << 20
+
+    def run(X, rows, cols, ldx, t, Q, ldq, S, lds):
+        st = mg.lib.mgemm_quantize_e4m3_block(X, rows, cols, ldx, t, Q, ldq, S, lds, None)
+        return st, mg.lib.gemm_last_error_message().decode()
+
+    assert run(fake, 4, 255, 256, mg.BF16, fake, 256, fake, 2)[0] == mg.ERR_UNSUPPORTED
+    assert run(fake + 2, 4, 256, 256, mg.BF16, fake, 256, fake, 2)[0] == mg.ERR_UNSUPPORTED
+    assert run(fake, 4, 256, 256, mg.F32, fake, 256, fake, 2)[0] == mg.ERR_UNSUPPORTED
+    for args in ((fake, 4, 256, 200, mg.BF16, fake, 256, fake, 2), (fake, 4, 256, 256, mg.BF16, fake, 256, fake, 1),
+                 (None, 4, 256, 256, mg.F16, fake, 256, fake, 2), (fake, -1, 256, 256, mg.F16, fake, 256, fake, 2)):
+        assert run(*args)[0] == mg.ERR_INVALID_ARG, args
+    assert run(None, 0, 256, 256, mg.BF16, None, 256, None, 2)[0] == mg.OK
