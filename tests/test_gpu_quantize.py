@@ -100,3 +100,36 @@ def test_quantized_rows_feed_the_block_scaled_product():
     err = np.abs(values(from_dev_bits(D), "f32") - ref)
     log(f"  quantised product: max err / tol = {(err / tol).max():.3f}")
     assert np.all(err <= tol)
+
+
+def test_quantized_h_feeds_the_grouped_block_scaled_fc2():
+    """The FP8 form of an MoE layer's FC2 input: h (bf16, experts of 0-300
+    rows) quantised on the GPU, then grouped_gemm_run_blockscaled with E4M3
+    expert weights and their block scales; per expert within the
+    block-scaled bound of the oracle's product of the oracle's own
+    quantisation (which the GPU's codes and scales equal bit for bit)."""
+    counts = [0, 37, 300, 1, 129, 0, 64]
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    rows, G, I, H = int(off[-1]), len(counts), 768, 384
+    rs = np.random.RandomState(78)
+    h = torch.from_numpy(rs.standard_normal((rows, I)) * 0.5).to(torch.bfloat16)
+    kb = I // 128
+    hq = torch.empty(rows, I, dtype=torch.uint8, device="cuda")
+    hs = torch.empty(rows, kb, dtype=torch.uint8, device="cuda")
+    mg.quantize_e4m3_block(h.cuda(), hq, hs)
+    W2 = datagen.matrix_e4m3((G, H, I), ("normal", 100.0), rs)
+    sb = np.stack([scales(-(-H // 128), I, -8, -6, rs) for _ in range(G)])
+    plan = mg.grouped_gemm_plan(G, rows, H, I, a_type="e4m3", d_type="f32", b_layout="col")
+    Y = torch.full((rows, H), float("nan"), dtype=torch.float32, device="cuda")
+    mg.grouped_gemm_run_blockscaled(plan, hq, torch.from_numpy(W2).cuda(), Y, torch.from_numpy(off).cuda(), hs,
+                                    torch.from_numpy(sb).cuda())
+    torch.cuda.synchronize()
+    qr, sr = oracle.quantize_e4m3_block(h.to(torch.float64).numpy())
+    assert np.array_equal(hq.cpu().numpy(), qr) and np.array_equal(hs.cpu().numpy(), sr)
+    ref = oracle.grouped_e4m3_block_ref(qr, W2, off, sr, sb)
+    got = values(from_dev_bits(Y), "f32")
+    for e in range(G):
+        lo, hi = int(off[e]), int(off[e + 1])
+        if hi > lo:
+            tol, _ = block_bound(qr[lo:hi], W2[e], sr[lo:hi], sb[e], ref[lo:hi], "f32")
+            assert np.all(np.abs(got[lo:hi] - ref[lo:hi]) <= tol), f"expert {e}"
